@@ -1,0 +1,295 @@
+"""Benchmark: draft+verify block-tokens/s of one fuse -> verify -> draft step.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+One step = reset of the context lengths (so every step sees the same
+workload), dflash_fuse_ctx of the n_d+1 verified target rows (speculative),
+dflash_verify against planted target logits, and dflash_draft_block of one
+block per sequence -- every stage of the hot path, on inputs already resident
+in HBM.  value = batch * block / step time.
+
+Also reported: the dominant kernel's achieved HBM bandwidth against the
+MI355X peak (algorithmic bytes per launch / mean launch time from HIP events
+recorded around every launch of that kernel inside the timed region), and the
+float64 numpy oracle timed on the host cores on a bounded sample of the same
+step.  A secondary line of the same JSON object covers the batch-32 ragged
+workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "draft+verify block-tokens/sec at batch 1/32; % HBM / MFMA roofline"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="qwen3-8b-shape-b1")
+    ap.add_argument("--secondary", default="qwen3-8b-shape-b32-ragged",
+                    help="comma-separated extra workloads reported under 'secondary' ('' for none)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--stage", default="lmhead", help="kernel stage timed with HIP events for the roofline")
+    ap.add_argument("--profile-stages", action="store_true", help="also time every stage (perturbs the step)")
+    return ap.parse_args()
+
+
+def stage_bytes(wl, batch, ctx_lens):
+    """Algorithmic HBM bytes per launch of each stage (weights once, inputs and outputs once)."""
+    S = 2 if wl.storage == "bf16" else 4
+    H, D, F, V = wl.hidden, wl.head_dim, wl.ffn, wl.vocab
+    Nq, Nk = wl.n_q_heads * D, wl.n_kv_heads * D
+    Md, Mf = batch * wl.block, batch * wl.t_new
+    act = 4  # activations move as hi/lo bf16 pairs (or fp32)
+    ctx = float(np.sum(ctx_lens))
+    b = {
+        "fuse_fc": H * wl.n_target_layers * H * S + Mf * wl.n_target_layers * H * S + Mf * H * (4 + act),
+        "ctx_kv": wl.n_layers * 2 * Nk * H * S + Mf * H * act + wl.n_layers * 2 * Mf * Nk * S,
+        "verify": Mf * V * 4,
+        "embed": Md * H * S + Md * H * (4 + act),
+        "qkv": (Nq + 2 * Nk) * H * S + Md * H * act + Md * (Nq * act + 2 * Nk * S),
+        "attn": (ctx + Md) * 2 * Nk * S + Md * Nq * 2 * act,
+        "oproj": H * Nq * S + Md * Nq * act + Md * H * (8 + act),
+        "gateup": 2 * F * H * S + Md * H * act + Md * F * act,
+        "down": H * F * S + Md * F * act + Md * H * (8 + act),
+        "lmhead": V * H * S + Md * H * act,
+    }
+    return b
+
+
+def stage_flops(wl, batch, ctx_lens):
+    H, D, F, V = wl.hidden, wl.head_dim, wl.ffn, wl.vocab
+    Nq, Nk = wl.n_q_heads * D, wl.n_kv_heads * D
+    Md, Mf = batch * wl.block, batch * wl.t_new
+    ctx = float(np.sum(ctx_lens))
+    return {
+        "fuse_fc": 2.0 * Mf * wl.n_target_layers * H * H,
+        "ctx_kv": 2.0 * Mf * H * wl.n_layers * 2 * Nk,
+        "qkv": 2.0 * Md * H * (Nq + 2 * Nk),
+        "attn": 4.0 * wl.block * wl.n_q_heads * D * (ctx + batch * wl.block),
+        "oproj": 2.0 * Md * Nq * H,
+        "gateup": 4.0 * Md * H * F,
+        "down": 2.0 * Md * F * H,
+        "lmhead": 2.0 * Md * H * V,
+    }
+
+
+PER_LAYER = ("qkv", "attn", "oproj", "gateup", "down")
+
+
+def step_totals(wl, batch, ctx_lens):
+    sb, sf = stage_bytes(wl, batch, ctx_lens), stage_flops(wl, batch, ctx_lens)
+    tb = sum(v * (wl.n_layers if k in PER_LAYER else 1) for k, v in sb.items())
+    tf = sum(v * (wl.n_layers if k in PER_LAYER else 1) for k, v in sf.items())
+    return tb, tf
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("gemm.hip", "common.h", "kernels.h"):
+        with open(os.path.join(ROOT, "block_diffusion_drafting_ctx_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(stage, workload):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they match the current source."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{stage}_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh)
+    if rec.get("source_hash") != source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+class Workbench:
+    """Resident inputs and a library context for one workload."""
+
+    def __init__(self, wl, seed=1):
+        import torch
+        from harness import gen
+        from block_diffusion_drafting_ctx_amd import Drafter, make_config
+
+        self.wl = wl
+        dev = "cuda"
+        B = wl.batch
+        self.ctx_lens = gen.context_lengths(wl, seed + 1, B)
+        self.w = gen.draft_weights(wl, seed, dev)
+        ks, vs = gen.context_kv(wl, self.ctx_lens, seed + 1, dev)
+        cfg = make_config(wl.hidden, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.n_layers, wl.ffn, wl.vocab,
+                          wl.block, wl.n_target_layers, B, wl.max_ctx, wl.t_new, wl.conv_width, wl.storage,
+                          wl.rms_eps, wl.rope_theta)
+        self.dr = Drafter(cfg, self.w, dev, ks, vs)
+        self.ctx0 = torch.from_numpy(self.ctx_lens).to(dev)
+        self.dr.ctx_len.copy_(self.ctx0)
+        self.hidden = gen.target_hidden(wl, B, wl.t_new, seed + 2, dev)
+        self.block_ids = torch.from_numpy(gen.block_ids(wl, B, seed + 6)).to(dev)
+        self.draft_ids = torch.zeros(B, wl.block, dtype=torch.int32, device=dev)  # draft output
+        self.n_acc = torch.zeros(B, dtype=torch.int32, device=dev)
+        self.bonus = torch.zeros(B, dtype=torch.int32, device=dev)
+        self.out_tok = torch.zeros(B, wl.t_new, dtype=torch.int32, device=dev)
+        # The block verified each step is the one drafted by an untimed first
+        # pass; the target logits plant the chosen acceptance lengths against it.
+        # Each step therefore commits the same rows and drafts from the same
+        # context, so every step does identical work.
+        self.verify_ids = torch.zeros(B, wl.block, dtype=torch.int32, device=dev)
+        self.dr.draft_block(self.block_ids, self.verify_ids)
+        torch.cuda.synchronize()
+        self.accept = gen.accept_lengths(wl, B, seed + 4)
+        self.logits = gen.planted_logits(wl, self.verify_ids.cpu().numpy(), self.accept, wl.n_d, seed + 5, dev)
+
+    def step(self):
+        wl = self.wl
+        self.dr.ctx_len.copy_(self.ctx0)
+        self.dr.fuse_ctx(self.hidden, commit=False)
+        self.dr.verify(self.logits, self.verify_ids, wl.block, wl.n_d, self.n_acc, self.bonus, self.out_tok)
+        self.dr.draft_block(self.block_ids, self.draft_ids)
+
+
+def time_workload(wl, steps, warmup, stage, profile_stages=False):
+    import torch
+    from block_diffusion_drafting_ctx_amd import _abi
+
+    wb = Workbench(wl)
+    for _ in range(warmup):
+        wb.step()
+    torch.cuda.synchronize()
+    err = wb.dr.check()
+    if err:
+        raise RuntimeError(f"device error word {err:#x}")
+    stages = list(_abi.STAGES) if profile_stages else [stage]
+    for s in stages:
+        _abi.dflash_stage_timing(wb.dr.ctx, s, True)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(steps):
+        wb.step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    per_stage = {}
+    for s in stages:
+        mean_ms, n = _abi.dflash_stage_time(wb.dr.ctx, s)
+        _abi.dflash_stage_timing(wb.dr.ctx, s, False)
+        per_stage[s] = (mean_ms, n)
+    assert wb.dr.check() == 0
+    n_acc = wb.n_acc.cpu().numpy()
+    if not np.array_equal(n_acc, wb.accept):
+        raise RuntimeError(f"planted acceptance not reproduced: {n_acc} vs {wb.accept}")
+    return wb, ms, per_stage
+
+
+def cpu_baseline(wb):
+    """The oracle, as it stands, on one full step of the workload's first sequence."""
+    import threadpoolctl
+    from oracle import DraftState, draft_block, fuse_ctx, verify_step
+    from tests.oracle_adapt import dims_of, np64, weights_of
+
+    wl = wb.wl
+    W = weights_of(wb.w)
+    dims = dims_of(wl)
+    b = 0
+    T = int(wb.ctx_lens[b])
+    st = DraftState(k=[np64(t[b:b + 1, :T + wl.t_new]) for t in wb.dr.kv_k],
+                    v=[np64(t[b:b + 1, :T + wl.t_new]) for t in wb.dr.kv_v],
+                    ctx_len=np.array([T], dtype=np.int64))
+    hid = [np64(h[b:b + 1]) for h in wb.hidden]
+    logits = wb.logits[b:b + 1].cpu().numpy()
+    drafts = wb.verify_ids[b:b + 1].cpu().numpy().reshape(-1)
+    ids = wb.block_ids[b:b + 1].cpu().numpy()
+    info = threadpoolctl.threadpool_info()
+    threads = max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [1])
+    t0 = time.perf_counter()
+    fuse_ctx(st, W, dims, hid, commit=False)
+    verify_step(st, logits, drafts, wl.block, wl.n_d)
+    draft_block(st, W, dims, ids)
+    dt = time.perf_counter() - t0
+    return {"value": round(wl.block / dt, 3), "unit": "block-tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"one full step of sequence 0 of {wl.name} (fuse {wl.t_new} rows, verify, draft of one "
+                      f"{wl.block}-row block through {wl.n_layers} layers and the full vocabulary), float64 numpy",
+            "seconds": round(dt, 3)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        sys.exit(2)
+    import torch
+    from harness import gen
+
+    if not torch.cuda.is_available():
+        raise RuntimeError("bench.py needs a GPU")
+    wl = gen.WORKLOADS[args.workload]
+    wb, ms, per_stage = time_workload(wl, args.steps, args.warmup, args.stage, args.profile_stages)
+    B = wl.batch
+    value = B * wl.block / (ms * 1e-3)
+    tb, tf = step_totals(wl, B, wb.ctx_lens)
+    sb = stage_bytes(wl, B, wb.ctx_lens)
+    mean_ms, n = per_stage[args.stage]
+    achieved = sb[args.stage] / (mean_ms * 1e-3) / 1e9
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "block-tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": wl.storage,
+        "data": "synthetic (seeded random-init draft weights and inputs)",
+        "config": {"workload": wl.name, "batch": B, "block": wl.block, "context": int(np.max(wb.ctx_lens)),
+                   "layers": wl.n_layers, "hidden": wl.hidden, "vocab": wl.vocab},
+        "roofline": {"bound": "hbm", "kernel": args.stage, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic_from_profiles(args.stage, wl.name),
+                     "algorithmic_bytes_per_launch": int(sb[args.stage]), "mean_launch_ms": round(mean_ms, 5),
+                     "launches": n},
+        "step_roofline": {"algorithmic_bytes": int(tb), "algorithmic_flops": int(tf),
+                          "hbm_frac": round(tb / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9), 4),
+                          "mfma_frac": round(tf / (ms * 1e-3) / (BF16_PEAK_TFLOPS * 1e12), 4)},
+    }
+    if args.profile_stages:
+        out["stages_ms"] = {k: round(v[0], 5) for k, v in per_stage.items()}
+    sec = []
+    for name in [s for s in args.secondary.split(",") if s]:
+        wl2 = gen.WORKLOADS[name]
+        del wb
+        torch.cuda.empty_cache()
+        wb2, ms2, ps2 = time_workload(wl2, max(5, args.steps // 2), args.warmup, args.stage)
+        tb2, tf2 = step_totals(wl2, wl2.batch, wb2.ctx_lens)
+        sf2 = stage_flops(wl2, wl2.batch, wb2.ctx_lens)
+        m2 = ps2[args.stage][0]
+        sec.append({"workload": name, "value": round(wl2.batch * wl2.block / (ms2 * 1e-3), 1),
+                    "ms_per_step": round(ms2, 4),
+                    "step_mfma_frac": round(tf2 / (ms2 * 1e-3) / (BF16_PEAK_TFLOPS * 1e12), 4),
+                    "step_hbm_frac": round(tb2 / (ms2 * 1e-3) / (HBM_PEAK_GBS * 1e9), 4),
+                    "lmhead_tflops": round(sf2["lmhead"] / (m2 * 1e-3) / 1e12, 1)})
+        wb = wb2
+    if sec:
+        out["secondary"] = sec
+    if not args.no_cpu_baseline:
+        wb_c = wb if wb.wl.name == wl.name else None
+        if wb_c is None:
+            del wb
+            torch.cuda.empty_cache()
+            wb_c = Workbench(wl)
+        out["cpu_baseline"] = cpu_baseline(wb_c)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,625 @@
+// C ABI of the drafting hot path (see include/dflash.h): argument checks,
+// workspace carving, launch planning and the per-call kernel sequences.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "../../include/dflash.h"
+#include "kernels.h"
+
+using namespace dfl;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+dflash_status fail(dflash_status s, const std::string& msg) {
+  g_last_error = msg;
+  return s;
+}
+
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+struct WsLayout {
+  size_t err, stats;
+  size_t x, ssq, y, xs_hi, xs_lo, q_hi, q_lo, kb, vb, o_hi, o_lo, act_hi, act_lo, lm_best, ver_best, part_o,
+      part_ml;
+  size_t total;
+  int md, mf, mmax, ssq_parts, attn_max_wgs_rows, lm_tiles, ver_chunks;
+};
+
+constexpr int kMaxNd = 64;
+constexpr int kVerifyChunk = 16384;  // vocab entries per workgroup of the verify argmax
+constexpr int kLmTileRows = 64;     // LM-head rows per workgroup tile (argmax partials per row)
+constexpr int kAttnTargetWgs = 1024;
+constexpr int kAttnMinCw = 256;
+
+// Keys per attention split for a batch: aim for about kAttnTargetWgs workgroups.
+int attn_cw(const dflash_config& c, int batch) {
+  const int total = c.max_ctx + c.block;
+  const int want = std::max(1, (kAttnTargetWgs + batch * c.n_kv_heads - 1) / (batch * c.n_kv_heads));
+  int cw = (total + want - 1) / want;
+  cw = ((cw + 63) / 64) * 64;
+  return std::max(cw, kAttnMinCw);
+}
+int attn_splits(const dflash_config& c, int cw) { return (c.max_ctx + c.block + cw - 1) / cw; }
+
+const char* validate(const dflash_config* c) {
+  if (!c) return "null config";
+  if (c->hidden <= 0 || c->hidden % 128) return "hidden must be a positive multiple of 128";
+  if (c->ffn <= 0 || c->ffn % 128) return "ffn must be a positive multiple of 128";
+  if (c->head_dim != 64 && c->head_dim != 128) return "head_dim must be 64 or 128";
+  if (c->n_kv_heads <= 0 || c->n_q_heads <= 0 || c->n_q_heads % c->n_kv_heads) return "bad head counts";
+  if ((c->n_q_heads * c->head_dim) % 128) return "n_q_heads*head_dim must be a multiple of 128";
+  if (c->n_q_heads / c->n_kv_heads * c->block > 128) return "block * (n_q_heads / n_kv_heads) must be <= 128";
+  if (c->n_layers <= 0 || c->n_layers > kMaxSeg / 2) return "n_layers must be in [1, 8]";
+  if (c->vocab <= 0 || c->vocab % 64) return "vocab must be a positive multiple of 64";
+  if (c->block < 1 || c->block > 64) return "block must be in [1, 64]";
+  if (c->n_target_layers < 1 || c->n_target_layers > 8) return "n_target_layers must be in [1, 8]";
+  if (c->max_batch < 1 || c->max_ctx < 1 || c->max_fuse_rows < 1) return "bad limits";
+  if (c->conv_width != 0 && c->conv_width != 3) return "conv_width must be 0 or 3";
+  if (c->conv_width == 3 && 16 % c->block) return "the block conv needs block to divide 16";
+  if (c->dtype != DFLASH_DTYPE_F32 && c->dtype != DFLASH_DTYPE_BF16) return "unknown dtype";
+  if (!(c->rms_eps >= 0.f) || !(c->rope_theta > 0.f)) return "bad eps / theta";
+  return nullptr;
+}
+
+WsLayout layout(const dflash_config& c) {
+  WsLayout L{};
+  const size_t S = c.dtype == DFLASH_DTYPE_BF16 ? 2 : 4;
+  const size_t H = c.hidden, D = c.head_dim;
+  L.md = c.max_batch * c.block;
+  L.mf = c.max_batch * c.max_fuse_rows;
+  L.mmax = std::max(L.md, L.mf);
+  L.ssq_parts = c.hidden / 16;
+  int attn_rows = 0;  // max over batch of batch * splits
+  for (int b = 1; b <= c.max_batch; ++b) attn_rows = std::max(attn_rows, b * attn_splits(c, attn_cw(c, b)));
+  L.attn_max_wgs_rows = attn_rows;
+  const size_t QR = (size_t)(c.n_q_heads / c.n_kv_heads) * c.block;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off = align256(off + bytes);
+    return o;
+  };
+  L.err = take(16);
+  L.stats = take(3 * 8);
+  L.x = take((size_t)L.md * H * 4);
+  L.ssq = take((size_t)L.ssq_parts * L.mmax * 4);
+  L.y = take((size_t)L.mf * H * 4);
+  L.xs_hi = take((size_t)L.mmax * H * 2);
+  L.xs_lo = take((size_t)L.mmax * H * 2);
+  L.q_hi = take((size_t)L.md * c.n_q_heads * D * 2);
+  L.q_lo = take((size_t)L.md * c.n_q_heads * D * 2);
+  L.kb = take((size_t)L.md * c.n_kv_heads * D * S);
+  L.vb = take((size_t)L.md * c.n_kv_heads * D * S);
+  L.o_hi = take((size_t)L.md * c.n_q_heads * D * 2);
+  L.o_lo = take((size_t)L.md * c.n_q_heads * D * 2);
+  L.act_hi = take((size_t)L.md * c.ffn * 2);
+  L.act_lo = take((size_t)L.md * c.ffn * 2);
+  L.lm_tiles = c.vocab / kLmTileRows;
+  L.ver_chunks = (c.vocab + kVerifyChunk - 1) / kVerifyChunk;
+  L.lm_best = take((size_t)L.lm_tiles * L.md * 8);
+  L.ver_best = take((size_t)c.max_batch * (kMaxNd + 1) * L.ver_chunks * 8);
+  L.part_o = take((size_t)attn_rows * c.n_kv_heads * QR * D * 4);
+  L.part_ml = take((size_t)attn_rows * c.n_kv_heads * QR * 2 * 4);
+  L.total = off;
+  return L;
+}
+
+struct EventPool {
+  bool enabled = false;
+  std::vector<hipEvent_t> begin, end;
+  size_t used = 0;
+};
+
+}  // namespace
+
+struct dflash_ctx {
+  dflash_config cfg;
+  WsLayout L;
+  char* ws;
+  const void* embed;
+  const void* w_fc;
+  const void* g_fc;
+  const void* g_final;
+  const void* w_lm;
+  std::vector<const void*> w_q, w_k, w_v, w_o, w_gate, w_up, w_down, g_in, g_post, conv;
+  std::vector<void*> kv_k, kv_v;
+  int32_t* ctx_len;
+  EventPool timing[DFLASH_N_STAGES];
+
+  template <typename T>
+  T* at(size_t off) const {
+    return reinterpret_cast<T*>(ws + off);
+  }
+  int storage() const { return cfg.dtype == DFLASH_DTYPE_BF16 ? ST_BF16 : ST_F32; }
+};
+
+namespace {
+
+struct StageScope {
+  dflash_ctx* c;
+  int stage;
+  hipStream_t s;
+  size_t slot = (size_t)-1;
+  StageScope(dflash_ctx* c_, int stage_, hipStream_t s_) : c(c_), stage(stage_), s(s_) {
+    EventPool& p = c->timing[stage];
+    if (p.enabled && p.used < p.begin.size()) {
+      slot = p.used++;
+      (void)hipEventRecord(p.begin[slot], s);
+    }
+  }
+  ~StageScope() {
+    if (slot != (size_t)-1) (void)hipEventRecord(c->timing[stage].end[slot], s);
+  }
+};
+
+dflash_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return DFLASH_OK;
+  return fail(DFLASH_EHIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+// Launch geometry for one skinny GEMM.
+bool plan_gemm(int storage, ProKind pro, EpiKind epi, int M, int N, int K, int P, GemmArgs* a, GemmLaunch* l) {
+  const int MR = M <= 16 ? 1 : (M <= 32 ? 2 : (M <= 64 ? 4 : 8));
+  const int U = MR == 1 ? 4 : (MR == 2 ? 2 : 1);
+  const int MT = 16 * MR;
+  const int WN = epi == EPI_ARGMAX ? 4 : (P > 0 ? 2 : 1);
+  const int NT = 16 * WN;
+  if (N % NT) return false;
+  if (P > 0 && (P % (NT / 2) || N % (2 * P))) return false;
+  const int maxthr = gemm_max_threads(storage, pro, MR);
+  int WK = std::min(maxthr / (64 * WN), std::max(1, K / 512));
+  while (WK > 1 && (K % (WK * 32 * U) || gemm_lds_bytes(epi, MR, WN, WK) > 64 * 1024)) --WK;
+  if (K % (WK * 32 * U)) return false;
+  if (gemm_lds_bytes(epi, MR, WN, WK) > 64 * 1024) return false;
+  a->M = M;
+  a->N = N;
+  a->K = K;
+  a->WN = WN;
+  a->WK = WK;
+  a->P = P;
+  a->kw = K / WK;
+  l->MR = MR;
+  l->mtiles = (M + MT - 1) / MT;
+  l->ntiles = N / NT;
+  l->threads = 64 * WN * WK;
+  l->lds = gemm_lds_bytes(epi, MR, WN, WK);
+  return true;
+}
+
+dflash_status run_gemm(dflash_ctx* c, int stage, ProKind pro, EpiKind epi, GemmArgs& a, int M, int N, int K, int P,
+                       hipStream_t s) {
+  GemmLaunch l{};
+  if (!plan_gemm(c->storage(), pro, epi, M, N, K, P, &a, &l))
+    return fail(DFLASH_EUNSUPPORTED, "no GEMM launch plan for M=" + std::to_string(M) + " N=" + std::to_string(N) +
+                                         " K=" + std::to_string(K));
+  StageScope sc(c, stage, s);
+  return hip_status(launch_gemm(c->storage(), pro, epi, a, l, s), "gemm launch");
+}
+
+void set_segments(GemmArgs& a, std::initializer_list<std::pair<const void*, int>> segs) {
+  a.nseg = 0;
+  int start = 0;
+  for (auto& sg : segs) {
+    a.seg_ptr[a.nseg] = sg.first;
+    a.seg_start[a.nseg] = start;
+    start += sg.second;
+    ++a.nseg;
+  }
+  a.seg_start[a.nseg] = start;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* dflash_last_error(void) { return g_last_error.c_str(); }
+
+const char* dflash_version(void) { return "dflash-mi355x 0.1 (gfx950)"; }
+
+size_t dflash_workspace_bytes(const dflash_config* cfg) {
+  if (validate(cfg)) return 0;
+  return layout(*cfg).total;
+}
+
+dflash_status dflash_create(const dflash_config* cfg, const dflash_weights* w, void* const* kv_k, void* const* kv_v,
+                            int32_t* ctx_len, void* workspace, size_t workspace_bytes, dflash_ctx** out) {
+  g_last_error.clear();
+  if (!out) return fail(DFLASH_EINVAL, "null output handle");
+  *out = nullptr;
+  if (const char* why = validate(cfg)) return fail(DFLASH_EUNSUPPORTED, why);
+  if (!w || !kv_k || !kv_v || !ctx_len || !workspace) return fail(DFLASH_EINVAL, "null argument");
+  if (reinterpret_cast<uintptr_t>(workspace) % 256) return fail(DFLASH_EINVAL, "workspace must be 256-byte aligned");
+  const WsLayout L = layout(*cfg);
+  if (workspace_bytes < L.total) return fail(DFLASH_EINVAL, "workspace too small");
+  if (!w->embed || !w->w_fc || !w->g_fc || !w->g_final || !w->w_lm) return fail(DFLASH_EINVAL, "null weight");
+  const int nl = cfg->n_layers;
+  const void* const* per[] = {w->w_q, w->w_k, w->w_v, w->w_o, w->w_gate, w->w_up, w->w_down, w->g_in, w->g_post};
+  for (auto arr : per) {
+    if (!arr) return fail(DFLASH_EINVAL, "null per-layer weight array");
+    for (int l = 0; l < nl; ++l)
+      if (!arr[l]) return fail(DFLASH_EINVAL, "null per-layer weight");
+  }
+  if (cfg->conv_width) {
+    if (!w->conv) return fail(DFLASH_EINVAL, "conv_width=3 needs conv taps");
+    for (int l = 0; l < nl; ++l)
+      if (!w->conv[l]) return fail(DFLASH_EINVAL, "null conv taps");
+  }
+  for (int l = 0; l < nl; ++l)
+    if (!kv_k[l] || !kv_v[l]) return fail(DFLASH_EINVAL, "null KV cache pointer");
+
+  dflash_ctx* c = new (std::nothrow) dflash_ctx();
+  if (!c) return fail(DFLASH_EINVAL, "out of host memory");
+  c->cfg = *cfg;
+  c->L = L;
+  c->ws = static_cast<char*>(workspace);
+  c->embed = w->embed;
+  c->w_fc = w->w_fc;
+  c->g_fc = w->g_fc;
+  c->g_final = w->g_final;
+  c->w_lm = w->w_lm;
+  c->w_q.assign(w->w_q, w->w_q + nl);
+  c->w_k.assign(w->w_k, w->w_k + nl);
+  c->w_v.assign(w->w_v, w->w_v + nl);
+  c->w_o.assign(w->w_o, w->w_o + nl);
+  c->w_gate.assign(w->w_gate, w->w_gate + nl);
+  c->w_up.assign(w->w_up, w->w_up + nl);
+  c->w_down.assign(w->w_down, w->w_down + nl);
+  c->g_in.assign(w->g_in, w->g_in + nl);
+  c->g_post.assign(w->g_post, w->g_post + nl);
+  c->conv.assign(nl, nullptr);
+  if (cfg->conv_width)
+    for (int l = 0; l < nl; ++l) c->conv[l] = w->conv[l];
+  c->kv_k.assign(kv_k, kv_k + nl);
+  c->kv_v.assign(kv_v, kv_v + nl);
+  c->ctx_len = ctx_len;
+  hipError_t e = hipMemset(workspace, 0, L.total);
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e != hipSuccess) {
+    delete c;
+    return hip_status(e, "workspace clear");
+  }
+  *out = c;
+  return DFLASH_OK;
+}
+
+dflash_status dflash_fuse_ctx(dflash_ctx* c, int32_t batch, const void* const* hidden, int32_t t_new,
+                              int32_t commit, float* feat_dbg, void* stream) {
+  g_last_error.clear();
+  if (!c) return fail(DFLASH_EINVAL, "null context");
+  const dflash_config& cf = c->cfg;
+  if (batch < 0 || batch > cf.max_batch) return fail(DFLASH_EINVAL, "batch out of range");
+  if (t_new < 0 || t_new > cf.max_fuse_rows) return fail(DFLASH_EINVAL, "t_new out of range");
+  if (batch == 0 || t_new == 0) return DFLASH_OK;
+  if (!hidden) return fail(DFLASH_EINVAL, "null hidden array");
+  for (int j = 0; j < cf.n_target_layers; ++j)
+    if (!hidden[j]) return fail(DFLASH_EINVAL, "null hidden-state pointer");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int M = batch * t_new, H = cf.hidden, D = cf.head_dim;
+  const WsLayout& L = c->L;
+
+  {  // K1: Y = concat(h) . W_fc^T; hi/lo of Y * g_fc; row sums of squares
+    GemmArgs a{};
+    set_segments(a, {{c->w_fc, H}});
+    for (int j = 0; j < cf.n_target_layers; ++j) a.src[j] = hidden[j];
+    a.n_src = cf.n_target_layers;
+    a.src_width = H;
+    a.out_f32 = c->at<float>(L.y);
+    a.out_hi = c->at<void>(L.xs_hi);
+    a.out_lo = c->at<void>(L.xs_lo);
+    a.gnext = c->g_fc;
+    a.ssq_out = c->at<float>(L.ssq);
+    a.ld_ssq = L.mmax;
+    dflash_status st = run_gemm(c, DFLASH_STAGE_FUSE_FC, PRO_CONCAT, EPI_F32_SSQ, a, M, H,
+                                H * cf.n_target_layers, 0, s);
+    if (st) return st;
+  }
+  {  // K2: c = RMSNorm(Y) g_fc;  [K^l ; V^l] = c . [W_k^l ; W_v^l]^T for all layers, RoPE, append
+    GemmArgs a{};
+    a.nseg = 0;
+    int start = 0;
+    for (int l = 0; l < cf.n_layers; ++l) {
+      a.seg_ptr[a.nseg] = c->w_k[l];
+      a.kv_cache[a.nseg] = c->kv_k[l];
+      a.seg_start[a.nseg++] = start;
+      start += cf.n_kv_heads * D;
+      a.seg_ptr[a.nseg] = c->w_v[l];
+      a.kv_cache[a.nseg] = c->kv_v[l];
+      a.seg_start[a.nseg++] = start;
+      start += cf.n_kv_heads * D;
+    }
+    a.seg_start[a.nseg] = start;
+    a.a_hi = c->at<void>(L.xs_hi);
+    a.a_lo = c->at<void>(L.xs_lo);
+    a.lda = H;
+    a.ssq_in = c->at<float>(L.ssq);
+    a.ssq_nparts = H / 16;
+    a.ld_ssq = L.mmax;
+    a.eps = cf.rms_eps;
+    a.block = t_new;
+    a.ctx_len = c->ctx_len;
+    a.max_ctx = cf.max_ctx;
+    a.rope_theta = cf.rope_theta;
+    a.head_dim = D;
+    a.n_q_heads = cf.n_q_heads;
+    a.n_kv_heads = cf.n_kv_heads;
+    a.err = c->at<uint32_t>(L.err);
+    dflash_status st = run_gemm(c, DFLASH_STAGE_CTX_KV, PRO_SPLIT, EPI_KV, a, M, start, H, D / 2, s);
+    if (st) return st;
+  }
+  if (feat_dbg) {
+    dflash_status st = hip_status(launch_feature_dbg(c->storage(), c->at<float>(L.y), c->at<float>(L.ssq), H / 16,
+                                                     L.mmax, c->g_fc, cf.rms_eps, M, H, feat_dbg, s),
+                                  "feature debug");
+    if (st) return st;
+  }
+  if (commit) return hip_status(launch_commit(c->ctx_len, batch, t_new, cf.max_ctx, s), "commit");
+  return DFLASH_OK;
+}
+
+dflash_status dflash_verify(dflash_ctx* c, int32_t batch, const float* logits, const int32_t* draft_ids,
+                            int32_t draft_stride, int32_t n_d, int32_t* n_accept, int32_t* bonus,
+                            int32_t* out_tokens, void* stream) {
+  g_last_error.clear();
+  if (!c) return fail(DFLASH_EINVAL, "null context");
+  const dflash_config& cf = c->cfg;
+  if (batch < 0 || batch > cf.max_batch) return fail(DFLASH_EINVAL, "batch out of range");
+  if (n_d < 0 || n_d > kMaxNd) return fail(DFLASH_EINVAL, "n_d out of range [0, 64]");
+  if (batch == 0) return DFLASH_OK;
+  if (!logits || !n_accept || !bonus || !out_tokens || (n_d > 0 && !draft_ids))
+    return fail(DFLASH_EINVAL, "null argument");
+  if (n_d > 0 && draft_stride < n_d) return fail(DFLASH_EINVAL, "draft_stride < n_d");
+  VerifyArgs a{};
+  a.logits = logits;
+  a.draft = draft_ids;
+  a.draft_stride = draft_stride;
+  a.n_d = n_d;
+  a.batch = batch;
+  a.V = cf.vocab;
+  a.max_ctx = cf.max_ctx;
+  a.chunk = kVerifyChunk;
+  a.nchunks = c->L.ver_chunks;
+  a.part = c->at<uint64_t>(c->L.ver_best);
+  a.n_accept = n_accept;
+  a.bonus = bonus;
+  a.out_tokens = out_tokens;
+  a.ctx_len = c->ctx_len;
+  a.stats = c->at<unsigned long long>(c->L.stats);
+  a.err = c->at<uint32_t>(c->L.err);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  StageScope sc(c, DFLASH_STAGE_VERIFY, s);
+  return hip_status(launch_verify(a, s), "verify launch");
+}
+
+dflash_status dflash_draft_block(dflash_ctx* c, int32_t batch, const int32_t* block_ids, int32_t* draft_ids,
+                                 float* logits_dbg, float* hidden_dbg, void* stream) {
+  g_last_error.clear();
+  if (!c) return fail(DFLASH_EINVAL, "null context");
+  const dflash_config& cf = c->cfg;
+  if (batch < 0 || batch > cf.max_batch) return fail(DFLASH_EINVAL, "batch out of range");
+  if (batch == 0) return DFLASH_OK;
+  if (!block_ids || !draft_ids) return fail(DFLASH_EINVAL, "null argument");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const WsLayout& L = c->L;
+  const int M = batch * cf.block, H = cf.hidden, D = cf.head_dim, F = cf.ffn;
+  const int Nq = cf.n_q_heads * D, Nk = cf.n_kv_heads * D;
+  float* x = c->at<float>(L.x);
+  float* ssq = c->at<float>(L.ssq);
+  void* xs_hi = c->at<void>(L.xs_hi);
+  void* xs_lo = c->at<void>(L.xs_lo);
+  dflash_status st;
+  {
+    StageScope sc(c, DFLASH_STAGE_EMBED, s);
+    st = hip_status(launch_embed(c->storage(), c->embed, c->g_in[0], block_ids, M, H, cf.vocab, x, xs_hi, xs_lo, ssq,
+                                 c->at<uint32_t>(L.err), s),
+                    "embed launch");
+    if (st) return st;
+  }
+  int ssq_parts = 1;
+  const int cw = attn_cw(cf, batch);
+  const int splits = attn_splits(cf, cw);
+  for (int l = 0; l < cf.n_layers; ++l) {
+    {  // RMSNorm -> Q/K/V, RoPE
+      GemmArgs a{};
+      set_segments(a, {{c->w_q[l], Nq}, {c->w_k[l], Nk}, {c->w_v[l], Nk}});
+      a.a_hi = xs_hi;
+      a.a_lo = xs_lo;
+      a.lda = H;
+      a.ssq_in = ssq;
+      a.ssq_nparts = ssq_parts;
+      a.ld_ssq = L.mmax;
+      a.eps = cf.rms_eps;
+      a.block = cf.block;
+      a.ctx_len = c->ctx_len;
+      a.rope_theta = cf.rope_theta;
+      a.head_dim = D;
+      a.n_q_heads = cf.n_q_heads;
+      a.n_kv_heads = cf.n_kv_heads;
+      a.q_scale = (float)(1.4426950408889634 / std::sqrt((double)D));
+      a.out_hi = c->at<void>(L.q_hi);
+      a.out_lo = c->at<void>(L.q_lo);
+      a.kb_out = c->at<void>(L.kb);
+      a.vb_out = c->at<void>(L.vb);
+      if ((st = run_gemm(c, DFLASH_STAGE_QKV, PRO_SPLIT, EPI_QKV, a, M, Nq + 2 * Nk, H, D / 2, s))) return st;
+    }
+    {  // attention over [context ; block]
+      AttnArgs a{};
+      a.q_hi = c->at<void>(L.q_hi);
+      a.q_lo = c->at<void>(L.q_lo);
+      a.kb = c->at<void>(L.kb);
+      a.vb = c->at<void>(L.vb);
+      a.kc = c->kv_k[l];
+      a.vc = c->kv_v[l];
+      a.ctx_len = c->ctx_len;
+      a.Bs = cf.block;
+      a.Hq = cf.n_q_heads;
+      a.Hkv = cf.n_kv_heads;
+      a.D = D;
+      a.max_ctx = cf.max_ctx;
+      a.CW = cw;
+      a.max_splits = splits;
+      a.part_o = c->at<float>(L.part_o);
+      a.part_ml = c->at<float>(L.part_ml);
+      a.out_hi = c->at<void>(L.o_hi);
+      a.out_lo = c->at<void>(L.o_lo);
+      a.batch = batch;
+      StageScope sc(c, DFLASH_STAGE_ATTN, s);
+      if ((st = hip_status(launch_attention(c->storage(), a, s), "attention launch"))) return st;
+    }
+    {  // O projection + residual (+ block conv); hi/lo of x * g_post, sums of squares
+      GemmArgs a{};
+      set_segments(a, {{c->w_o[l], H}});
+      a.a_hi = c->at<void>(L.o_hi);
+      a.a_lo = c->at<void>(L.o_lo);
+      a.lda = Nq;
+      a.x = x;
+      a.conv = c->conv[l];
+      a.block = cf.block;
+      a.gnext = c->g_post[l];
+      a.out_hi = xs_hi;
+      a.out_lo = xs_lo;
+      a.ssq_out = ssq;
+      a.ld_ssq = L.mmax;
+      if ((st = run_gemm(c, DFLASH_STAGE_OPROJ, PRO_SPLIT, EPI_RESID, a, M, H, Nq, 0, s))) return st;
+    }
+    ssq_parts = H / 16;
+    {  // RMSNorm -> gate/up, SiLU product
+      GemmArgs a{};
+      set_segments(a, {{c->w_gate[l], F}, {c->w_up[l], F}});
+      a.a_hi = xs_hi;
+      a.a_lo = xs_lo;
+      a.lda = H;
+      a.ssq_in = ssq;
+      a.ssq_nparts = ssq_parts;
+      a.ld_ssq = L.mmax;
+      a.eps = cf.rms_eps;
+      a.out_hi = c->at<void>(L.act_hi);
+      a.out_lo = c->at<void>(L.act_lo);
+      if ((st = run_gemm(c, DFLASH_STAGE_GATEUP, PRO_SPLIT, EPI_SWIGLU, a, M, 2 * F, H, F, s))) return st;
+    }
+    {  // down projection + residual; hi/lo of x * (next layer's g_in, or g_final)
+      GemmArgs a{};
+      set_segments(a, {{c->w_down[l], H}});
+      a.a_hi = c->at<void>(L.act_hi);
+      a.a_lo = c->at<void>(L.act_lo);
+      a.lda = F;
+      a.x = x;
+      a.conv = nullptr;
+      a.block = cf.block;
+      a.gnext = l + 1 < cf.n_layers ? c->g_in[l + 1] : c->g_final;
+      a.out_hi = xs_hi;
+      a.out_lo = xs_lo;
+      a.ssq_out = ssq;
+      a.ld_ssq = L.mmax;
+      if ((st = run_gemm(c, DFLASH_STAGE_DOWN, PRO_SPLIT, EPI_RESID, a, M, H, F, 0, s))) return st;
+    }
+  }
+  if (hidden_dbg) {
+    if ((st = hip_status(launch_copy_f32(x, hidden_dbg, (size_t)M * H, s), "hidden copy"))) return st;
+  }
+  {  // final RMSNorm -> LM head -> argmax
+    GemmArgs a{};
+    set_segments(a, {{c->w_lm, cf.vocab}});
+    a.a_hi = xs_hi;
+    a.a_lo = xs_lo;
+    a.lda = H;
+    a.ssq_in = ssq;
+    a.ssq_nparts = ssq_parts;
+    a.ld_ssq = L.mmax;
+    a.eps = cf.rms_eps;
+    a.best_part = c->at<uint64_t>(L.lm_best);
+    a.ld_best = M;
+    a.logits_dbg = logits_dbg;
+    if ((st = run_gemm(c, DFLASH_STAGE_LMHEAD, PRO_SPLIT, EPI_ARGMAX, a, M, cf.vocab, H, 0, s))) return st;
+    if ((st = hip_status(launch_argmax_reduce(c->at<uint64_t>(L.lm_best), cf.vocab / kLmTileRows, M, M, draft_ids, s),
+                         "argmax reduce launch")))
+      return st;
+  }
+  return DFLASH_OK;
+}
+
+dflash_status dflash_check(dflash_ctx* c, uint32_t* error_bits, void* stream) {
+  g_last_error.clear();
+  if (!c || !error_bits) return fail(DFLASH_EINVAL, "null argument");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint32_t v = 0;
+  hipError_t e = hipMemcpyAsync(&v, c->at<uint32_t>(c->L.err), 4, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_status(e, "error word read");
+  *error_bits = v;
+  if (v) return fail(DFLASH_EDEVICE, "device error word is set");
+  return DFLASH_OK;
+}
+
+dflash_status dflash_clear_errors(dflash_ctx* c, void* stream) {
+  g_last_error.clear();
+  if (!c) return fail(DFLASH_EINVAL, "null context");
+  return hip_status(launch_clear_u32(c->at<uint32_t>(c->L.err), 1, static_cast<hipStream_t>(stream)), "clear");
+}
+
+dflash_status dflash_stats(dflash_ctx* c, uint64_t out3[3], void* stream) {
+  g_last_error.clear();
+  if (!c || !out3) return fail(DFLASH_EINVAL, "null argument");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hipMemcpyAsync(out3, c->at<uint64_t>(c->L.stats), 24, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  return hip_status(e, "stats read");
+}
+
+dflash_status dflash_stage_timing(dflash_ctx* c, int32_t stage, int32_t enable) {
+  g_last_error.clear();
+  if (!c) return fail(DFLASH_EINVAL, "null context");
+  if (stage < 0 || stage >= DFLASH_N_STAGES) return fail(DFLASH_EINVAL, "bad stage");
+  EventPool& p = c->timing[stage];
+  if (enable && p.begin.empty()) {
+    const size_t n = 4096;
+    p.begin.resize(n);
+    p.end.resize(n);
+    for (size_t i = 0; i < n; ++i) {
+      hipError_t e = hipEventCreate(&p.begin[i]);
+      if (e == hipSuccess) e = hipEventCreate(&p.end[i]);
+      if (e != hipSuccess) return hip_status(e, "event create");
+    }
+  }
+  p.enabled = enable != 0;
+  return DFLASH_OK;
+}
+
+dflash_status dflash_stage_time(dflash_ctx* c, int32_t stage, double* mean_ms, int64_t* count, void* stream) {
+  g_last_error.clear();
+  if (!c || !mean_ms || !count) return fail(DFLASH_EINVAL, "null argument");
+  if (stage < 0 || stage >= DFLASH_N_STAGES) return fail(DFLASH_EINVAL, "bad stage");
+  hipError_t e = hipStreamSynchronize(static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_status(e, "sync");
+  EventPool& p = c->timing[stage];
+  double total = 0.0;
+  for (size_t i = 0; i < p.used; ++i) {
+    float ms = 0.f;
+    e = hipEventElapsedTime(&ms, p.begin[i], p.end[i]);
+    if (e != hipSuccess) return hip_status(e, "event time");
+    total += ms;
+  }
+  *count = (int64_t)p.used;
+  *mean_ms = p.used ? total / (double)p.used : 0.0;
+  p.used = 0;
+  return DFLASH_OK;
+}
+
+void dflash_destroy(dflash_ctx* c) {
+  if (!c) return;
+  for (auto& p : c->timing) {
+    for (auto ev : p.begin) (void)hipEventDestroy(ev);
+    for (auto ev : p.end) (void)hipEventDestroy(ev);
+  }
+  delete c;
+}
+
+}  // extern "C"

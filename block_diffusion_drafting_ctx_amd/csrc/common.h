@@ -1,0 +1,162 @@
+// Device-side helpers shared by the gfx950 kernels of the drafting hot path.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dfl {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+// bfloat16 values live in memory as raw 16-bit words.
+typedef uint16_t bf16_t;
+
+// Eight consecutive storage elements as raw bits: 16 bytes for bf16, 32 for fp32.
+struct Raw8 {
+  u32x4 lo, hi;
+};
+
+template <typename S>
+__device__ __forceinline__ void load_raw8(Raw8& r, const S* p);
+template <>
+__device__ __forceinline__ void load_raw8<bf16_t>(Raw8& r, const bf16_t* p) {
+  r.lo = *reinterpret_cast<const u32x4*>(p);
+}
+template <>
+__device__ __forceinline__ void load_raw8<float>(Raw8& r, const float* p) {
+  r.lo = reinterpret_cast<const u32x4*>(p)[0];
+  r.hi = reinterpret_cast<const u32x4*>(p)[1];
+}
+
+// Streaming (non-temporal) variant for data read exactly once per step (weights, logits).
+template <typename S>
+__device__ __forceinline__ void load_raw8_nt(Raw8& r, const S* p);
+template <>
+__device__ __forceinline__ void load_raw8_nt<bf16_t>(Raw8& r, const bf16_t* p) {
+  r.lo = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+template <>
+__device__ __forceinline__ void load_raw8_nt<float>(Raw8& r, const float* p) {
+  r.lo = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  r.hi = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p) + 1);
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+// fp32 -> bf16 round-to-nearest-even (hardware conversion on gfx950).
+__device__ __forceinline__ bf16_t f32_to_bf16_bits(float f) {
+  return __builtin_bit_cast(bf16_t, (__bf16)f);
+}
+
+__device__ __forceinline__ bf16x8 f32x8_to_bf16x8(f32x4 a, f32x4 b) {
+  bf16x8 r;
+  r[0] = (__bf16)a[0]; r[1] = (__bf16)a[1]; r[2] = (__bf16)a[2]; r[3] = (__bf16)a[3];
+  r[4] = (__bf16)b[0]; r[5] = (__bf16)b[1]; r[6] = (__bf16)b[2]; r[7] = (__bf16)b[3];
+  return r;
+}
+
+// Raw storage bits -> bf16x8 MFMA operand.
+template <typename S>
+__device__ __forceinline__ bf16x8 raw_to_bf16x8(const Raw8& r);
+template <>
+__device__ __forceinline__ bf16x8 raw_to_bf16x8<bf16_t>(const Raw8& r) {
+  return __builtin_bit_cast(bf16x8, r.lo);
+}
+template <>
+__device__ __forceinline__ bf16x8 raw_to_bf16x8<float>(const Raw8& r) {
+  return f32x8_to_bf16x8(__builtin_bit_cast(f32x4, r.lo), __builtin_bit_cast(f32x4, r.hi));
+}
+
+// Raw storage bits -> 8 floats.
+template <typename S>
+__device__ __forceinline__ void raw_to_f32x8(const Raw8& r, float* out);
+template <>
+__device__ __forceinline__ void raw_to_f32x8<bf16_t>(const Raw8& r, float* out) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    out[2 * i] = __uint_as_float(r.lo[i] << 16);
+    out[2 * i + 1] = __uint_as_float(r.lo[i] & 0xffff0000u);
+  }
+}
+template <>
+__device__ __forceinline__ void raw_to_f32x8<float>(const Raw8& r, float* out) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    out[i] = __uint_as_float(r.lo[i]);
+    out[4 + i] = __uint_as_float(r.hi[i]);
+  }
+}
+
+template <typename S>
+__device__ __forceinline__ float load_f32(const S* p);
+template <>
+__device__ __forceinline__ float load_f32<float>(const float* p) { return *p; }
+template <>
+__device__ __forceinline__ float load_f32<bf16_t>(const bf16_t* p) { return bf16_bits_to_f32(*p); }
+
+template <typename S>
+__device__ __forceinline__ void store_from_f32(S* p, float v);
+template <>
+__device__ __forceinline__ void store_from_f32<float>(float* p, float v) { *p = v; }
+template <>
+__device__ __forceinline__ void store_from_f32<bf16_t>(bf16_t* p, float v) { *p = f32_to_bf16_bits(v); }
+
+// 16x16x32 bf16 matrix-core product, fp32 accumulate.
+// Operand lanes: A row (lane & 15), B column (lane & 15), 8 k-values per lane
+// whose k-slot depends on (lane >> 4); A and B loaded with the same slot map
+// contract the same k.  Result: lane holds column (lane & 15), rows
+// 4 * (lane >> 4) + [0, 4).
+__device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------- argmax key
+// Monotone packing of (value, index) into one u64: higher value wins, exact
+// ties go to the lower index, NaN ranks below every number (so it is never
+// chosen unless the whole row is NaN, in which case index 0 wins), -0 == +0.
+__device__ __forceinline__ uint64_t argmax_key(float v, uint32_t idx) {
+  uint32_t hi;
+  if (v != v) {
+    hi = 0u;
+  } else {
+    uint32_t u = __float_as_uint(v == 0.0f ? 0.0f : v);
+    hi = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  }
+  return (static_cast<uint64_t>(hi) << 32) | static_cast<uint64_t>(0xffffffffu - idx);
+}
+__device__ __forceinline__ int32_t argmax_key_index(uint64_t key) {
+  return static_cast<int32_t>(0xffffffffu - static_cast<uint32_t>(key));
+}
+
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
+  uint32_t lo = __shfl_xor(static_cast<uint32_t>(v), m);
+  uint32_t hi = __shfl_xor(static_cast<uint32_t>(v >> 32), m);
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    uint64_t o = shfl_xor_u64(v, m);
+    v = o > v ? o : v;
+  }
+  return v;
+}
+__device__ __forceinline__ float wave_sum_f32(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
+  return v;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ float silu_f32(float x) {
+  return x / (1.0f + fast_exp2(-x * 1.4426950408889634f));
+}
+
+}  // namespace dfl

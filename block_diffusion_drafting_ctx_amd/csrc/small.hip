@@ -1,0 +1,194 @@
+// Verify (greedy target argmax + accepted prefix + commit), block embedding,
+// context commit and small helpers.  Cross-workgroup results always go
+// through plain stores and a following kernel: a fence-and-ticket handoff
+// costs tens of nanoseconds per workgroup on this chip.
+#include "common.h"
+#include "kernels.h"
+
+namespace dfl {
+
+// ---------------------------------------------------------------- verify
+// Pass 1, grid (vocab chunks, rows = batch*(n_d+1)), 256 threads: stream the
+// target logits once (16-byte non-temporal loads) and fold (value, index) into
+// one packed key per (row, chunk) -- order independent, so the result is exact.
+__global__ void __launch_bounds__(256) verify_argmax_kernel(const VerifyArgs a) {
+  __shared__ uint64_t s_best[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int row = blockIdx.y;
+  const int v0 = blockIdx.x * a.chunk;
+  const int v1 = min(a.V, v0 + a.chunk);
+  const float* p = a.logits + (size_t)row * a.V;
+  uint64_t best = 0;
+  for (int v = v0 + 4 * tid; v < v1; v += 4 * 256) {
+    const f32x4 x = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p + v));
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint64_t k = argmax_key(x[e], (uint32_t)(v + e));
+      best = k > best ? k : best;
+    }
+  }
+  best = wave_max_u64(best);
+  if (lane == 0) s_best[wave] = best;
+  __syncthreads();
+  if (tid == 0) {
+    uint64_t bb = s_best[0];
+    for (int w = 1; w < 4; ++w) bb = s_best[w] > bb ? s_best[w] : bb;
+    a.part[(size_t)row * a.nchunks + blockIdx.x] = bb;
+  }
+}
+
+// Pass 2, one workgroup per sequence: greedy tokens g_i, accepted prefix n,
+// bonus g_n, committed tokens, context-length advance (rollback of the rest)
+// and the step counters.
+__global__ void __launch_bounds__(64) verify_commit_kernel(const VerifyArgs a) {
+  __shared__ int s_g[65];
+  __shared__ int s_n;
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const int R = a.n_d + 1;
+  for (int i = tid; i < R; i += 64) {
+    const uint64_t* pr = a.part + ((size_t)b * R + i) * a.nchunks;
+    uint64_t best = 0;
+    for (int c = 0; c < a.nchunks; ++c) best = pr[c] > best ? pr[c] : best;
+    s_g[i] = argmax_key_index(best);
+  }
+  __syncthreads();
+  if (tid == 0) {
+    const int32_t* d = a.draft + (size_t)b * a.draft_stride;
+    int n = 0;
+    while (n < a.n_d && d[n] == s_g[n]) ++n;
+    s_n = n;
+    a.n_accept[b] = n;
+    a.bonus[b] = s_g[n];
+    const int t0 = a.ctx_len[b];
+    if (t0 < 0 || t0 + R > a.max_ctx) {
+      atomicOr(a.err, 4u);
+    } else {
+      a.ctx_len[b] = t0 + n + 1;
+    }
+    atomicAdd(&a.stats[0], 1ull);
+    atomicAdd(&a.stats[1], (unsigned long long)n);
+    atomicAdd(&a.stats[2], (unsigned long long)a.n_d);
+  }
+  __syncthreads();
+  for (int i = tid; i < R; i += 64) a.out_tokens[(size_t)b * R + i] = i <= s_n ? s_g[i] : -1;
+}
+
+hipError_t launch_verify(const VerifyArgs& a, hipStream_t stream) {
+  dim3 grid(a.nchunks, a.batch * (a.n_d + 1)), block(256);
+  hipLaunchKernelGGL(verify_argmax_kernel, grid, block, 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(verify_commit_kernel, dim3(a.batch), dim3(64), 0, stream, a);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- embedding
+// x[m] = E[ids[m]] as fp32, the hi/lo pair of x * gain (the first layer's
+// RMSNorm gain) and the row's sum of squares (one partial per row).
+template <typename S>
+__global__ void __launch_bounds__(256) embed_kernel(const S* embed, const S* gain, const int32_t* ids, int H, int V,
+                                                    float* x, bf16_t* xs_hi, bf16_t* xs_lo, float* ssq,
+                                                    uint32_t* err) {
+  __shared__ float s_part[4];
+  const int m = blockIdx.x, tid = threadIdx.x;
+  const int id = ids[m];
+  const bool ok = id >= 0 && id < V;
+  if (!ok && tid == 0) atomicOr(err, 2u);
+  const S* e = embed + (size_t)(ok ? id : 0) * H;
+  float s = 0.f;
+  for (int k = 8 * tid; k < H; k += 8 * 256) {
+    Raw8 raw, graw;
+    load_raw8<S>(raw, e + k);
+    load_raw8<S>(graw, gain + k);
+    float f[8], gf[8];
+    raw_to_f32x8<S>(raw, f);
+    raw_to_f32x8<S>(graw, gf);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      f[i] = ok ? f[i] : 0.f;
+      s += f[i] * f[i];
+      const size_t idx = (size_t)m * H + k + i;
+      const float v = f[i] * gf[i];
+      const bf16_t hbits = f32_to_bf16_bits(v);
+      xs_hi[idx] = hbits;
+      xs_lo[idx] = f32_to_bf16_bits(v - bf16_bits_to_f32(hbits));
+    }
+    f32x4* dst = reinterpret_cast<f32x4*>(x + (size_t)m * H + k);
+    dst[0] = f32x4{f[0], f[1], f[2], f[3]};
+    dst[1] = f32x4{f[4], f[5], f[6], f[7]};
+  }
+  s = wave_sum_f32(s);
+  if ((tid & 63) == 0) s_part[tid >> 6] = s;
+  __syncthreads();
+  if (tid == 0) ssq[m] = s_part[0] + s_part[1] + s_part[2] + s_part[3];
+}
+
+hipError_t launch_embed(int storage, const void* embed, const void* gain, const int32_t* ids, int M, int H, int V,
+                        float* x, void* xs_hi, void* xs_lo, float* ssq, uint32_t* err, hipStream_t stream) {
+  if (storage == ST_BF16)
+    hipLaunchKernelGGL(embed_kernel<bf16_t>, dim3(M), dim3(256), 0, stream, (const bf16_t*)embed,
+                       (const bf16_t*)gain, ids, H, V, x, (bf16_t*)xs_hi, (bf16_t*)xs_lo, ssq, err);
+  else
+    hipLaunchKernelGGL(embed_kernel<float>, dim3(M), dim3(256), 0, stream, (const float*)embed,
+                       (const float*)gain, ids, H, V, x, (bf16_t*)xs_hi, (bf16_t*)xs_lo, ssq, err);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- commit
+__global__ void commit_kernel(int32_t* ctx_len, int batch, int t_new, int max_ctx) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b < batch && ctx_len[b] + t_new <= max_ctx) ctx_len[b] += t_new;
+}
+
+hipError_t launch_commit(int32_t* ctx_len, int batch, int t_new, int max_ctx, hipStream_t stream) {
+  hipLaunchKernelGGL(commit_kernel, dim3((batch + 255) / 256), dim3(256), 0, stream, ctx_len, batch, t_new, max_ctx);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- helpers
+__global__ void copy_f32_kernel(const float* src, float* dst, size_t n) {
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+    dst[i] = src[i];
+}
+
+hipError_t launch_copy_f32(const float* src, float* dst, size_t n, hipStream_t stream) {
+  const int blocks = (int)((n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024);
+  hipLaunchKernelGGL(copy_f32_kernel, dim3(blocks > 0 ? blocks : 1), dim3(256), 0, stream, src, dst, n);
+  return hipGetLastError();
+}
+
+// c = y * rinv * g with rinv from the partial sums of squares (debug output
+// of the fused context feature; the same scale the K/V projection applies).
+template <typename S>
+__global__ void feature_dbg_kernel(const float* y, const float* ssq, int nparts, int ld_ssq, const S* gain,
+                                   float eps, int H, float* out) {
+  const int m = blockIdx.x;
+  float s = 0.f;
+  for (int p = 0; p < nparts; ++p) s += ssq[p * ld_ssq + m];
+  const float rinv = 1.0f / sqrtf(s / (float)H + eps);
+  for (int k = threadIdx.x; k < H; k += blockDim.x)
+    out[(size_t)m * H + k] = y[(size_t)m * H + k] * load_f32<S>(gain + k) * rinv;
+}
+
+hipError_t launch_feature_dbg(int storage, const float* y, const float* ssq, int nparts, int ld_ssq,
+                              const void* gain, float eps, int M, int H, float* out, hipStream_t stream) {
+  if (storage == ST_BF16)
+    hipLaunchKernelGGL(feature_dbg_kernel<bf16_t>, dim3(M), dim3(256), 0, stream, y, ssq, nparts, ld_ssq,
+                       (const bf16_t*)gain, eps, H, out);
+  else
+    hipLaunchKernelGGL(feature_dbg_kernel<float>, dim3(M), dim3(256), 0, stream, y, ssq, nparts, ld_ssq,
+                       (const float*)gain, eps, H, out);
+  return hipGetLastError();
+}
+
+__global__ void clear_u32_kernel(uint32_t* p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+hipError_t launch_clear_u32(uint32_t* p, int n, hipStream_t stream) {
+  hipLaunchKernelGGL(clear_u32_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, p, n);
+  return hipGetLastError();
+}
+
+}  // namespace dfl

@@ -33,14 +33,12 @@ def argmax_lowest(v: np.ndarray) -> int:
     finite data.)
     """
     v = np.asarray(v)
-    valid = np.flatnonzero(~np.isnan(v))
-    if valid.size == 0:
+    valid = ~np.isnan(v)
+    if not valid.any():
         return 0
-    best = int(valid[0])
-    for i in valid[1:]:
-        if v[i] > v[best]:
-            best = int(i)
-    return best
+    top = np.max(v[valid])
+    # first index holding the top value (NaN compares unequal, -0.0 == +0.0)
+    return int(np.flatnonzero(v == top)[0])
 
 
 def greedy_verify(logits: np.ndarray, draft: np.ndarray, n_d: int) -> Tuple[int, int, List[int]]:

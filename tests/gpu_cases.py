@@ -1,0 +1,204 @@
+"""One fuse -> verify -> draft step on the GPU library, checked against the oracle.
+
+Used by the GPU parity tests and by ``__graft_entry__.smoke()``.  Inputs come
+from ``harness.gen`` only; the oracle's starting state is copied from the
+generator's tensors before the library touches them, so no oracle input and
+no expected value comes from the HIP path.
+
+Bars (floating point: bf16 operands, fp32 accumulation on the GPU):
+  context feature, cache rows, final hidden state: relative L2 <= 1e-2;
+  logits: max |diff| <= 5e-2 * std(oracle logits);
+  draft ids: equal wherever the oracle's top-1 minus top-2 margin > 0.1;
+  verify (accepted length, bonus, committed tokens, context lengths,
+  counters): bit-exact.
+"""
+
+from __future__ import annotations
+
+import sys
+from dataclasses import dataclass, field
+from typing import List, Optional, Sequence
+
+import numpy as np
+import torch
+
+from harness import gen
+from oracle import DraftState, draft_block, fuse_ctx, verify_step, AcceptanceStats
+from tests.oracle_adapt import dims_of, np64, weights_of
+
+REL_L2 = 1e-2
+LOGIT_TOL = 5e-2
+MARGIN = 0.1
+
+
+def rel_l2(a, b) -> float:
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
+
+
+def top2_margin(logits: np.ndarray) -> np.ndarray:
+    part = np.partition(logits, -2, axis=-1)
+    return part[..., -1] - part[..., -2]
+
+
+def log(msg: str) -> None:
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def config_for(wl: gen.Workload, batch: int, max_fuse_rows: Optional[int] = None):
+    from block_diffusion_drafting_ctx_amd import make_config
+
+    return make_config(wl.hidden, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.n_layers, wl.ffn, wl.vocab,
+                       wl.block, wl.n_target_layers, batch, wl.max_ctx,
+                       max_fuse_rows or wl.t_new, wl.conv_width, wl.storage, wl.rms_eps, wl.rope_theta)
+
+
+@dataclass
+class StepResult:
+    checks: List[str] = field(default_factory=list)
+    worst: dict = field(default_factory=dict)
+
+    def note(self, key: str, value: float) -> None:
+        self.worst[key] = max(self.worst.get(key, 0.0), value)
+
+
+def run_step(wl: gen.Workload, seed: int, device="cuda", seqs: Optional[Sequence[int]] = None,
+             prefill: bool = False, poison: bool = False, n_d: Optional[int] = None,
+             check_oracle: bool = True) -> StepResult:
+    """Run one step on the library and compare with the oracle on `seqs`."""
+    from block_diffusion_drafting_ctx_amd import Drafter
+
+    res = StepResult()
+    B = wl.batch
+    n_d = wl.n_d if n_d is None else n_d
+    t_new = n_d + 1
+    seqs = list(range(B)) if seqs is None else list(seqs)
+    log(f"[case] {wl.name} B={B} seed={seed} prefill={prefill} poison={poison} n_d={n_d} seqs={seqs}")
+    gdev = device if wl.hidden >= 1024 else "cpu"  # big inputs are drawn on the GPU
+    w = gen.draft_weights(wl, seed, gdev)
+    w_dev = _to(w, device)
+    if prefill:
+        ctx_lens = np.zeros(B, dtype=np.int32)
+        ks = vs = None
+        pre = gen.target_hidden(wl, B, wl.ctx_hi, seed + 1, gdev)
+    else:
+        ctx_lens = gen.context_lengths(wl, seed + 1, B)
+        ks, vs = gen.context_kv(wl, ctx_lens, seed + 1, gdev, poison=poison)
+    hid = gen.target_hidden(wl, B, t_new, seed + 2, gdev)
+    drafts = gen.draft_tokens(wl, B, n_d, seed + 3)
+    accept = gen.accept_lengths(wl, B, seed + 4, n_d)
+    logits = gen.planted_logits(wl, drafts, accept, n_d, seed + 5, gdev)
+    ids = gen.block_ids(wl, B, seed + 6)
+
+    # oracle copies taken before the library runs
+    W = weights_of(w) if check_oracle else None
+    dims = dims_of(wl)
+    if check_oracle:
+        if prefill:
+            st = DraftState.empty(dims, len(seqs), wl.max_ctx)
+        else:
+            st = DraftState(k=[np64(t[seqs]) for t in ks], v=[np64(t[seqs]) for t in vs],
+                            ctx_len=ctx_lens[seqs].astype(np.int64).copy())
+
+    cfg = config_for(wl, B, max(t_new, wl.ctx_hi if prefill else 0))
+    kv_dev = None if ks is None else ([t.to(device) for t in ks], [t.to(device) for t in vs])
+    dr = Drafter(cfg, w_dev, device, *(kv_dev or (None, None)))
+    dr.ctx_len.copy_(torch.from_numpy(ctx_lens))
+    M_f = B * t_new
+    H = wl.hidden
+    if prefill:
+        pre_feat = torch.empty(B, wl.ctx_hi, H, dtype=torch.float32, device=device)
+        dr.fuse_ctx([h.to(device) for h in pre], commit=True, feat_dbg=pre_feat)
+    feat = torch.empty(B, t_new, H, dtype=torch.float32, device=device)
+    dr.fuse_ctx([h.to(device) for h in hid], commit=False, feat_dbg=feat)
+    ctx_after_fuse = dr.ctx_len.clone()
+    d_dev = torch.from_numpy(drafts).to(device)
+    n_acc = torch.full((B,), -7, dtype=torch.int32, device=device)
+    bonus = torch.full((B,), -7, dtype=torch.int32, device=device)
+    out_tok = torch.full((B, t_new), -7, dtype=torch.int32, device=device)
+    dr.verify(logits.to(device), d_dev, n_d, n_d, n_acc, bonus, out_tok)
+    ctx_after_verify = dr.ctx_len.clone()
+    ids_dev = torch.from_numpy(ids).to(device)
+    draft_ids = torch.full((B, wl.block), -7, dtype=torch.int32, device=device)
+    lg_dbg = torch.empty(B, wl.block, wl.vocab, dtype=torch.float32, device=device)
+    hid_dbg = torch.empty(B, wl.block, H, dtype=torch.float32, device=device)
+    dr.draft_block(ids_dev, draft_ids, lg_dbg, hid_dbg)
+    torch.cuda.synchronize()
+    err = dr.check()
+    assert err == 0, f"device error word {err:#x}"
+    stats = dr.stats()
+    log(f"[case] {wl.name}: library step done, stats={stats}")
+
+    # ---------------- verify: bit-exact against the oracle on all sequences
+    lg_np = logits.cpu().numpy()
+    exp_n = np.zeros(B, np.int64)
+    for b in range(B):
+        from oracle import greedy_verify
+
+        n, bon, toks = greedy_verify(lg_np[b], drafts[b], n_d)
+        exp_n[b] = n
+        assert int(n_acc[b]) == n, f"seq {b}: accepted {int(n_acc[b])} != {n}"
+        assert int(bonus[b]) == bon, f"seq {b}: bonus {int(bonus[b])} != {bon}"
+        got = out_tok[b].cpu().numpy()
+        assert list(got[: n + 1]) == toks and np.all(got[n + 1:] == -1), f"seq {b}: out tokens"
+        base = int(ctx_lens[b]) + (wl.ctx_hi if prefill else 0)
+        assert int(ctx_after_fuse[b]) == base
+        assert int(ctx_after_verify[b]) == base + n + 1
+    np.testing.assert_array_equal(exp_n, accept)  # the planted lengths
+    assert stats == [B, int(exp_n.sum()), B * n_d]
+    res.checks.append("verify bit-exact")
+    if not check_oracle:
+        return res
+
+    # ---------------- oracle: same call sequence on the sampled sequences
+    if prefill:
+        c_pre = fuse_ctx(st, W, dims, [np64(h[seqs]) for h in pre], commit=True)
+        e = rel_l2(pre_feat.cpu().numpy()[seqs], c_pre)
+        res.note("prefill_feature_rel_l2", e)
+        assert e <= REL_L2, f"prefill feature rel L2 {e}"
+    c = fuse_ctx(st, W, dims, [np64(h[seqs]) for h in hid], commit=False)
+    e = rel_l2(feat.cpu().numpy()[seqs], c)
+    res.note("feature_rel_l2", e)
+    assert e <= REL_L2, f"feature rel L2 {e}"
+    for j, b in enumerate(seqs):
+        t0 = int(st.ctx_len[j])
+        lo = 0 if prefill else t0
+        for l in range(wl.n_layers):
+            for name, cache, ref in (("K", dr.kv_k[l], st.k[l]), ("V", dr.kv_v[l], st.v[l])):
+                got = np64(cache[b, lo:t0 + t_new])
+                e = rel_l2(got, ref[j, lo:t0 + t_new])
+                res.note(f"cache_{name}_rel_l2", e)
+                assert e <= REL_L2, f"seq {b} layer {l} cache {name} rel L2 {e}"
+    lg_sel = lg_np[seqs]
+    verify_step(st, lg_sel, drafts[seqs].reshape(-1), n_d, n_d, AcceptanceStats())
+    for j, b in enumerate(seqs):
+        assert int(st.ctx_len[j]) == int(ctx_after_verify[b])
+    d_or, l_or, h_or = draft_block(st, W, dims, ids[seqs])
+    h_gpu = hid_dbg.cpu().numpy()[seqs]
+    l_gpu = lg_dbg.cpu().numpy()[seqs]
+    i_gpu = draft_ids.cpu().numpy()[seqs]
+    for j, b in enumerate(seqs):
+        e = rel_l2(h_gpu[j], h_or[j])
+        res.note("hidden_rel_l2", e)
+        assert e <= REL_L2, f"seq {b} final hidden rel L2 {e}"
+        tol = LOGIT_TOL * float(np.std(l_or[j]))
+        dmax = float(np.max(np.abs(l_gpu[j] - l_or[j])))
+        res.note("logit_maxdiff_over_std", dmax / float(np.std(l_or[j])))
+        assert dmax <= tol, f"seq {b} logits max diff {dmax} > {tol}"
+        marg = top2_margin(l_or[j])
+        sure = marg > MARGIN
+        assert np.all(i_gpu[j][sure] == d_or[j][sure]), f"seq {b} draft ids differ where margin > {MARGIN}"
+        res.note("rows_with_margin", float(sure.sum()))
+    res.checks.append("oracle parity")
+    log(f"[case] {wl.name}: parity ok {res.worst}")
+    dr.close()
+    return res
+
+
+def _to(w: dict, device) -> dict:
+    out = {k: (v.to(device) if isinstance(v, torch.Tensor) else v) for k, v in w.items() if k != "layers"}
+    out["layers"] = [{k: (v.to(device) if isinstance(v, torch.Tensor) else v) for k, v in lw.items()}
+                     for lw in w["layers"]]
+    return out
