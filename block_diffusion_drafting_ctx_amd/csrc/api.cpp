@@ -6,8 +6,10 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <initializer_list>
 #include <new>
 #include <string>
+#include <utility>
 #include <vector>
 
 #include "../../include/dflash.h"
@@ -26,21 +28,12 @@ dflash_status fail(dflash_status s, const std::string& msg) {
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-struct WsLayout {
-  size_t err, stats;
-  size_t x, ssq, y, xs_hi, xs_lo, q_hi, q_lo, kb, vb, o_hi, o_lo, act_hi, act_lo, lm_best, ver_best, part_o,
-      part_ml;
-  size_t total;
-  int md, mf, mmax, ssq_parts, attn_max_wgs_rows, lm_tiles, ver_chunks;
-};
-
 constexpr int kMaxNd = 64;
 constexpr int kVerifyChunk = 16384;  // vocab entries per workgroup of the verify argmax
-constexpr int kLmTileRows = 64;     // LM-head rows per workgroup tile (argmax partials per row)
-constexpr int kAttnTargetWgs = 1024;
-constexpr int kAttnMinCw = 256;
+constexpr int kAttnTargetWgs = 512;  // attention workgroups to aim for (two per compute unit)
+constexpr int kAttnMinCw = 128;      // fewest keys per attention split
 
-// Keys per attention split for a batch: aim for about kAttnTargetWgs workgroups.
+// Keys per attention split for a batch.
 int attn_cw(const dflash_config& c, int batch) {
   const int total = c.max_ctx + c.block;
   const int want = std::max(1, (kAttnTargetWgs + batch * c.n_kv_heads - 1) / (batch * c.n_kv_heads));
@@ -70,10 +63,79 @@ const char* validate(const dflash_config* c) {
   return nullptr;
 }
 
+// ---------------------------------------------------------------- GEMM planning
+// Launch geometry of one GEMM.  gemm_as (activation stationary, split-K) when
+// the activation slice fits LDS, else gemm_ws (one k-slice).
+bool plan_gemm(int storage, int src, int out, bool lo, int M, int N, int K, GemmArgs* a, GemmLaunch* l) {
+  if (M < 1 || N % 64 || K % 128) return false;
+  const int ntiles = N / 16;
+  const bool lo_eff = src == SRC_SPLIT ? lo : storage == ST_F32;
+  *l = GemmLaunch{};
+  l->src = src;
+  l->out = out;
+  l->lo = lo;
+  a->M = M;
+  a->N = N;
+  a->K = K;
+  const int ksl = gemm_as_ksl(M, K, lo_eff, out == OUT_ARGMAX);
+  if (ksl > 0) {
+    const int NW = ntiles >= 1024 ? 8 : 4;
+    l->kind = GEMM_AS;
+    l->MR = M <= 16 ? 1 : 2;
+    l->KS = K / ksl;
+    l->grid = dim3((ntiles + NW - 1) / NW, l->KS);
+    l->threads = 64 * NW;
+    l->lds = gemm_as_lds(M, ksl, lo_eff);
+    l->argmax_tiles = ntiles;
+    a->ksl = ksl;
+    a->tpw = NW;
+    return true;
+  }
+  const int MR = M <= 16 ? 1 : (M <= 32 ? 2 : (M <= 64 ? 4 : 8));
+  const int U = MR == 1 ? 4 : (MR == 2 ? 2 : 1);
+  const int WN = out == OUT_ARGMAX ? 4 : 1;
+  const int maxthr = gemm_ws_max_threads(MR);
+  int WK = std::min(maxthr / (64 * WN), std::max(1, K / 512));
+  while (WK > 1 && (K % (WK * 32 * U) || gemm_ws_lds(MR, WN, WK) > 64 * 1024)) --WK;
+  if (K % (WK * 32 * U) || gemm_ws_lds(MR, WN, WK) > 64 * 1024) return false;
+  l->kind = GEMM_WS;
+  l->MR = MR;
+  l->KS = 1;
+  l->grid = dim3(ntiles / WN, (M + 16 * MR - 1) / (16 * MR));
+  l->threads = 64 * WN * WK;
+  l->lds = gemm_ws_lds(MR, WN, WK);
+  l->argmax_tiles = ntiles / WN;
+  a->WN = WN;
+  a->WK = WK;
+  a->kw = K / WK;
+  return true;
+}
+
+// Floats of partial tiles the planner needs for a product of this shape.
+size_t partial_floats(int storage, int src, bool lo, int Mmax, int N, int K) {
+  size_t best = 0;
+  for (int M : {std::min(16, Mmax), std::min(32, Mmax), Mmax}) {
+    GemmArgs a{};
+    GemmLaunch l{};
+    if (plan_gemm(storage, src, OUT_PARTIAL, lo, M, N, K, &a, &l)) best = std::max(best, (size_t)l.KS * M * N);
+  }
+  return best;
+}
+
+struct WsLayout {
+  size_t err, stats;
+  size_t x, ssq, y, xs_hi, xs_lo, q_hi, q_lo, kb, vb, o_hi, o_lo, act_hi, act_lo, part, lm_best, ver_best, part_o,
+      part_ml;
+  size_t total;
+  int md, mf, mmax, ssq_parts, attn_max_wgs_rows, ver_chunks;
+};
+
 WsLayout layout(const dflash_config& c) {
   WsLayout L{};
-  const size_t S = c.dtype == DFLASH_DTYPE_BF16 ? 2 : 4;
-  const size_t H = c.hidden, D = c.head_dim;
+  const int st = c.dtype == DFLASH_DTYPE_BF16 ? ST_BF16 : ST_F32;
+  const size_t S = st == ST_BF16 ? 2 : 4;
+  const size_t H = c.hidden, D = c.head_dim, F = c.ffn;
+  const int Nq = c.n_q_heads * c.head_dim, Nk = c.n_kv_heads * c.head_dim;
   L.md = c.max_batch * c.block;
   L.mf = c.max_batch * c.max_fuse_rows;
   L.mmax = std::max(L.md, L.mf);
@@ -82,6 +144,13 @@ WsLayout layout(const dflash_config& c) {
   for (int b = 1; b <= c.max_batch; ++b) attn_rows = std::max(attn_rows, b * attn_splits(c, attn_cw(c, b)));
   L.attn_max_wgs_rows = attn_rows;
   const size_t QR = (size_t)(c.n_q_heads / c.n_kv_heads) * c.block;
+  size_t parts = 0;
+  parts = std::max(parts, partial_floats(st, SRC_CONCAT, false, L.mf, c.hidden, c.hidden * c.n_target_layers));
+  parts = std::max(parts, partial_floats(st, SRC_SPLIT, false, L.mf, 2 * c.n_layers * Nk, c.hidden));
+  parts = std::max(parts, partial_floats(st, SRC_SPLIT, true, L.md, Nq + 2 * Nk, c.hidden));
+  parts = std::max(parts, partial_floats(st, SRC_SPLIT, true, L.md, c.hidden, Nq));
+  parts = std::max(parts, partial_floats(st, SRC_SPLIT, true, L.md, 2 * c.ffn, c.hidden));
+  parts = std::max(parts, partial_floats(st, SRC_SPLIT, true, L.md, c.hidden, c.ffn));
   size_t off = 0;
   auto take = [&](size_t bytes) {
     size_t o = off;
@@ -95,17 +164,17 @@ WsLayout layout(const dflash_config& c) {
   L.y = take((size_t)L.mf * H * 4);
   L.xs_hi = take((size_t)L.mmax * H * 2);
   L.xs_lo = take((size_t)L.mmax * H * 2);
-  L.q_hi = take((size_t)L.md * c.n_q_heads * D * 2);
-  L.q_lo = take((size_t)L.md * c.n_q_heads * D * 2);
-  L.kb = take((size_t)L.md * c.n_kv_heads * D * S);
-  L.vb = take((size_t)L.md * c.n_kv_heads * D * S);
-  L.o_hi = take((size_t)L.md * c.n_q_heads * D * 2);
-  L.o_lo = take((size_t)L.md * c.n_q_heads * D * 2);
-  L.act_hi = take((size_t)L.md * c.ffn * 2);
-  L.act_lo = take((size_t)L.md * c.ffn * 2);
-  L.lm_tiles = c.vocab / kLmTileRows;
+  L.q_hi = take((size_t)L.md * Nq * 2);
+  L.q_lo = take((size_t)L.md * Nq * 2);
+  L.kb = take((size_t)L.md * Nk * S);
+  L.vb = take((size_t)L.md * Nk * S);
+  L.o_hi = take((size_t)L.md * Nq * 2);
+  L.o_lo = take((size_t)L.md * Nq * 2);
+  L.act_hi = take((size_t)L.md * F * 2);
+  L.act_lo = take((size_t)L.md * F * 2);
+  L.part = take(parts * 4);
+  L.lm_best = take((size_t)(c.vocab / 16) * L.md * 8);
   L.ver_chunks = (c.vocab + kVerifyChunk - 1) / kVerifyChunk;
-  L.lm_best = take((size_t)L.lm_tiles * L.md * 8);
   L.ver_best = take((size_t)c.max_batch * (kMaxNd + 1) * L.ver_chunks * 8);
   L.part_o = take((size_t)attn_rows * c.n_kv_heads * QR * D * 4);
   L.part_ml = take((size_t)attn_rows * c.n_kv_heads * QR * 2 * 4);
@@ -166,45 +235,6 @@ dflash_status hip_status(hipError_t e, const char* what) {
   return fail(DFLASH_EHIP, std::string(what) + ": " + hipGetErrorString(e));
 }
 
-// Launch geometry for one skinny GEMM.
-bool plan_gemm(int storage, ProKind pro, EpiKind epi, int M, int N, int K, int P, GemmArgs* a, GemmLaunch* l) {
-  const int MR = M <= 16 ? 1 : (M <= 32 ? 2 : (M <= 64 ? 4 : 8));
-  const int U = MR == 1 ? 4 : (MR == 2 ? 2 : 1);
-  const int MT = 16 * MR;
-  const int WN = epi == EPI_ARGMAX ? 4 : (P > 0 ? 2 : 1);
-  const int NT = 16 * WN;
-  if (N % NT) return false;
-  if (P > 0 && (P % (NT / 2) || N % (2 * P))) return false;
-  const int maxthr = gemm_max_threads(storage, pro, MR);
-  int WK = std::min(maxthr / (64 * WN), std::max(1, K / 512));
-  while (WK > 1 && (K % (WK * 32 * U) || gemm_lds_bytes(epi, MR, WN, WK) > 64 * 1024)) --WK;
-  if (K % (WK * 32 * U)) return false;
-  if (gemm_lds_bytes(epi, MR, WN, WK) > 64 * 1024) return false;
-  a->M = M;
-  a->N = N;
-  a->K = K;
-  a->WN = WN;
-  a->WK = WK;
-  a->P = P;
-  a->kw = K / WK;
-  l->MR = MR;
-  l->mtiles = (M + MT - 1) / MT;
-  l->ntiles = N / NT;
-  l->threads = 64 * WN * WK;
-  l->lds = gemm_lds_bytes(epi, MR, WN, WK);
-  return true;
-}
-
-dflash_status run_gemm(dflash_ctx* c, int stage, ProKind pro, EpiKind epi, GemmArgs& a, int M, int N, int K, int P,
-                       hipStream_t s) {
-  GemmLaunch l{};
-  if (!plan_gemm(c->storage(), pro, epi, M, N, K, P, &a, &l))
-    return fail(DFLASH_EUNSUPPORTED, "no GEMM launch plan for M=" + std::to_string(M) + " N=" + std::to_string(N) +
-                                         " K=" + std::to_string(K));
-  StageScope sc(c, stage, s);
-  return hip_status(launch_gemm(c->storage(), pro, epi, a, l, s), "gemm launch");
-}
-
 void set_segments(GemmArgs& a, std::initializer_list<std::pair<const void*, int>> segs) {
   a.nseg = 0;
   int start = 0;
@@ -217,13 +247,33 @@ void set_segments(GemmArgs& a, std::initializer_list<std::pair<const void*, int>
   a.seg_start[a.nseg] = start;
 }
 
+// Main kernel of one product into the partial-tile buffer, then its finish kernel.
+dflash_status gemm_partial(dflash_ctx* c, GemmArgs& a, int src, bool lo, int M, int N, int K, GemmLaunch* l,
+                           hipStream_t s) {
+  if (!plan_gemm(c->storage(), src, OUT_PARTIAL, lo, M, N, K, &a, l))
+    return fail(DFLASH_EUNSUPPORTED, "no GEMM launch plan for M=" + std::to_string(M) + " N=" + std::to_string(N) +
+                                         " K=" + std::to_string(K));
+  a.part = c->at<float>(c->L.part);
+  return hip_status(launch_gemm(c->storage(), a, *l, s), "gemm launch");
+}
+
+dflash_status finish(dflash_ctx* c, FinishKind kind, FinishArgs& f, const GemmLaunch& l, int M, int N,
+                     hipStream_t s) {
+  f.part = c->at<float>(c->L.part);
+  f.KS = l.KS;
+  f.ntiles = N / 16;
+  f.M = M;
+  f.N = N;
+  return hip_status(launch_finish(c->storage(), kind, f, s), "finish launch");
+}
+
 }  // namespace
 
 extern "C" {
 
 const char* dflash_last_error(void) { return g_last_error.c_str(); }
 
-const char* dflash_version(void) { return "dflash-mi355x 0.1 (gfx950)"; }
+const char* dflash_version(void) { return "dflash-mi355x 0.2 (gfx950)"; }
 
 size_t dflash_workspace_bytes(const dflash_config* cfg) {
   if (validate(cfg)) return 0;
@@ -305,61 +355,66 @@ dflash_status dflash_fuse_ctx(dflash_ctx* c, int32_t batch, const void* const* h
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int M = batch * t_new, H = cf.hidden, D = cf.head_dim;
   const WsLayout& L = c->L;
-
-  {  // K1: Y = concat(h) . W_fc^T; hi/lo of Y * g_fc; row sums of squares
+  dflash_status st;
+  {  // Y = concat(h) . W_fc^T; hi/lo of Y * g_fc; row sums of squares
+    StageScope sc(c, DFLASH_STAGE_FUSE_FC, s);
     GemmArgs a{};
+    GemmLaunch l{};
     set_segments(a, {{c->w_fc, H}});
     for (int j = 0; j < cf.n_target_layers; ++j) a.src[j] = hidden[j];
     a.n_src = cf.n_target_layers;
     a.src_width = H;
-    a.out_f32 = c->at<float>(L.y);
-    a.out_hi = c->at<void>(L.xs_hi);
-    a.out_lo = c->at<void>(L.xs_lo);
-    a.gnext = c->g_fc;
-    a.ssq_out = c->at<float>(L.ssq);
-    a.ld_ssq = L.mmax;
-    dflash_status st = run_gemm(c, DFLASH_STAGE_FUSE_FC, PRO_CONCAT, EPI_F32_SSQ, a, M, H,
-                                H * cf.n_target_layers, 0, s);
-    if (st) return st;
+    if ((st = gemm_partial(c, a, SRC_CONCAT, false, M, H, H * cf.n_target_layers, &l, s))) return st;
+    FinishArgs f{};
+    f.out_f32 = c->at<float>(L.y);
+    f.gnext = c->g_fc;
+    f.out_hi = c->at<void>(L.xs_hi);
+    f.out_lo = c->at<void>(L.xs_lo);
+    f.ssq_out = c->at<float>(L.ssq);
+    f.ld_ssq = L.mmax;
+    f.block = t_new;
+    if ((st = finish(c, FIN_ROWTILE, f, l, M, H, s))) return st;
   }
-  {  // K2: c = RMSNorm(Y) g_fc;  [K^l ; V^l] = c . [W_k^l ; W_v^l]^T for all layers, RoPE, append
+  int nkv = 0;
+  {  // c = RMSNorm(Y) g_fc;  [K^l ; V^l] = c . [W_k^l ; W_v^l]^T for all layers, RoPE, append
+    StageScope sc(c, DFLASH_STAGE_CTX_KV, s);
     GemmArgs a{};
+    GemmLaunch l{};
+    FinishArgs f{};
     a.nseg = 0;
-    int start = 0;
-    for (int l = 0; l < cf.n_layers; ++l) {
-      a.seg_ptr[a.nseg] = c->w_k[l];
-      a.kv_cache[a.nseg] = c->kv_k[l];
-      a.seg_start[a.nseg++] = start;
-      start += cf.n_kv_heads * D;
-      a.seg_ptr[a.nseg] = c->w_v[l];
-      a.kv_cache[a.nseg] = c->kv_v[l];
-      a.seg_start[a.nseg++] = start;
-      start += cf.n_kv_heads * D;
+    for (int l2 = 0; l2 < cf.n_layers; ++l2) {
+      for (int kv = 0; kv < 2; ++kv) {
+        a.seg_ptr[a.nseg] = kv ? c->w_v[l2] : c->w_k[l2];
+        f.kv_cache[a.nseg] = kv ? c->kv_v[l2] : c->kv_k[l2];
+        a.seg_start[a.nseg++] = nkv;
+        nkv += cf.n_kv_heads * D;
+      }
     }
-    a.seg_start[a.nseg] = start;
+    a.seg_start[a.nseg] = nkv;
     a.a_hi = c->at<void>(L.xs_hi);
-    a.a_lo = c->at<void>(L.xs_lo);
     a.lda = H;
-    a.ssq_in = c->at<float>(L.ssq);
-    a.ssq_nparts = H / 16;
-    a.ld_ssq = L.mmax;
-    a.eps = cf.rms_eps;
-    a.block = t_new;
-    a.ctx_len = c->ctx_len;
-    a.max_ctx = cf.max_ctx;
-    a.rope_theta = cf.rope_theta;
-    a.head_dim = D;
-    a.n_q_heads = cf.n_q_heads;
-    a.n_kv_heads = cf.n_kv_heads;
-    a.err = c->at<uint32_t>(L.err);
-    dflash_status st = run_gemm(c, DFLASH_STAGE_CTX_KV, PRO_SPLIT, EPI_KV, a, M, start, H, D / 2, s);
-    if (st) return st;
+    // hi only: the context K/V are storage-rounded anyway
+    if ((st = gemm_partial(c, a, SRC_SPLIT, false, M, nkv, H, &l, s))) return st;
+    f.ssq_in = c->at<float>(L.ssq);
+    f.ssq_nparts = H / 16;
+    f.ld_ssq = L.mmax;
+    f.kdim = H;
+    f.eps = cf.rms_eps;
+    f.block = t_new;
+    f.ctx_len = c->ctx_len;
+    f.max_ctx = cf.max_ctx;
+    f.rope_theta = cf.rope_theta;
+    f.head_dim = D;
+    f.n_q_heads = cf.n_q_heads;
+    f.n_kv_heads = cf.n_kv_heads;
+    f.err = c->at<uint32_t>(L.err);
+    if ((st = finish(c, FIN_KV, f, l, M, nkv, s))) return st;
   }
   if (feat_dbg) {
-    dflash_status st = hip_status(launch_feature_dbg(c->storage(), c->at<float>(L.y), c->at<float>(L.ssq), H / 16,
-                                                     L.mmax, c->g_fc, cf.rms_eps, M, H, feat_dbg, s),
-                                  "feature debug");
-    if (st) return st;
+    if ((st = hip_status(launch_feature_dbg(c->storage(), c->at<float>(L.y), c->at<float>(L.ssq), H / 16, L.mmax,
+                                            c->g_fc, cf.rms_eps, M, H, feat_dbg, s),
+                         "feature debug")))
+      return st;
   }
   if (commit) return hip_status(launch_commit(c->ctx_len, batch, t_new, cf.max_ctx, s), "commit");
   return DFLASH_OK;
@@ -426,31 +481,40 @@ dflash_status dflash_draft_block(dflash_ctx* c, int32_t batch, const int32_t* bl
   int ssq_parts = 1;
   const int cw = attn_cw(cf, batch);
   const int splits = attn_splits(cf, cw);
+  auto norm = [&](FinishArgs& f) {
+    f.ssq_in = ssq;
+    f.ssq_nparts = ssq_parts;
+    f.ld_ssq = L.mmax;
+    f.kdim = H;
+    f.eps = cf.rms_eps;
+  };
   for (int l = 0; l < cf.n_layers; ++l) {
     {  // RMSNorm -> Q/K/V, RoPE
+      StageScope sc(c, DFLASH_STAGE_QKV, s);
       GemmArgs a{};
+      GemmLaunch gl{};
       set_segments(a, {{c->w_q[l], Nq}, {c->w_k[l], Nk}, {c->w_v[l], Nk}});
       a.a_hi = xs_hi;
       a.a_lo = xs_lo;
       a.lda = H;
-      a.ssq_in = ssq;
-      a.ssq_nparts = ssq_parts;
-      a.ld_ssq = L.mmax;
-      a.eps = cf.rms_eps;
-      a.block = cf.block;
-      a.ctx_len = c->ctx_len;
-      a.rope_theta = cf.rope_theta;
-      a.head_dim = D;
-      a.n_q_heads = cf.n_q_heads;
-      a.n_kv_heads = cf.n_kv_heads;
-      a.q_scale = (float)(1.4426950408889634 / std::sqrt((double)D));
-      a.out_hi = c->at<void>(L.q_hi);
-      a.out_lo = c->at<void>(L.q_lo);
-      a.kb_out = c->at<void>(L.kb);
-      a.vb_out = c->at<void>(L.vb);
-      if ((st = run_gemm(c, DFLASH_STAGE_QKV, PRO_SPLIT, EPI_QKV, a, M, Nq + 2 * Nk, H, D / 2, s))) return st;
+      if ((st = gemm_partial(c, a, SRC_SPLIT, true, M, Nq + 2 * Nk, H, &gl, s))) return st;
+      FinishArgs f{};
+      norm(f);
+      f.block = cf.block;
+      f.ctx_len = c->ctx_len;
+      f.rope_theta = cf.rope_theta;
+      f.head_dim = D;
+      f.n_q_heads = cf.n_q_heads;
+      f.n_kv_heads = cf.n_kv_heads;
+      f.q_scale = (float)(1.4426950408889634 / std::sqrt((double)D));
+      f.out_hi = c->at<void>(L.q_hi);
+      f.out_lo = c->at<void>(L.q_lo);
+      f.kb_out = c->at<void>(L.kb);
+      f.vb_out = c->at<void>(L.vb);
+      if ((st = finish(c, FIN_QKV, f, gl, M, Nq + 2 * Nk, s))) return st;
     }
     {  // attention over [context ; block]
+      StageScope sc(c, DFLASH_STAGE_ATTN, s);
       AttnArgs a{};
       a.q_hi = c->at<void>(L.q_hi);
       a.q_lo = c->at<void>(L.q_lo);
@@ -471,75 +535,86 @@ dflash_status dflash_draft_block(dflash_ctx* c, int32_t batch, const int32_t* bl
       a.out_hi = c->at<void>(L.o_hi);
       a.out_lo = c->at<void>(L.o_lo);
       a.batch = batch;
-      StageScope sc(c, DFLASH_STAGE_ATTN, s);
       if ((st = hip_status(launch_attention(c->storage(), a, s), "attention launch"))) return st;
     }
     {  // O projection + residual (+ block conv); hi/lo of x * g_post, sums of squares
+      StageScope sc(c, DFLASH_STAGE_OPROJ, s);
       GemmArgs a{};
+      GemmLaunch gl{};
       set_segments(a, {{c->w_o[l], H}});
       a.a_hi = c->at<void>(L.o_hi);
       a.a_lo = c->at<void>(L.o_lo);
       a.lda = Nq;
-      a.x = x;
-      a.conv = c->conv[l];
-      a.block = cf.block;
-      a.gnext = c->g_post[l];
-      a.out_hi = xs_hi;
-      a.out_lo = xs_lo;
-      a.ssq_out = ssq;
-      a.ld_ssq = L.mmax;
-      if ((st = run_gemm(c, DFLASH_STAGE_OPROJ, PRO_SPLIT, EPI_RESID, a, M, H, Nq, 0, s))) return st;
+      if ((st = gemm_partial(c, a, SRC_SPLIT, true, M, H, Nq, &gl, s))) return st;
+      FinishArgs f{};
+      f.x = x;
+      f.conv = c->conv[l];
+      f.block = cf.block;
+      f.gnext = c->g_post[l];
+      f.out_hi = xs_hi;
+      f.out_lo = xs_lo;
+      f.ssq_out = ssq;
+      f.ld_ssq = L.mmax;
+      if ((st = finish(c, FIN_ROWTILE, f, gl, M, H, s))) return st;
     }
     ssq_parts = H / 16;
     {  // RMSNorm -> gate/up, SiLU product
+      StageScope sc(c, DFLASH_STAGE_GATEUP, s);
       GemmArgs a{};
+      GemmLaunch gl{};
       set_segments(a, {{c->w_gate[l], F}, {c->w_up[l], F}});
       a.a_hi = xs_hi;
       a.a_lo = xs_lo;
       a.lda = H;
-      a.ssq_in = ssq;
-      a.ssq_nparts = ssq_parts;
-      a.ld_ssq = L.mmax;
-      a.eps = cf.rms_eps;
-      a.out_hi = c->at<void>(L.act_hi);
-      a.out_lo = c->at<void>(L.act_lo);
-      if ((st = run_gemm(c, DFLASH_STAGE_GATEUP, PRO_SPLIT, EPI_SWIGLU, a, M, 2 * F, H, F, s))) return st;
+      if ((st = gemm_partial(c, a, SRC_SPLIT, true, M, 2 * F, H, &gl, s))) return st;
+      FinishArgs f{};
+      norm(f);
+      f.out_hi = c->at<void>(L.act_hi);
+      f.out_lo = c->at<void>(L.act_lo);
+      if ((st = finish(c, FIN_SWIGLU, f, gl, M, 2 * F, s))) return st;
     }
     {  // down projection + residual; hi/lo of x * (next layer's g_in, or g_final)
+      StageScope sc(c, DFLASH_STAGE_DOWN, s);
       GemmArgs a{};
+      GemmLaunch gl{};
       set_segments(a, {{c->w_down[l], H}});
       a.a_hi = c->at<void>(L.act_hi);
       a.a_lo = c->at<void>(L.act_lo);
       a.lda = F;
-      a.x = x;
-      a.conv = nullptr;
-      a.block = cf.block;
-      a.gnext = l + 1 < cf.n_layers ? c->g_in[l + 1] : c->g_final;
-      a.out_hi = xs_hi;
-      a.out_lo = xs_lo;
-      a.ssq_out = ssq;
-      a.ld_ssq = L.mmax;
-      if ((st = run_gemm(c, DFLASH_STAGE_DOWN, PRO_SPLIT, EPI_RESID, a, M, H, F, 0, s))) return st;
+      if ((st = gemm_partial(c, a, SRC_SPLIT, true, M, H, F, &gl, s))) return st;
+      FinishArgs f{};
+      f.x = x;
+      f.block = cf.block;
+      f.gnext = l + 1 < cf.n_layers ? c->g_in[l + 1] : c->g_final;
+      f.out_hi = xs_hi;
+      f.out_lo = xs_lo;
+      f.ssq_out = ssq;
+      f.ld_ssq = L.mmax;
+      if ((st = finish(c, FIN_ROWTILE, f, gl, M, H, s))) return st;
     }
   }
   if (hidden_dbg) {
     if ((st = hip_status(launch_copy_f32(x, hidden_dbg, (size_t)M * H, s), "hidden copy"))) return st;
   }
-  {  // final RMSNorm -> LM head -> argmax
+  {  // final RMSNorm -> LM head -> argmax (the positive row scale does not move the argmax)
+    StageScope sc(c, DFLASH_STAGE_LMHEAD, s);
     GemmArgs a{};
+    GemmLaunch gl{};
     set_segments(a, {{c->w_lm, cf.vocab}});
     a.a_hi = xs_hi;
-    a.a_lo = xs_lo;
     a.lda = H;
+    a.best_part = c->at<uint64_t>(L.lm_best);
+    a.ld_best = M;
+    a.logits_dbg = logits_dbg;
     a.ssq_in = ssq;
     a.ssq_nparts = ssq_parts;
     a.ld_ssq = L.mmax;
     a.eps = cf.rms_eps;
-    a.best_part = c->at<uint64_t>(L.lm_best);
-    a.ld_best = M;
-    a.logits_dbg = logits_dbg;
-    if ((st = run_gemm(c, DFLASH_STAGE_LMHEAD, PRO_SPLIT, EPI_ARGMAX, a, M, cf.vocab, H, 0, s))) return st;
-    if ((st = hip_status(launch_argmax_reduce(c->at<uint64_t>(L.lm_best), cf.vocab / kLmTileRows, M, M, draft_ids, s),
+    // hi only: the logits feed an argmax and the logit bar, not the residual stream
+    if (!plan_gemm(c->storage(), SRC_SPLIT, OUT_ARGMAX, false, M, cf.vocab, H, &a, &gl))
+      return fail(DFLASH_EUNSUPPORTED, "no LM-head launch plan");
+    if ((st = hip_status(launch_gemm(c->storage(), a, gl, s), "LM head launch"))) return st;
+    if ((st = hip_status(launch_argmax_reduce(c->at<uint64_t>(L.lm_best), gl.argmax_tiles, M, M, draft_ids, s),
                          "argmax reduce launch")))
       return st;
   }

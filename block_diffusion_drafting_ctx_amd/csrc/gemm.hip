@@ -1,60 +1,35 @@
-// Weight-streaming matrix-core GEMM for the skinny products of the drafting
-// hot path: Y[M, N] = A[M, K] . W[N, K]^T with M = rows of a drafted block
-// (or verified rows for the fusion), N, K up to the vocabulary.
+// Weight-streaming matrix-core GEMMs for the skinny products of the drafting
+// hot path, Y[M, N] = A[M, K] . W[N, K]^T, and the kernels that finish them.
 //
-// Design (gfx950, 64-wide waves):
-//  * A workgroup owns NT = 16*WN output columns (weight rows) and MT = 16*MR
-//    output rows; its WN x WK waves split the columns 16 rows each (WN) and
-//    the reduction dimension (WK).  Each weight element is loaded from HBM
-//    exactly once, straight into registers in the 16x16x32 MFMA operand
-//    layout (16 rows x 64 contiguous bytes per load instruction, non-temporal
-//    so the stream does not evict activations from L2).
-//  * Activations arrive as a pair of bf16 arrays (hi, lo) with a = hi + lo,
-//    written once by the producing kernel; each fragment costs two MFMAs.
-//    The activation then carries about 16 mantissa bits, so only the weights
-//    are bf16 -- a plain bf16 activation path loses about 1% of the final
-//    hidden state over five random layers.  RMSNorm is applied as a row
-//    scale: producers store hi/lo of (x * gain) and the consumer multiplies
-//    its result rows by 1/rms computed from the producer's partial sums of
-//    squares (the product is linear in the row scale).
-//  * Loads for the next unrolled step are issued before the MFMAs of the
-//    current one (two register stages).
-//  * The WK partial tiles are summed in a fixed order through LDS
-//    (deterministic, no float atomics), then a per-tile epilogue runs with
-//    the whole MT x NT tile in LDS: this is what lets RoPE pair column d with
-//    d + D/2 and SwiGLU pair gate row f with up row f (tile rows come in two
-//    halves P rows apart), and the block conv read rows i-1 and i+1.
+// The N axis is the concatenation of one or more weight matrices ("segments",
+// e.g. W_q | W_k | W_v, or W_gate | W_up, or every layer's W_k | W_v) and is
+// cut into tiles of 16 weight rows.  A main kernel produces fp32 partial
+// tiles part[k-slice][tile][m][16]; a finish kernel sums the k-slices in a
+// fixed order (deterministic) and applies the epilogue of the stage.  Only
+// the LM head folds its epilogue (a running argmax) into the main kernel.
+//
+// Main kernels (gfx950, 64-wide waves, v_mfma_f32_16x16x32_bf16):
+//  * gemm_as ("activation stationary", M <= 32): a workgroup copies the
+//    activation rows of one k-slice into LDS once, then every wave streams the
+//    16 weight rows of its tile for that slice straight from HBM into
+//    registers in MFMA operand layout (16 rows x 64 contiguous bytes per load,
+//    non-temporal, 8 k-steps per register stage, next stage in flight while
+//    the current one feeds the matrix cores).  No barrier in the loop.
+//    Measured on MI355X this streams weights at ~5 TB/s where re-reading the
+//    activations per wave from L2 halves the rate.
+//  * gemm_ws (any M): waves read the activations from L2 themselves; used
+//    when the activation slice does not fit LDS.
+// Activations are a pair of bf16 arrays (hi, lo) with a = hi + lo (two MFMAs
+// per fragment); the stages whose outputs do not feed the residual stream
+// (context K/V, LM head) use hi only.  RMSNorm is a row scale applied by the
+// finish kernel (the product is linear in it): producers store hi/lo of
+// (x * gain) plus partial sums of squares of x.
 #include "common.h"
 #include "kernels.h"
 
 namespace dfl {
 
-__device__ __forceinline__ int tile_row(int tile, int j, int NT, int P) {
-  if (P == 0) return tile * NT + j;
-  const int half = NT >> 1;
-  const int per = P / half;
-  return (tile / per) * 2 * P + (tile % per) * half + (j % half) + (j / half) * P;
-}
-
-// Threads per workgroup the register budget allows.
-__host__ __device__ constexpr int gemm_max_threads_for(bool wide, int MR) {
-  return MR <= 2 ? (wide ? 512 : 1024) : (MR == 4 ? 512 : 256);
-}
-
-template <typename S, int MR, int PRO>
-struct GemmShape {
-  static constexpr int MT = 16 * MR;
-  static constexpr int U = MR == 1 ? 4 : (MR == 2 ? 2 : 1);  // k-steps per register stage
-  static constexpr bool WIDE = PRO == PRO_SPLIT || sizeof(S) == 4;
-  static constexpr int MAXT = gemm_max_threads_for(WIDE, MR);
-};
-
-template <typename S, int MR, int PRO>
-struct Stage {
-  Raw8 w[GemmShape<S, MR, PRO>::U];
-  Raw8 a[GemmShape<S, MR, PRO>::U][MR];  // split: .lo = hi bits, .hi = lo bits
-};
-
+// ------------------------------------------------------------------ helpers
 __device__ __forceinline__ void rope_pair(float& lo, float& hi, int pos, int d, int D, float theta) {
   const double inv_freq = exp(-(2.0 * (double)d / (double)D) * log((double)theta));
   double s, c;
@@ -65,63 +40,216 @@ __device__ __forceinline__ void rope_pair(float& lo, float& hi, int pos, int d, 
   hi = a * sf + b * cf;
 }
 
-// v -> (hi, lo) bf16 pair with v ~= hi + lo.
+// v -> (hi, lo) bf16 pair with v ~= hi + lo (lo may be null: hi only).
 __device__ __forceinline__ void split_store(bf16_t* hi, bf16_t* lo, size_t idx, float v) {
   const bf16_t h = f32_to_bf16_bits(v);
   hi[idx] = h;
-  lo[idx] = f32_to_bf16_bits(v - bf16_bits_to_f32(h));
+  if (lo) lo[idx] = f32_to_bf16_bits(v - bf16_bits_to_f32(h));
 }
 
-template <typename S, int MR, int PRO, int EPI>
-__global__ void __launch_bounds__((GemmShape<S, MR, PRO>::MAXT)) gemm_ws_kernel(const GemmArgs g) {
-  constexpr int MT = GemmShape<S, MR, PRO>::MT;
-  constexpr int U = GemmShape<S, MR, PRO>::U;
-  extern __shared__ __align__(16) float smem[];
+// W row pointer of lane (lane & 15) of 16-row tile t, at column k.
+template <typename S>
+__device__ __forceinline__ const S* tile_row_ptr(const GemmArgs& g, int t, int lane, int k) {
+  const int n = t * 16;
+  int s = 0;
+  while (s + 1 < g.nseg && n >= g.seg_start[s + 1]) ++s;
+  return reinterpret_cast<const S*>(g.seg_ptr[s]) + (size_t)(n - g.seg_start[s] + (lane & 15)) * g.K + k +
+         (lane >> 4) * 8;
+}
 
+__device__ __forceinline__ float row_rinv(const float* ssq, int nparts, int ld, int m, int kdim, float eps) {
+  float s = 0.f;
+  for (int p = 0; p < nparts; ++p) s += ssq[p * ld + m];
+  return 1.0f / sqrtf(s / (float)kdim + eps);
+}
+
+// Packed (value, index) keys of a 16 x 16 MFMA result tile: the largest key per
+// activation row m over the tile's 16 columns, valid in every lane after the
+// cross-group reduction.
+__device__ __forceinline__ uint64_t tile_row_best(const f32x4& v, int n0, int lane) {
+  uint64_t best = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint64_t k = argmax_key(v[i], (uint32_t)(n0 + 4 * (lane >> 4) + i));
+    best = k > best ? k : best;
+  }
+  uint64_t o = shfl_xor_u64(best, 16);
+  best = o > best ? o : best;
+  o = shfl_xor_u64(best, 32);
+  return o > best ? o : best;
+}
+
+// ------------------------------------------------------------------ gemm_as
+template <int MR>
+struct AsShape {
+  static constexpr int MT = 16 * MR;
+  static constexpr int U = 8 / MR;  // k-steps per register stage
+};
+
+template <typename S, int MR, int SRC, bool LO, int OUT>
+__global__ void __launch_bounds__(512) gemm_as_kernel(const GemmArgs g) {
+  constexpr int MT = AsShape<MR>::MT;
+  constexpr int U = AsShape<MR>::U;
+  extern __shared__ __align__(16) bf16_t sa[];  // [LO ? 2 : 1][MT][ksl + 8]
+  const int LDSW = g.ksl + 8;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
+  const int ks = blockIdx.y, k0 = ks * g.ksl;
+  const int ntiles = g.N >> 4;
+  const int t0 = blockIdx.x * g.tpw, t1 = min(ntiles, t0 + g.tpw);
+  int tile = t0 + wave;
+  const int niter = g.ksl / (32 * U);
+
+  Raw8 wb0[U], wb1[U];
+  auto fetch = [&](Raw8(&wb)[U], const S* p, int it) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) load_raw8_nt<S>(wb[u], p + (it * U + u) * 32);
+  };
+  const S* wp = tile_row_ptr<S>(g, tile < t1 ? tile : t0, lane, k0);
+  if (tile < t1) fetch(wb0, wp, 0);  // first weight stage flies while the activations are staged
+
+  // ---- activation slice -> LDS (rows beyond M repeat row M-1; never stored)
+  const int pr = g.ksl / 8;  // 8-element pieces per row
+  for (int p = tid; p < MT * pr; p += blockDim.x) {
+    const int row = p / pr, col = (p - row * pr) * 8;
+    const int m = min(row, g.M - 1);
+    bf16x8 hv, lv;
+    if constexpr (SRC == SRC_SPLIT) {
+      const size_t o = (size_t)m * g.lda + k0 + col;
+      hv = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(reinterpret_cast<const bf16_t*>(g.a_hi) + o));
+      if (LO)
+        lv = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(reinterpret_cast<const bf16_t*>(g.a_lo) + o));
+    } else {
+      const int kg = k0 + col;
+      const int j = kg / g.src_width;
+      Raw8 raw;
+      load_raw8<S>(raw, reinterpret_cast<const S*>(g.src[j]) + (size_t)m * g.src_width + (kg - j * g.src_width));
+      if constexpr (sizeof(S) == 2) {
+        hv = raw_to_bf16x8<S>(raw);
+      } else {  // fp32 sources: split on the fly
+        float f[8];
+        raw_to_f32x8<S>(raw, f);
+        f32x4 l0, l1;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) hv[e] = (__bf16)f[e];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          l0[e] = f[e] - (float)hv[e];
+          l1[e] = f[4 + e] - (float)hv[4 + e];
+        }
+        lv = f32x8_to_bf16x8(l0, l1);
+      }
+    }
+    *reinterpret_cast<bf16x8*>(&sa[row * LDSW + col]) = hv;
+    if (LO) *reinterpret_cast<bf16x8*>(&sa[(MT + row) * LDSW + col]) = lv;
+  }
+  __syncthreads();
+
+  const bf16_t* ah = &sa[(lane & 15) * LDSW + (lane >> 4) * 8];
+  const bf16_t* al = &sa[(MT + (lane & 15)) * LDSW + (lane >> 4) * 8];
+  for (; tile < t1; tile += nw) {
+    f32x4 acc[MR];
+#pragma unroll
+    for (int mi = 0; mi < MR; ++mi) acc[mi] = f32x4{0.f, 0.f, 0.f, 0.f};
+    auto compute = [&](Raw8(&wb)[U], int it) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int kk = (it * U + u) * 32;
+        const bf16x8 wv = raw_to_bf16x8<S>(wb[u]);
+#pragma unroll
+        for (int mi = 0; mi < MR; ++mi) {
+          acc[mi] = mfma16x16x32(wv, *reinterpret_cast<const bf16x8*>(ah + 16 * mi * LDSW + kk), acc[mi]);
+          if (LO) acc[mi] = mfma16x16x32(wv, *reinterpret_cast<const bf16x8*>(al + 16 * mi * LDSW + kk), acc[mi]);
+        }
+      }
+    };
+    const int next = tile + nw;
+    const S* np = tile_row_ptr<S>(g, next < t1 ? next : tile, lane, k0);
+    for (int it = 0; it < niter; it += 2) {
+      if (it + 1 < niter) fetch(wb1, wp, it + 1);
+      else if (next < t1) fetch(wb1, np, 0);
+      compute(wb0, it);
+      if (it + 1 < niter) {
+        if (it + 2 < niter) fetch(wb0, wp, it + 2);
+        else if (next < t1) fetch(wb0, np, 0);
+        compute(wb1, it + 1);
+      }
+    }
+    if ((niter & 1) && next < t1) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) wb0[u] = wb1[u];
+    }
+    wp = np;
+
+    // lane holds Y[m = 16*mi + (lane & 15)][n = 16*tile + 4*(lane >> 4) + i]
+#pragma unroll
+    for (int mi = 0; mi < MR; ++mi) {
+      const int m = 16 * mi + (lane & 15);
+      if constexpr (OUT == OUT_PARTIAL) {
+        if (m < g.M)
+          *reinterpret_cast<f32x4*>(g.part + (((size_t)ks * ntiles + tile) * g.M + m) * 16 + 4 * (lane >> 4)) =
+              acc[mi];
+      } else {
+        const uint64_t best = tile_row_best(acc[mi], tile * 16, lane);
+        if ((lane >> 4) == 0 && m < g.M) g.best_part[(size_t)tile * g.ld_best + m] = best;
+        if (g.logits_dbg != nullptr && m < g.M) {
+          const float r = row_rinv(g.ssq_in, g.ssq_nparts, g.ld_ssq, m, g.K, g.eps);
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            g.logits_dbg[(size_t)m * g.N + tile * 16 + 4 * (lane >> 4) + i] = acc[mi][i] * r;
+        }
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ gemm_ws
+// Activations from L2 per wave; WN waves split 16-row tiles, WK waves split K
+// (fixed-order LDS reduction).  One k-slice.
+template <int MR>
+struct WsShape {
+  static constexpr int MT = 16 * MR;
+  static constexpr int U = MR == 1 ? 4 : (MR == 2 ? 2 : 1);
+  static constexpr int MAXT = MR <= 4 ? 512 : 256;
+};
+
+template <typename S, int MR, int SRC, bool LO, int OUT>
+__global__ void __launch_bounds__((WsShape<MR>::MAXT)) gemm_ws_kernel(const GemmArgs g) {
+  constexpr int MT = WsShape<MR>::MT;
+  constexpr int U = WsShape<MR>::U;
+  extern __shared__ __align__(16) float smem[];  // [WK][MT][NT]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nthr = blockDim.x;
   const int WN = g.WN, WK = g.WK;
   const int wn = wave % WN, wk = wave / WN;
   const int NT = 16 * WN;
-  const int tile = blockIdx.x;
   const int m0 = blockIdx.y * MT;
+  const int tile = blockIdx.x * WN + wn;  // 16-row tile of this wave
+  const S* wp = tile_row_ptr<S>(g, tile, lane, wk * g.kw);
 
-  float* red = smem;                    // [WK][MT][NT]
-  float* rinv_s = smem + WK * MT * NT;  // [MT]
-  float* aux = rinv_s + MT;             // [MT][NT]
-
-  const bool row_scale = PRO == PRO_SPLIT && g.ssq_in != nullptr;
-
-  // ---- the 16 weight rows of this wave
-  const int n0 = tile_row(tile, 16 * wn, NT, g.P);
-  int sgi = 0;
-  while (sgi + 1 < g.nseg && n0 >= g.seg_start[sgi + 1]) ++sgi;
-  const S* wp = reinterpret_cast<const S*>(g.seg_ptr[sgi]) +
-                (size_t)(n0 - g.seg_start[sgi] + (lane & 15)) * g.K + (size_t)wk * g.kw + (lane >> 4) * 8;
-
-  // ---- activation rows of this lane (padding rows clamp to the last real row)
   int arow[MR];
 #pragma unroll
   for (int mi = 0; mi < MR; ++mi) arow[mi] = min(m0 + 16 * mi + (lane & 15), g.M - 1);
   const int kbase = wk * g.kw + (lane >> 4) * 8;
 
-  auto fetch = [&](Stage<S, MR, PRO>& st, int it) {
+  struct Stage {
+    Raw8 w[U];
+    Raw8 a[U][MR];
+  };
+  auto fetch = [&](Stage& st, int it) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int ks = (it * U + u) * 32;
       load_raw8_nt<S>(st.w[u], wp + ks);
       const int k = kbase + ks;
-      if constexpr (PRO == PRO_SPLIT) {
-        const bf16_t* ah = reinterpret_cast<const bf16_t*>(g.a_hi);
-        const bf16_t* al = reinterpret_cast<const bf16_t*>(g.a_lo);
+      if constexpr (SRC == SRC_SPLIT) {
 #pragma unroll
         for (int mi = 0; mi < MR; ++mi) {
           const size_t o = (size_t)arow[mi] * g.lda + k;
-          st.a[u][mi].lo = *reinterpret_cast<const u32x4*>(ah + o);
-          st.a[u][mi].hi = *reinterpret_cast<const u32x4*>(al + o);
+          st.a[u][mi].lo = *reinterpret_cast<const u32x4*>(reinterpret_cast<const bf16_t*>(g.a_hi) + o);
+          if (LO) st.a[u][mi].hi = *reinterpret_cast<const u32x4*>(reinterpret_cast<const bf16_t*>(g.a_lo) + o);
         }
-      } else {  // PRO_CONCAT
-        const int kstep = wk * g.kw + ks;  // uniform across the wave
+      } else {
+        const int kstep = wk * g.kw + ks;
         const int j = kstep / g.src_width;
         const S* src = reinterpret_cast<const S*>(g.src[j]);
         const int off = k - j * g.src_width;
@@ -130,20 +258,18 @@ __global__ void __launch_bounds__((GemmShape<S, MR, PRO>::MAXT)) gemm_ws_kernel(
       }
     }
   };
-
   f32x4 acc[MR];
 #pragma unroll
   for (int mi = 0; mi < MR; ++mi) acc[mi] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  auto compute = [&](const Stage<S, MR, PRO>& st) {
+  auto compute = [&](const Stage& st) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const bf16x8 wv = raw_to_bf16x8<S>(st.w[u]);
 #pragma unroll
       for (int mi = 0; mi < MR; ++mi) {
-        if constexpr (PRO == PRO_SPLIT) {
+        if constexpr (SRC == SRC_SPLIT) {
           acc[mi] = mfma16x16x32(wv, __builtin_bit_cast(bf16x8, st.a[u][mi].lo), acc[mi]);
-          acc[mi] = mfma16x16x32(wv, __builtin_bit_cast(bf16x8, st.a[u][mi].hi), acc[mi]);
+          if (LO) acc[mi] = mfma16x16x32(wv, __builtin_bit_cast(bf16x8, st.a[u][mi].hi), acc[mi]);
         } else if constexpr (sizeof(S) == 2) {
           acc[mi] = mfma16x16x32(wv, raw_to_bf16x8<S>(st.a[u][mi]), acc[mi]);
         } else {  // fp32 sources: split on the fly
@@ -164,29 +290,9 @@ __global__ void __launch_bounds__((GemmShape<S, MR, PRO>::MAXT)) gemm_ws_kernel(
       }
     }
   };
-
   const int niter = g.kw / (32 * U);
-  Stage<S, MR, PRO> s0, s1;
+  Stage s0, s1;
   if (niter > 0) fetch(s0, 0);
-
-  // Row scale 1/rms from the producer's partial sums of squares (16 lanes per
-  // row), computed while the first weight loads are in flight; it is applied
-  // after the reduction below.
-  if (row_scale) {
-    for (int base = 0; base < MT * 16; base += nthr) {
-      const int t = base + tid;
-      const int m = t >> 4, part = t & 15;
-      const int mm = min(m0 + m, g.M - 1);
-      float ss = 0.f;
-      if (m < MT)
-        for (int p = part; p < g.ssq_nparts; p += 16) ss += g.ssq_in[p * g.ld_ssq + mm];
-      ss += __shfl_xor(ss, 8);
-      ss += __shfl_xor(ss, 4);
-      ss += __shfl_xor(ss, 2);
-      ss += __shfl_xor(ss, 1);
-      if (part == 0 && m < MT) rinv_s[m] = 1.0f / sqrtf(ss / (float)g.K + g.eps);
-    }
-  }
   for (int it = 0; it < niter; it += 2) {
     if (it + 1 < niter) fetch(s1, it + 1);
     compute(s0);
@@ -196,151 +302,30 @@ __global__ void __launch_bounds__((GemmShape<S, MR, PRO>::MAXT)) gemm_ws_kernel(
     }
   }
 
-  // ---- partial tiles -> LDS, fixed-order reduction over WK, row scale
+  float* red = smem;
 #pragma unroll
-  for (int mi = 0; mi < MR; ++mi) {
-    float* dst = red + ((wk * MT + 16 * mi + (lane & 15)) * NT + 16 * wn + 4 * (lane >> 4));
-    *reinterpret_cast<f32x4*>(dst) = acc[mi];
-  }
+  for (int mi = 0; mi < MR; ++mi)
+    *reinterpret_cast<f32x4*>(red + ((wk * MT + 16 * mi + (lane & 15)) * NT + 16 * wn + 4 * (lane >> 4))) = acc[mi];
   __syncthreads();
   const int tsz = MT * NT;
-  if (WK > 1 || row_scale) {
-    for (int e = tid; e < tsz; e += nthr) {
-      float v = red[e];
-      for (int w = 1; w < WK; ++w) v += red[w * tsz + e];
-      if (row_scale) v *= rinv_s[e / NT];
-      red[e] = v;
-    }
-    __syncthreads();
+  for (int e = tid; e < tsz; e += nthr) {
+    float v = red[e];
+    for (int w = 1; w < WK; ++w) v += red[w * tsz + e];
+    red[e] = v;
   }
-
-  // ---- epilogues: tile value of (row m0 + m, column tile_row(j)) is red[m * NT + j]
-  if constexpr (EPI == EPI_F32_SSQ || EPI == EPI_RESID) {
-    const float* src = red;
-    const S* gn = reinterpret_cast<const S*>(g.gnext);
-    bf16_t* oh = reinterpret_cast<bf16_t*>(g.out_hi);
-    bf16_t* ol = reinterpret_cast<bf16_t*>(g.out_lo);
-    if constexpr (EPI == EPI_RESID) {
-      for (int e = tid; e < tsz; e += nthr) {
-        const int m = e / NT, j = e - m * NT;
-        if (m0 + m < g.M) red[e] += g.x[(size_t)(m0 + m) * g.N + tile_row(tile, j, NT, g.P)];
-      }
-      __syncthreads();
-      if (g.conv != nullptr) {
-        const S* cw = reinterpret_cast<const S*>(g.conv);
-        for (int e = tid; e < tsz; e += nthr) {
-          const int m = e / NT, j = e - m * NT;
-          const int gm = m0 + m;
-          if (gm >= g.M) continue;
-          const int n = tile_row(tile, j, NT, g.P);
-          const int i = gm % g.block;
-          const float v = red[e];
-          float y = load_f32<S>(cw + 3 * n + 1) * v;
-          if (i > 0) y += load_f32<S>(cw + 3 * n) * red[e - NT];
-          if (i < g.block - 1 && gm + 1 < g.M) y += load_f32<S>(cw + 3 * n + 2) * red[e + NT];
-          aux[e] = v + y;
-        }
-        __syncthreads();
-        src = aux;
-      }
-    }
+  __syncthreads();
+  if constexpr (OUT == OUT_PARTIAL) {
     for (int e = tid; e < tsz; e += nthr) {
       const int m = e / NT, j = e - m * NT;
-      if (m0 + m >= g.M) continue;
-      const int n = tile_row(tile, j, NT, g.P);
-      const size_t idx = (size_t)(m0 + m) * g.N + n;
-      const float v = src[e];
-      if constexpr (EPI == EPI_RESID) g.x[idx] = v;
-      else g.out_f32[idx] = v;
-      split_store(oh, ol, idx, v * load_f32<S>(gn + n));
+      if (m0 + m < g.M) g.part[((size_t)(blockIdx.x * WN + (j >> 4)) * g.M + m0 + m) * 16 + (j & 15)] = red[e];
     }
-    // row sums of squares: 16 lanes per row
-    for (int base = 0; base < MT * 16; base += nthr) {
-      const int t = base + tid;
-      const int m = t >> 4, part = t & 15;
-      float s = 0.f;
-      if (m < MT)
-        for (int j = part; j < NT; j += 16) {
-          const float v = src[m * NT + j];
-          s += v * v;
-        }
-      s += __shfl_xor(s, 8);
-      s += __shfl_xor(s, 4);
-      s += __shfl_xor(s, 2);
-      s += __shfl_xor(s, 1);
-      if (part == 0 && m < MT && m0 + m < g.M) g.ssq_out[(size_t)tile * g.ld_ssq + m0 + m] = s;
-    }
-  } else if constexpr (EPI == EPI_SWIGLU) {
-    const int half = NT >> 1;
-    const int F = g.N >> 1;
-    bf16_t* oh = reinterpret_cast<bf16_t*>(g.out_hi);
-    bf16_t* ol = reinterpret_cast<bf16_t*>(g.out_lo);
-    for (int e = tid; e < MT * half; e += nthr) {
-      const int m = e / half, jj = e - m * half;
-      if (m0 + m >= g.M) continue;
-      const int f = tile_row(tile, jj, NT, g.P);
-      const float gv = red[m * NT + jj], uv = red[m * NT + jj + half];
-      split_store(oh, ol, (size_t)(m0 + m) * F + f, silu_f32(gv) * uv);
-    }
-  } else if constexpr (EPI == EPI_QKV) {
-    const int half = NT >> 1;
-    const int D = g.head_dim;
-    const int Nq = g.n_q_heads * D, Nk = g.n_kv_heads * D;
-    bf16_t* qh = reinterpret_cast<bf16_t*>(g.out_hi);
-    bf16_t* ql = reinterpret_cast<bf16_t*>(g.out_lo);
-    S* ko = reinterpret_cast<S*>(g.kb_out);
-    S* vo = reinterpret_cast<S*>(g.vb_out);
-    for (int e = tid; e < MT * half; e += nthr) {
-      const int m = e / half, jj = e - m * half;
-      const int gm = m0 + m;
-      if (gm >= g.M) continue;
-      const int n = tile_row(tile, jj, NT, g.P);  // d < D/2 of its head
-      float lo = red[m * NT + jj], hi = red[m * NT + jj + half];
-      const int pos = g.ctx_len[gm / g.block] + gm % g.block;
-      if (n < Nq) {
-        rope_pair(lo, hi, pos, n % D, D, g.rope_theta);
-        split_store(qh, ql, (size_t)gm * Nq + n, lo * g.q_scale);
-        split_store(qh, ql, (size_t)gm * Nq + n + D / 2, hi * g.q_scale);
-      } else if (n < Nq + Nk) {
-        const int nn = n - Nq;
-        rope_pair(lo, hi, pos, nn % D, D, g.rope_theta);
-        store_from_f32<S>(ko + (size_t)gm * Nk + nn, lo);
-        store_from_f32<S>(ko + (size_t)gm * Nk + nn + D / 2, hi);
-      } else {
-        const int nn = n - Nq - Nk;
-        store_from_f32<S>(vo + (size_t)gm * Nk + nn, lo);
-        store_from_f32<S>(vo + (size_t)gm * Nk + nn + D / 2, hi);
-      }
-    }
-  } else if constexpr (EPI == EPI_KV) {
-    const int half = NT >> 1;
-    const int D = g.head_dim, Hkv = g.n_kv_heads;
-    const int seg_rows = Hkv * D;
-    for (int e = tid; e < MT * half; e += nthr) {
-      const int m = e / half, jj = e - m * half;
-      const int gm = m0 + m;
-      if (gm >= g.M) continue;
-      const int b = gm / g.block, i = gm % g.block;
-      const int t0 = g.ctx_len[b];
-      if (t0 < 0 || t0 + g.block > g.max_ctx) {
-        atomicOr(g.err, 1u);
-        continue;
-      }
-      const int pos = t0 + i;
-      const int n = tile_row(tile, jj, NT, g.P);
-      const int seg = n / seg_rows, r = n - seg * seg_rows;
-      const int head = r / D, d = r - head * D;
-      float lo = red[m * NT + jj], hi = red[m * NT + jj + half];
-      if ((seg & 1) == 0) rope_pair(lo, hi, pos, d, D, g.rope_theta);
-      S* dst = reinterpret_cast<S*>(g.kv_cache[seg]) + (((size_t)b * g.max_ctx + pos) * Hkv + head) * D + d;
-      store_from_f32<S>(dst, lo);
-      store_from_f32<S>(dst + D / 2, hi);
-    }
-  } else if constexpr (EPI == EPI_ARGMAX) {
+  } else {
     if (g.logits_dbg != nullptr) {
       for (int e = tid; e < tsz; e += nthr) {
         const int m = e / NT, j = e - m * NT;
-        if (m0 + m < g.M) g.logits_dbg[(size_t)(m0 + m) * g.N + tile_row(tile, j, NT, g.P)] = red[e];
+        if (m0 + m < g.M)
+          g.logits_dbg[(size_t)(m0 + m) * g.N + blockIdx.x * NT + j] =
+              red[e] * row_rinv(g.ssq_in, g.ssq_nparts, g.ld_ssq, m0 + m, g.K, g.eps);
       }
     }
     for (int base = 0; base < MT * 16; base += nthr) {
@@ -349,7 +334,7 @@ __global__ void __launch_bounds__((GemmShape<S, MR, PRO>::MAXT)) gemm_ws_kernel(
       uint64_t best = 0;
       if (m < MT)
         for (int j = part; j < NT; j += 16) {
-          const uint64_t k = argmax_key(red[m * NT + j], (uint32_t)tile_row(tile, j, NT, g.P));
+          const uint64_t k = argmax_key(red[m * NT + j], (uint32_t)(blockIdx.x * NT + j));
           best = k > best ? k : best;
         }
 #pragma unroll
@@ -357,11 +342,12 @@ __global__ void __launch_bounds__((GemmShape<S, MR, PRO>::MAXT)) gemm_ws_kernel(
         const uint64_t o = shfl_xor_u64(best, s);
         best = o > best ? o : best;
       }
-      if (part == 0 && m < MT && m0 + m < g.M) g.best_part[(size_t)tile * g.ld_best + m0 + m] = best;
+      if (part == 0 && m < MT && m0 + m < g.M) g.best_part[(size_t)blockIdx.x * g.ld_best + m0 + m] = best;
     }
   }
 }
 
+// ------------------------------------------------------------------ argmax reduce
 // draft id of each row = index of the largest packed key over the LM-head tiles.
 __global__ void __launch_bounds__(256) argmax_reduce_kernel(const uint64_t* part, int ntiles, int ld, int32_t* ids) {
   __shared__ uint64_t s_best[4];
@@ -381,55 +367,288 @@ __global__ void __launch_bounds__(256) argmax_reduce_kernel(const uint64_t* part
   }
 }
 
-hipError_t launch_argmax_reduce(const uint64_t* part, int ntiles, int ld, int M, int32_t* ids, hipStream_t stream) {
-  hipLaunchKernelGGL(argmax_reduce_kernel, dim3(M), dim3(256), 0, stream, part, ntiles, ld, ids);
+// ------------------------------------------------------------------ finish kernels
+// Sum of the k-slices of output (m, n) in slice order.
+__device__ __forceinline__ float ksum(const FinishArgs& f, int m, int n) {
+  const int tile = n >> 4, j = n & 15;
+  float v = 0.f;
+  for (int s = 0; s < f.KS; ++s) v += f.part[(((size_t)s * f.ntiles + tile) * f.M + m) * 16 + j];
+  return v;
+}
+
+// rinv of every row into LDS (16 lanes per row); 1 when the stage has no norm.
+__device__ __forceinline__ void rows_rinv(const FinishArgs& f, float* s_r) {
+  for (int base = 0; base < f.M * 16; base += blockDim.x) {
+    const int t = base + threadIdx.x;
+    const int m = t >> 4, part = t & 15;
+    float ss = 0.f;
+    if (f.ssq_in != nullptr && m < f.M)
+      for (int p = part; p < f.ssq_nparts; p += 16) ss += f.ssq_in[p * f.ld_ssq + m];
+    ss += __shfl_xor(ss, 8);
+    ss += __shfl_xor(ss, 4);
+    ss += __shfl_xor(ss, 2);
+    ss += __shfl_xor(ss, 1);
+    if (part == 0 && m < f.M) s_r[m] = f.ssq_in != nullptr ? 1.0f / sqrtf(ss / (float)f.kdim + f.eps) : 1.0f;
+  }
+  __syncthreads();
+}
+
+// Sum of squares over the 16 columns of a tile per row: e = m * 16 + j.
+__device__ __forceinline__ void tile_ssq_store(const FinishArgs& f, const float* vals, int tile) {
+  for (int base = 0; base < f.M * 16; base += blockDim.x) {
+    const int e = base + threadIdx.x;
+    const int m = e >> 4;
+    const float v = (m < f.M) ? vals[e] : 0.f;
+    float s = v * v;
+    s += __shfl_xor(s, 8);
+    s += __shfl_xor(s, 4);
+    s += __shfl_xor(s, 2);
+    s += __shfl_xor(s, 1);
+    if ((e & 15) == 0 && m < f.M) f.ssq_out[(size_t)tile * f.ld_ssq + m] = s;
+  }
+}
+
+// y = sum (+ x residual, + width-3 block conv); x / out_f32 = y; hi/lo of
+// y * gnext; sums of squares per tile.  grid: N/16 tiles.
+template <typename S>
+__global__ void __launch_bounds__(256) finish_rowtile_kernel(const FinishArgs f) {
+  extern __shared__ __align__(16) float sv[];  // [2][M * 16]
+  const int tile = blockIdx.x;
+  const int tot = f.M * 16;
+  float* v0 = sv;
+  float* v1 = sv + tot;
+  for (int e = threadIdx.x; e < tot; e += blockDim.x) {
+    const int m = e >> 4, n = tile * 16 + (e & 15);
+    float v = ksum(f, m, n);
+    if (f.x != nullptr) v += f.x[(size_t)m * f.N + n];
+    v0[e] = v;
+  }
+  __syncthreads();
+  const float* src = v0;
+  if (f.conv != nullptr) {
+    const S* cw = reinterpret_cast<const S*>(f.conv);
+    for (int e = threadIdx.x; e < tot; e += blockDim.x) {
+      const int m = e >> 4, n = tile * 16 + (e & 15);
+      const int i = m % f.block;
+      const float v = v0[e];
+      float y = load_f32<S>(cw + 3 * n + 1) * v;
+      if (i > 0) y += load_f32<S>(cw + 3 * n) * v0[e - 16];
+      if (i < f.block - 1 && m + 1 < f.M) y += load_f32<S>(cw + 3 * n + 2) * v0[e + 16];
+      v1[e] = v + y;
+    }
+    __syncthreads();
+    src = v1;
+  }
+  const S* gn = reinterpret_cast<const S*>(f.gnext);
+  bf16_t* oh = reinterpret_cast<bf16_t*>(f.out_hi);
+  bf16_t* ol = reinterpret_cast<bf16_t*>(f.out_lo);
+  for (int e = threadIdx.x; e < tot; e += blockDim.x) {
+    const int m = e >> 4, n = tile * 16 + (e & 15);
+    const size_t idx = (size_t)m * f.N + n;
+    const float v = src[e];
+    if (f.x != nullptr) f.x[idx] = v;
+    if (f.out_f32 != nullptr) f.out_f32[idx] = v;
+    split_store(oh, ol, idx, v * load_f32<S>(gn + n));
+  }
+  tile_ssq_store(f, src, tile);
+}
+
+// act[m, c] = silu(rinv * y_gate) * (rinv * y_up) as a hi/lo pair.  grid: F/16 tiles.
+__global__ void __launch_bounds__(256) finish_swiglu_kernel(const FinishArgs f) {
+  extern __shared__ __align__(16) float s_r[];
+  rows_rinv(f, s_r);
+  const int F = f.N >> 1;
+  const int tile = blockIdx.x;
+  bf16_t* oh = reinterpret_cast<bf16_t*>(f.out_hi);
+  bf16_t* ol = reinterpret_cast<bf16_t*>(f.out_lo);
+  for (int e = threadIdx.x; e < f.M * 16; e += blockDim.x) {
+    const int m = e >> 4, c = tile * 16 + (e & 15);
+    const float r = s_r[m];
+    const float gv = ksum(f, m, c) * r, uv = ksum(f, m, F + c) * r;
+    split_store(oh, ol, (size_t)m * F + c, silu_f32(gv) * uv);
+  }
+}
+
+// Block Q/K/V: RoPE on Q and K at position ctx_len[b] + i; Q scaled and stored
+// as a hi/lo pair, K and V in storage type.  grid: one workgroup per head of
+// the concatenated [Q | K | V] output.
+template <typename S>
+__global__ void __launch_bounds__(256) finish_qkv_kernel(const FinishArgs f) {
+  extern __shared__ __align__(16) float s_r[];
+  rows_rinv(f, s_r);
+  const int D = f.head_dim, half = D >> 1;
+  const int Nq = f.n_q_heads * D, Nk = f.n_kv_heads * D;
+  const int n0 = blockIdx.x * D;
+  bf16_t* qh = reinterpret_cast<bf16_t*>(f.out_hi);
+  bf16_t* ql = reinterpret_cast<bf16_t*>(f.out_lo);
+  S* ko = reinterpret_cast<S*>(f.kb_out);
+  S* vo = reinterpret_cast<S*>(f.vb_out);
+  for (int e = threadIdx.x; e < f.M * half; e += blockDim.x) {
+    const int m = e / half, d = e - m * half;
+    const int n = n0 + d;
+    const float r = s_r[m];
+    float lo = ksum(f, m, n) * r, hi = ksum(f, m, n + half) * r;
+    const int pos = f.ctx_len[m / f.block] + m % f.block;
+    if (n < Nq) {
+      rope_pair(lo, hi, pos, d, D, f.rope_theta);
+      split_store(qh, ql, (size_t)m * Nq + n, lo * f.q_scale);
+      split_store(qh, ql, (size_t)m * Nq + n + half, hi * f.q_scale);
+    } else if (n < Nq + Nk) {
+      const int nn = n - Nq;
+      rope_pair(lo, hi, pos, d, D, f.rope_theta);
+      store_from_f32<S>(ko + (size_t)m * Nk + nn, lo);
+      store_from_f32<S>(ko + (size_t)m * Nk + nn + half, hi);
+    } else {
+      const int nn = n - Nq - Nk;
+      store_from_f32<S>(vo + (size_t)m * Nk + nn, lo);
+      store_from_f32<S>(vo + (size_t)m * Nk + nn + half, hi);
+    }
+  }
+}
+
+// Context K/V of every layer (segments K^0, V^0, K^1, V^1, ...): RoPE on K at
+// position ctx_len[b] + i, scatter to cache row ctx_len[b] + i.  A sequence
+// whose rows would pass max_ctx is skipped and flagged.  grid: one workgroup
+// per head of the concatenated output.
+template <typename S>
+__global__ void __launch_bounds__(256) finish_kv_kernel(const FinishArgs f) {
+  extern __shared__ __align__(16) float s_r[];
+  rows_rinv(f, s_r);
+  const int D = f.head_dim, half = D >> 1, Hkv = f.n_kv_heads;
+  const int seg_rows = Hkv * D;
+  const int n0 = blockIdx.x * D;
+  const int seg = n0 / seg_rows, head = (n0 - seg * seg_rows) / D;
+  for (int e = threadIdx.x; e < f.M * half; e += blockDim.x) {
+    const int m = e / half, d = e - m * half;
+    const int b = m / f.block, i = m - b * f.block;
+    const int t0 = f.ctx_len[b];
+    if (t0 < 0 || t0 + f.block > f.max_ctx) {
+      if (d == 0) atomicOr(f.err, 1u);
+      continue;
+    }
+    const int pos = t0 + i;
+    const float r = s_r[m];
+    float lo = ksum(f, m, n0 + d) * r, hi = ksum(f, m, n0 + d + half) * r;
+    if ((seg & 1) == 0) rope_pair(lo, hi, pos, d, D, f.rope_theta);
+    S* dst = reinterpret_cast<S*>(f.kv_cache[seg]) + (((size_t)b * f.max_ctx + pos) * Hkv + head) * D + d;
+    store_from_f32<S>(dst, lo);
+    store_from_f32<S>(dst + half, hi);
+  }
+}
+
+// ------------------------------------------------------------------ launchers
+int gemm_as_ksl(int M, int K, bool lo, bool argmax) {
+  const int MR = M <= 16 ? 1 : (M <= 32 ? 2 : 0);
+  if (MR == 0) return 0;
+  const int narr = lo ? 2 : 1;
+  const int step = 256;  // whole register stages: 8 k-steps (MR = 1) or two of 4 (MR = 2)
+  auto lds = [&](int ksl) { return (size_t)narr * 16 * MR * (ksl + 8) * 2; };
+  if (K % step) return 0;
+  if (argmax) return lds(K) <= kGemmAsMaxLds ? K : 0;
+  if (lds(K) <= kGemmAsSliceLds) return K;
+  for (int ksl = 2048; ksl >= step; ksl >>= 1)
+    if (K % ksl == 0 && lds(ksl) <= kGemmAsSliceLds) return ksl;
+  return 0;
+}
+
+size_t gemm_as_lds(int M, int ksl, bool lo) {
+  const int MR = M <= 16 ? 1 : 2;
+  return (size_t)(lo ? 2 : 1) * 16 * MR * (ksl + 8) * 2;
+}
+
+size_t gemm_ws_lds(int MR, int WN, int WK) { return (size_t)WK * 16 * MR * 16 * WN * sizeof(float); }
+int gemm_ws_max_threads(int MR) { return MR <= 4 ? 512 : 256; }
+
+template <typename Kern>
+static void allow_lds(Kern kernel, size_t bytes) {
+  if (bytes > 64 * 1024)
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)bytes);
+}
+
+template <typename S, int MR, int SRC, bool LO, int OUT>
+static hipError_t launch_as(const GemmArgs& a, const GemmLaunch& l, hipStream_t st) {
+  auto k = gemm_as_kernel<S, MR, SRC, LO, OUT>;
+  allow_lds(k, l.lds);
+  hipLaunchKernelGGL(k, l.grid, dim3(l.threads), l.lds, st, a);
+  return hipGetLastError();
+}
+template <typename S, int MR, int SRC, bool LO, int OUT>
+static hipError_t launch_ws(const GemmArgs& a, const GemmLaunch& l, hipStream_t st) {
+  hipLaunchKernelGGL((gemm_ws_kernel<S, MR, SRC, LO, OUT>), l.grid, dim3(l.threads), l.lds, st, a);
   return hipGetLastError();
 }
 
-int gemm_max_threads(int storage, ProKind pro, int MR) {
-  return gemm_max_threads_for(pro == PRO_SPLIT || storage == ST_F32, MR);
-}
-
-size_t gemm_lds_bytes(EpiKind epi, int MR, int WN, int WK) {
-  const size_t MT = 16 * MR, NT = 16 * WN;
-  size_t b = (WK * MT * NT + MT) * sizeof(float);
-  if (epi == EPI_RESID) b += MT * NT * sizeof(float);
-  return b;
-}
-
-template <typename S, int MR, int PRO, int EPI>
-static hipError_t launch_one(const GemmArgs& a, const GemmLaunch& l, hipStream_t stream) {
-  dim3 grid(l.ntiles, l.mtiles), block(l.threads);
-  hipLaunchKernelGGL((gemm_ws_kernel<S, MR, PRO, EPI>), grid, block, l.lds, stream, a);
-  return hipGetLastError();
-}
-
-template <typename S, int PRO, int EPI>
-static hipError_t launch_mr(const GemmArgs& a, const GemmLaunch& l, hipStream_t stream) {
+template <typename S, int SRC, bool LO, int OUT>
+static hipError_t dispatch_mr(const GemmArgs& a, const GemmLaunch& l, hipStream_t st) {
+  if (l.kind == GEMM_AS) {
+    if (l.MR == 1) return launch_as<S, 1, SRC, LO, OUT>(a, l, st);
+    if (l.MR == 2) return launch_as<S, 2, SRC, LO, OUT>(a, l, st);
+    return hipErrorInvalidValue;
+  }
   switch (l.MR) {
-    case 1: return launch_one<S, 1, PRO, EPI>(a, l, stream);
-    case 2: return launch_one<S, 2, PRO, EPI>(a, l, stream);
-    case 4: return launch_one<S, 4, PRO, EPI>(a, l, stream);
-    case 8: return launch_one<S, 8, PRO, EPI>(a, l, stream);
+    case 1: return launch_ws<S, 1, SRC, LO, OUT>(a, l, st);
+    case 2: return launch_ws<S, 2, SRC, LO, OUT>(a, l, st);
+    case 4: return launch_ws<S, 4, SRC, LO, OUT>(a, l, st);
+    case 8: return launch_ws<S, 8, SRC, LO, OUT>(a, l, st);
   }
   return hipErrorInvalidValue;
 }
 
 template <typename S>
-static hipError_t launch_s(ProKind pro, EpiKind epi, const GemmArgs& a, const GemmLaunch& l, hipStream_t stream) {
-  if (pro == PRO_CONCAT && epi == EPI_F32_SSQ) return launch_mr<S, PRO_CONCAT, EPI_F32_SSQ>(a, l, stream);
-  if (pro == PRO_SPLIT && epi == EPI_KV) return launch_mr<S, PRO_SPLIT, EPI_KV>(a, l, stream);
-  if (pro == PRO_SPLIT && epi == EPI_QKV) return launch_mr<S, PRO_SPLIT, EPI_QKV>(a, l, stream);
-  if (pro == PRO_SPLIT && epi == EPI_RESID) return launch_mr<S, PRO_SPLIT, EPI_RESID>(a, l, stream);
-  if (pro == PRO_SPLIT && epi == EPI_SWIGLU) return launch_mr<S, PRO_SPLIT, EPI_SWIGLU>(a, l, stream);
-  if (pro == PRO_SPLIT && epi == EPI_ARGMAX) return launch_mr<S, PRO_SPLIT, EPI_ARGMAX>(a, l, stream);
-  return hipErrorInvalidValue;
+static hipError_t dispatch_s(const GemmArgs& a, const GemmLaunch& l, hipStream_t st) {
+  if (l.src == SRC_CONCAT) {
+    if (l.out != OUT_PARTIAL) return hipErrorInvalidValue;
+    // fp32 sources are split on the fly; bf16 sources are exact
+    if constexpr (sizeof(S) == 4) return dispatch_mr<S, SRC_CONCAT, true, OUT_PARTIAL>(a, l, st);
+    else return dispatch_mr<S, SRC_CONCAT, false, OUT_PARTIAL>(a, l, st);
+  }
+  if (l.out == OUT_ARGMAX)
+    return l.lo ? dispatch_mr<S, SRC_SPLIT, true, OUT_ARGMAX>(a, l, st)
+                : dispatch_mr<S, SRC_SPLIT, false, OUT_ARGMAX>(a, l, st);
+  return l.lo ? dispatch_mr<S, SRC_SPLIT, true, OUT_PARTIAL>(a, l, st)
+              : dispatch_mr<S, SRC_SPLIT, false, OUT_PARTIAL>(a, l, st);
 }
 
-hipError_t launch_gemm(int storage, ProKind pro, EpiKind epi, const GemmArgs& a, const GemmLaunch& l,
-                       hipStream_t stream) {
-  if (storage == ST_BF16) return launch_s<bf16_t>(pro, epi, a, l, stream);
-  return launch_s<float>(pro, epi, a, l, stream);
+hipError_t launch_gemm(int storage, const GemmArgs& a, const GemmLaunch& l, hipStream_t stream) {
+  if (storage == ST_BF16) return dispatch_s<bf16_t>(a, l, stream);
+  return dispatch_s<float>(a, l, stream);
+}
+
+hipError_t launch_argmax_reduce(const uint64_t* part, int ntiles, int ld, int M, int32_t* ids, hipStream_t stream) {
+  hipLaunchKernelGGL(argmax_reduce_kernel, dim3(M), dim3(256), 0, stream, part, ntiles, ld, ids);
+  return hipGetLastError();
+}
+
+template <typename S>
+static hipError_t launch_finish_s(FinishKind kind, const FinishArgs& f, hipStream_t st) {
+  const size_t rl = (size_t)f.M * sizeof(float);
+  switch (kind) {
+    case FIN_ROWTILE: {
+      const size_t l = (size_t)2 * f.M * 16 * sizeof(float);
+      auto k = finish_rowtile_kernel<S>;
+      allow_lds(k, l);
+      hipLaunchKernelGGL(k, dim3(f.N / 16), dim3(256), l, st, f);
+      break;
+    }
+    case FIN_SWIGLU:
+      hipLaunchKernelGGL(finish_swiglu_kernel, dim3(f.N / 32), dim3(256), rl, st, f);
+      break;
+    case FIN_QKV:
+      hipLaunchKernelGGL(finish_qkv_kernel<S>, dim3(f.N / f.head_dim), dim3(256), rl, st, f);
+      break;
+    case FIN_KV:
+      hipLaunchKernelGGL(finish_kv_kernel<S>, dim3(f.N / f.head_dim), dim3(256), rl, st, f);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_finish(int storage, FinishKind kind, const FinishArgs& f, hipStream_t stream) {
+  if (storage == ST_BF16) return launch_finish_s<bf16_t>(kind, f, stream);
+  return launch_finish_s<float>(kind, f, stream);
 }
 
 }  // namespace dfl

@@ -11,83 +11,103 @@ namespace dfl {
 enum StorageType { ST_F32 = 0, ST_BF16 = 1 };
 
 // ------------------------------------------------------------------ GEMM
-// Y[M, N] = A[M, K] . W[N, K]^T with a fused prologue (how the bf16 A operand
-// is formed) and epilogue (what is done with the fp32 result tile).
-enum ProKind {
-  PRO_SPLIT = 0,   // A = a_hi + a_lo, two bf16 arrays [M, lda]; with ssq_in set, result
-                   //   rows are scaled by rinv[m] = 1/sqrt(sum_p ssq[p][m] / K + eps)
-  PRO_CONCAT = 1   // A: concat of n_src arrays [M, src_width] of storage type S
+// Y[M, N] = A[M, K] . W[N, K]^T.  The N axis concatenates weight segments and
+// is cut into 16-row tiles.  The main kernel writes fp32 partial tiles
+// part[k-slice][tile][m][16] (OUT_PARTIAL) that a finish kernel sums and
+// post-processes, or per-tile argmax keys (OUT_ARGMAX, one k-slice).
+enum SrcKind {
+  SRC_SPLIT = 0,   // A = a_hi (+ a_lo): bf16 arrays [M, lda]
+  SRC_CONCAT = 1   // A: concat of n_src arrays [M, src_width] of the storage type
 };
-enum EpiKind {
-  EPI_F32_SSQ = 0,  // out fp32 [M, ldo] = Y; ssq_out[tile][m] = sum over the tile's columns of Y^2
-  EPI_KV = 1,       // context K/V: RoPE on K segments, scatter to the per-layer caches
-  EPI_QKV = 2,      // block Q/K/V: RoPE on Q and K, Q scaled, store Q (bf16), K/V (S)
-  EPI_RESID = 3,    // x[m, n] += Y (+ width-3 block conv); ssq_out of the new x
-  EPI_SWIGLU = 4,   // act[m, f] = bf16(silu(Y_gate) * Y_up)
-  EPI_ARGMAX = 5    // per row: running (max, index) over the vocabulary -> draft ids
-};
+enum OutKind { OUT_PARTIAL = 0, OUT_ARGMAX = 1 };
+enum GemmKind { GEMM_AS = 0, GEMM_WS = 1 };
 
 constexpr int kMaxSeg = 16;
+constexpr size_t kGemmAsSliceLds = 68 * 1024;  // activation slice of a split-K workgroup (2 per CU)
+constexpr size_t kGemmAsMaxLds = 150 * 1024;   // whole-K activation (LM head, 1 workgroup per CU)
 
 struct GemmArgs {
   int M, N, K;
-  int WN, WK;  // waves per workgroup along N (16 rows each) and along K
-  int P;       // pair stride in rows (0: each tile is NT contiguous rows)
-  int kw;      // K per wave
   // W row segments: global row n in [seg_start[s], seg_start[s+1]) is row
   // n - seg_start[s] of matrix seg_ptr[s] (all with row length K).
   int nseg;
   const void* seg_ptr[kMaxSeg];
   int seg_start[kMaxSeg + 1];
-
-  // prologue
-  const void* a_hi;  // PRO_SPLIT bf16 [M, lda]
+  // activations
+  const void* a_hi;
   const void* a_lo;
   int lda;
-  const void* src[8];  // PRO_CONCAT sources, each [M, src_width]
+  const void* src[8];
   int n_src, src_width;
-  const float* ssq_in;  // PRO_SPLIT row scale: partial sums of squares [nparts][ld_ssq] or null
+  // launch geometry (filled by the planner)
+  int ksl, tpw;   // GEMM_AS: k-slice length, tiles per workgroup
+  int WN, WK, kw;  // GEMM_WS: waves along N and K, K per wave
+  // outputs
+  float* part;          // OUT_PARTIAL
+  uint64_t* best_part;  // OUT_ARGMAX [argmax tiles][ld_best]
+  int ld_best;
+  float* logits_dbg;    // OUT_ARGMAX nullable [M, N], row-scaled by rinv
+  const float* ssq_in;  // row scale of logits_dbg
   int ssq_nparts, ld_ssq;
   float eps;
-
-  // epilogue
-  float* out_f32;   // EPI_F32_SSQ output [M, N]
-  void* out_hi;     // bf16 hi/lo outputs: EPI_F32_SSQ / EPI_RESID (value * gnext), [M, N];
-  void* out_lo;     //   EPI_SWIGLU [M, N/2]; EPI_QKV query [M, Hq*D] (RoPE, scaled)
-  const void* gnext;  // EPI_F32_SSQ / EPI_RESID: gain of the consumer's RMSNorm [N] (storage type)
-  float* ssq_out;   // EPI_F32_SSQ / EPI_RESID: [ntiles][ld_ssq]
-  float* x;         // EPI_RESID residual stream fp32 [M, N]
-  const void* conv;  // EPI_RESID: [N, 3] taps (storage type) or null
-  int block;         // rows per sequence (Bs for the draft, t_new for fuse)
-  const int32_t* ctx_len;
-  int max_ctx;
-  float rope_theta;
-  int head_dim;
-  int n_q_heads, n_kv_heads;
-  float q_scale;
-  void* kb_out;  // EPI_QKV storage type [M, Hkv*D]
-  void* vb_out;
-  void* kv_cache[kMaxSeg];  // EPI_KV: one cache per segment (K^0, V^0, K^1, V^1, ...)
-  uint32_t* err;
-  uint64_t* best_part;  // EPI_ARGMAX per-tile packed (value, index) keys [ntiles][ld_best]
-  int ld_best;
-  float* logits_dbg;    // EPI_ARGMAX nullable [M, N]
 };
 
 struct GemmLaunch {
-  int MR;       // 16-row m-subtiles per workgroup
-  int mtiles;   // grid.y
-  int ntiles;   // grid.x
-  int threads;  // 64 * WN * WK
-  size_t lds;   // dynamic LDS bytes
+  int kind;   // GemmKind
+  int src, out, lo;
+  int MR;
+  dim3 grid;
+  int threads;
+  size_t lds;
+  int KS;            // k-slices written (OUT_PARTIAL)
+  int argmax_tiles;  // OUT_ARGMAX: tiles per row in best_part
 };
 
-hipError_t launch_gemm(int storage, ProKind pro, EpiKind epi, const GemmArgs& a, const GemmLaunch& l,
-                       hipStream_t stream);
-size_t gemm_lds_bytes(EpiKind epi, int MR, int WN, int WK);
+hipError_t launch_gemm(int storage, const GemmArgs& a, const GemmLaunch& l, hipStream_t stream);
+// k-slice length gemm_as can use for (M, K) (0: gemm_as does not fit).
+int gemm_as_ksl(int M, int K, bool lo, bool argmax);
+size_t gemm_as_lds(int M, int ksl, bool lo);
+size_t gemm_ws_lds(int MR, int WN, int WK);
+int gemm_ws_max_threads(int MR);
 // ids[m] = index of the largest key over part[t][m], t < ntiles.
 hipError_t launch_argmax_reduce(const uint64_t* part, int ntiles, int ld, int M, int32_t* ids, hipStream_t stream);
-int gemm_max_threads(int storage, ProKind pro, int MR);
+
+// ------------------------------------------------------------------ GEMM finish
+enum FinishKind {
+  FIN_ROWTILE = 0,  // y = sum (+ x residual, + block conv): x / out_f32, hi/lo of y*gnext, ssq per tile
+  FIN_SWIGLU = 1,   // act = silu(r*gate) * (r*up) as hi/lo
+  FIN_QKV = 2,      // RoPE(q, k), q scaled as hi/lo, k and v in storage type
+  FIN_KV = 3        // context K/V with RoPE on K into the per-layer caches
+};
+
+struct FinishArgs {
+  const float* part;
+  int KS, ntiles, M, N;
+  // row scale rinv[m] = 1/sqrt(sum_p ssq_in[p][m] / kdim + eps); null: none
+  const float* ssq_in;
+  int ssq_nparts, ld_ssq, kdim;
+  float eps;
+  // FIN_ROWTILE
+  float* x;           // residual stream [M, N] (read and written) or null
+  float* out_f32;     // plain output [M, N] or null
+  const void* conv;   // [N, 3] taps (storage type) or null
+  const void* gnext;  // [N] gain of the consumer's RMSNorm (storage type)
+  float* ssq_out;     // [N/16][ld_ssq]
+  void* out_hi;       // FIN_ROWTILE [M, N]; FIN_SWIGLU [M, N/2]; FIN_QKV query [M, Hq*D]
+  void* out_lo;       //   (null: hi only)
+  int block;          // rows per sequence
+  // FIN_QKV / FIN_KV
+  const int32_t* ctx_len;
+  int max_ctx;
+  float rope_theta;
+  int head_dim, n_q_heads, n_kv_heads;
+  float q_scale;
+  void* kb_out;  // FIN_QKV [M, Hkv*D] storage type
+  void* vb_out;
+  void* kv_cache[kMaxSeg];  // FIN_KV: one per segment
+  uint32_t* err;
+};
+hipError_t launch_finish(int storage, FinishKind kind, const FinishArgs& f, hipStream_t stream);
 
 // ------------------------------------------------------------------ attention
 struct AttnArgs {
