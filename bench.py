@@ -46,6 +46,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--stage", default="lmhead", help="kernel stage timed with HIP events for the roofline")
     ap.add_argument("--profile-stages", action="store_true", help="also time every stage (perturbs the step)")
+    ap.add_argument("--eager", action="store_true",
+                    help="launch the step's kernels one by one instead of replaying a captured HIP graph")
     return ap.parse_args()
 
 
@@ -163,7 +165,14 @@ class Workbench:
         self.dr.draft_block(self.block_ids, self.draft_ids)
 
 
-def time_workload(wl, steps, warmup, stage, profile_stages=False):
+def time_workload(wl, steps, warmup, stage, profile_stages=False, graph=True):
+    """Time `steps` steps; returns (workbench, ms per step, {stage: (mean launch ms, launches)}).
+
+    With graph=True the step (every library call of it) is captured once into
+    a HIP graph and the timed steps are graph replays.  Kernel durations do not
+    depend on how the kernels were launched, so the stage launch times are then
+    taken from HIP events of an eager pass of the same number of steps run
+    right after (the library records no events inside a captured graph)."""
     import torch
     from block_diffusion_drafting_ctx_amd import _abi
 
@@ -175,16 +184,35 @@ def time_workload(wl, steps, warmup, stage, profile_stages=False):
     if err:
         raise RuntimeError(f"device error word {err:#x}")
     stages = list(_abi.STAGES) if profile_stages else [stage]
+
+    def timed(run):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(steps):
+            run()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    if graph:
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(g, stream=side):
+                wb.step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        for _ in range(max(2, warmup)):
+            g.replay()
+        ms = timed(g.replay)
+        wb.graph = g
     for s in stages:
         _abi.dflash_stage_timing(wb.dr.ctx, s, True)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record()
-    for _ in range(steps):
-        wb.step()
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / steps
+    ms_eager = timed(wb.step)
+    if not graph:
+        ms = ms_eager
     per_stage = {}
     for s in stages:
         mean_ms, n = _abi.dflash_stage_time(wb.dr.ctx, s)
@@ -194,6 +222,7 @@ def time_workload(wl, steps, warmup, stage, profile_stages=False):
     n_acc = wb.n_acc.cpu().numpy()
     if not np.array_equal(n_acc, wb.accept):
         raise RuntimeError(f"planted acceptance not reproduced: {n_acc} vs {wb.accept}")
+    wb.ms_eager = ms_eager
     return wb, ms, per_stage
 
 
@@ -239,7 +268,8 @@ def main():
     if not torch.cuda.is_available():
         raise RuntimeError("bench.py needs a GPU")
     wl = gen.WORKLOADS[args.workload]
-    wb, ms, per_stage = time_workload(wl, args.steps, args.warmup, args.stage, args.profile_stages)
+    wb, ms, per_stage = time_workload(wl, args.steps, args.warmup, args.stage, args.profile_stages,
+                                      graph=not args.eager)
     B = wl.batch
     value = B * wl.block / (ms * 1e-3)
     tb, tf = step_totals(wl, B, wb.ctx_lens)
@@ -252,7 +282,8 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": wl.storage,
         "data": "synthetic (seeded random-init draft weights and inputs)",
         "config": {"workload": wl.name, "batch": B, "block": wl.block, "context": int(np.max(wb.ctx_lens)),
-                   "layers": wl.n_layers, "hidden": wl.hidden, "vocab": wl.vocab},
+                   "layers": wl.n_layers, "hidden": wl.hidden, "vocab": wl.vocab,
+                   "launch": "eager" if args.eager else "hip-graph replay of the whole step"},
         "roofline": {"bound": "hbm", "kernel": args.stage, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic_from_profiles(args.stage, wl.name),
@@ -262,6 +293,7 @@ def main():
                           "hbm_frac": round(tb / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9), 4),
                           "mfma_frac": round(tf / (ms * 1e-3) / (BF16_PEAK_TFLOPS * 1e12), 4)},
     }
+    out["ms_per_step_eager"] = round(wb.ms_eager, 4)
     if args.profile_stages:
         out["stages_ms"] = {k: round(v[0], 5) for k, v in per_stage.items()}
     sec = []
@@ -269,7 +301,7 @@ def main():
         wl2 = gen.WORKLOADS[name]
         del wb
         torch.cuda.empty_cache()
-        wb2, ms2, ps2 = time_workload(wl2, max(5, args.steps // 2), args.warmup, args.stage)
+        wb2, ms2, ps2 = time_workload(wl2, max(5, args.steps // 2), args.warmup, args.stage, graph=not args.eager)
         tb2, tf2 = step_totals(wl2, wl2.batch, wb2.ctx_lens)
         sf2 = stage_flops(wl2, wl2.batch, wb2.ctx_lens)
         m2 = ps2[args.stage][0]

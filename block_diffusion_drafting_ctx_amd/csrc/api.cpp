@@ -218,9 +218,13 @@ struct StageScope {
   int stage;
   hipStream_t s;
   size_t slot = (size_t)-1;
+  // Stage events are host-timed records; under stream capture (where a plain
+  // record would only be a dependency marker) nothing is recorded.
   StageScope(dflash_ctx* c_, int stage_, hipStream_t s_) : c(c_), stage(stage_), s(s_) {
     EventPool& p = c->timing[stage];
     if (p.enabled && p.used < p.begin.size()) {
+      hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+      if (hipStreamIsCapturing(s, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return;
       slot = p.used++;
       (void)hipEventRecord(p.begin[slot], s);
     }
