@@ -31,15 +31,15 @@ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 constexpr int kMaxNd = 64;
 constexpr int kVerifyChunk = 16384;  // vocab entries per workgroup of the verify argmax
 constexpr int kAttnTargetWgs = 512;  // attention workgroups to aim for (two per compute unit)
-constexpr int kAttnMinCw = 128;      // fewest keys per attention split
+constexpr int kAttnStage = 128;      // keys per attention LDS stage (splits are whole stages)
 
 // Keys per attention split for a batch.
 int attn_cw(const dflash_config& c, int batch) {
   const int total = c.max_ctx + c.block;
   const int want = std::max(1, (kAttnTargetWgs + batch * c.n_kv_heads - 1) / (batch * c.n_kv_heads));
   int cw = (total + want - 1) / want;
-  cw = ((cw + 63) / 64) * 64;
-  return std::max(cw, kAttnMinCw);
+  cw = ((cw + kAttnStage - 1) / kAttnStage) * kAttnStage;
+  return std::max(cw, kAttnStage);
 }
 int attn_splits(const dflash_config& c, int cw) { return (c.max_ctx + c.block + cw - 1) / cw; }
 
@@ -124,10 +124,10 @@ size_t partial_floats(int storage, int src, bool lo, int Mmax, int N, int K) {
 
 struct WsLayout {
   size_t err, stats;
-  size_t x, ssq, y, xs_hi, xs_lo, q_hi, q_lo, kb, vb, o_hi, o_lo, act_hi, act_lo, part, lm_best, ver_best, part_o,
-      part_ml;
+  size_t x, ssq, rinv, y, xs_hi, xs_lo, q_hi, q_lo, kb, vb, o_hi, o_lo, act_hi, act_lo, part, lm_best, ver_best,
+      part_o, part_ml, rope;
   size_t total;
-  int md, mf, mmax, ssq_parts, attn_max_wgs_rows, ver_chunks;
+  int md, mf, mmax, ssq_parts, attn_max_wgs_rows, ver_chunks, rope_rows;
 };
 
 WsLayout layout(const dflash_config& c) {
@@ -161,6 +161,7 @@ WsLayout layout(const dflash_config& c) {
   L.stats = take(3 * 8);
   L.x = take((size_t)L.md * H * 4);
   L.ssq = take((size_t)L.ssq_parts * L.mmax * 4);
+  L.rinv = take((size_t)L.mmax * 4);
   L.y = take((size_t)L.mf * H * 4);
   L.xs_hi = take((size_t)L.mmax * H * 2);
   L.xs_lo = take((size_t)L.mmax * H * 2);
@@ -178,6 +179,9 @@ WsLayout layout(const dflash_config& c) {
   L.ver_best = take((size_t)c.max_batch * (kMaxNd + 1) * L.ver_chunks * 8);
   L.part_o = take((size_t)attn_rows * c.n_kv_heads * QR * D * 4);
   L.part_ml = take((size_t)attn_rows * c.n_kv_heads * QR * 2 * 4);
+  // RoPE positions reach max_ctx + rows per sequence - 1 (block rows, or fused rows)
+  L.rope_rows = c.max_ctx + std::max(c.block, c.max_fuse_rows);
+  L.rope = take((size_t)L.rope_rows * (D / 2) * 8);
   L.total = off;
   return L;
 }
@@ -336,6 +340,8 @@ dflash_status dflash_create(const dflash_config* cfg, const dflash_weights* w, v
   c->kv_v.assign(kv_v, kv_v + nl);
   c->ctx_len = ctx_len;
   hipError_t e = hipMemset(workspace, 0, L.total);
+  if (e == hipSuccess)
+    e = launch_rope_table(c->at<float2>(L.rope), L.rope_rows, cfg->head_dim, cfg->rope_theta, nullptr);
   if (e == hipSuccess) e = hipDeviceSynchronize();
   if (e != hipSuccess) {
     delete c;
@@ -397,17 +403,18 @@ dflash_status dflash_fuse_ctx(dflash_ctx* c, int32_t batch, const void* const* h
     a.seg_start[a.nseg] = nkv;
     a.a_hi = c->at<void>(L.xs_hi);
     a.lda = H;
+    a.ssq_in = c->at<float>(L.ssq);
+    a.ssq_nparts = H / 16;
+    a.ld_ssq = L.mmax;
+    a.eps = cf.rms_eps;
+    a.rinv_out = c->at<float>(L.rinv);
     // hi only: the context K/V are storage-rounded anyway
     if ((st = gemm_partial(c, a, SRC_SPLIT, false, M, nkv, H, &l, s))) return st;
-    f.ssq_in = c->at<float>(L.ssq);
-    f.ssq_nparts = H / 16;
-    f.ld_ssq = L.mmax;
-    f.kdim = H;
-    f.eps = cf.rms_eps;
+    f.rinv = c->at<float>(L.rinv);
+    f.rope = c->at<float2>(L.rope);
     f.block = t_new;
     f.ctx_len = c->ctx_len;
     f.max_ctx = cf.max_ctx;
-    f.rope_theta = cf.rope_theta;
     f.head_dim = D;
     f.n_q_heads = cf.n_q_heads;
     f.n_kv_heads = cf.n_kv_heads;
@@ -485,12 +492,16 @@ dflash_status dflash_draft_block(dflash_ctx* c, int32_t batch, const int32_t* bl
   int ssq_parts = 1;
   const int cw = attn_cw(cf, batch);
   const int splits = attn_splits(cf, cw);
-  auto norm = [&](FinishArgs& f) {
-    f.ssq_in = ssq;
-    f.ssq_nparts = ssq_parts;
-    f.ld_ssq = L.mmax;
-    f.kdim = H;
-    f.eps = cf.rms_eps;
+  float* rinv = c->at<float>(L.rinv);
+  // RMSNorm of the product's activation rows: its main kernel turns the
+  // partial sums of squares into row scales for the finish kernel
+  auto norm = [&](GemmArgs& a, FinishArgs& f) {
+    a.ssq_in = ssq;
+    a.ssq_nparts = ssq_parts;
+    a.ld_ssq = L.mmax;
+    a.eps = cf.rms_eps;
+    a.rinv_out = rinv;
+    f.rinv = rinv;
   };
   for (int l = 0; l < cf.n_layers; ++l) {
     {  // RMSNorm -> Q/K/V, RoPE
@@ -501,12 +512,13 @@ dflash_status dflash_draft_block(dflash_ctx* c, int32_t batch, const int32_t* bl
       a.a_hi = xs_hi;
       a.a_lo = xs_lo;
       a.lda = H;
-      if ((st = gemm_partial(c, a, SRC_SPLIT, true, M, Nq + 2 * Nk, H, &gl, s))) return st;
       FinishArgs f{};
-      norm(f);
+      norm(a, f);
+      if ((st = gemm_partial(c, a, SRC_SPLIT, true, M, Nq + 2 * Nk, H, &gl, s))) return st;
+      f.rope = c->at<float2>(L.rope);
+      f.max_ctx = cf.max_ctx;
       f.block = cf.block;
       f.ctx_len = c->ctx_len;
-      f.rope_theta = cf.rope_theta;
       f.head_dim = D;
       f.n_q_heads = cf.n_q_heads;
       f.n_kv_heads = cf.n_kv_heads;
@@ -570,9 +582,9 @@ dflash_status dflash_draft_block(dflash_ctx* c, int32_t batch, const int32_t* bl
       a.a_hi = xs_hi;
       a.a_lo = xs_lo;
       a.lda = H;
-      if ((st = gemm_partial(c, a, SRC_SPLIT, true, M, 2 * F, H, &gl, s))) return st;
       FinishArgs f{};
-      norm(f);
+      norm(a, f);
+      if ((st = gemm_partial(c, a, SRC_SPLIT, true, M, 2 * F, H, &gl, s))) return st;
       f.out_hi = c->at<void>(L.act_hi);
       f.out_lo = c->at<void>(L.act_lo);
       if ((st = finish(c, FIN_SWIGLU, f, gl, M, 2 * F, s))) return st;

@@ -1,34 +1,46 @@
 // Non-causal grouped-query attention of a drafted block over
 // [cached context ; the block itself], split over the key axis.
 //
-// One workgroup = (sequence b, KV head, key split).  Its query rows are the
-// G query heads of that KV head times the Bs block rows (QR = G*Bs rows,
-// one 16-row tile per compute wave), so every context K/V byte is read from
-// HBM once per step.  Keys stream through LDS in chunks of 64, double
-// buffered: the next chunk's K/V loads are in flight (in registers) while the
-// current chunk is consumed, with one barrier per chunk.  Scores are formed
-// transposed (S^T = K Q^T, 16x16x32 MFMA) so that each lane owns one query
-// row: the online-softmax max and scale are per lane, and the probabilities
-// stay in registers and feed O^T = V^T P^T directly as the B operand (V is
-// stored transposed in LDS).  Queries and probabilities enter the bf16
+// One workgroup = (sequence b, KV head, key split) with 8 waves.  Its query
+// rows are the G query heads of that KV head times the Bs block rows
+// (QR = G*Bs rows, 16-row tiles); the waves are (query tile, key group)
+// pairs, so with four query tiles two groups of four waves each take half of
+// every 128-key stage and are merged through LDS at the end.  Every context
+// K/V byte is read from HBM once per step, and all of a stage's K/V loads are
+// issued together (one round of memory latency per stage).
+//
+// Scores are formed transposed (S^T = K Q^T, 16x16x32 MFMA) so that each lane
+// owns one query row: the online-softmax max and scale are per lane, and the
+// probabilities stay in registers and feed O^T = V^T P^T directly as the B
+// operand.  V is stored transposed in LDS as key pairs (one dword = two keys
+// of one dimension) with an XOR swizzle of the key-pair column by the
+// dimension, which keeps the transposing stores at two-way bank conflicts and
+// the operand reads conflict-free.  Queries and probabilities enter the bf16
 // products as hi/lo pairs (two MFMAs each), keys and values as stored.
 // Splits write unnormalised partials (O, running max, running sum) that a
-// second kernel merges in split order (deterministic; no cross-workgroup
+// second kernel merges in a fixed order (deterministic; no cross-workgroup
 // atomics, which cost tens of nanoseconds each on this chip).
 #include "common.h"
 #include "kernels.h"
 
 namespace dfl {
 
-constexpr int kChunk = 64;  // keys per LDS stage
+constexpr int kStage = 128;   // keys per LDS stage
+constexpr int kUnit = 32;     // keys per softmax update / PV product
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
 
 template <int D>
 struct AttnLds {
-  static constexpr int KS = D + 8;       // K row stride (elements)
-  static constexpr int VS = kChunk + 8;  // V^T row stride (elements)
-  bf16_t k[kChunk * KS];
-  bf16_t vt[D * VS];
+  static constexpr int KS = D + 8;        // K row stride (elements)
+  static constexpr int VW = kStage / 2;   // V^T row length in dwords (key pairs)
+  bf16_t k[kStage * KS];
+  uint32_t vt[D * VW];
 };
+
+// Column of key pair kp in V^T row d.  Even, so a pair of key pairs stays
+// adjacent and in order.
+__device__ __forceinline__ int vt_col(int d, int kp) { return kp ^ (((d >> 3) ^ (d & 15)) << 1 & 30); }
 
 __device__ __forceinline__ void split_out(bf16_t* hi, bf16_t* lo, size_t idx, float v) {
   const bf16_t h = f32_to_bf16_bits(v);
@@ -36,42 +48,34 @@ __device__ __forceinline__ void split_out(bf16_t* hi, bf16_t* lo, size_t idx, fl
   lo[idx] = f32_to_bf16_bits(v - bf16_bits_to_f32(h));
 }
 
-// Threads of an attention workgroup: one wave per 16 query rows, at least four
-// (the extra waves only help staging).
-__host__ __device__ inline int attn_threads(int QR) {
-  const int w = (QR + 15) / 16;
-  return 64 * (w < 4 ? 4 : w);
+// Waves per query-tile set and key groups for QT query tiles.
+__host__ __device__ inline int attn_qtp(int QT) { return QT <= 1 ? 1 : QT <= 2 ? 2 : QT <= 4 ? 4 : 8; }
+__host__ __device__ inline int attn_kg(int QT) {
+  const int g = kWaves / attn_qtp(QT);
+  return g > kStage / kUnit ? kStage / kUnit : g;
 }
 
 template <typename S, int D>
-__global__ void __launch_bounds__(512) attention_kernel(const AttnArgs a) {
+__global__ void __launch_bounds__(kThreads) attention_kernel(const AttnArgs a) {
   extern __shared__ __align__(16) unsigned char lds_raw[];
-  AttnLds<D>* lds = reinterpret_cast<AttnLds<D>*>(lds_raw);  // [2]
+  AttnLds<D>& L = *reinterpret_cast<AttnLds<D>*>(lds_raw);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int nthr = blockDim.x;
   const int b = blockIdx.z, kvh = blockIdx.y, sp = blockIdx.x;
   const int G = a.Hq / a.Hkv;
   const int QR = G * a.Bs;
   const int QT = (QR + 15) / 16;
+  const int QTP = attn_qtp(QT), KG = attn_kg(QT);
+  const int UPG = (kStage / kUnit) / KG;  // units per key group
+  const int qt = wave % QTP, kg = wave / QTP;
+  const bool computes = qt < QT && kg < KG;
 
-  // a caller-set length outside [0, max_ctx] is clamped so no access leaves the cache
-  const int T = min(max(a.ctx_len[b], 0), a.max_ctx);
-  const int total = T + a.Bs;
-  const int ns = (total + a.CW - 1) / a.CW;
-  if (sp >= ns) return;
-  const int j0 = sp * a.CW;
-  const int j1 = min(total, j0 + a.CW);
-  const int nchunks = (j1 - j0 + kChunk - 1) / kChunk;
-
-  // ---- this lane's query row
-  const int r = 16 * wave + (lane & 15);
-  const bool computes = wave < QT;
-  const bool qvalid = r < QR;
+  // ---- this lane's query row (loads issued before the context length arrives)
+  const int r = 16 * qt + (lane & 15);
+  const bool qvalid = computes && r < QR;
   const int rr = qvalid ? r : 0;
   const int gq = rr / a.Bs, iq = rr - gq * a.Bs;
-  const int h = kvh * G + gq;
   const int HqD = a.Hq * D;
-  const size_t qoff = (size_t)(b * a.Bs + iq) * HqD + h * D;
+  const size_t qoff = (size_t)(b * a.Bs + iq) * HqD + (kvh * G + gq) * D;
   bf16x8 qf[D / 32], qr[D / 32];  // query = qf + qr (hi/lo pair)
   {
     const bf16_t* qh = reinterpret_cast<const bf16_t*>(a.q_hi) + qoff;
@@ -87,6 +91,15 @@ __global__ void __launch_bounds__(512) attention_kernel(const AttnArgs a) {
     }
   }
 
+  // a caller-set length outside [0, max_ctx] is clamped so no access leaves the cache
+  const int T = min(max(a.ctx_len[b], 0), a.max_ctx);
+  const int total = T + a.Bs;
+  const int ns = (total + a.CW - 1) / a.CW;
+  if (sp >= ns) return;
+  const int j0 = sp * a.CW;
+  const int j1 = min(total, j0 + a.CW);
+  const int nstages = (j1 - j0 + kStage - 1) / kStage;
+
   const S* kc = reinterpret_cast<const S*>(a.kc);
   const S* vc = reinterpret_cast<const S*>(a.vc);
   const S* kb = reinterpret_cast<const S*>(a.kb);
@@ -97,61 +110,62 @@ __global__ void __launch_bounds__(512) attention_kernel(const AttnArgs a) {
                  : blk + (size_t)(b * a.Bs + (j - T)) * row + kvh * D;
   };
 
-  // ---- staging through registers: K as 8-element pieces, V as key pairs
+  // ---- staging through registers.  K: (key, 8-dim piece) items, 16 lanes per
+  // key row.  V: (key pair, piece) items; the two half-waves of 16 lanes take
+  // key pairs 16 apart (the bank pattern the V^T swizzle is built for).
   constexpr int PIECES = D / 8;
-  constexpr int KITEMS = kChunk * PIECES;        // K pieces per chunk
-  constexpr int VITEMS = (kChunk / 2) * PIECES;  // V key-pair pieces per chunk
-  constexpr int KPT = (KITEMS + 255) / 256;      // per thread (workgroups have >= 256 threads)
-  constexpr int VPT = (VITEMS + 255) / 256;
+  constexpr int KITEMS = kStage * PIECES;
+  constexpr int VITEMS = (kStage / 2) * PIECES;
+  constexpr int KPT = KITEMS / kThreads;
+  constexpr int VPT = VITEMS / kThreads;
+  static_assert(KITEMS % kThreads == 0 && VITEMS % kThreads == 0, "stage items must fill the workgroup");
   Raw8 kreg[KPT], vreg[VPT][2];
+  auto v_item = [&](int idx, int& kp, int& p) {
+    p = idx % PIECES;
+    const int h = (idx / PIECES) & 1, rest = idx / (2 * PIECES);
+    kp = (rest & 15) + 16 * h + 32 * (rest >> 4);
+  };
   auto stage_load = [&](int c0) {
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
-      const int idx = tid + i * nthr;
-      if (idx < KITEMS) {
-        const int key = idx / PIECES, p8 = (idx - key * PIECES) * 8;
-        const int j = c0 + key;
-        if (j < j1) load_raw8<S>(kreg[i], key_ptr(kc, kb, j) + p8);
-      }
+      const int idx = tid + i * kThreads;
+      const int key = idx / PIECES, p8 = (idx % PIECES) * 8;
+      const int j = c0 + key;
+      if (j < j1) load_raw8<S>(kreg[i], key_ptr(kc, kb, j) + p8);
     }
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
-      const int idx = tid + i * nthr;
-      if (idx < VITEMS) {
-        const int kp = idx / PIECES, p8 = (idx - kp * PIECES) * 8;
+      int kp, p;
+      v_item(tid + i * kThreads, kp, p);
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const int j = c0 + 2 * kp + t;
-          if (j < j1) load_raw8<S>(vreg[i][t], key_ptr(vc, vb, j) + p8);
-        }
+      for (int t = 0; t < 2; ++t) {
+        const int j = c0 + 2 * kp + t;
+        if (j < j1) load_raw8<S>(vreg[i][t], key_ptr(vc, vb, j) + 8 * p);
       }
     }
   };
-  auto stage_store = [&](AttnLds<D>& L, int c0) {
+  auto stage_store = [&](int c0) {
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
-      const int idx = tid + i * nthr;
-      if (idx < KITEMS) {
-        const int key = idx / PIECES, p8 = (idx - key * PIECES) * 8;
-        const bf16x8 v = c0 + key < j1 ? raw_to_bf16x8<S>(kreg[i]) : bf16x8{};
-        *reinterpret_cast<bf16x8*>(&L.k[key * AttnLds<D>::KS + p8]) = v;
-      }
+      const int idx = tid + i * kThreads;
+      const int key = idx / PIECES, p8 = (idx % PIECES) * 8;
+      const bf16x8 v = c0 + key < j1 ? raw_to_bf16x8<S>(kreg[i]) : bf16x8{};
+      *reinterpret_cast<bf16x8*>(&L.k[key * AttnLds<D>::KS + p8]) = v;
     }
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
-      const int idx = tid + i * nthr;
-      if (idx < VITEMS) {
-        const int kp = idx / PIECES, p8 = (idx - kp * PIECES) * 8;
-        float v0[8], v1[8];
-        raw_to_f32x8<S>(vreg[i][0], v0);
-        raw_to_f32x8<S>(vreg[i][1], v1);
-        const bool ok0 = c0 + 2 * kp < j1, ok1 = c0 + 2 * kp + 1 < j1;
+      int kp, p;
+      v_item(tid + i * kThreads, kp, p);
+      float v0[8], v1[8];
+      raw_to_f32x8<S>(vreg[i][0], v0);
+      raw_to_f32x8<S>(vreg[i][1], v1);
+      const bool ok0 = c0 + 2 * kp < j1, ok1 = c0 + 2 * kp + 1 < j1;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint32_t lo = ok0 ? (uint32_t)f32_to_bf16_bits(v0[e]) : 0u;
-          const uint32_t hi = ok1 ? (uint32_t)f32_to_bf16_bits(v1[e]) : 0u;
-          *reinterpret_cast<uint32_t*>(&L.vt[(p8 + e) * AttnLds<D>::VS + 2 * kp]) = lo | (hi << 16);
-        }
+      for (int e = 0; e < 8; ++e) {
+        const int d = 8 * p + e;
+        const uint32_t lo = ok0 ? (uint32_t)f32_to_bf16_bits(v0[e]) : 0u;
+        const uint32_t hi = ok1 ? (uint32_t)f32_to_bf16_bits(v1[e]) : 0u;
+        L.vt[d * AttnLds<D>::VW + vt_col(d, kp)] = lo | (hi << 16);
       }
     }
   };
@@ -162,79 +176,114 @@ __global__ void __launch_bounds__(512) attention_kernel(const AttnArgs a) {
   for (int ds = 0; ds < D / 16; ++ds) o[ds] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   stage_load(j0);
-  stage_store(lds[0], j0);
+  stage_store(j0);
   __syncthreads();
-  for (int c = 0; c < nchunks; ++c) {
-    const int c0 = j0 + c * kChunk;
-    AttnLds<D>& L = lds[c & 1];
-    if (c + 1 < nchunks) stage_load(c0 + kChunk);  // in flight during this chunk
+  for (int st = 0; st < nstages; ++st) {
+    const int c0 = j0 + st * kStage;
+    if (st + 1 < nstages) stage_load(c0 + kStage);  // in flight during this stage
     if (computes) {
-      // ---- scores S^T[key][q] for 4 key subtiles of 16
-      f32x4 sc[4];
+      for (int uu = 0; uu < UPG; ++uu) {
+        const int u = kg * UPG + uu;  // 32-key unit of the stage
+        const int k0 = c0 + kUnit * u;
+        if (k0 >= j1) break;
+        // ---- scores S^T[key][q] for the unit's two 16-key subtiles
+        f32x4 sc[2];
 #pragma unroll
-      for (int st = 0; st < 4; ++st) {
-        sc[st] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int h = 0; h < 2; ++h) {
+          sc[h] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int s = 0; s < D / 32; ++s) {
-          const bf16x8 kf = *reinterpret_cast<const bf16x8*>(
-              &L.k[(16 * st + (lane & 15)) * AttnLds<D>::KS + 32 * s + 8 * (lane >> 4)]);
-          sc[st] = mfma16x16x32(kf, qf[s], sc[st]);
-          sc[st] = mfma16x16x32(kf, qr[s], sc[st]);
+          for (int s = 0; s < D / 32; ++s) {
+            const bf16x8 kf = *reinterpret_cast<const bf16x8*>(
+                &L.k[(kUnit * u + 16 * h + (lane & 15)) * AttnLds<D>::KS + 32 * s + 8 * (lane >> 4)]);
+            sc[h] = mfma16x16x32(kf, qf[s], sc[h]);
+            sc[h] = mfma16x16x32(kf, qr[s], sc[h]);
+          }
         }
-      }
-      // lane holds keys c0 + 16*st + 4*(lane>>4) + e for query row (lane & 15)
-      float cmax = -INFINITY;
+        // lane holds keys k0 + 16*h + 4*(lane>>4) + e for query row (lane & 15)
+        float cmax = -INFINITY;
 #pragma unroll
-      for (int st = 0; st < 4; ++st)
+        for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int j = c0 + 16 * st + 4 * (lane >> 4) + e;
-          if (j >= j1) sc[st][e] = -INFINITY;
-          cmax = fmaxf(cmax, sc[st][e]);
-        }
-      cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
-      cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
-      const float m_new = fmaxf(m_run, cmax);
-      const float alpha = fast_exp2(m_run - m_new);
-      float psum = 0.f;
+          for (int e = 0; e < 4; ++e) {
+            if (k0 + 16 * h + 4 * (lane >> 4) + e >= j1) sc[h][e] = -INFINITY;
+            cmax = fmaxf(cmax, sc[h][e]);
+          }
+        cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
+        cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
+        const float m_new = fmaxf(m_run, cmax);
+        const float alpha = fast_exp2(m_run - m_new);
+        float psum = 0.f;
 #pragma unroll
-      for (int st = 0; st < 4; ++st)
+        for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          sc[st][e] = fast_exp2(sc[st][e] - m_new);
-          psum += sc[st][e];
-        }
-      l_run = l_run * alpha + psum;
-      m_run = m_new;
-#pragma unroll
-      for (int ds = 0; ds < D / 16; ++ds) o[ds] *= alpha;
-
-      // ---- O^T[d][q] += V^T[d][keys] P^T[keys][q], 32 keys per product; P as a hi/lo pair
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
+          for (int e = 0; e < 4; ++e) {
+            sc[h][e] = fast_exp2(sc[h][e] - m_new);
+            psum += sc[h][e];
+          }
+        l_run = l_run * alpha + psum;
+        m_run = m_new;
+        // ---- O^T[d][q] += V^T[d][keys] P^T[keys][q]; P as a hi/lo pair
         bf16x8 ph, pl;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          ph[e] = (__bf16)sc[2 * t][e];
-          ph[4 + e] = (__bf16)sc[2 * t + 1][e];
-          pl[e] = (__bf16)(sc[2 * t][e] - (float)ph[e]);
-          pl[4 + e] = (__bf16)(sc[2 * t + 1][e] - (float)ph[4 + e]);
+          ph[e] = (__bf16)sc[0][e];
+          ph[4 + e] = (__bf16)sc[1][e];
+          pl[e] = (__bf16)(sc[0][e] - (float)ph[e]);
+          pl[4 + e] = (__bf16)(sc[1][e] - (float)ph[4 + e]);
         }
+        const int kp0 = (kUnit / 2) * u + 2 * (lane >> 4);  // keys k0 + 4*(lane>>4) + [0, 4)
 #pragma unroll
         for (int ds = 0; ds < D / 16; ++ds) {
-          const bf16_t* vrow = &L.vt[(16 * ds + (lane & 15)) * AttnLds<D>::VS + 32 * t + 4 * (lane >> 4)];
-          const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow);
-          const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + 16);
+          const int d = 16 * ds + (lane & 15);
+          const uint32_t* vrow = &L.vt[d * AttnLds<D>::VW];
+          const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow + vt_col(d, kp0));
+          const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + vt_col(d, kp0 + 8));
           const bf16x8 vf = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+          o[ds] *= alpha;
           o[ds] = mfma16x16x32(vf, ph, o[ds]);
           o[ds] = mfma16x16x32(vf, pl, o[ds]);
         }
       }
     }
-    if (c + 1 < nchunks) stage_store(lds[(c + 1) & 1], c0 + kChunk);
-    __syncthreads();
+    if (st + 1 < nstages) {
+      __syncthreads();
+      stage_store(c0 + kStage);
+      __syncthreads();
+    }
   }
-  if (!computes) return;
+
+  // ---- merge the key groups of each query tile through LDS (group 0 keeps the result)
+  if (KG > 1) {
+    __syncthreads();  // every wave is done reading K / V^T
+    float* mg = reinterpret_cast<float*>(lds_raw);
+    constexpr int REC = D / 4 + 2;  // floats per lane record: O^T values, max, partial sum
+    if (computes && kg > 0) {
+      float* rec = mg + (((kg - 1) * QTP + qt) * 64 + lane) * REC;
+#pragma unroll
+      for (int ds = 0; ds < D / 16; ++ds)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) rec[4 * ds + e] = o[ds][e];
+      rec[D / 4] = m_run;
+      rec[D / 4 + 1] = l_run;
+    }
+    __syncthreads();
+    if (computes && kg == 0) {
+      for (int g2 = 1; g2 < KG; ++g2) {
+        const float* rec = mg + (((g2 - 1) * QTP + qt) * 64 + lane) * REC;
+        const float m2 = rec[D / 4], l2 = rec[D / 4 + 1];
+        const float mn = fmaxf(m_run, m2);  // finite: group 0 always has a valid key
+        const float w1 = fast_exp2(m_run - mn);
+        const float w2 = m2 == -INFINITY ? 0.f : fast_exp2(m2 - mn);
+#pragma unroll
+        for (int ds = 0; ds < D / 16; ++ds)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[ds][e] = o[ds][e] * w1 + rec[4 * ds + e] * w2;
+        l_run = l_run * w1 + l2 * w2;
+        m_run = mn;
+      }
+    }
+  }
+  if (!computes || kg != 0) return;
 
   // lane (q = lane & 15) holds O^T rows d = 16*ds + 4*(lane>>4) + e
   float l_tot = l_run + __shfl_xor(l_run, 16);
@@ -264,8 +313,10 @@ __global__ void __launch_bounds__(512) attention_kernel(const AttnArgs a) {
   }
 }
 
-// Merge of the split partials of one (sequence, KV head): one thread per
-// (query row, 4 dims), splits folded in split order.  grid: (row-chunks, Hkv, B).
+// Merge of the split partials of one (sequence, KV head).  A wave covers four
+// (query row, 4 dims) items; its 16 lane groups take splits g, g+16, ... so all
+// partial loads are issued together, and the groups are folded by a fixed
+// butterfly (deterministic).  grid: (item groups of 16, Hkv, B), 256 threads.
 template <int D>
 __global__ void __launch_bounds__(256) attention_combine_kernel(const AttnArgs a) {
   const int b = blockIdx.z, kvh = blockIdx.y;
@@ -274,25 +325,60 @@ __global__ void __launch_bounds__(256) attention_combine_kernel(const AttnArgs a
   if (ns <= 1) return;  // written directly by the split kernel
   const int G = a.Hq / a.Hkv;
   const int QR = G * a.Bs;
-  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= QR * (D / 4)) return;
-  const int r = idx / (D / 4), d4 = (idx - r * (D / 4)) * 4;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int sg = lane >> 2;
+  const int item = blockIdx.x * 16 + wave * 4 + (lane & 3);
+  const bool valid = item < QR * (D / 4);
+  const int it = valid ? item : 0;
+  const int r = it / (D / 4), d4 = (it - r * (D / 4)) * 4;
   const size_t pbase = ((size_t)(b * a.Hkv + kvh) * a.max_splits);
   const float* ml = a.part_ml + (pbase * QR + r) * 2;
   const float* po = a.part_o + (pbase * QR + r) * D + d4;
   const size_t sstride_ml = (size_t)QR * 2, sstride_o = (size_t)QR * D;
-  float mx = -INFINITY;
-#pragma unroll 4
-  for (int s = 0; s < ns; ++s) mx = fmaxf(mx, ml[s * sstride_ml]);
-  float lsum = 0.f;
+
+  float m = -INFINITY, l = 0.f;
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-  for (int s = 0; s < ns; ++s) {
-    const float wgt = fast_exp2(ml[s * sstride_ml] - mx);
-    lsum += ml[s * sstride_ml + 1] * wgt;
-    acc += *reinterpret_cast<const f32x4*>(po + s * sstride_o) * wgt;
+  for (int s0 = 0; s0 < ns; s0 += 64) {
+    float mv[4], lv[4];
+    f32x4 ov[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int s = s0 + sg + 16 * k;
+      mv[k] = -INFINITY;
+      lv[k] = 0.f;
+      ov[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (s < ns) {
+        mv[k] = ml[s * sstride_ml];
+        lv[k] = ml[s * sstride_ml + 1];
+        ov[k] = *reinterpret_cast<const f32x4*>(po + s * sstride_o);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float mn = fmaxf(m, mv[k]);
+      if (mn == -INFINITY) continue;
+      const float w1 = m == -INFINITY ? 0.f : fast_exp2(m - mn);
+      const float w2 = mv[k] == -INFINITY ? 0.f : fast_exp2(mv[k] - mn);
+      acc = acc * w1 + ov[k] * w2;
+      l = l * w1 + lv[k] * w2;
+      m = mn;
+    }
   }
-  const float inv = 1.0f / lsum;
+#pragma unroll
+  for (int x = 4; x <= 32; x <<= 1) {
+    const float mo = __shfl_xor(m, x), lo = __shfl_xor(l, x);
+    f32x4 ao;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) ao[e] = __shfl_xor(acc[e], x);
+    const float mn = fmaxf(m, mo);
+    const float w1 = m == -INFINITY ? 0.f : fast_exp2(m - mn);
+    const float w2 = mo == -INFINITY ? 0.f : fast_exp2(mo - mn);
+    acc = acc * w1 + ao * w2;
+    l = l * w1 + lo * w2;
+    m = mn;
+  }
+  if (sg != 0 || !valid) return;
+  const float inv = 1.0f / l;
   const int gq = r / a.Bs, iq = r - gq * a.Bs;
   const size_t orow = (size_t)(b * a.Bs + iq) * (a.Hq * D) + (kvh * G + gq) * D + d4;
   bf16_t* out_h = reinterpret_cast<bf16_t*>(a.out_hi);
@@ -304,17 +390,17 @@ __global__ void __launch_bounds__(256) attention_combine_kernel(const AttnArgs a
 template <typename S, int D>
 static hipError_t launch_attention_d(const AttnArgs& a, hipStream_t stream) {
   const int QR = (a.Hq / a.Hkv) * a.Bs;
-  const size_t lds = 2 * sizeof(AttnLds<D>);
+  if (QR > 16 * kWaves || a.CW % kStage) return hipErrorInvalidValue;
+  const size_t lds = sizeof(AttnLds<D>);
   auto k = attention_kernel<S, D>;
   if (lds > 64 * 1024)
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize,
                               (int)lds);
-  hipLaunchKernelGGL(k, dim3(a.max_splits, a.Hkv, a.batch), dim3(attn_threads(QR)), lds, stream, a);
+  hipLaunchKernelGGL(k, dim3(a.max_splits, a.Hkv, a.batch), dim3(kThreads), lds, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.max_splits <= 1) return e;
-  const int nthreads = QR * (D / 4);
-  hipLaunchKernelGGL(attention_combine_kernel<D>, dim3((nthreads + 255) / 256, a.Hkv, a.batch), dim3(256), 0,
-                     stream, a);
+  const int items = QR * (D / 4);
+  hipLaunchKernelGGL(attention_combine_kernel<D>, dim3((items + 15) / 16, a.Hkv, a.batch), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -30,16 +30,6 @@
 namespace dfl {
 
 // ------------------------------------------------------------------ helpers
-__device__ __forceinline__ void rope_pair(float& lo, float& hi, int pos, int d, int D, float theta) {
-  const double inv_freq = exp(-(2.0 * (double)d / (double)D) * log((double)theta));
-  double s, c;
-  sincos((double)pos * inv_freq, &s, &c);
-  const float cf = (float)c, sf = (float)s;
-  const float a = lo, b = hi;
-  lo = a * cf - b * sf;
-  hi = a * sf + b * cf;
-}
-
 // v -> (hi, lo) bf16 pair with v ~= hi + lo (lo may be null: hi only).
 __device__ __forceinline__ void split_store(bf16_t* hi, bf16_t* lo, size_t idx, float v) {
   const bf16_t h = f32_to_bf16_bits(v);
@@ -61,6 +51,35 @@ __device__ __forceinline__ float row_rinv(const float* ssq, int nparts, int ld, 
   float s = 0.f;
   for (int p = 0; p < nparts; ++p) s += ssq[p * ld + m];
   return 1.0f / sqrtf(s / (float)kdim + eps);
+}
+
+// rinv_out[m] = 1/sqrt(sum_p ssq_in[p][m] / K + eps), computed by the
+// workgroups of k-slice 0 after their tiles: chunks of blockDim/16 rows go
+// round-robin over blockIdx.x, 16 lanes per row, all partial loads of a lane
+// issued together, fixed summation order.
+__device__ void write_rinv(const GemmArgs& g) {
+  const int rows = blockDim.x >> 4;
+  for (int r0 = blockIdx.x * rows; r0 < g.M; r0 += gridDim.x * rows) {
+    const int m = r0 + (threadIdx.x >> 4), part = threadIdx.x & 15;
+    float ss = 0.f;
+    if (m < g.M) {
+      for (int p0 = 0; p0 < g.ssq_nparts; p0 += 256) {
+        float v[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int p = p0 + part + 16 * i;
+          v[i] = p < g.ssq_nparts ? g.ssq_in[(size_t)p * g.ld_ssq + m] : 0.f;
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) ss += v[i];
+      }
+    }
+    ss += __shfl_xor(ss, 8);
+    ss += __shfl_xor(ss, 4);
+    ss += __shfl_xor(ss, 2);
+    ss += __shfl_xor(ss, 1);
+    if (part == 0 && m < g.M) g.rinv_out[m] = 1.0f / sqrtf(ss / (float)g.K + g.eps);
+  }
 }
 
 // Packed (value, index) keys of a 16 x 16 MFMA result tile: the largest key per
@@ -200,6 +219,7 @@ __global__ void __launch_bounds__(512) gemm_as_kernel(const GemmArgs g) {
       }
     }
   }
+  if (g.rinv_out != nullptr && blockIdx.y == 0) write_rinv(g);
 }
 
 // ------------------------------------------------------------------ gemm_ws
@@ -319,6 +339,7 @@ __global__ void __launch_bounds__((WsShape<MR>::MAXT)) gemm_ws_kernel(const Gemm
       const int m = e / NT, j = e - m * NT;
       if (m0 + m < g.M) g.part[((size_t)(blockIdx.x * WN + (j >> 4)) * g.M + m0 + m) * 16 + (j & 15)] = red[e];
     }
+    if (g.rinv_out != nullptr && blockIdx.y == 0) write_rinv(g);
   } else {
     if (g.logits_dbg != nullptr) {
       for (int e = tid; e < tsz; e += nthr) {
@@ -368,172 +389,235 @@ __global__ void __launch_bounds__(256) argmax_reduce_kernel(const uint64_t* part
 }
 
 // ------------------------------------------------------------------ finish kernels
+// Every finish kernel is elementwise over its outputs and issues all the
+// global loads an output needs at once (one round of memory latency): the
+// k-slice partials of that output, the row scale and the epilogue operands.
+
 // Sum of the k-slices of output (m, n) in slice order.
 __device__ __forceinline__ float ksum(const FinishArgs& f, int m, int n) {
   const int tile = n >> 4, j = n & 15;
+  const size_t stride = (size_t)f.ntiles * f.M * 16;
+  const float* p = f.part + ((size_t)tile * f.M + m) * 16 + j;
   float v = 0.f;
-  for (int s = 0; s < f.KS; ++s) v += f.part[(((size_t)s * f.ntiles + tile) * f.M + m) * 16 + j];
+  for (int s0 = 0; s0 < f.KS; s0 += 16) {
+    float t[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) t[i] = s0 + i < f.KS ? p[(size_t)(s0 + i) * stride] : 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if (s0 + i < f.KS) v += t[i];
+  }
   return v;
 }
 
-// rinv of every row into LDS (16 lanes per row); 1 when the stage has no norm.
-__device__ __forceinline__ void rows_rinv(const FinishArgs& f, float* s_r) {
-  for (int base = 0; base < f.M * 16; base += blockDim.x) {
-    const int t = base + threadIdx.x;
-    const int m = t >> 4, part = t & 15;
-    float ss = 0.f;
-    if (f.ssq_in != nullptr && m < f.M)
-      for (int p = part; p < f.ssq_nparts; p += 16) ss += f.ssq_in[p * f.ld_ssq + m];
-    ss += __shfl_xor(ss, 8);
-    ss += __shfl_xor(ss, 4);
-    ss += __shfl_xor(ss, 2);
-    ss += __shfl_xor(ss, 1);
-    if (part == 0 && m < f.M) s_r[m] = f.ssq_in != nullptr ? 1.0f / sqrtf(ss / (float)f.kdim + f.eps) : 1.0f;
+// ksum of two outputs of one row with all loads of both issued together.
+__device__ __forceinline__ void ksum2(const FinishArgs& f, int m, int n0, int n1, float& v0, float& v1) {
+  const size_t stride = (size_t)f.ntiles * f.M * 16;
+  const float* p0 = f.part + ((size_t)(n0 >> 4) * f.M + m) * 16 + (n0 & 15);
+  const float* p1 = f.part + ((size_t)(n1 >> 4) * f.M + m) * 16 + (n1 & 15);
+  v0 = 0.f;
+  v1 = 0.f;
+  for (int s0 = 0; s0 < f.KS; s0 += 8) {
+    float t0[8], t1[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      t0[i] = s0 + i < f.KS ? p0[(size_t)(s0 + i) * stride] : 0.f;
+      t1[i] = s0 + i < f.KS ? p1[(size_t)(s0 + i) * stride] : 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (s0 + i < f.KS) {
+        v0 += t0[i];
+        v1 += t1[i];
+      }
   }
-  __syncthreads();
 }
 
-// Sum of squares over the 16 columns of a tile per row: e = m * 16 + j.
-__device__ __forceinline__ void tile_ssq_store(const FinishArgs& f, const float* vals, int tile) {
-  for (int base = 0; base < f.M * 16; base += blockDim.x) {
-    const int e = base + threadIdx.x;
-    const int m = e >> 4;
-    const float v = (m < f.M) ? vals[e] : 0.f;
-    float s = v * v;
-    s += __shfl_xor(s, 8);
-    s += __shfl_xor(s, 4);
-    s += __shfl_xor(s, 2);
-    s += __shfl_xor(s, 1);
-    if ((e & 15) == 0 && m < f.M) f.ssq_out[(size_t)tile * f.ld_ssq + m] = s;
+// Two-column partial loads for KS <= 8, split into issue and reduce so that
+// independent loads (row scale, context length, RoPE table) can be placed in
+// between.
+struct KPair {
+  float a[8], b[8];
+};
+__device__ __forceinline__ void kpair_issue(const FinishArgs& f, int m, int n0, int n1, KPair& k) {
+  const size_t stride = (size_t)f.ntiles * f.M * 16;
+  const float* p0 = f.part + ((size_t)(n0 >> 4) * f.M + m) * 16 + (n0 & 15);
+  const float* p1 = f.part + ((size_t)(n1 >> 4) * f.M + m) * 16 + (n1 & 15);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    k.a[i] = i < f.KS ? p0[(size_t)i * stride] : 0.f;
+    k.b[i] = i < f.KS ? p1[(size_t)i * stride] : 0.f;
   }
+}
+__device__ __forceinline__ void kpair_reduce(const FinishArgs& f, const KPair& k, float& v0, float& v1) {
+  v0 = 0.f;
+  v1 = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    if (i < f.KS) {
+      v0 += k.a[i];
+      v1 += k.b[i];
+    }
+}
+
+__device__ __forceinline__ float row_scale(const FinishArgs& f, int m) { return f.rinv != nullptr ? f.rinv[m] : 1.0f; }
+
+// Rotation of the pair (lo, hi) by the tabulated angle of (position, pair index).
+__device__ __forceinline__ void rope_apply(float& lo, float& hi, float2 cs) {
+  const float a = lo, b = hi;
+  lo = a * cs.x - b * cs.y;
+  hi = a * cs.y + b * cs.x;
 }
 
 // y = sum (+ x residual, + width-3 block conv); x / out_f32 = y; hi/lo of
-// y * gnext; sums of squares per tile.  grid: N/16 tiles.
+// y * gnext; sums of squares per (tile, row).  grid: (N/16 tiles, row groups
+// of 16); thread (r, j) = (tid >> 4, tid & 15).  A conv block never crosses a
+// 16-row group (the block divides 16).
 template <typename S>
 __global__ void __launch_bounds__(256) finish_rowtile_kernel(const FinishArgs f) {
-  extern __shared__ __align__(16) float sv[];  // [2][M * 16]
-  const int tile = blockIdx.x;
-  const int tot = f.M * 16;
-  float* v0 = sv;
-  float* v1 = sv + tot;
-  for (int e = threadIdx.x; e < tot; e += blockDim.x) {
-    const int m = e >> 4, n = tile * 16 + (e & 15);
-    float v = ksum(f, m, n);
-    if (f.x != nullptr) v += f.x[(size_t)m * f.N + n];
-    v0[e] = v;
-  }
-  __syncthreads();
-  const float* src = v0;
+  __shared__ float v0[256];
+  const int tile = blockIdx.x, r = threadIdx.x >> 4, j = threadIdx.x & 15;
+  const int m = 16 * blockIdx.y + r, n = tile * 16 + j;
+  const bool ok = m < f.M;
+  const size_t idx = (size_t)m * f.N + n;
+  // epilogue operands first: their loads fly with the partial loads
+  const float xr = ok && f.x != nullptr ? f.x[idx] : 0.f;
+  const float gnv = load_f32<S>(reinterpret_cast<const S*>(f.gnext) + n);
+  float c0 = 0.f, c1 = 0.f, c2 = 0.f;
   if (f.conv != nullptr) {
     const S* cw = reinterpret_cast<const S*>(f.conv);
-    for (int e = threadIdx.x; e < tot; e += blockDim.x) {
-      const int m = e >> 4, n = tile * 16 + (e & 15);
-      const int i = m % f.block;
-      const float v = v0[e];
-      float y = load_f32<S>(cw + 3 * n + 1) * v;
-      if (i > 0) y += load_f32<S>(cw + 3 * n) * v0[e - 16];
-      if (i < f.block - 1 && m + 1 < f.M) y += load_f32<S>(cw + 3 * n + 2) * v0[e + 16];
-      v1[e] = v + y;
-    }
-    __syncthreads();
-    src = v1;
+    c0 = load_f32<S>(cw + 3 * n);
+    c1 = load_f32<S>(cw + 3 * n + 1);
+    c2 = load_f32<S>(cw + 3 * n + 2);
   }
-  const S* gn = reinterpret_cast<const S*>(f.gnext);
-  bf16_t* oh = reinterpret_cast<bf16_t*>(f.out_hi);
-  bf16_t* ol = reinterpret_cast<bf16_t*>(f.out_lo);
-  for (int e = threadIdx.x; e < tot; e += blockDim.x) {
-    const int m = e >> 4, n = tile * 16 + (e & 15);
-    const size_t idx = (size_t)m * f.N + n;
-    const float v = src[e];
+  float v = 0.f;
+  if (ok) v = ksum(f, m, n) + xr;
+  if (f.conv != nullptr) {
+    v0[threadIdx.x] = v;
+    __syncthreads();
+    const int i = m % f.block;
+    float y = c1 * v;
+    if (i > 0) y += c0 * v0[threadIdx.x - 16];
+    if (i < f.block - 1 && m + 1 < f.M) y += c2 * v0[threadIdx.x + 16];
+    v = v + y;
+  }
+  if (ok) {
     if (f.x != nullptr) f.x[idx] = v;
     if (f.out_f32 != nullptr) f.out_f32[idx] = v;
-    split_store(oh, ol, idx, v * load_f32<S>(gn + n));
+    split_store(reinterpret_cast<bf16_t*>(f.out_hi), reinterpret_cast<bf16_t*>(f.out_lo), idx, v * gnv);
   }
-  tile_ssq_store(f, src, tile);
+  float sq = ok ? v * v : 0.f;
+  sq += __shfl_xor(sq, 8);
+  sq += __shfl_xor(sq, 4);
+  sq += __shfl_xor(sq, 2);
+  sq += __shfl_xor(sq, 1);
+  if (j == 0 && ok) f.ssq_out[(size_t)tile * f.ld_ssq + m] = sq;
 }
 
-// act[m, c] = silu(rinv * y_gate) * (rinv * y_up) as a hi/lo pair.  grid: F/16 tiles.
+// act[m, c] = silu(rinv * y_gate) * (rinv * y_up) as a hi/lo pair.  One
+// thread per output, ordered (tile, row, column in tile) so the partial reads
+// are contiguous.
 __global__ void __launch_bounds__(256) finish_swiglu_kernel(const FinishArgs f) {
-  extern __shared__ __align__(16) float s_r[];
-  rows_rinv(f, s_r);
   const int F = f.N >> 1;
-  const int tile = blockIdx.x;
-  bf16_t* oh = reinterpret_cast<bf16_t*>(f.out_hi);
-  bf16_t* ol = reinterpret_cast<bf16_t*>(f.out_lo);
-  for (int e = threadIdx.x; e < f.M * 16; e += blockDim.x) {
-    const int m = e >> 4, c = tile * 16 + (e & 15);
-    const float r = s_r[m];
-    const float gv = ksum(f, m, c) * r, uv = ksum(f, m, F + c) * r;
-    split_store(oh, ol, (size_t)m * F + c, silu_f32(gv) * uv);
-  }
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  if (e >= f.M * F) return;
+  const int tile = e / (f.M * 16), rem = e - tile * (f.M * 16);
+  const int m = rem >> 4, c = tile * 16 + (rem & 15);
+  KPair kp;
+  const bool fast = f.KS <= 8;
+  if (fast) kpair_issue(f, m, c, F + c, kp);
+  const float r = row_scale(f, m);
+  float gv, uv;
+  if (fast) kpair_reduce(f, kp, gv, uv);
+  else ksum2(f, m, c, F + c, gv, uv);
+  gv *= r;
+  uv *= r;
+  split_store(reinterpret_cast<bf16_t*>(f.out_hi), reinterpret_cast<bf16_t*>(f.out_lo), (size_t)m * F + c,
+              silu_f32(gv) * uv);
 }
 
 // Block Q/K/V: RoPE on Q and K at position ctx_len[b] + i; Q scaled and stored
-// as a hi/lo pair, K and V in storage type.  grid: one workgroup per head of
-// the concatenated [Q | K | V] output.
+// as a hi/lo pair, K and V in storage type.  One thread per rotation pair
+// (row, head of the concatenated [Q | K | V] output, d < D/2).
 template <typename S>
 __global__ void __launch_bounds__(256) finish_qkv_kernel(const FinishArgs f) {
-  extern __shared__ __align__(16) float s_r[];
-  rows_rinv(f, s_r);
   const int D = f.head_dim, half = D >> 1;
+  const int pairs = f.N >> 1;
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  if (e >= f.M * pairs) return;
+  const int m = e / pairs, rem = e - m * pairs;
+  const int hd = rem / half, d = rem - hd * half;
+  const int n = hd * D + d;
   const int Nq = f.n_q_heads * D, Nk = f.n_kv_heads * D;
-  const int n0 = blockIdx.x * D;
-  bf16_t* qh = reinterpret_cast<bf16_t*>(f.out_hi);
-  bf16_t* ql = reinterpret_cast<bf16_t*>(f.out_lo);
-  S* ko = reinterpret_cast<S*>(f.kb_out);
-  S* vo = reinterpret_cast<S*>(f.vb_out);
-  for (int e = threadIdx.x; e < f.M * half; e += blockDim.x) {
-    const int m = e / half, d = e - m * half;
-    const int n = n0 + d;
-    const float r = s_r[m];
-    float lo = ksum(f, m, n) * r, hi = ksum(f, m, n + half) * r;
-    const int pos = f.ctx_len[m / f.block] + m % f.block;
-    if (n < Nq) {
-      rope_pair(lo, hi, pos, d, D, f.rope_theta);
-      split_store(qh, ql, (size_t)m * Nq + n, lo * f.q_scale);
-      split_store(qh, ql, (size_t)m * Nq + n + half, hi * f.q_scale);
-    } else if (n < Nq + Nk) {
-      const int nn = n - Nq;
-      rope_pair(lo, hi, pos, d, D, f.rope_theta);
-      store_from_f32<S>(ko + (size_t)m * Nk + nn, lo);
-      store_from_f32<S>(ko + (size_t)m * Nk + nn + half, hi);
-    } else {
-      const int nn = n - Nq - Nk;
-      store_from_f32<S>(vo + (size_t)m * Nk + nn, lo);
-      store_from_f32<S>(vo + (size_t)m * Nk + nn + half, hi);
-    }
+  const int b = m / f.block;
+  KPair kp;
+  const bool fast = f.KS <= 8;
+  if (fast) kpair_issue(f, m, n, n + half, kp);
+  const float r = row_scale(f, m);
+  const int ctx = f.ctx_len[b];
+  // a caller-set length outside [0, max_ctx] is clamped (the table covers every clamped position)
+  const int pos = min(max(ctx, 0), f.max_ctx) + (m - b * f.block);
+  const float2 cs = f.rope[(size_t)pos * half + d];
+  float lo, hi;
+  if (fast) kpair_reduce(f, kp, lo, hi);
+  else ksum2(f, m, n, n + half, lo, hi);
+  lo *= r;
+  hi *= r;
+  if (n < Nq) {
+    bf16_t* qh = reinterpret_cast<bf16_t*>(f.out_hi);
+    bf16_t* ql = reinterpret_cast<bf16_t*>(f.out_lo);
+    rope_apply(lo, hi, cs);
+    split_store(qh, ql, (size_t)m * Nq + n, lo * f.q_scale);
+    split_store(qh, ql, (size_t)m * Nq + n + half, hi * f.q_scale);
+  } else if (n < Nq + Nk) {
+    S* ko = reinterpret_cast<S*>(f.kb_out) + (size_t)m * Nk + (n - Nq);
+    rope_apply(lo, hi, cs);
+    store_from_f32<S>(ko, lo);
+    store_from_f32<S>(ko + half, hi);
+  } else {
+    S* vo = reinterpret_cast<S*>(f.vb_out) + (size_t)m * Nk + (n - Nq - Nk);
+    store_from_f32<S>(vo, lo);
+    store_from_f32<S>(vo + half, hi);
   }
 }
 
 // Context K/V of every layer (segments K^0, V^0, K^1, V^1, ...): RoPE on K at
 // position ctx_len[b] + i, scatter to cache row ctx_len[b] + i.  A sequence
-// whose rows would pass max_ctx is skipped and flagged.  grid: one workgroup
-// per head of the concatenated output.
+// whose rows would pass max_ctx is skipped and flagged.  One thread per
+// rotation pair (row, head of the concatenated output, d < D/2).
 template <typename S>
 __global__ void __launch_bounds__(256) finish_kv_kernel(const FinishArgs f) {
-  extern __shared__ __align__(16) float s_r[];
-  rows_rinv(f, s_r);
   const int D = f.head_dim, half = D >> 1, Hkv = f.n_kv_heads;
-  const int seg_rows = Hkv * D;
-  const int n0 = blockIdx.x * D;
-  const int seg = n0 / seg_rows, head = (n0 - seg * seg_rows) / D;
-  for (int e = threadIdx.x; e < f.M * half; e += blockDim.x) {
-    const int m = e / half, d = e - m * half;
-    const int b = m / f.block, i = m - b * f.block;
-    const int t0 = f.ctx_len[b];
-    if (t0 < 0 || t0 + f.block > f.max_ctx) {
-      if (d == 0) atomicOr(f.err, 1u);
-      continue;
-    }
-    const int pos = t0 + i;
-    const float r = s_r[m];
-    float lo = ksum(f, m, n0 + d) * r, hi = ksum(f, m, n0 + d + half) * r;
-    if ((seg & 1) == 0) rope_pair(lo, hi, pos, d, D, f.rope_theta);
-    S* dst = reinterpret_cast<S*>(f.kv_cache[seg]) + (((size_t)b * f.max_ctx + pos) * Hkv + head) * D + d;
-    store_from_f32<S>(dst, lo);
-    store_from_f32<S>(dst + half, hi);
+  const int pairs = f.N >> 1;
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  if (e >= f.M * pairs) return;
+  const int m = e / pairs, rem = e - m * pairs;
+  const int hd = rem / half, d = rem - hd * half;
+  const int seg = hd / Hkv, head = hd - seg * Hkv;
+  const int b = m / f.block, i = m - b * f.block;
+  const int n = hd * D + d;
+  KPair kp;
+  const bool fast = f.KS <= 8;
+  if (fast) kpair_issue(f, m, n, n + half, kp);
+  const float r = row_scale(f, m);
+  const int t0 = f.ctx_len[b];
+  const bool bad = t0 < 0 || t0 + f.block > f.max_ctx;
+  const int pos = bad ? 0 : t0 + i;
+  float2 cs = make_float2(1.f, 0.f);
+  if ((seg & 1) == 0) cs = f.rope[(size_t)pos * half + d];
+  float lo, hi;
+  if (fast) kpair_reduce(f, kp, lo, hi);
+  else ksum2(f, m, n, n + half, lo, hi);
+  if (bad) {
+    if (rem == 0 && i == 0) atomicOr(f.err, 1u);
+    return;
   }
+  lo *= r;
+  hi *= r;
+  if ((seg & 1) == 0) rope_apply(lo, hi, cs);
+  S* dst = reinterpret_cast<S*>(f.kv_cache[seg]) + (((size_t)b * f.max_ctx + pos) * Hkv + head) * D + d;
+  store_from_f32<S>(dst, lo);
+  store_from_f32<S>(dst + half, hi);
 }
 
 // ------------------------------------------------------------------ launchers
@@ -622,23 +706,19 @@ hipError_t launch_argmax_reduce(const uint64_t* part, int ntiles, int ld, int M,
 
 template <typename S>
 static hipError_t launch_finish_s(FinishKind kind, const FinishArgs& f, hipStream_t st) {
-  const size_t rl = (size_t)f.M * sizeof(float);
+  const int pair_blocks = (int)(((size_t)f.M * (f.N / 2) + 255) / 256);
   switch (kind) {
-    case FIN_ROWTILE: {
-      const size_t l = (size_t)2 * f.M * 16 * sizeof(float);
-      auto k = finish_rowtile_kernel<S>;
-      allow_lds(k, l);
-      hipLaunchKernelGGL(k, dim3(f.N / 16), dim3(256), l, st, f);
+    case FIN_ROWTILE:
+      hipLaunchKernelGGL(finish_rowtile_kernel<S>, dim3(f.N / 16, (f.M + 15) / 16), dim3(256), 0, st, f);
       break;
-    }
     case FIN_SWIGLU:
-      hipLaunchKernelGGL(finish_swiglu_kernel, dim3(f.N / 32), dim3(256), rl, st, f);
+      hipLaunchKernelGGL(finish_swiglu_kernel, dim3(pair_blocks), dim3(256), 0, st, f);
       break;
     case FIN_QKV:
-      hipLaunchKernelGGL(finish_qkv_kernel<S>, dim3(f.N / f.head_dim), dim3(256), rl, st, f);
+      hipLaunchKernelGGL(finish_qkv_kernel<S>, dim3(pair_blocks), dim3(256), 0, st, f);
       break;
     case FIN_KV:
-      hipLaunchKernelGGL(finish_kv_kernel<S>, dim3(f.N / f.head_dim), dim3(256), rl, st, f);
+      hipLaunchKernelGGL(finish_kv_kernel<S>, dim3(pair_blocks), dim3(256), 0, st, f);
       break;
     default:
       return hipErrorInvalidValue;

@@ -47,9 +47,14 @@ struct GemmArgs {
   uint64_t* best_part;  // OUT_ARGMAX [argmax tiles][ld_best]
   int ld_best;
   float* logits_dbg;    // OUT_ARGMAX nullable [M, N], row-scaled by rinv
-  const float* ssq_in;  // row scale of logits_dbg
+  // RMSNorm of the activation rows: ssq_in[p][m] (p < ssq_nparts, leading
+  // dimension ld_ssq) are partial sums of squares over the K columns.
+  const float* ssq_in;
   int ssq_nparts, ld_ssq;
   float eps;
+  // nullable: workgroup (0, 0) writes rinv_out[m] = 1/sqrt(sum_p ssq_in[p][m]/K + eps)
+  // after its tiles, for the finish kernel of this product
+  float* rinv_out;
 };
 
 struct GemmLaunch {
@@ -83,10 +88,8 @@ enum FinishKind {
 struct FinishArgs {
   const float* part;
   int KS, ntiles, M, N;
-  // row scale rinv[m] = 1/sqrt(sum_p ssq_in[p][m] / kdim + eps); null: none
-  const float* ssq_in;
-  int ssq_nparts, ld_ssq, kdim;
-  float eps;
+  const float* rinv;  // row scale [M] (written by the product's main kernel); null: none
+  int ld_ssq;
   // FIN_ROWTILE
   float* x;           // residual stream [M, N] (read and written) or null
   float* out_f32;     // plain output [M, N] or null
@@ -97,9 +100,9 @@ struct FinishArgs {
   void* out_lo;       //   (null: hi only)
   int block;          // rows per sequence
   // FIN_QKV / FIN_KV
+  const float2* rope;  // [max_ctx + max rows per sequence][head_dim / 2] (cos, sin)
   const int32_t* ctx_len;
   int max_ctx;
-  float rope_theta;
   int head_dim, n_q_heads, n_kv_heads;
   float q_scale;
   void* kb_out;  // FIN_QKV [M, Hkv*D] storage type
@@ -153,6 +156,8 @@ hipError_t launch_verify(const VerifyArgs& a, hipStream_t stream);
 hipError_t launch_embed(int storage, const void* embed, const void* gain, const int32_t* ids, int M, int H, int V,
                         float* x, void* xs_hi, void* xs_lo, float* ssq, uint32_t* err, hipStream_t stream);
 hipError_t launch_commit(int32_t* ctx_len, int batch, int t_new, int max_ctx, hipStream_t stream);
+// table[p][i] = (cos, sin)(p * theta^(-2i/D)), evaluated in double precision.
+hipError_t launch_rope_table(float2* table, int rows, int head_dim, float theta, hipStream_t stream);
 hipError_t launch_copy_f32(const float* src, float* dst, size_t n, hipStream_t stream);
 hipError_t launch_feature_dbg(int storage, const float* y, const float* ssq, int nparts, int ld_ssq,
                               const void* gain, float eps, int M, int H, float* out, hipStream_t stream);

@@ -145,6 +145,27 @@ hipError_t launch_commit(int32_t* ctx_len, int batch, int t_new, int max_ctx, hi
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------- RoPE table
+// (cos, sin) of p * theta^(-2i/D) for every position p < rows and pair i < D/2,
+// evaluated in double precision and rounded once to fp32.
+__global__ void rope_table_kernel(float2* table, int rows, int head_dim, float theta) {
+  const int half = head_dim / 2;
+  const size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= (size_t)rows * half) return;
+  const int p = (int)(e / half), i = (int)(e - (size_t)p * half);
+  const double inv_freq = exp(-(2.0 * (double)i / (double)head_dim) * log((double)theta));
+  double sn, cs;
+  sincos((double)p * inv_freq, &sn, &cs);
+  table[e] = make_float2((float)cs, (float)sn);
+}
+
+hipError_t launch_rope_table(float2* table, int rows, int head_dim, float theta, hipStream_t stream) {
+  const size_t n = (size_t)rows * (head_dim / 2);
+  hipLaunchKernelGGL(rope_table_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, table, rows, head_dim,
+                     theta);
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------- helpers
 __global__ void copy_f32_kernel(const float* src, float* dst, size_t n) {
   for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
