@@ -30,6 +30,7 @@ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 constexpr int kMaxNd = 64;
 constexpr int kVerifyChunk = 16384;  // vocab entries per workgroup of the verify argmax
+constexpr int kMtTargetWgs = 256;    // gemm_mt workgroups to aim for (one per compute unit)
 constexpr int kAttnTargetWgs = 512;  // attention workgroups to aim for (two per compute unit)
 constexpr int kAttnStage = 128;      // keys per attention LDS stage (splits are whole stages)
 
@@ -64,8 +65,8 @@ const char* validate(const dflash_config* c) {
 }
 
 // ---------------------------------------------------------------- GEMM planning
-// Launch geometry of one GEMM.  gemm_as (activation stationary, split-K) when
-// the activation slice fits LDS, else gemm_ws (one k-slice).
+// Launch geometry of one GEMM.  gemm_as (activation stationary, split-K) for
+// up to 32 rows when the activation slice fits LDS, else gemm_mt (LDS-tiled).
 bool plan_gemm(int storage, int src, int out, bool lo, int M, int N, int K, GemmArgs* a, GemmLaunch* l) {
   if (M < 1 || N % 64 || K % 128) return false;
   const int ntiles = N / 16;
@@ -91,30 +92,33 @@ bool plan_gemm(int storage, int src, int out, bool lo, int M, int N, int K, Gemm
     a->tpw = NW;
     return true;
   }
-  const int MR = M <= 16 ? 1 : (M <= 32 ? 2 : (M <= 64 ? 4 : 8));
-  const int U = MR == 1 ? 4 : (MR == 2 ? 2 : 1);
-  const int WN = out == OUT_ARGMAX ? 4 : 1;
-  const int maxthr = gemm_ws_max_threads(MR);
-  int WK = std::min(maxthr / (64 * WN), std::max(1, K / 512));
-  while (WK > 1 && (K % (WK * 32 * U) || gemm_ws_lds(MR, WN, WK) > 64 * 1024)) --WK;
-  if (K % (WK * 32 * U) || gemm_ws_lds(MR, WN, WK) > 64 * 1024) return false;
-  l->kind = GEMM_WS;
-  l->MR = MR;
-  l->KS = 1;
-  l->grid = dim3(ntiles / WN, (M + 16 * MR - 1) / (16 * MR));
-  l->threads = 64 * WN * WK;
-  l->lds = gemm_ws_lds(MR, WN, WK);
-  l->argmax_tiles = ntiles / WN;
-  a->WN = WN;
-  a->WK = WK;
-  a->kw = K / WK;
+  // gemm_mt: BM = 64 * MF rows by 128 columns per workgroup; split K until
+  // the grid fills the chip (one 8-wave workgroup per compute unit)
+  const int MF = M <= 64 ? 1 : (M <= 128 ? 2 : 4);
+  const int nbm = (M + 64 * MF - 1) / (64 * MF);
+  const int nbn = (N + 127) / 128;
+  int KS = 1;
+  if (out == OUT_PARTIAL)
+    while (nbn * nbm * KS < kMtTargetWgs && (K / 32) % (2 * KS) == 0 && K / (2 * KS) >= 256) KS *= 2;
+  const int units = nbn * KS;
+  l->kind = GEMM_MT;
+  l->MR = MF;
+  l->KS = KS;
+  l->grid = dim3(((units + 7) / 8) * 8 * nbm);
+  l->threads = 512;
+  l->lds = gemm_mt_lds_bytes(MF, lo_eff);
+  l->argmax_tiles = nbn;
+  a->nbm = nbm;
+  a->nbn = nbn;
+  a->KS = KS;
+  a->kslice = K / KS;
   return true;
 }
 
 // Floats of partial tiles the planner needs for a product of this shape.
 size_t partial_floats(int storage, int src, bool lo, int Mmax, int N, int K) {
   size_t best = 0;
-  for (int M : {std::min(16, Mmax), std::min(32, Mmax), Mmax}) {
+  for (int M = 1; M <= Mmax; ++M) {
     GemmArgs a{};
     GemmLaunch l{};
     if (plan_gemm(storage, src, OUT_PARTIAL, lo, M, N, K, &a, &l)) best = std::max(best, (size_t)l.KS * M * N);

@@ -17,8 +17,8 @@
 //    the current one feeds the matrix cores).  No barrier in the loop.
 //    Measured on MI355X this streams weights at ~5 TB/s where re-reading the
 //    activations per wave from L2 halves the rate.
-//  * gemm_ws (any M): waves read the activations from L2 themselves; used
-//    when the activation slice does not fit LDS.
+//  * gemm_mt (M > 32, or no gemm_as fit): LDS-tiled 64*MF x 128 blocks,
+//    double-buffered 32-deep k stages, optional split-K.
 // Activations are a pair of bf16 arrays (hi, lo) with a = hi + lo (two MFMAs
 // per fragment); the stages whose outputs do not feed the residual stream
 // (context K/V, LM head) use hi only.  RMSNorm is a row scale applied by the
@@ -55,11 +55,11 @@ __device__ __forceinline__ float row_rinv(const float* ssq, int nparts, int ld, 
 
 // rinv_out[m] = 1/sqrt(sum_p ssq_in[p][m] / K + eps), computed by the
 // workgroups of k-slice 0 after their tiles: chunks of blockDim/16 rows go
-// round-robin over blockIdx.x, 16 lanes per row, all partial loads of a lane
-// issued together, fixed summation order.
-__device__ void write_rinv(const GemmArgs& g) {
+// round-robin over those workgroups (index idx of count), 16 lanes per row,
+// all partial loads of a lane issued together, fixed summation order.
+__device__ void write_rinv(const GemmArgs& g, int idx, int count) {
   const int rows = blockDim.x >> 4;
-  for (int r0 = blockIdx.x * rows; r0 < g.M; r0 += gridDim.x * rows) {
+  for (int r0 = idx * rows; r0 < g.M; r0 += count * rows) {
     const int m = r0 + (threadIdx.x >> 4), part = threadIdx.x & 15;
     float ss = 0.f;
     if (m < g.M) {
@@ -219,171 +219,245 @@ __global__ void __launch_bounds__(512) gemm_as_kernel(const GemmArgs g) {
       }
     }
   }
-  if (g.rinv_out != nullptr && blockIdx.y == 0) write_rinv(g);
+  if (g.rinv_out != nullptr && blockIdx.y == 0) write_rinv(g, blockIdx.x, gridDim.x);
 }
 
-// ------------------------------------------------------------------ gemm_ws
-// Activations from L2 per wave; WN waves split 16-row tiles, WK waves split K
-// (fixed-order LDS reduction).  One k-slice.
-template <int MR>
-struct WsShape {
-  static constexpr int MT = 16 * MR;
-  static constexpr int U = MR == 1 ? 4 : (MR == 2 ? 2 : 1);
-  static constexpr int MAXT = MR <= 4 ? 512 : 256;
+// ------------------------------------------------------------------ gemm_mt
+// LDS-tiled product for M > 32 (batched drafting, batched fusion).  A
+// workgroup of 8 waves computes a BM x 128 block of Y (BM = 64 * MF): the
+// waves are 4 along M (16*MF rows each) by 2 along N (64 columns each), so a
+// wave holds 4 x MF 16x16 accumulators and reads 4 weight and MF (x2 for
+// hi/lo) activation fragments per 32-deep k-step.  K advances in stages of 32
+// through a double-buffered LDS ring; the global loads of stage t+2 are issued
+// into registers before the matrix work of stage t (two stages of latency
+// cover), and stored to LDS after it.  One barrier per stage.
+//
+// Blocks are numbered so that the M blocks sharing a weight block are
+// dispatched back to back on the same XCD (workgroup L runs on XCD L % 8), so
+// the weight block is fetched from HBM once into that XCD's L2.
+template <int MF>
+struct MtShape {
+  static constexpr int BM = 64 * MF;
+  static constexpr int BN = 128;
+  static constexpr int BK = 32;
+  static constexpr int LDK = BK + 8;  // LDS row stride (elements): conflict-free 16-byte fragment reads
+  static constexpr int APT = (BM * 4 + 511) / 512;  // activation pieces per thread per array
 };
 
-template <typename S, int MR, int SRC, bool LO, int OUT>
-__global__ void __launch_bounds__((WsShape<MR>::MAXT)) gemm_ws_kernel(const GemmArgs g) {
-  constexpr int MT = WsShape<MR>::MT;
-  constexpr int U = WsShape<MR>::U;
-  extern __shared__ __align__(16) float smem[];  // [WK][MT][NT]
+template <typename S, int MF, int SRC, bool LO>
+struct MtRegs {
+  Raw8 w;
+  Raw8 a[MtShape<MF>::APT];
+  Raw8 l[LO && SRC == SRC_SPLIT ? MtShape<MF>::APT : 1];
+};
+
+size_t gemm_mt_lds_bytes(int MF, bool lo) {
+  const int BM = 64 * MF;
+  return (size_t)2 * ((lo ? 2 : 1) * BM + 128) * (32 + 8) * 2;
+}
+
+template <typename S, int MF, int SRC, bool LO, int OUT>
+__global__ void __launch_bounds__(512) gemm_mt_kernel(const GemmArgs g) {
+  using Sh = MtShape<MF>;
+  constexpr int BM = Sh::BM, BN = Sh::BN, BK = Sh::BK, LDK = Sh::LDK, APT = Sh::APT;
+  constexpr int NA = LO ? 2 : 1;
+  constexpr int STAGE = (NA * BM + BN) * LDK;
+  extern __shared__ __align__(16) bf16_t sm[];  // [2][NA*BM + BN][LDK]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int nthr = blockDim.x;
-  const int WN = g.WN, WK = g.WK;
-  const int wn = wave % WN, wk = wave / WN;
-  const int NT = 16 * WN;
-  const int m0 = blockIdx.y * MT;
-  const int tile = blockIdx.x * WN + wn;  // 16-row tile of this wave
-  const S* wp = tile_row_ptr<S>(g, tile, lane, wk * g.kw);
+  const int wm = wave & 3, wn = wave >> 2;
 
-  int arow[MR];
-#pragma unroll
-  for (int mi = 0; mi < MR; ++mi) arow[mi] = min(m0 + 16 * mi + (lane & 15), g.M - 1);
-  const int kbase = wk * g.kw + (lane >> 4) * 8;
+  // ---- block -> (n block, m block, k slice)
+  const int L = blockIdx.x, xcd = L & 7, slot = L >> 3;
+  const int mb = slot % g.nbm;
+  const int unit = (slot / g.nbm) * 8 + xcd;
+  if (unit >= g.nbn * g.KS) return;  // grid padding
+  const int nb = unit % g.nbn, ks = unit / g.nbn;
+  const int n0 = nb * BN, m0 = mb * BM;
+  const int kbeg = ks * g.kslice, nk = g.kslice / BK;
 
-  struct Stage {
-    Raw8 w[U];
-    Raw8 a[U][MR];
-  };
-  auto fetch = [&](Stage& st, int it) {
+  // ---- per-thread load sources (fixed rows, k advances)
+  const int wrow = tid >> 2, wpc = (tid & 3) * 8;
+  const S* wsrc;
+  {
+    const int n = min(n0 + wrow, g.N - 1);
+    int sg = 0;
+    while (sg + 1 < g.nseg && n >= g.seg_start[sg + 1]) ++sg;
+    wsrc = reinterpret_cast<const S*>(g.seg_ptr[sg]) + (size_t)(n - g.seg_start[sg]) * g.K + wpc;
+  }
+  auto arow = [&](int i) { return (tid + i * 512) >> 2; };
+  auto apc = [&](int i) { return ((tid + i * 512) & 3) * 8; };
+  auto aok = [&](int i) { return tid + i * 512 < BM * 4; };
+
+  auto gload = [&](MtRegs<S, MF, SRC, LO>& r, int kt) {
+    const int k = kbeg + kt * BK;
+    load_raw8<S>(r.w, wsrc + k);
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int ks = (it * U + u) * 32;
-      load_raw8_nt<S>(st.w[u], wp + ks);
-      const int k = kbase + ks;
+    for (int i = 0; i < APT; ++i) {
+      if (!aok(i)) continue;
+      const int m = min(m0 + arow(i), g.M - 1);
       if constexpr (SRC == SRC_SPLIT) {
-#pragma unroll
-        for (int mi = 0; mi < MR; ++mi) {
-          const size_t o = (size_t)arow[mi] * g.lda + k;
-          st.a[u][mi].lo = *reinterpret_cast<const u32x4*>(reinterpret_cast<const bf16_t*>(g.a_hi) + o);
-          if (LO) st.a[u][mi].hi = *reinterpret_cast<const u32x4*>(reinterpret_cast<const bf16_t*>(g.a_lo) + o);
-        }
+        const size_t o = (size_t)m * g.lda + k + apc(i);
+        r.a[i].lo = *reinterpret_cast<const u32x4*>(reinterpret_cast<const bf16_t*>(g.a_hi) + o);
+        if constexpr (LO) r.l[i].lo = *reinterpret_cast<const u32x4*>(reinterpret_cast<const bf16_t*>(g.a_lo) + o);
       } else {
-        const int kstep = wk * g.kw + ks;
-        const int j = kstep / g.src_width;
-        const S* src = reinterpret_cast<const S*>(g.src[j]);
-        const int off = k - j * g.src_width;
-#pragma unroll
-        for (int mi = 0; mi < MR; ++mi) load_raw8<S>(st.a[u][mi], src + (size_t)arow[mi] * g.src_width + off);
+        const int kg = k + apc(i);
+        const int j = kg / g.src_width;
+        load_raw8<S>(r.a[i], reinterpret_cast<const S*>(g.src[j]) + (size_t)m * g.src_width + (kg - j * g.src_width));
       }
     }
   };
-  f32x4 acc[MR];
+  auto sstore = [&](const MtRegs<S, MF, SRC, LO>& r, int buf) {
+    bf16_t* st = sm + buf * STAGE;
+    *reinterpret_cast<bf16x8*>(&st[(NA * BM + wrow) * LDK + wpc]) = raw_to_bf16x8<S>(r.w);
 #pragma unroll
-  for (int mi = 0; mi < MR; ++mi) acc[mi] = f32x4{0.f, 0.f, 0.f, 0.f};
-  auto compute = [&](const Stage& st) {
+    for (int i = 0; i < APT; ++i) {
+      if (!aok(i)) continue;
+      bf16x8 hv, lv;
+      if constexpr (SRC == SRC_SPLIT) {
+        hv = __builtin_bit_cast(bf16x8, r.a[i].lo);
+        if constexpr (LO) lv = __builtin_bit_cast(bf16x8, r.l[i].lo);
+      } else if constexpr (sizeof(S) == 2) {
+        hv = raw_to_bf16x8<S>(r.a[i]);
+      } else {  // fp32 sources: split on the fly
+        float f[8];
+        raw_to_f32x8<S>(r.a[i], f);
+        f32x4 l0, l1;
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const bf16x8 wv = raw_to_bf16x8<S>(st.w[u]);
+        for (int e = 0; e < 8; ++e) hv[e] = (__bf16)f[e];
 #pragma unroll
-      for (int mi = 0; mi < MR; ++mi) {
-        if constexpr (SRC == SRC_SPLIT) {
-          acc[mi] = mfma16x16x32(wv, __builtin_bit_cast(bf16x8, st.a[u][mi].lo), acc[mi]);
-          if (LO) acc[mi] = mfma16x16x32(wv, __builtin_bit_cast(bf16x8, st.a[u][mi].hi), acc[mi]);
-        } else if constexpr (sizeof(S) == 2) {
-          acc[mi] = mfma16x16x32(wv, raw_to_bf16x8<S>(st.a[u][mi]), acc[mi]);
-        } else {  // fp32 sources: split on the fly
-          float f[8];
-          raw_to_f32x8<S>(st.a[u][mi], f);
-          bf16x8 hv;
-          f32x4 l0, l1;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) hv[e] = (__bf16)f[e];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            l0[e] = f[e] - (float)hv[e];
-            l1[e] = f[4 + e] - (float)hv[4 + e];
-          }
-          acc[mi] = mfma16x16x32(wv, hv, acc[mi]);
-          acc[mi] = mfma16x16x32(wv, f32x8_to_bf16x8(l0, l1), acc[mi]);
+        for (int e = 0; e < 4; ++e) {
+          l0[e] = f[e] - (float)hv[e];
+          l1[e] = f[4 + e] - (float)hv[4 + e];
         }
+        lv = f32x8_to_bf16x8(l0, l1);
       }
+      *reinterpret_cast<bf16x8*>(&st[arow(i) * LDK + apc(i)]) = hv;
+      if constexpr (LO) *reinterpret_cast<bf16x8*>(&st[(BM + arow(i)) * LDK + apc(i)]) = lv;
     }
   };
-  const int niter = g.kw / (32 * U);
-  Stage s0, s1;
-  if (niter > 0) fetch(s0, 0);
-  for (int it = 0; it < niter; it += 2) {
-    if (it + 1 < niter) fetch(s1, it + 1);
-    compute(s0);
-    if (it + 1 < niter) {
-      if (it + 2 < niter) fetch(s0, it + 2);
-      compute(s1);
+
+  f32x4 acc[4][MF];
+#pragma unroll
+  for (int fn = 0; fn < 4; ++fn)
+#pragma unroll
+    for (int fm = 0; fm < MF; ++fm) acc[fn][fm] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](int buf) {
+    const bf16_t* st = sm + buf * STAGE;
+    const int fr = (lane & 15) * LDK + 8 * (lane >> 4);
+    bf16x8 wf[4], af[MF], al[MF];
+#pragma unroll
+    for (int fn = 0; fn < 4; ++fn)
+      wf[fn] = *reinterpret_cast<const bf16x8*>(&st[(NA * BM + 64 * wn + 16 * fn) * LDK + fr]);
+#pragma unroll
+    for (int fm = 0; fm < MF; ++fm) {
+      af[fm] = *reinterpret_cast<const bf16x8*>(&st[(16 * MF * wm + 16 * fm) * LDK + fr]);
+      if constexpr (LO) al[fm] = *reinterpret_cast<const bf16x8*>(&st[(BM + 16 * MF * wm + 16 * fm) * LDK + fr]);
     }
+#pragma unroll
+    for (int fn = 0; fn < 4; ++fn)
+#pragma unroll
+      for (int fm = 0; fm < MF; ++fm) {
+        acc[fn][fm] = mfma16x16x32(wf[fn], af[fm], acc[fn][fm]);
+        if constexpr (LO) acc[fn][fm] = mfma16x16x32(wf[fn], al[fm], acc[fn][fm]);
+      }
+  };
+
+  // ---- pipeline: registers R0/R1 alternate, LDS buffers alternate
+  MtRegs<S, MF, SRC, LO> r0, r1;
+  gload(r0, 0);
+  if (nk > 1) gload(r1, 1);
+  sstore(r0, 0);
+  __syncthreads();
+  auto step = [&](MtRegs<S, MF, SRC, LO>& cur, MtRegs<S, MF, SRC, LO>& nxt, int kt) {
+    // cur: free (its stage kt is in LDS);  nxt: stage kt+1 in flight
+    if (kt + 2 < nk) gload(cur, kt + 2);
+    compute(kt & 1);
+    if (kt + 1 < nk) sstore(nxt, (kt + 1) & 1);
+    __syncthreads();
+  };
+  for (int kt = 0; kt < nk; kt += 2) {
+    step(r0, r1, kt);
+    if (kt + 1 < nk) step(r1, r0, kt + 1);
   }
 
-  float* red = smem;
-#pragma unroll
-  for (int mi = 0; mi < MR; ++mi)
-    *reinterpret_cast<f32x4*>(red + ((wk * MT + 16 * mi + (lane & 15)) * NT + 16 * wn + 4 * (lane >> 4))) = acc[mi];
-  __syncthreads();
-  const int tsz = MT * NT;
-  for (int e = tid; e < tsz; e += nthr) {
-    float v = red[e];
-    for (int w = 1; w < WK; ++w) v += red[w * tsz + e];
-    red[e] = v;
-  }
-  __syncthreads();
+  // ---- epilogue.  lane holds Y[m = (lane & 15) + row base][n = 4*(lane >> 4) + i + column base]
   if constexpr (OUT == OUT_PARTIAL) {
-    for (int e = tid; e < tsz; e += nthr) {
-      const int m = e / NT, j = e - m * NT;
-      if (m0 + m < g.M) g.part[((size_t)(blockIdx.x * WN + (j >> 4)) * g.M + m0 + m) * 16 + (j & 15)] = red[e];
-    }
-    if (g.rinv_out != nullptr && blockIdx.y == 0) write_rinv(g);
-  } else {
-    if (g.logits_dbg != nullptr) {
-      for (int e = tid; e < tsz; e += nthr) {
-        const int m = e / NT, j = e - m * NT;
-        if (m0 + m < g.M)
-          g.logits_dbg[(size_t)(m0 + m) * g.N + blockIdx.x * NT + j] =
-              red[e] * row_rinv(g.ssq_in, g.ssq_nparts, g.ld_ssq, m0 + m, g.K, g.eps);
-      }
-    }
-    for (int base = 0; base < MT * 16; base += nthr) {
-      const int t = base + tid;
-      const int m = t >> 4, part = t & 15;
-      uint64_t best = 0;
-      if (m < MT)
-        for (int j = part; j < NT; j += 16) {
-          const uint64_t k = argmax_key(red[m * NT + j], (uint32_t)(blockIdx.x * NT + j));
-          best = k > best ? k : best;
-        }
+    const int ntiles = g.N >> 4;
 #pragma unroll
-      for (int s = 8; s >= 1; s >>= 1) {
-        const uint64_t o = shfl_xor_u64(best, s);
-        best = o > best ? o : best;
+    for (int fn = 0; fn < 4; ++fn) {
+      const int n = n0 + 64 * wn + 16 * fn;
+      if (n >= g.N) continue;
+#pragma unroll
+      for (int fm = 0; fm < MF; ++fm) {
+        const int m = m0 + 16 * MF * wm + 16 * fm + (lane & 15);
+        if (m < g.M)
+          *reinterpret_cast<f32x4*>(g.part + (((size_t)ks * ntiles + (n >> 4)) * g.M + m) * 16 + 4 * (lane >> 4)) =
+              acc[fn][fm];
       }
-      if (part == 0 && m < MT && m0 + m < g.M) g.best_part[(size_t)blockIdx.x * g.ld_best + m0 + m] = best;
+    }
+    if (g.rinv_out != nullptr && ks == 0) write_rinv(g, nb * g.nbm + mb, g.nbn * g.nbm);
+  } else {
+    uint64_t* sb = reinterpret_cast<uint64_t*>(sm);  // [2][BM]; the ring is idle after the last barrier
+#pragma unroll
+    for (int fm = 0; fm < MF; ++fm) {
+      uint64_t best = 0;
+#pragma unroll
+      for (int fn = 0; fn < 4; ++fn) {
+        const int n = n0 + 64 * wn + 16 * fn;
+        if (n < g.N) {
+          const uint64_t t = tile_row_best(acc[fn][fm], n, lane);
+          best = t > best ? t : best;
+        }
+      }
+      if ((lane >> 4) == 0) sb[wn * BM + 16 * MF * wm + 16 * fm + (lane & 15)] = best;
+    }
+    if (g.logits_dbg != nullptr) {
+#pragma unroll
+      for (int fn = 0; fn < 4; ++fn) {
+        const int n = n0 + 64 * wn + 16 * fn;
+        if (n >= g.N) continue;
+#pragma unroll
+        for (int fm = 0; fm < MF; ++fm) {
+          const int m = m0 + 16 * MF * wm + 16 * fm + (lane & 15);
+          if (m >= g.M) continue;
+          const float r = row_rinv(g.ssq_in, g.ssq_nparts, g.ld_ssq, m, g.K, g.eps);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) g.logits_dbg[(size_t)m * g.N + n + 4 * (lane >> 4) + i] = acc[fn][fm][i] * r;
+        }
+      }
+    }
+    __syncthreads();
+    for (int rr = tid; rr < BM; rr += 512) {
+      const uint64_t a = sb[rr], b = sb[BM + rr];
+      if (m0 + rr < g.M) g.best_part[(size_t)nb * g.ld_best + m0 + rr] = a > b ? a : b;
     }
   }
 }
 
 // ------------------------------------------------------------------ argmax reduce
-// draft id of each row = index of the largest packed key over the LM-head tiles.
-__global__ void __launch_bounds__(256) argmax_reduce_kernel(const uint64_t* part, int ntiles, int ld, int32_t* ids) {
-  __shared__ uint64_t s_best[4];
+// draft id of each row = index of the largest packed key over the LM-head
+// column blocks.  One workgroup of 1024 threads per row; a thread's loads are
+// issued together (8 per round).
+__global__ void __launch_bounds__(1024) argmax_reduce_kernel(const uint64_t* part, int ntiles, int ld, int32_t* ids) {
+  __shared__ uint64_t s_best[16];
   const int m = blockIdx.x, tid = threadIdx.x;
   uint64_t best = 0;
-  for (int t = tid; t < ntiles; t += 256) {
-    const uint64_t k = part[(size_t)t * ld + m];
-    best = k > best ? k : best;
+  for (int t0 = 0; t0 < ntiles; t0 += 8 * 1024) {
+    uint64_t v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int t = t0 + i * 1024 + tid;
+      v[i] = t < ntiles ? part[(size_t)t * ld + m] : 0ull;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) best = v[i] > best ? v[i] : best;
   }
   best = wave_max_u64(best);
   if ((tid & 63) == 0) s_best[tid >> 6] = best;
   __syncthreads();
   if (tid == 0) {
     uint64_t b = s_best[0];
-    for (int w = 1; w < 4; ++w) b = s_best[w] > b ? s_best[w] : b;
+    for (int w = 1; w < 16; ++w) b = s_best[w] > b ? s_best[w] : b;
     ids[m] = argmax_key_index(b);
   }
 }
@@ -640,8 +714,6 @@ size_t gemm_as_lds(int M, int ksl, bool lo) {
   return (size_t)(lo ? 2 : 1) * 16 * MR * (ksl + 8) * 2;
 }
 
-size_t gemm_ws_lds(int MR, int WN, int WK) { return (size_t)WK * 16 * MR * 16 * WN * sizeof(float); }
-int gemm_ws_max_threads(int MR) { return MR <= 4 ? 512 : 256; }
 
 template <typename Kern>
 static void allow_lds(Kern kernel, size_t bytes) {
@@ -657,9 +729,11 @@ static hipError_t launch_as(const GemmArgs& a, const GemmLaunch& l, hipStream_t 
   hipLaunchKernelGGL(k, l.grid, dim3(l.threads), l.lds, st, a);
   return hipGetLastError();
 }
-template <typename S, int MR, int SRC, bool LO, int OUT>
-static hipError_t launch_ws(const GemmArgs& a, const GemmLaunch& l, hipStream_t st) {
-  hipLaunchKernelGGL((gemm_ws_kernel<S, MR, SRC, LO, OUT>), l.grid, dim3(l.threads), l.lds, st, a);
+template <typename S, int MF, int SRC, bool LO, int OUT>
+static hipError_t launch_mt(const GemmArgs& a, const GemmLaunch& l, hipStream_t st) {
+  auto k = gemm_mt_kernel<S, MF, SRC, LO, OUT>;
+  allow_lds(k, l.lds);
+  hipLaunchKernelGGL(k, l.grid, dim3(l.threads), l.lds, st, a);
   return hipGetLastError();
 }
 
@@ -670,11 +744,10 @@ static hipError_t dispatch_mr(const GemmArgs& a, const GemmLaunch& l, hipStream_
     if (l.MR == 2) return launch_as<S, 2, SRC, LO, OUT>(a, l, st);
     return hipErrorInvalidValue;
   }
-  switch (l.MR) {
-    case 1: return launch_ws<S, 1, SRC, LO, OUT>(a, l, st);
-    case 2: return launch_ws<S, 2, SRC, LO, OUT>(a, l, st);
-    case 4: return launch_ws<S, 4, SRC, LO, OUT>(a, l, st);
-    case 8: return launch_ws<S, 8, SRC, LO, OUT>(a, l, st);
+  switch (l.MR) {  // GEMM_MT: MR = MF
+    case 1: return launch_mt<S, 1, SRC, LO, OUT>(a, l, st);
+    case 2: return launch_mt<S, 2, SRC, LO, OUT>(a, l, st);
+    case 4: return launch_mt<S, 4, SRC, LO, OUT>(a, l, st);
   }
   return hipErrorInvalidValue;
 }
@@ -700,7 +773,7 @@ hipError_t launch_gemm(int storage, const GemmArgs& a, const GemmLaunch& l, hipS
 }
 
 hipError_t launch_argmax_reduce(const uint64_t* part, int ntiles, int ld, int M, int32_t* ids, hipStream_t stream) {
-  hipLaunchKernelGGL(argmax_reduce_kernel, dim3(M), dim3(256), 0, stream, part, ntiles, ld, ids);
+  hipLaunchKernelGGL(argmax_reduce_kernel, dim3(M), dim3(1024), 0, stream, part, ntiles, ld, ids);
   return hipGetLastError();
 }
 

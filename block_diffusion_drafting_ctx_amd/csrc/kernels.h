@@ -20,7 +20,7 @@ enum SrcKind {
   SRC_CONCAT = 1   // A: concat of n_src arrays [M, src_width] of the storage type
 };
 enum OutKind { OUT_PARTIAL = 0, OUT_ARGMAX = 1 };
-enum GemmKind { GEMM_AS = 0, GEMM_WS = 1 };
+enum GemmKind { GEMM_AS = 0, GEMM_MT = 1 };
 
 constexpr int kMaxSeg = 16;
 constexpr size_t kGemmAsSliceLds = 68 * 1024;  // activation slice of a split-K workgroup (2 per CU)
@@ -40,8 +40,8 @@ struct GemmArgs {
   const void* src[8];
   int n_src, src_width;
   // launch geometry (filled by the planner)
-  int ksl, tpw;   // GEMM_AS: k-slice length, tiles per workgroup
-  int WN, WK, kw;  // GEMM_WS: waves along N and K, K per wave
+  int ksl, tpw;             // GEMM_AS: k-slice length, tiles per workgroup
+  int nbm, nbn, KS, kslice;  // GEMM_MT: M blocks, N blocks, k-slices, k-slice length
   // outputs
   float* part;          // OUT_PARTIAL
   uint64_t* best_part;  // OUT_ARGMAX [argmax tiles][ld_best]
@@ -72,8 +72,8 @@ hipError_t launch_gemm(int storage, const GemmArgs& a, const GemmLaunch& l, hipS
 // k-slice length gemm_as can use for (M, K) (0: gemm_as does not fit).
 int gemm_as_ksl(int M, int K, bool lo, bool argmax);
 size_t gemm_as_lds(int M, int ksl, bool lo);
-size_t gemm_ws_lds(int MR, int WN, int WK);
-int gemm_ws_max_threads(int MR);
+// LDS bytes of gemm_mt with BM = 64 * MF rows (lo: hi/lo activation pair).
+size_t gemm_mt_lds_bytes(int MF, bool lo);
 // ids[m] = index of the largest key over part[t][m], t < ntiles.
 hipError_t launch_argmax_reduce(const uint64_t* part, int ntiles, int ld, int M, int32_t* ids, hipStream_t stream);
 
