@@ -92,11 +92,12 @@ bool plan_gemm(int storage, int src, int out, bool lo, int M, int N, int K, Gemm
     a->tpw = NW;
     return true;
   }
-  // gemm_mt: BM = 64 * MF rows by 128 columns per workgroup; split K until
-  // the grid fills the chip (one 8-wave workgroup per compute unit)
+  // gemm_mt: BM = 64 * MF rows by BN = 32 * NF columns per workgroup; split K
+  // until the grid fills the chip (one 8-wave workgroup per compute unit)
   const int MF = M <= 64 ? 1 : (M <= 128 ? 2 : 4);
+  const int BN = 32 * gemm_mt_nf(MF);
   const int nbm = (M + 64 * MF - 1) / (64 * MF);
-  const int nbn = (N + 127) / 128;
+  const int nbn = (N + BN - 1) / BN;
   int KS = 1;
   if (out == OUT_PARTIAL)
     while (nbn * nbm * KS < kMtTargetWgs && (K / 32) % (2 * KS) == 0 && K / (2 * KS) >= 256) KS *= 2;

@@ -224,44 +224,53 @@ __global__ void __launch_bounds__(512) gemm_as_kernel(const GemmArgs g) {
 
 // ------------------------------------------------------------------ gemm_mt
 // LDS-tiled product for M > 32 (batched drafting, batched fusion).  A
-// workgroup of 8 waves computes a BM x 128 block of Y (BM = 64 * MF): the
-// waves are 4 along M (16*MF rows each) by 2 along N (64 columns each), so a
-// wave holds 4 x MF 16x16 accumulators and reads 4 weight and MF (x2 for
-// hi/lo) activation fragments per 32-deep k-step.  K advances in stages of 32
-// through a double-buffered LDS ring; the global loads of stage t+2 are issued
-// into registers before the matrix work of stage t (two stages of latency
-// cover), and stored to LDS after it.  One barrier per stage.
+// workgroup of 8 waves computes a BM x BN block of Y with BM = 64*MF and
+// BN = 32*NF: the waves are 4 along M (16*MF rows each) by 2 along N (16*NF
+// columns each), so a wave holds NF x MF 16x16 accumulators and reads NF
+// weight and MF (x2 for hi/lo) activation fragments per 32-deep k-step.  The
+// fragment reads per matrix-core op fall as the wave tile grows, which is what
+// keeps LDS bandwidth below its 128 B/clk limit at MF = 4, NF = 8.  K advances
+// in stages of 32 through a double-buffered LDS ring; global loads run DEPTH
+// stages ahead in registers (2 for the small tiles, 1 where the accumulators
+// need the registers and a stage's matrix work alone covers the latency).
+// One barrier per stage.
 //
 // Blocks are numbered so that the M blocks sharing a weight block are
 // dispatched back to back on the same XCD (workgroup L runs on XCD L % 8), so
 // the weight block is fetched from HBM once into that XCD's L2.
-template <int MF>
+template <int MF, int NF>
 struct MtShape {
   static constexpr int BM = 64 * MF;
-  static constexpr int BN = 128;
+  static constexpr int BN = 32 * NF;
   static constexpr int BK = 32;
   static constexpr int LDK = BK + 8;  // LDS row stride (elements): conflict-free 16-byte fragment reads
   static constexpr int APT = (BM * 4 + 511) / 512;  // activation pieces per thread per array
+  static constexpr int WPT = (BN * 4 + 511) / 512;  // weight pieces per thread
+  static constexpr int DEPTH = NF >= 8 ? 1 : 2;
 };
 
-template <typename S, int MF, int SRC, bool LO>
+template <int MF, int SRC, bool LO>
 struct MtRegs {
-  Raw8 w;
-  Raw8 a[MtShape<MF>::APT];
-  Raw8 l[LO && SRC == SRC_SPLIT ? MtShape<MF>::APT : 1];
+  Raw8 w[MtShape<MF, (MF >= 4 ? 8 : 4)>::WPT];
+  Raw8 a[MtShape<MF, 4>::APT];
+  Raw8 l[LO && SRC == SRC_SPLIT ? MtShape<MF, 4>::APT : 1];
 };
+
+int gemm_mt_nf(int MF) { return MF >= 4 ? 8 : 4; }
 
 size_t gemm_mt_lds_bytes(int MF, bool lo) {
-  const int BM = 64 * MF;
-  return (size_t)2 * ((lo ? 2 : 1) * BM + 128) * (32 + 8) * 2;
+  const int BM = 64 * MF, BN = 32 * gemm_mt_nf(MF);
+  return (size_t)2 * ((lo ? 2 : 1) * BM + BN) * (32 + 8) * 2;
 }
 
 template <typename S, int MF, int SRC, bool LO, int OUT>
 __global__ void __launch_bounds__(512) gemm_mt_kernel(const GemmArgs g) {
-  using Sh = MtShape<MF>;
-  constexpr int BM = Sh::BM, BN = Sh::BN, BK = Sh::BK, LDK = Sh::LDK, APT = Sh::APT;
+  constexpr int NF = MF >= 4 ? 8 : 4;
+  using Sh = MtShape<MF, NF>;
+  constexpr int BM = Sh::BM, BN = Sh::BN, BK = Sh::BK, LDK = Sh::LDK, APT = Sh::APT, WPT = Sh::WPT;
   constexpr int NA = LO ? 2 : 1;
   constexpr int STAGE = (NA * BM + BN) * LDK;
+  using Regs = MtRegs<MF, SRC, LO>;
   extern __shared__ __align__(16) bf16_t sm[];  // [2][NA*BM + BN][LDK]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave & 3, wn = wave >> 2;
@@ -276,39 +285,42 @@ __global__ void __launch_bounds__(512) gemm_mt_kernel(const GemmArgs g) {
   const int kbeg = ks * g.kslice, nk = g.kslice / BK;
 
   // ---- per-thread load sources (fixed rows, k advances)
-  const int wrow = tid >> 2, wpc = (tid & 3) * 8;
-  const S* wsrc;
-  {
-    const int n = min(n0 + wrow, g.N - 1);
+  const S* wsrc[WPT];
+#pragma unroll
+  for (int i = 0; i < WPT; ++i) {
+    const int n = min(n0 + ((tid + i * 512) >> 2), g.N - 1);
     int sg = 0;
     while (sg + 1 < g.nseg && n >= g.seg_start[sg + 1]) ++sg;
-    wsrc = reinterpret_cast<const S*>(g.seg_ptr[sg]) + (size_t)(n - g.seg_start[sg]) * g.K + wpc;
+    wsrc[i] = reinterpret_cast<const S*>(g.seg_ptr[sg]) + (size_t)(n - g.seg_start[sg]) * g.K + (tid & 3) * 8;
   }
-  auto arow = [&](int i) { return (tid + i * 512) >> 2; };
-  auto apc = [&](int i) { return ((tid + i * 512) & 3) * 8; };
+  auto prow = [&](int i) { return (tid + i * 512) >> 2; };  // row of a thread's i-th piece
+  const int pc = (tid & 3) * 8;                             // its column within the stage
   auto aok = [&](int i) { return tid + i * 512 < BM * 4; };
 
-  auto gload = [&](MtRegs<S, MF, SRC, LO>& r, int kt) {
+  auto gload = [&](Regs& r, int kt) {
     const int k = kbeg + kt * BK;
-    load_raw8<S>(r.w, wsrc + k);
+#pragma unroll
+    for (int i = 0; i < WPT; ++i) load_raw8<S>(r.w[i], wsrc[i] + k);
 #pragma unroll
     for (int i = 0; i < APT; ++i) {
       if (!aok(i)) continue;
-      const int m = min(m0 + arow(i), g.M - 1);
+      const int m = min(m0 + prow(i), g.M - 1);
       if constexpr (SRC == SRC_SPLIT) {
-        const size_t o = (size_t)m * g.lda + k + apc(i);
+        const size_t o = (size_t)m * g.lda + k + pc;
         r.a[i].lo = *reinterpret_cast<const u32x4*>(reinterpret_cast<const bf16_t*>(g.a_hi) + o);
         if constexpr (LO) r.l[i].lo = *reinterpret_cast<const u32x4*>(reinterpret_cast<const bf16_t*>(g.a_lo) + o);
       } else {
-        const int kg = k + apc(i);
+        const int kg = k + pc;
         const int j = kg / g.src_width;
         load_raw8<S>(r.a[i], reinterpret_cast<const S*>(g.src[j]) + (size_t)m * g.src_width + (kg - j * g.src_width));
       }
     }
   };
-  auto sstore = [&](const MtRegs<S, MF, SRC, LO>& r, int buf) {
+  auto sstore = [&](const Regs& r, int buf) {
     bf16_t* st = sm + buf * STAGE;
-    *reinterpret_cast<bf16x8*>(&st[(NA * BM + wrow) * LDK + wpc]) = raw_to_bf16x8<S>(r.w);
+#pragma unroll
+    for (int i = 0; i < WPT; ++i)
+      *reinterpret_cast<bf16x8*>(&st[(NA * BM + prow(i)) * LDK + pc]) = raw_to_bf16x8<S>(r.w[i]);
 #pragma unroll
     for (int i = 0; i < APT; ++i) {
       if (!aok(i)) continue;
@@ -331,61 +343,73 @@ __global__ void __launch_bounds__(512) gemm_mt_kernel(const GemmArgs g) {
         }
         lv = f32x8_to_bf16x8(l0, l1);
       }
-      *reinterpret_cast<bf16x8*>(&st[arow(i) * LDK + apc(i)]) = hv;
-      if constexpr (LO) *reinterpret_cast<bf16x8*>(&st[(BM + arow(i)) * LDK + apc(i)]) = lv;
+      *reinterpret_cast<bf16x8*>(&st[prow(i) * LDK + pc]) = hv;
+      if constexpr (LO) *reinterpret_cast<bf16x8*>(&st[(BM + prow(i)) * LDK + pc]) = lv;
     }
   };
 
-  f32x4 acc[4][MF];
+  f32x4 acc[NF][MF];
 #pragma unroll
-  for (int fn = 0; fn < 4; ++fn)
+  for (int fn = 0; fn < NF; ++fn)
 #pragma unroll
     for (int fm = 0; fm < MF; ++fm) acc[fn][fm] = f32x4{0.f, 0.f, 0.f, 0.f};
   auto compute = [&](int buf) {
     const bf16_t* st = sm + buf * STAGE;
     const int fr = (lane & 15) * LDK + 8 * (lane >> 4);
-    bf16x8 wf[4], af[MF], al[MF];
-#pragma unroll
-    for (int fn = 0; fn < 4; ++fn)
-      wf[fn] = *reinterpret_cast<const bf16x8*>(&st[(NA * BM + 64 * wn + 16 * fn) * LDK + fr]);
+    bf16x8 af[MF], al[MF];
 #pragma unroll
     for (int fm = 0; fm < MF; ++fm) {
       af[fm] = *reinterpret_cast<const bf16x8*>(&st[(16 * MF * wm + 16 * fm) * LDK + fr]);
       if constexpr (LO) al[fm] = *reinterpret_cast<const bf16x8*>(&st[(BM + 16 * MF * wm + 16 * fm) * LDK + fr]);
     }
 #pragma unroll
-    for (int fn = 0; fn < 4; ++fn)
+    for (int fn = 0; fn < NF; ++fn) {
+      const bf16x8 wf = *reinterpret_cast<const bf16x8*>(&st[(NA * BM + 16 * NF * wn + 16 * fn) * LDK + fr]);
 #pragma unroll
       for (int fm = 0; fm < MF; ++fm) {
-        acc[fn][fm] = mfma16x16x32(wf[fn], af[fm], acc[fn][fm]);
-        if constexpr (LO) acc[fn][fm] = mfma16x16x32(wf[fn], al[fm], acc[fn][fm]);
+        acc[fn][fm] = mfma16x16x32(wf, af[fm], acc[fn][fm]);
+        if constexpr (LO) acc[fn][fm] = mfma16x16x32(wf, al[fm], acc[fn][fm]);
       }
+    }
   };
 
-  // ---- pipeline: registers R0/R1 alternate, LDS buffers alternate
-  MtRegs<S, MF, SRC, LO> r0, r1;
-  gload(r0, 0);
-  if (nk > 1) gload(r1, 1);
-  sstore(r0, 0);
-  __syncthreads();
-  auto step = [&](MtRegs<S, MF, SRC, LO>& cur, MtRegs<S, MF, SRC, LO>& nxt, int kt) {
-    // cur: free (its stage kt is in LDS);  nxt: stage kt+1 in flight
-    if (kt + 2 < nk) gload(cur, kt + 2);
-    compute(kt & 1);
-    if (kt + 1 < nk) sstore(nxt, (kt + 1) & 1);
+  // ---- pipeline
+  if constexpr (Sh::DEPTH == 1) {
+    Regs r;
+    gload(r, 0);
+    sstore(r, 0);
     __syncthreads();
-  };
-  for (int kt = 0; kt < nk; kt += 2) {
-    step(r0, r1, kt);
-    if (kt + 1 < nk) step(r1, r0, kt + 1);
+    for (int kt = 0; kt < nk; ++kt) {
+      if (kt + 1 < nk) gload(r, kt + 1);
+      compute(kt & 1);
+      if (kt + 1 < nk) sstore(r, (kt + 1) & 1);
+      __syncthreads();
+    }
+  } else {  // registers r0 / r1 alternate
+    Regs r0, r1;
+    gload(r0, 0);
+    if (nk > 1) gload(r1, 1);
+    sstore(r0, 0);
+    __syncthreads();
+    auto step = [&](Regs& cur, Regs& nxt, int kt) {
+      // cur: free (its stage kt is in LDS);  nxt: stage kt+1 in flight
+      if (kt + 2 < nk) gload(cur, kt + 2);
+      compute(kt & 1);
+      if (kt + 1 < nk) sstore(nxt, (kt + 1) & 1);
+      __syncthreads();
+    };
+    for (int kt = 0; kt < nk; kt += 2) {
+      step(r0, r1, kt);
+      if (kt + 1 < nk) step(r1, r0, kt + 1);
+    }
   }
 
   // ---- epilogue.  lane holds Y[m = (lane & 15) + row base][n = 4*(lane >> 4) + i + column base]
   if constexpr (OUT == OUT_PARTIAL) {
     const int ntiles = g.N >> 4;
 #pragma unroll
-    for (int fn = 0; fn < 4; ++fn) {
-      const int n = n0 + 64 * wn + 16 * fn;
+    for (int fn = 0; fn < NF; ++fn) {
+      const int n = n0 + 16 * NF * wn + 16 * fn;
       if (n >= g.N) continue;
 #pragma unroll
       for (int fm = 0; fm < MF; ++fm) {
@@ -402,8 +426,8 @@ __global__ void __launch_bounds__(512) gemm_mt_kernel(const GemmArgs g) {
     for (int fm = 0; fm < MF; ++fm) {
       uint64_t best = 0;
 #pragma unroll
-      for (int fn = 0; fn < 4; ++fn) {
-        const int n = n0 + 64 * wn + 16 * fn;
+      for (int fn = 0; fn < NF; ++fn) {
+        const int n = n0 + 16 * NF * wn + 16 * fn;
         if (n < g.N) {
           const uint64_t t = tile_row_best(acc[fn][fm], n, lane);
           best = t > best ? t : best;
@@ -413,8 +437,8 @@ __global__ void __launch_bounds__(512) gemm_mt_kernel(const GemmArgs g) {
     }
     if (g.logits_dbg != nullptr) {
 #pragma unroll
-      for (int fn = 0; fn < 4; ++fn) {
-        const int n = n0 + 64 * wn + 16 * fn;
+      for (int fn = 0; fn < NF; ++fn) {
+        const int n = n0 + 16 * NF * wn + 16 * fn;
         if (n >= g.N) continue;
 #pragma unroll
         for (int fm = 0; fm < MF; ++fm) {

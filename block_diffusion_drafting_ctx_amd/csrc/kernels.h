@@ -72,7 +72,9 @@ hipError_t launch_gemm(int storage, const GemmArgs& a, const GemmLaunch& l, hipS
 // k-slice length gemm_as can use for (M, K) (0: gemm_as does not fit).
 int gemm_as_ksl(int M, int K, bool lo, bool argmax);
 size_t gemm_as_lds(int M, int ksl, bool lo);
-// LDS bytes of gemm_mt with BM = 64 * MF rows (lo: hi/lo activation pair).
+// gemm_mt block: BM = 64 * MF rows by BN = 32 * gemm_mt_nf(MF) columns;
+// LDS bytes of its stage ring (lo: hi/lo activation pair).
+int gemm_mt_nf(int MF);
 size_t gemm_mt_lds_bytes(int MF, bool lo);
 // ids[m] = index of the largest key over part[t][m], t < ntiles.
 hipError_t launch_argmax_reduce(const uint64_t* part, int ntiles, int ld, int M, int32_t* ids, hipStream_t stream);
