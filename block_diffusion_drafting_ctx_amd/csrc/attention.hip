@@ -125,23 +125,22 @@ __global__ void __launch_bounds__(kThreads) attention_kernel(const AttnArgs a) {
     const int h = (idx / PIECES) & 1, rest = idx / (2 * PIECES);
     kp = (rest & 15) + 16 * h + 32 * (rest >> 4);
   };
+  // Loads are unconditional (keys past the split re-read its last key and are
+  // zeroed at the store): branch-free address selects keep the loads of a
+  // stage in flight together.
   auto stage_load = [&](int c0) {
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
       const int idx = tid + i * kThreads;
       const int key = idx / PIECES, p8 = (idx % PIECES) * 8;
-      const int j = c0 + key;
-      if (j < j1) load_raw8<S>(kreg[i], key_ptr(kc, kb, j) + p8);
+      load_raw8<S>(kreg[i], key_ptr(kc, kb, min(c0 + key, j1 - 1)) + p8);
     }
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
       int kp, p;
       v_item(tid + i * kThreads, kp, p);
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const int j = c0 + 2 * kp + t;
-        if (j < j1) load_raw8<S>(vreg[i][t], key_ptr(vc, vb, j) + 8 * p);
-      }
+      for (int t = 0; t < 2; ++t) load_raw8<S>(vreg[i][t], key_ptr(vc, vb, min(c0 + 2 * kp + t, j1 - 1)) + 8 * p);
     }
   };
   auto stage_store = [&](int c0) {
