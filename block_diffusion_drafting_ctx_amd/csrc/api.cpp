@@ -30,7 +30,8 @@ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 constexpr int kMaxNd = 64;
 constexpr int kVerifyChunk = 16384;  // vocab entries per workgroup of the verify argmax
-constexpr int kMtTargetWgs = 256;    // gemm_mt workgroups to aim for (one per compute unit)
+constexpr int kCUs = 256;            // compute units of the chip
+constexpr int kMtTargetWgs = kCUs;   // gemm_mt workgroups to aim for (one per compute unit)
 constexpr int kAttnTargetWgs = 512;  // attention workgroups to aim for (two per compute unit)
 constexpr int kAttnStage = 128;      // keys per attention LDS stage (splits are whole stages)
 
@@ -80,16 +81,23 @@ bool plan_gemm(int storage, int src, int out, bool lo, int M, int N, int K, Gemm
   a->K = K;
   const int ksl = gemm_as_ksl(M, K, lo_eff, out == OUT_ARGMAX);
   if (ksl > 0) {
-    const int NW = ntiles >= 1024 ? 8 : 4;
+    // one workgroup per compute unit: the k-slices share the chip, a
+    // workgroup stages its activation slice once and its waves stream
+    // ceil(tpw / NW) tiles each (at most 16 waves)
+    const int KS = K / ksl;
+    const int per_slice = std::max(1, kCUs / KS);
+    const int tpw = (ntiles + per_slice - 1) / per_slice;
+    const int per_wave = (tpw + 15) / 16;
+    const int NW = (tpw + per_wave - 1) / per_wave;
     l->kind = GEMM_AS;
     l->MR = M <= 16 ? 1 : 2;
-    l->KS = K / ksl;
-    l->grid = dim3((ntiles + NW - 1) / NW, l->KS);
+    l->KS = KS;
+    l->grid = dim3((ntiles + tpw - 1) / tpw, KS);
     l->threads = 64 * NW;
     l->lds = gemm_as_lds(M, ksl, lo_eff);
     l->argmax_tiles = ntiles;
     a->ksl = ksl;
-    a->tpw = NW;
+    a->tpw = tpw;
     return true;
   }
   // gemm_mt: BM = 64 * MF rows by BN = 32 * NF columns per workgroup; split K

@@ -106,7 +106,7 @@ struct AsShape {
 };
 
 template <typename S, int MR, int SRC, bool LO, int OUT>
-__global__ void __launch_bounds__(512) gemm_as_kernel(const GemmArgs g) {
+__global__ void __launch_bounds__(1024) gemm_as_kernel(const GemmArgs g) {
   constexpr int MT = AsShape<MR>::MT;
   constexpr int U = AsShape<MR>::U;
   extern __shared__ __align__(16) bf16_t sa[];  // [LO ? 2 : 1][MT][ksl + 8]
@@ -126,27 +126,44 @@ __global__ void __launch_bounds__(512) gemm_as_kernel(const GemmArgs g) {
   const S* wp = tile_row_ptr<S>(g, tile < t1 ? tile : t0, lane, k0);
   if (tile < t1) fetch(wb0, wp, 0);  // first weight stage flies while the activations are staged
 
-  // ---- activation slice -> LDS (rows beyond M repeat row M-1; never stored)
+  // ---- activation slice -> LDS (rows beyond M repeat row M-1; never stored).
+  // A thread issues the loads of C pieces before storing any of them, so the
+  // staging costs one round of memory latency per C pieces, not one per piece.
   const int pr = g.ksl / 8;  // 8-element pieces per row
-  for (int p = tid; p < MT * pr; p += blockDim.x) {
-    const int row = p / pr, col = (p - row * pr) * 8;
-    const int m = min(row, g.M - 1);
-    bf16x8 hv, lv;
-    if constexpr (SRC == SRC_SPLIT) {
-      const size_t o = (size_t)m * g.lda + k0 + col;
-      hv = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(reinterpret_cast<const bf16_t*>(g.a_hi) + o));
-      if (LO)
-        lv = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(reinterpret_cast<const bf16_t*>(g.a_lo) + o));
-    } else {
-      const int kg = k0 + col;
-      const int j = kg / g.src_width;
-      Raw8 raw;
-      load_raw8<S>(raw, reinterpret_cast<const S*>(g.src[j]) + (size_t)m * g.src_width + (kg - j * g.src_width));
-      if constexpr (sizeof(S) == 2) {
-        hv = raw_to_bf16x8<S>(raw);
+  const int npieces = MT * pr;
+  constexpr int C = (LO || SRC == SRC_CONCAT) ? 4 : 8;
+  for (int p0 = 0; p0 < npieces; p0 += C * (int)blockDim.x) {
+    Raw8 rh[C], rl[C];
+#pragma unroll
+    for (int i = 0; i < C; ++i) {
+      const int p = p0 + i * (int)blockDim.x + tid;
+      if (p >= npieces) continue;
+      const int row = p / pr, col = (p - row * pr) * 8;
+      const int m = min(row, g.M - 1);
+      if constexpr (SRC == SRC_SPLIT) {
+        const size_t o = (size_t)m * g.lda + k0 + col;
+        rh[i].lo = *reinterpret_cast<const u32x4*>(reinterpret_cast<const bf16_t*>(g.a_hi) + o);
+        if constexpr (LO) rl[i].lo = *reinterpret_cast<const u32x4*>(reinterpret_cast<const bf16_t*>(g.a_lo) + o);
+      } else {
+        const int kg = k0 + col;
+        const int j = kg / g.src_width;
+        load_raw8<S>(rh[i], reinterpret_cast<const S*>(g.src[j]) + (size_t)m * g.src_width + (kg - j * g.src_width));
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < C; ++i) {
+      const int p = p0 + i * (int)blockDim.x + tid;
+      if (p >= npieces) continue;
+      const int row = p / pr, col = (p - row * pr) * 8;
+      bf16x8 hv, lv;
+      if constexpr (SRC == SRC_SPLIT) {
+        hv = __builtin_bit_cast(bf16x8, rh[i].lo);
+        if constexpr (LO) lv = __builtin_bit_cast(bf16x8, rl[i].lo);
+      } else if constexpr (sizeof(S) == 2) {
+        hv = raw_to_bf16x8<S>(rh[i]);
       } else {  // fp32 sources: split on the fly
         float f[8];
-        raw_to_f32x8<S>(raw, f);
+        raw_to_f32x8<S>(rh[i], f);
         f32x4 l0, l1;
 #pragma unroll
         for (int e = 0; e < 8; ++e) hv[e] = (__bf16)f[e];
@@ -157,9 +174,9 @@ __global__ void __launch_bounds__(512) gemm_as_kernel(const GemmArgs g) {
         }
         lv = f32x8_to_bf16x8(l0, l1);
       }
+      *reinterpret_cast<bf16x8*>(&sa[row * LDSW + col]) = hv;
+      if constexpr (LO) *reinterpret_cast<bf16x8*>(&sa[(MT + row) * LDSW + col]) = lv;
     }
-    *reinterpret_cast<bf16x8*>(&sa[row * LDSW + col]) = hv;
-    if (LO) *reinterpret_cast<bf16x8*>(&sa[(MT + row) * LDSW + col]) = lv;
   }
   __syncthreads();
 
