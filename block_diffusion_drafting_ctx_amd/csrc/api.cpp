@@ -79,15 +79,15 @@ bool plan_gemm(int storage, int src, int out, bool lo, int M, int N, int K, Gemm
   a->M = M;
   a->N = N;
   a->K = K;
-  const int ksl = gemm_as_ksl(M, K, lo_eff, out == OUT_ARGMAX);
+  const int ksl = gemm_as_ksl(M, K, lo_eff, out == OUT_ARGMAX, ntiles, kCUs);
   if (ksl > 0) {
     // one workgroup per compute unit: the k-slices share the chip, a
     // workgroup stages its activation slice once and its waves stream
-    // ceil(tpw / NW) tiles each (at most 16 waves)
+    // ceil(tpw / NW) tiles each (at most 8 waves)
     const int KS = K / ksl;
     const int per_slice = std::max(1, kCUs / KS);
     const int tpw = (ntiles + per_slice - 1) / per_slice;
-    const int per_wave = (tpw + 15) / 16;
+    const int per_wave = (tpw + 7) / 8;
     const int NW = (tpw + per_wave - 1) / per_wave;
     l->kind = GEMM_AS;
     l->MR = M <= 16 ? 1 : 2;

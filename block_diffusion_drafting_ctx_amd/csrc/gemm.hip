@@ -106,12 +106,15 @@ struct AsShape {
 };
 
 template <typename S, int MR, int SRC, bool LO, int OUT>
-__global__ void __launch_bounds__(1024) gemm_as_kernel(const GemmArgs g) {
+__global__ void __launch_bounds__(512) gemm_as_kernel(const GemmArgs g) {
   constexpr int MT = AsShape<MR>::MT;
   constexpr int U = AsShape<MR>::U;
   extern __shared__ __align__(16) bf16_t sa[];  // [LO ? 2 : 1][MT][ksl + 8]
   const int LDSW = g.ksl + 8;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, nw = blockDim.x >> 6;
+  // wave-uniform: keeps the tile -> weight-segment lookup on the scalar unit
+  // (a vector load of the segment table would drain the weight stream)
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ks = blockIdx.y, k0 = ks * g.ksl;
   const int ntiles = g.N >> 4;
   const int t0 = blockIdx.x * g.tpw, t1 = min(ntiles, t0 + g.tpw);
@@ -124,14 +127,16 @@ __global__ void __launch_bounds__(1024) gemm_as_kernel(const GemmArgs g) {
     for (int u = 0; u < U; ++u) load_raw8_nt<S>(wb[u], p + (it * U + u) * 32);
   };
   const S* wp = tile_row_ptr<S>(g, tile < t1 ? tile : t0, lane, k0);
-  if (tile < t1) fetch(wb0, wp, 0);  // first weight stage flies while the activations are staged
 
   // ---- activation slice -> LDS (rows beyond M repeat row M-1; never stored).
   // A thread issues the loads of C pieces before storing any of them, so the
   // staging costs one round of memory latency per C pieces, not one per piece.
+  // The first weight stage is fetched right behind the first chunk: a compute
+  // unit returns loads in order, so activations fetched after the weight
+  // stream would wait for it.
   const int pr = g.ksl / 8;  // 8-element pieces per row
   const int npieces = MT * pr;
-  constexpr int C = (LO || SRC == SRC_CONCAT) ? 4 : 8;
+  constexpr int C = SRC == SRC_CONCAT ? 4 : 8;
   for (int p0 = 0; p0 < npieces; p0 += C * (int)blockDim.x) {
     Raw8 rh[C], rl[C];
 #pragma unroll
@@ -150,6 +155,7 @@ __global__ void __launch_bounds__(1024) gemm_as_kernel(const GemmArgs g) {
         load_raw8<S>(rh[i], reinterpret_cast<const S*>(g.src[j]) + (size_t)m * g.src_width + (kg - j * g.src_width));
       }
     }
+    if (p0 == 0 && tile < t1) fetch(wb0, wp, 0);
 #pragma unroll
     for (int i = 0; i < C; ++i) {
       const int p = p0 + i * (int)blockDim.x + tid;
@@ -736,18 +742,22 @@ __global__ void __launch_bounds__(256) finish_kv_kernel(const FinishArgs f) {
 }
 
 // ------------------------------------------------------------------ launchers
-int gemm_as_ksl(int M, int K, bool lo, bool argmax) {
+int gemm_as_ksl(int M, int K, bool lo, bool argmax, int ntiles, int cus) {
   const int MR = M <= 16 ? 1 : (M <= 32 ? 2 : 0);
   if (MR == 0) return 0;
   const int narr = lo ? 2 : 1;
-  const int step = 256;  // whole register stages: 8 k-steps (MR = 1) or two of 4 (MR = 2)
+  const int step = 256;  // whole register stages at either MR
   auto lds = [&](int ksl) { return (size_t)narr * 16 * MR * (ksl + 8) * 2; };
   if (K % step) return 0;
   if (argmax) return lds(K) <= kGemmAsMaxLds ? K : 0;
-  if (lds(K) <= kGemmAsSliceLds) return K;
-  for (int ksl = 2048; ksl >= step; ksl >>= 1)
-    if (K % ksl == 0 && lds(ksl) <= kGemmAsSliceLds) return ksl;
-  return 0;
+  // the longest slice (fewest partials) that still gives every compute unit
+  // 8 tile-slices to stream, else the shortest slice that fits
+  int best = 0;
+  for (int ksl = step; ksl <= K; ksl += step) {
+    if (K % ksl || lds(ksl) > kGemmAsSliceLds) continue;
+    if (best == 0 || (long)ntiles * (K / ksl) >= 8L * cus) best = ksl;
+  }
+  return best;
 }
 
 size_t gemm_as_lds(int M, int ksl, bool lo) {

@@ -23,8 +23,8 @@ enum OutKind { OUT_PARTIAL = 0, OUT_ARGMAX = 1 };
 enum GemmKind { GEMM_AS = 0, GEMM_MT = 1 };
 
 constexpr int kMaxSeg = 16;
-constexpr size_t kGemmAsSliceLds = 68 * 1024;  // activation slice of a split-K workgroup (2 per CU)
-constexpr size_t kGemmAsMaxLds = 150 * 1024;   // whole-K activation (LM head, 1 workgroup per CU)
+constexpr size_t kGemmAsSliceLds = 100 * 1024;  // split-K activation slice of a gemm_as workgroup
+constexpr size_t kGemmAsMaxLds = 150 * 1024;    // whole-K activation (LM head; one workgroup per CU)
 
 struct GemmArgs {
   int M, N, K;
@@ -69,8 +69,9 @@ struct GemmLaunch {
 };
 
 hipError_t launch_gemm(int storage, const GemmArgs& a, const GemmLaunch& l, hipStream_t stream);
-// k-slice length gemm_as can use for (M, K) (0: gemm_as does not fit).
-int gemm_as_ksl(int M, int K, bool lo, bool argmax);
+// k-slice length gemm_as uses for (M, K) over ntiles 16-row tiles on cus
+// compute units (0: gemm_as does not fit).
+int gemm_as_ksl(int M, int K, bool lo, bool argmax, int ntiles, int cus);
 size_t gemm_as_lds(int M, int ksl, bool lo);
 // gemm_mt block: BM = 64 * MF rows by BN = 32 * gemm_mt_nf(MF) columns;
 // LDS bytes of its stage ring (lo: hi/lo activation pair).
