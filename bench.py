@@ -48,6 +48,9 @@ def parse():
     ap.add_argument("--profile-stages", action="store_true", help="also time every stage (perturbs the step)")
     ap.add_argument("--eager", action="store_true",
                     help="launch the step's kernels one by one instead of replaying a captured HIP graph")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="after timing, run one device-to-device copy of this many MiB (the known-size kernel "
+                         "that scales rocprofv3 FETCH_SIZE / WRITE_SIZE counts)")
     return ap.parse_args()
 
 
@@ -313,6 +316,15 @@ def main():
         wb = wb2
     if sec:
         out["secondary"] = sec
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        out["copy_calibration_bytes"] = n
+        del src, dst
     if not args.no_cpu_baseline:
         wb_c = wb if wb.wl.name == wl.name else None
         if wb_c is None:

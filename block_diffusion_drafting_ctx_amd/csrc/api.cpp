@@ -625,7 +625,8 @@ dflash_status dflash_draft_block(dflash_ctx* c, int32_t batch, const int32_t* bl
   if (hidden_dbg) {
     if ((st = hip_status(launch_copy_f32(x, hidden_dbg, (size_t)M * H, s), "hidden copy"))) return st;
   }
-  {  // final RMSNorm -> LM head -> argmax (the positive row scale does not move the argmax)
+  GemmLaunch lm{};
+  {  // final RMSNorm -> LM head -> per-tile argmax (the positive row scale does not move the argmax)
     StageScope sc(c, DFLASH_STAGE_LMHEAD, s);
     GemmArgs a{};
     GemmLaunch gl{};
@@ -643,11 +644,11 @@ dflash_status dflash_draft_block(dflash_ctx* c, int32_t batch, const int32_t* bl
     if (!plan_gemm(c->storage(), SRC_SPLIT, OUT_ARGMAX, false, M, cf.vocab, H, &a, &gl))
       return fail(DFLASH_EUNSUPPORTED, "no LM-head launch plan");
     if ((st = hip_status(launch_gemm(c->storage(), a, gl, s), "LM head launch"))) return st;
-    if ((st = hip_status(launch_argmax_reduce(c->at<uint64_t>(L.lm_best), gl.argmax_tiles, M, M, draft_ids, s),
-                         "argmax reduce launch")))
-      return st;
+    lm = gl;
   }
-  return DFLASH_OK;
+  // argmax over the tiles' keys -> draft ids
+  return hip_status(launch_argmax_reduce(c->at<uint64_t>(L.lm_best), lm.argmax_tiles, M, M, draft_ids, s),
+                    "argmax reduce launch");
 }
 
 dflash_status dflash_check(dflash_ctx* c, uint32_t* error_bits, void* stream) {

@@ -28,8 +28,12 @@
  *  - Matrices are row-major [out_features, in_features].  "S" below is the
  *    storage type chosen by dflash_config.dtype (float or bfloat16) for
  *    weights, gains, the KV cache and the target hidden states.  All matrix
- *    products run bf16 x bf16 -> fp32 on the matrix cores (fp32 storage is
- *    rounded to bf16 on load); the residual stream and softmax stay fp32.
+ *    products run on the bf16 matrix cores with fp32 accumulation (fp32
+ *    weights are rounded to bf16 on load).  Activations that feed the
+ *    residual stream, the attention queries and the attention probabilities
+ *    enter the products as a pair of bf16 values (value = hi + lo, two
+ *    products each); the context K/V projection and the LM head take the hi
+ *    part only.  The residual stream and the softmax stay fp32.
  *  - Errors the host can see (null pointer, bad size, unsupported shape)
  *    return DFLASH_EINVAL / DFLASH_EUNSUPPORTED before anything is enqueued;
  *    dflash_last_error() then holds a message.  HIP launch failures return
@@ -81,7 +85,7 @@ enum {
   DFLASH_STAGE_OPROJ = 6,    /* output projection + residual (+ local conv) */
   DFLASH_STAGE_GATEUP = 7,   /* RMSNorm -> gate/up projection, SiLU product */
   DFLASH_STAGE_DOWN = 8,     /* down projection + residual */
-  DFLASH_STAGE_LMHEAD = 9,   /* final RMSNorm -> LM head -> streaming argmax */
+  DFLASH_STAGE_LMHEAD = 9,   /* final RMSNorm -> LM head with per-tile argmax (the LM-head kernel alone) */
   DFLASH_N_STAGES = 10
 };
 
@@ -143,7 +147,9 @@ size_t dflash_workspace_bytes(const dflash_config* cfg);
  *     read and advanced by the library, may be set by the caller between
  *     calls (stream ordered).
  *  workspace: device buffer of dflash_workspace_bytes(cfg) bytes.  It is
- *     cleared here with a synchronous memset (create is not capturable).
+ *     cleared here with a synchronous memset and receives the RoPE cos/sin
+ *     table (create is not capturable); it belongs to the context until
+ *     dflash_destroy and must not be written by the caller.
  * On success *out receives the context. */
 dflash_status dflash_create(const dflash_config* cfg, const dflash_weights* w,
                             void* const* kv_k, void* const* kv_v, int32_t* ctx_len,
