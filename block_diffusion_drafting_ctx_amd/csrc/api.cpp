@@ -29,7 +29,7 @@ dflash_status fail(dflash_status s, const std::string& msg) {
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 constexpr int kMaxNd = 64;
-constexpr int kVerifyChunk = 16384;  // vocab entries per workgroup of the verify argmax
+constexpr int kVerifyChunk = 8192;  // vocab entries per workgroup of the verify argmax (8 loads per thread)
 constexpr int kCUs = 256;            // compute units of the chip
 constexpr int kMtTargetWgs = kCUs;   // gemm_mt workgroups to aim for (one per compute unit)
 constexpr int kAttnTargetWgs = 512;  // attention workgroups to aim for (two per compute unit)
@@ -94,8 +94,8 @@ bool plan_gemm(int storage, int src, int out, bool lo, int M, int N, int K, Gemm
     l->KS = KS;
     l->grid = dim3((ntiles + tpw - 1) / tpw, KS);
     l->threads = 64 * NW;
-    l->lds = gemm_as_lds(M, ksl, lo_eff);
-    l->argmax_tiles = ntiles;
+    l->lds = std::max(gemm_as_lds(M, ksl, lo_eff), (size_t)NW * 16 * l->MR * 8);
+    l->argmax_tiles = (ntiles + tpw - 1) / tpw;  // one key per workgroup and row
     a->ksl = ksl;
     a->tpw = tpw;
     return true;

@@ -188,6 +188,9 @@ __global__ void __launch_bounds__(512) gemm_as_kernel(const GemmArgs g) {
 
   const bf16_t* ah = &sa[(lane & 15) * LDSW + (lane >> 4) * 8];
   const bf16_t* al = &sa[(MT + (lane & 15)) * LDSW + (lane >> 4) * 8];
+  uint64_t wbest[MR];  // OUT_ARGMAX: running best key of row 16*mi + (lane & 15) over this wave's tiles
+#pragma unroll
+  for (int mi = 0; mi < MR; ++mi) wbest[mi] = 0;
   for (; tile < t1; tile += nw) {
     f32x4 acc[MR];
 #pragma unroll
@@ -232,7 +235,7 @@ __global__ void __launch_bounds__(512) gemm_as_kernel(const GemmArgs g) {
               acc[mi];
       } else {
         const uint64_t best = tile_row_best(acc[mi], tile * 16, lane);
-        if ((lane >> 4) == 0 && m < g.M) g.best_part[(size_t)tile * g.ld_best + m] = best;
+        wbest[mi] = best > wbest[mi] ? best : wbest[mi];
         if (g.logits_dbg != nullptr && m < g.M) {
           const float r = row_rinv(g.ssq_in, g.ssq_nparts, g.ld_ssq, m, g.K, g.eps);
 #pragma unroll
@@ -240,6 +243,22 @@ __global__ void __launch_bounds__(512) gemm_as_kernel(const GemmArgs g) {
             g.logits_dbg[(size_t)m * g.N + tile * 16 + 4 * (lane >> 4) + i] = acc[mi][i] * r;
         }
       }
+    }
+  }
+  if constexpr (OUT == OUT_ARGMAX) {
+    // one key per (workgroup, row): fold the waves' running bests through LDS
+    // (the activation slice is no longer read once every wave is past its tiles)
+    __syncthreads();
+    uint64_t* sb = reinterpret_cast<uint64_t*>(sa);  // [nw][MT]
+    if ((lane >> 4) == 0) {
+#pragma unroll
+      for (int mi = 0; mi < MR; ++mi) sb[wave * MT + 16 * mi + (lane & 15)] = wbest[mi];
+    }
+    __syncthreads();
+    for (int m = tid; m < MT; m += blockDim.x) {
+      uint64_t b = sb[m];
+      for (int w = 1; w < nw; ++w) b = sb[w * MT + m] > b ? sb[w * MT + m] : b;
+      if (m < g.M) g.best_part[(size_t)blockIdx.x * g.ld_best + m] = b;
     }
   }
   if (g.rinv_out != nullptr && blockIdx.y == 0) write_rinv(g, blockIdx.x, gridDim.x);
@@ -483,30 +502,34 @@ __global__ void __launch_bounds__(512) gemm_mt_kernel(const GemmArgs g) {
 
 // ------------------------------------------------------------------ argmax reduce
 // draft id of each row = index of the largest packed key over the LM-head
-// column blocks.  One workgroup of 1024 threads per row; a thread's loads are
-// issued together (8 per round).
-__global__ void __launch_bounds__(1024) argmax_reduce_kernel(const uint64_t* part, int ntiles, int ld, int32_t* ids) {
-  __shared__ uint64_t s_best[16];
-  const int m = blockIdx.x, tid = threadIdx.x;
+// workgroups' keys part[t][m] (t < ntiles, leading dimension ld).  A
+// workgroup of 1024 threads covers 16 rows: thread (c, r) = (tid >> 4,
+// tid & 15) reads keys t = c, c + 64, ... of row r (16 rows = one contiguous
+// 128-byte line per t), 8 loads issued together, then an LDS fold over c.
+__global__ void __launch_bounds__(1024) argmax_reduce_kernel(const uint64_t* part, int ntiles, int ld, int M,
+                                                             int32_t* ids) {
+  __shared__ uint64_t s_best[64][16];
+  const int r = threadIdx.x & 15, c = threadIdx.x >> 4;
+  const int m = blockIdx.x * 16 + r;
+  const bool ok = m < M;
   uint64_t best = 0;
-  for (int t0 = 0; t0 < ntiles; t0 += 8 * 1024) {
+  for (int t0 = c; t0 < ntiles; t0 += 8 * 64) {
     uint64_t v[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int t = t0 + i * 1024 + tid;
-      v[i] = t < ntiles ? part[(size_t)t * ld + m] : 0ull;
+      const int t = t0 + 64 * i;
+      v[i] = ok && t < ntiles ? part[(size_t)t * ld + m] : 0ull;
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i) best = v[i] > best ? v[i] : best;
   }
-  best = wave_max_u64(best);
-  if ((tid & 63) == 0) s_best[tid >> 6] = best;
+  s_best[c][r] = best;
   __syncthreads();
-  if (tid == 0) {
-    uint64_t b = s_best[0];
-    for (int w = 1; w < 16; ++w) b = s_best[w] > b ? s_best[w] : b;
-    ids[m] = argmax_key_index(b);
+  for (int s = 32; s >= 1; s >>= 1) {
+    if (c < s) s_best[c][r] = s_best[c + s][r] > s_best[c][r] ? s_best[c + s][r] : s_best[c][r];
+    __syncthreads();
   }
+  if (c == 0 && ok) ids[m] = argmax_key_index(s_best[0][r]);
 }
 
 // ------------------------------------------------------------------ finish kernels
@@ -824,7 +847,7 @@ hipError_t launch_gemm(int storage, const GemmArgs& a, const GemmLaunch& l, hipS
 }
 
 hipError_t launch_argmax_reduce(const uint64_t* part, int ntiles, int ld, int M, int32_t* ids, hipStream_t stream) {
-  hipLaunchKernelGGL(argmax_reduce_kernel, dim3(M), dim3(1024), 0, stream, part, ntiles, ld, ids);
+  hipLaunchKernelGGL(argmax_reduce_kernel, dim3((M + 15) / 16), dim3(1024), 0, stream, part, ntiles, ld, M, ids);
   return hipGetLastError();
 }
 

@@ -65,7 +65,7 @@ struct GemmLaunch {
   int threads;
   size_t lds;
   int KS;            // k-slices written (OUT_PARTIAL)
-  int argmax_tiles;  // OUT_ARGMAX: tiles per row in best_part
+  int argmax_tiles;  // OUT_ARGMAX: key columns per row in best_part (one per workgroup / column block)
 };
 
 hipError_t launch_gemm(int storage, const GemmArgs& a, const GemmLaunch& l, hipStream_t stream);

@@ -9,22 +9,34 @@ namespace dfl {
 
 // ---------------------------------------------------------------- verify
 // Pass 1, grid (vocab chunks, rows = batch*(n_d+1)), 256 threads: stream the
-// target logits once (16-byte non-temporal loads) and fold (value, index) into
-// one packed key per (row, chunk) -- order independent, so the result is exact.
+// target logits once (16-byte non-temporal loads, 8 per thread issued
+// together) and fold (value, index) into one packed key per (row, chunk) --
+// order independent, so the result is exact.
 __global__ void __launch_bounds__(256) verify_argmax_kernel(const VerifyArgs a) {
   __shared__ uint64_t s_best[4];
+  constexpr int PER = 8;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int row = blockIdx.y;
   const int v0 = blockIdx.x * a.chunk;
   const int v1 = min(a.V, v0 + a.chunk);
   const float* p = a.logits + (size_t)row * a.V;
   uint64_t best = 0;
-  for (int v = v0 + 4 * tid; v < v1; v += 4 * 256) {
-    const f32x4 x = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p + v));
+  for (int vb = v0; vb < v1; vb += 4 * 256 * PER) {
+    f32x4 x[PER];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const uint64_t k = argmax_key(x[e], (uint32_t)(v + e));
-      best = k > best ? k : best;
+    for (int i = 0; i < PER; ++i) {
+      const int v = vb + 4 * (tid + 256 * i);  // V is a multiple of 64: a piece never straddles v1
+      if (v < v1) x[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p + v));
+    }
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int v = vb + 4 * (tid + 256 * i);
+      if (v >= v1) continue;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint64_t k = argmax_key(x[i][e], (uint32_t)(v + e));
+        best = k > best ? k : best;
+      }
     }
   }
   best = wave_max_u64(best);
