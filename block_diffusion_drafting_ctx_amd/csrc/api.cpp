@@ -32,16 +32,17 @@ constexpr int kMaxNd = 64;
 constexpr int kVerifyChunk = 8192;  // vocab entries per workgroup of the verify argmax (8 loads per thread)
 constexpr int kCUs = 256;            // compute units of the chip
 constexpr int kMtTargetWgs = kCUs;   // gemm_mt workgroups to aim for (one per compute unit)
-constexpr int kAttnTargetWgs = 512;  // attention workgroups to aim for (two per compute unit)
-constexpr int kAttnStage = 128;      // keys per attention LDS stage (splits are whole stages)
-
-// Keys per attention split for a batch.
+// Keys per attention split for a batch, in multiples of 16 keys.  Equal
+// contexts: as many splits as keep every (sequence, KV head, split)
+// workgroup in one dispatch round (one 8-wave workgroup per compute unit fits
+// the attention kernel's registers).  At least 2 splits per sequence, so that
+// ragged batches are balanced by the dispatcher (splits past a sequence's
+// keys exit at once).
 int attn_cw(const dflash_config& c, int batch) {
   const int total = c.max_ctx + c.block;
-  const int want = std::max(1, (kAttnTargetWgs + batch * c.n_kv_heads - 1) / (batch * c.n_kv_heads));
-  int cw = (total + want - 1) / want;
-  cw = ((cw + kAttnStage - 1) / kAttnStage) * kAttnStage;
-  return std::max(cw, kAttnStage);
+  const int splits = std::max(2, kCUs / (batch * c.n_kv_heads));
+  const int cw = (total + splits - 1) / splits;
+  return std::max(16, ((cw + 15) / 16) * 16);
 }
 int attn_splits(const dflash_config& c, int cw) { return (c.max_ctx + c.block + cw - 1) / cw; }
 

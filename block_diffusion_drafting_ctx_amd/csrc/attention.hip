@@ -389,7 +389,7 @@ __global__ void __launch_bounds__(256) attention_combine_kernel(const AttnArgs a
 template <typename S, int D>
 static hipError_t launch_attention_d(const AttnArgs& a, hipStream_t stream) {
   const int QR = (a.Hq / a.Hkv) * a.Bs;
-  if (QR > 16 * kWaves || a.CW % kStage) return hipErrorInvalidValue;
+  if (QR > 16 * kWaves || a.CW <= 0 || a.CW % 16) return hipErrorInvalidValue;
   const size_t lds = sizeof(AttnLds<D>);
   auto k = attention_kernel<S, D>;
   if (lds > 64 * 1024)
