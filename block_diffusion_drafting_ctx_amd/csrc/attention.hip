@@ -48,15 +48,15 @@ __device__ __forceinline__ void split_out(bf16_t* hi, bf16_t* lo, size_t idx, fl
   lo[idx] = f32_to_bf16_bits(v - bf16_bits_to_f32(h));
 }
 
-// Waves per query-tile set and key groups for QT query tiles.
+// Waves per key group (a power of two covering QT query tiles).
 __host__ __device__ inline int attn_qtp(int QT) { return QT <= 1 ? 1 : QT <= 2 ? 2 : QT <= 4 ? 4 : 8; }
-__host__ __device__ inline int attn_kg(int QT) {
-  const int g = kWaves / attn_qtp(QT);
-  return g > kStage / kUnit ? kStage / kUnit : g;
-}
 
-template <typename S, int D>
+// QTP (waves per key group, >= the query tiles) is a template parameter so
+// that a wave's key units unroll completely.
+template <typename S, int D, int QTP>
 __global__ void __launch_bounds__(kThreads) attention_kernel(const AttnArgs a) {
+  constexpr int KG = kWaves / QTP < kStage / kUnit ? kWaves / QTP : kStage / kUnit;  // key groups
+  constexpr int UPG = (kStage / kUnit) / KG;  // 32-key units per key group and stage
   extern __shared__ __align__(16) unsigned char lds_raw[];
   AttnLds<D>& L = *reinterpret_cast<AttnLds<D>*>(lds_raw);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -64,8 +64,6 @@ __global__ void __launch_bounds__(kThreads) attention_kernel(const AttnArgs a) {
   const int G = a.Hq / a.Hkv;
   const int QR = G * a.Bs;
   const int QT = (QR + 15) / 16;
-  const int QTP = attn_qtp(QT), KG = attn_kg(QT);
-  const int UPG = (kStage / kUnit) / KG;  // units per key group
   const int qt = wave % QTP, kg = wave / QTP;
   const bool computes = qt < QT && kg < KG;
 
@@ -181,66 +179,79 @@ __global__ void __launch_bounds__(kThreads) attention_kernel(const AttnArgs a) {
     const int c0 = j0 + st * kStage;
     if (st + 1 < nstages) stage_load(c0 + kStage);  // in flight during this stage
     if (computes) {
+      // ---- scores S^T[key][q] of all the wave's units (independent MFMA
+      // chains), then one softmax update and one rescale for the stage
+      f32x4 sc[UPG][2];
+#pragma unroll
       for (int uu = 0; uu < UPG; ++uu) {
-        const int u = kg * UPG + uu;  // 32-key unit of the stage
-        const int k0 = c0 + kUnit * u;
-        if (k0 >= j1) break;
-        // ---- scores S^T[key][q] for the unit's two 16-key subtiles
-        f32x4 sc[2];
+        const int u = kg * UPG + uu;
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          sc[h] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int h = 0; h < 2; ++h) sc[uu][h] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (c0 + kUnit * u >= j1) continue;
 #pragma unroll
-          for (int s = 0; s < D / 32; ++s) {
+        for (int s = 0; s < D / 32; ++s)
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
             const bf16x8 kf = *reinterpret_cast<const bf16x8*>(
                 &L.k[(kUnit * u + 16 * h + (lane & 15)) * AttnLds<D>::KS + 32 * s + 8 * (lane >> 4)]);
-            sc[h] = mfma16x16x32(kf, qf[s], sc[h]);
-            sc[h] = mfma16x16x32(kf, qr[s], sc[h]);
+            sc[uu][h] = mfma16x16x32(kf, qf[s], sc[uu][h]);
+            sc[uu][h] = mfma16x16x32(kf, qr[s], sc[uu][h]);
           }
-        }
-        // lane holds keys k0 + 16*h + 4*(lane>>4) + e for query row (lane & 15)
-        float cmax = -INFINITY;
+      }
+      // lane holds keys c0 + 32*u + 16*h + 4*(lane>>4) + e for query row (lane & 15)
+      float cmax = -INFINITY;
+#pragma unroll
+      for (int uu = 0; uu < UPG; ++uu)
 #pragma unroll
         for (int h = 0; h < 2; ++h)
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            if (k0 + 16 * h + 4 * (lane >> 4) + e >= j1) sc[h][e] = -INFINITY;
-            cmax = fmaxf(cmax, sc[h][e]);
+            if (c0 + kUnit * (kg * UPG + uu) + 16 * h + 4 * (lane >> 4) + e >= j1) sc[uu][h][e] = -INFINITY;
+            cmax = fmaxf(cmax, sc[uu][h][e]);
           }
-        cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
-        cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
-        const float m_new = fmaxf(m_run, cmax);
+      cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
+      cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
+      const float m_new = fmaxf(m_run, cmax);
+      if (m_new != -INFINITY) {  // some key of this wave's share of the stage is valid
         const float alpha = fast_exp2(m_run - m_new);
         float psum = 0.f;
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
+        for (int uu = 0; uu < UPG; ++uu)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            sc[h][e] = fast_exp2(sc[h][e] - m_new);
-            psum += sc[h][e];
-          }
+          for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              sc[uu][h][e] = fast_exp2(sc[uu][h][e] - m_new);
+              psum += sc[uu][h][e];
+            }
         l_run = l_run * alpha + psum;
         m_run = m_new;
+#pragma unroll
+        for (int ds = 0; ds < D / 16; ++ds) o[ds] *= alpha;
         // ---- O^T[d][q] += V^T[d][keys] P^T[keys][q]; P as a hi/lo pair
-        bf16x8 ph, pl;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          ph[e] = (__bf16)sc[0][e];
-          ph[4 + e] = (__bf16)sc[1][e];
-          pl[e] = (__bf16)(sc[0][e] - (float)ph[e]);
-          pl[4 + e] = (__bf16)(sc[1][e] - (float)ph[4 + e]);
-        }
-        const int kp0 = (kUnit / 2) * u + 2 * (lane >> 4);  // keys k0 + 4*(lane>>4) + [0, 4)
+        for (int uu = 0; uu < UPG; ++uu) {
+          const int u = kg * UPG + uu;
+          if (c0 + kUnit * u >= j1) continue;
+          bf16x8 ph, pl;
 #pragma unroll
-        for (int ds = 0; ds < D / 16; ++ds) {
-          const int d = 16 * ds + (lane & 15);
-          const uint32_t* vrow = &L.vt[d * AttnLds<D>::VW];
-          const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow + vt_col(d, kp0));
-          const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + vt_col(d, kp0 + 8));
-          const bf16x8 vf = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
-          o[ds] *= alpha;
-          o[ds] = mfma16x16x32(vf, ph, o[ds]);
-          o[ds] = mfma16x16x32(vf, pl, o[ds]);
+          for (int e = 0; e < 4; ++e) {
+            ph[e] = (__bf16)sc[uu][0][e];
+            ph[4 + e] = (__bf16)sc[uu][1][e];
+            pl[e] = (__bf16)(sc[uu][0][e] - (float)ph[e]);
+            pl[4 + e] = (__bf16)(sc[uu][1][e] - (float)ph[4 + e]);
+          }
+          const int kp0 = (kUnit / 2) * u + 2 * (lane >> 4);  // keys 32*u + 4*(lane>>4) + [0, 4)
+#pragma unroll
+          for (int ds = 0; ds < D / 16; ++ds) {
+            const int d = 16 * ds + (lane & 15);
+            const uint32_t* vrow = &L.vt[d * AttnLds<D>::VW];
+            const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow + vt_col(d, kp0));
+            const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + vt_col(d, kp0 + 8));
+            const bf16x8 vf = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+            o[ds] = mfma16x16x32(vf, ph, o[ds]);
+            o[ds] = mfma16x16x32(vf, pl, o[ds]);
+          }
         }
       }
     }
@@ -251,32 +262,31 @@ __global__ void __launch_bounds__(kThreads) attention_kernel(const AttnArgs a) {
     }
   }
 
-  // ---- merge the key groups of each query tile through LDS (group 0 keeps the result)
-  if (KG > 1) {
+  // ---- merge the key groups of each query tile through LDS (group 0 keeps the
+  // result).  Records are [group-1][tile][d-slice][lane] 16-byte slots, so a
+  // wave's LDS traffic is conflict-free 16-byte accesses.
+  if constexpr (KG > 1) {
     __syncthreads();  // every wave is done reading K / V^T
-    float* mg = reinterpret_cast<float*>(lds_raw);
-    constexpr int REC = D / 4 + 2;  // floats per lane record: O^T values, max, partial sum
+    f32x4* mo = reinterpret_cast<f32x4*>(lds_raw);                       // [KG-1][QTP][D/16][64]
+    float* mml = reinterpret_cast<float*>(mo + (KG - 1) * QTP * (D / 16) * 64);  // [KG-1][QTP][64][2]
     if (computes && kg > 0) {
-      float* rec = mg + (((kg - 1) * QTP + qt) * 64 + lane) * REC;
+      const int g = (kg - 1) * QTP + qt;
 #pragma unroll
-      for (int ds = 0; ds < D / 16; ++ds)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) rec[4 * ds + e] = o[ds][e];
-      rec[D / 4] = m_run;
-      rec[D / 4 + 1] = l_run;
+      for (int ds = 0; ds < D / 16; ++ds) mo[(g * (D / 16) + ds) * 64 + lane] = o[ds];
+      mml[(g * 64 + lane) * 2] = m_run;
+      mml[(g * 64 + lane) * 2 + 1] = l_run;
     }
     __syncthreads();
     if (computes && kg == 0) {
+#pragma unroll
       for (int g2 = 1; g2 < KG; ++g2) {
-        const float* rec = mg + (((g2 - 1) * QTP + qt) * 64 + lane) * REC;
-        const float m2 = rec[D / 4], l2 = rec[D / 4 + 1];
+        const int g = (g2 - 1) * QTP + qt;
+        const float m2 = mml[(g * 64 + lane) * 2], l2 = mml[(g * 64 + lane) * 2 + 1];
         const float mn = fmaxf(m_run, m2);  // finite: group 0 always has a valid key
         const float w1 = fast_exp2(m_run - mn);
         const float w2 = m2 == -INFINITY ? 0.f : fast_exp2(m2 - mn);
 #pragma unroll
-        for (int ds = 0; ds < D / 16; ++ds)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) o[ds][e] = o[ds][e] * w1 + rec[4 * ds + e] * w2;
+        for (int ds = 0; ds < D / 16; ++ds) o[ds] = o[ds] * w1 + mo[(g * (D / 16) + ds) * 64 + lane] * w2;
         l_run = l_run * w1 + l2 * w2;
         m_run = mn;
       }
@@ -391,7 +401,9 @@ static hipError_t launch_attention_d(const AttnArgs& a, hipStream_t stream) {
   const int QR = (a.Hq / a.Hkv) * a.Bs;
   if (QR > 16 * kWaves || a.CW <= 0 || a.CW % 16) return hipErrorInvalidValue;
   const size_t lds = sizeof(AttnLds<D>);
-  auto k = attention_kernel<S, D>;
+  const int qtp = attn_qtp((QR + 15) / 16);
+  auto k = qtp == 1 ? attention_kernel<S, D, 1>
+                    : qtp == 2 ? attention_kernel<S, D, 2> : qtp == 4 ? attention_kernel<S, D, 4> : attention_kernel<S, D, 8>;
   if (lds > 64 * 1024)
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize,
                               (int)lds);
