@@ -117,7 +117,9 @@ __global__ void __launch_bounds__(kThreads) attention_kernel(const AttnArgs a) {
   constexpr int KPT = KITEMS / kThreads;
   constexpr int VPT = VITEMS / kThreads;
   static_assert(KITEMS % kThreads == 0 && VITEMS % kThreads == 0, "stage items must fill the workgroup");
-  Raw8 kreg[KPT], vreg[VPT][2];
+  struct StageRegs {
+    Raw8 k[KPT], v[VPT][2];
+  };
   auto v_item = [&](int idx, int& kp, int& p) {
     p = idx % PIECES;
     const int h = (idx / PIECES) & 1, rest = idx / (2 * PIECES);
@@ -126,27 +128,27 @@ __global__ void __launch_bounds__(kThreads) attention_kernel(const AttnArgs a) {
   // Loads are unconditional (keys past the split re-read its last key and are
   // zeroed at the store): branch-free address selects keep the loads of a
   // stage in flight together.
-  auto stage_load = [&](int c0) {
+  auto stage_load = [&](StageRegs& R, int c0) {
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
       const int idx = tid + i * kThreads;
       const int key = idx / PIECES, p8 = (idx % PIECES) * 8;
-      load_raw8<S>(kreg[i], key_ptr(kc, kb, min(c0 + key, j1 - 1)) + p8);
+      load_raw8<S>(R.k[i], key_ptr(kc, kb, min(c0 + key, j1 - 1)) + p8);
     }
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
       int kp, p;
       v_item(tid + i * kThreads, kp, p);
 #pragma unroll
-      for (int t = 0; t < 2; ++t) load_raw8<S>(vreg[i][t], key_ptr(vc, vb, min(c0 + 2 * kp + t, j1 - 1)) + 8 * p);
+      for (int t = 0; t < 2; ++t) load_raw8<S>(R.v[i][t], key_ptr(vc, vb, min(c0 + 2 * kp + t, j1 - 1)) + 8 * p);
     }
   };
-  auto stage_store = [&](int c0) {
+  auto stage_store = [&](const StageRegs& R, int c0) {
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
       const int idx = tid + i * kThreads;
       const int key = idx / PIECES, p8 = (idx % PIECES) * 8;
-      const bf16x8 v = c0 + key < j1 ? raw_to_bf16x8<S>(kreg[i]) : bf16x8{};
+      const bf16x8 v = c0 + key < j1 ? raw_to_bf16x8<S>(R.k[i]) : bf16x8{};
       *reinterpret_cast<bf16x8*>(&L.k[key * AttnLds<D>::KS + p8]) = v;
     }
 #pragma unroll
@@ -154,8 +156,8 @@ __global__ void __launch_bounds__(kThreads) attention_kernel(const AttnArgs a) {
       int kp, p;
       v_item(tid + i * kThreads, kp, p);
       float v0[8], v1[8];
-      raw_to_f32x8<S>(vreg[i][0], v0);
-      raw_to_f32x8<S>(vreg[i][1], v1);
+      raw_to_f32x8<S>(R.v[i][0], v0);
+      raw_to_f32x8<S>(R.v[i][1], v1);
       const bool ok0 = c0 + 2 * kp < j1, ok1 = c0 + 2 * kp + 1 < j1;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -172,12 +174,21 @@ __global__ void __launch_bounds__(kThreads) attention_kernel(const AttnArgs a) {
 #pragma unroll
   for (int ds = 0; ds < D / 16; ++ds) o[ds] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  stage_load(j0);
-  stage_store(j0);
+  // Stages are fetched PF ahead through a pair of register sets: with PF = 2
+  // the loads of stage st+2 are issued before the matrix work of stage st and
+  // stage st+1 (fetched a stage earlier) is stored to LDS after it; the widest
+  // wave layout (eight query tiles) and fp32 storage need the registers and
+  // fetch one ahead.
+  constexpr int PF = (QTP >= 8 || sizeof(S) == 4) ? 1 : 2;
+  StageRegs ra, rb;
+  stage_load(ra, j0);
+  if (PF == 2 && nstages > 1) stage_load(rb, j0 + kStage);
+  stage_store(ra, j0);
   __syncthreads();
-  for (int st = 0; st < nstages; ++st) {
+  auto step = [&](StageRegs& fr, StageRegs& nx, int st) {
     const int c0 = j0 + st * kStage;
-    if (st + 1 < nstages) stage_load(c0 + kStage);  // in flight during this stage
+    if (PF == 2 && st + 2 < nstages) stage_load(fr, c0 + 2 * kStage);  // fr's stage st is already in LDS
+    if (PF == 1 && st + 1 < nstages) stage_load(nx, c0 + kStage);
     if (computes) {
       // ---- scores S^T[key][q] of all the wave's units (independent MFMA
       // chains), then one softmax update and one rescale for the stage
@@ -257,8 +268,16 @@ __global__ void __launch_bounds__(kThreads) attention_kernel(const AttnArgs a) {
     }
     if (st + 1 < nstages) {
       __syncthreads();
-      stage_store(c0 + kStage);
+      stage_store(nx, c0 + kStage);
       __syncthreads();
+    }
+  };
+  if constexpr (PF == 1) {
+    for (int st = 0; st < nstages; ++st) step(ra, ra, st);
+  } else {
+    for (int st = 0; st < nstages; st += 2) {
+      step(ra, rb, st);
+      if (st + 1 < nstages) step(rb, ra, st + 1);
     }
   }
 
