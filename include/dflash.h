@@ -39,7 +39,8 @@
  *    dflash_last_error() then holds a message.  HIP launch failures return
  *    DFLASH_EHIP.  Errors only the device can see (a context that would
  *    overflow max_ctx, a token id out of range) set a sticky bit in the
- *    device error word, skip the affected sequence's writes, and are reported
+ *    device error word and skip the affected sequence's writes (an
+ *    out-of-range token is embedded as zeros instead), and are reported
  *    by dflash_check().  No C++ exception crosses this boundary.
  *  - One host thread drives a context at a time, and its calls must be
  *    ordered (one stream, or streams synchronised by the caller): the calls

@@ -66,8 +66,10 @@ class StepResult:
 
 def run_step(wl: gen.Workload, seed: int, device="cuda", seqs: Optional[Sequence[int]] = None,
              prefill: bool = False, poison: bool = False, n_d: Optional[int] = None,
-             check_oracle: bool = True) -> StepResult:
-    """Run one step on the library and compare with the oracle on `seqs`."""
+             check_oracle: bool = True, accept: Optional[Sequence[int]] = None) -> StepResult:
+    """Run one step on the library and compare with the oracle on `seqs`.
+
+    `accept` overrides the planted acceptance lengths (one per sequence)."""
     from block_diffusion_drafting_ctx_amd import Drafter
 
     res = StepResult()
@@ -88,7 +90,8 @@ def run_step(wl: gen.Workload, seed: int, device="cuda", seqs: Optional[Sequence
         ks, vs = gen.context_kv(wl, ctx_lens, seed + 1, gdev, poison=poison)
     hid = gen.target_hidden(wl, B, t_new, seed + 2, gdev)
     drafts = gen.draft_tokens(wl, B, n_d, seed + 3)
-    accept = gen.accept_lengths(wl, B, seed + 4, n_d)
+    accept = (gen.accept_lengths(wl, B, seed + 4, n_d) if accept is None
+              else np.asarray(accept, dtype=np.int32))
     logits = gen.planted_logits(wl, drafts, accept, n_d, seed + 5, gdev)
     ids = gen.block_ids(wl, B, seed + 6)
 
@@ -202,3 +205,75 @@ def _to(w: dict, device) -> dict:
     out["layers"] = [{k: (v.to(device) if isinstance(v, torch.Tensor) else v) for k, v in lw.items()}
                      for lw in w["layers"]]
     return out
+
+
+def run_error_paths(wl: gen.Workload, seed: int, device="cuda") -> None:
+    """Device-detected faults, forced from the host: a context that would pass
+    max_ctx (fuse and verify skip that sequence's writes and commit) and a
+    block token outside the vocabulary (embedded as zeros).  The other
+    sequences must still match the oracle bit for bit / within the bars, and
+    the sticky error word must name exactly the faults."""
+    from block_diffusion_drafting_ctx_amd import Drafter, _abi
+
+    B = wl.batch
+    assert B >= 3
+    n_d, t_new = wl.n_d, wl.t_new
+    log(f"[case] {wl.name} error paths B={B} seed={seed}")
+    w = gen.draft_weights(wl, seed, "cpu")
+    w_dev = _to(w, device)
+    ctx_lens = gen.context_lengths(wl, seed + 1, B)
+    ctx_lens[1] = wl.max_ctx - t_new + 1  # fuse (t_new rows) and verify would pass max_ctx
+    ks, vs = gen.context_kv(wl, np.minimum(ctx_lens, wl.max_ctx), seed + 1, "cpu")
+    hid = gen.target_hidden(wl, B, t_new, seed + 2, "cpu")
+    drafts = gen.draft_tokens(wl, B, n_d, seed + 3)
+    accept = gen.accept_lengths(wl, B, seed + 4, n_d)
+    logits = gen.planted_logits(wl, drafts, accept, n_d, seed + 5, "cpu")
+    ids = gen.block_ids(wl, B, seed + 6)
+    ids[2, 1] = wl.vocab  # out of range
+
+    W = weights_of(w)
+    dims = dims_of(wl)
+    good = [0]
+    st = DraftState(k=[np64(t[good]) for t in ks], v=[np64(t[good]) for t in vs],
+                    ctx_len=ctx_lens[good].astype(np.int64).copy())
+    cfg = config_for(wl, B)
+    dr = Drafter(cfg, w_dev, device, [t.to(device) for t in ks], [t.to(device) for t in vs])
+    dr.ctx_len.copy_(torch.from_numpy(ctx_lens))
+    k1_before = [dr.kv_k[l][1].clone() for l in range(wl.n_layers)]
+    feat = torch.empty(B, t_new, wl.hidden, dtype=torch.float32, device=device)
+    dr.fuse_ctx([h.to(device) for h in hid], commit=False, feat_dbg=feat)
+    n_acc = torch.full((B,), -7, dtype=torch.int32, device=device)
+    bonus = torch.full((B,), -7, dtype=torch.int32, device=device)
+    out_tok = torch.full((B, t_new), -7, dtype=torch.int32, device=device)
+    dr.verify(logits.to(device), torch.from_numpy(drafts).to(device), n_d, n_d, n_acc, bonus, out_tok)
+    ctx_after = dr.ctx_len.cpu().numpy()
+    draft_ids = torch.full((B, wl.block), -7, dtype=torch.int32, device=device)
+    hid_dbg = torch.empty(B, wl.block, wl.hidden, dtype=torch.float32, device=device)
+    dr.draft_block(torch.from_numpy(ids).to(device), draft_ids, None, hid_dbg)
+    torch.cuda.synchronize()
+    err = dr.check()
+    want = _abi.ERR_FUSE_OVERFLOW | _abi.ERR_VERIFY_OVERFLOW | _abi.ERR_TOKEN_RANGE
+    assert err == want, f"error word {err:#x}, expected {want:#x}"
+    # the overflowing sequence: cache untouched, length not advanced
+    for l in range(wl.n_layers):
+        assert torch.equal(dr.kv_k[l][1], k1_before[l]), f"layer {l}: cache of the overflowing sequence written"
+    assert int(ctx_after[1]) == int(ctx_lens[1])
+    # the healthy sequences: verify bit-exact, sequence 0 matches the oracle
+    from oracle import greedy_verify
+
+    lg_np = logits.numpy()
+    for b in (0, 2):
+        n, bon, toks = greedy_verify(lg_np[b], drafts[b], n_d)
+        assert int(n_acc[b]) == n and int(bonus[b]) == bon
+        assert int(ctx_after[b]) == int(ctx_lens[b]) + n + 1
+    c = fuse_ctx(st, W, dims, [np64(h[good]) for h in hid], commit=False)
+    assert rel_l2(feat.cpu().numpy()[good], c) <= REL_L2
+    verify_step(st, lg_np[good], drafts[good].reshape(-1), n_d, n_d, AcceptanceStats())
+    _, _, h_or = draft_block(st, W, dims, ids[good])
+    e = rel_l2(hid_dbg.cpu().numpy()[good][0], h_or[0])
+    assert e <= REL_L2, f"healthy sequence hidden rel L2 {e}"
+    dr.clear_errors()
+    torch.cuda.synchronize()
+    assert dr.check() == 0
+    log(f"[case] {wl.name}: error paths ok (error word {err:#x})")
+    dr.close()

@@ -9,7 +9,7 @@ import pytest
 import torch
 
 from harness import gen
-from tests.gpu_cases import run_step
+from tests.gpu_cases import run_error_paths, run_step
 
 pytestmark = pytest.mark.gpu
 
@@ -44,6 +44,52 @@ def test_tiny_head128_gqa5():
 def test_anchor_layout_fewer_drafts():
     # n_d = block - 1 (anchor layout): logits rows = block, fused rows = block
     run_step(TINY, seed=16, n_d=TINY.block - 1)
+
+
+def test_empty_contexts():
+    # no committed context at all: attention runs over the block alone
+    wl = gen.Workload("tiny-empty", 256, 4, 2, 64, 2, 512, 1024, 8, 3, 3, 0, 0, "bf16", accept_hi=8)
+    run_step(wl, seed=17, poison=True)
+
+
+def test_full_and_zero_acceptance():
+    wl = gen.Workload("tiny-accept", 256, 4, 2, 64, 2, 512, 1024, 8, 3, 4, 10, 90, "bf16", accept_hi=8)
+    run_step(wl, seed=18, accept=[8, 0, 8, 0])
+
+
+def test_zero_drafts_verifies_the_bonus_row_only():
+    run_step(TINY, seed=19, n_d=0)
+
+
+def test_device_faults_set_error_bits_and_spare_other_sequences():
+    wl = gen.Workload("tiny-faults", 256, 4, 2, 64, 2, 512, 1024, 8, 3, 3, 10, 60, "bf16", accept_hi=8)
+    run_error_paths(wl, seed=21)
+
+
+def test_host_checks_reject_bad_sizes():
+    from block_diffusion_drafting_ctx_amd import Drafter, _abi
+    from tests.gpu_cases import config_for
+
+    wl = gen.Workload("tiny-host", 256, 4, 2, 64, 2, 512, 1024, 8, 3, 2, 10, 20, "bf16")
+    w = {k: v for k, v in gen.draft_weights(wl, 3, "cuda").items()}
+    dr = Drafter(config_for(wl, 2), w, "cuda")
+    H, V = wl.hidden, wl.vocab
+    too_many = [torch.zeros(3, wl.t_new, H, dtype=torch.bfloat16, device="cuda") for _ in range(3)]
+    too_long = [torch.zeros(2, wl.t_new + 1, H, dtype=torch.bfloat16, device="cuda") for _ in range(3)]
+    for hid in (too_many, too_long):
+        with pytest.raises(_abi.DFlashError):
+            dr.fuse_ctx(hid, commit=False)
+    i32 = lambda *s: torch.zeros(*s, dtype=torch.int32, device="cuda")  # noqa: E731
+    lg = torch.zeros(2, 66, V, dtype=torch.float32, device="cuda")
+    with pytest.raises(_abi.DFlashError):  # n_d above 64
+        dr.verify(lg, i32(2, 65), 65, 65, i32(2), i32(2), i32(2, 66))
+    with pytest.raises(_abi.DFlashError):  # batch above max_batch
+        dr.draft_block(i32(3, wl.block), i32(3, wl.block))
+    # batch 0 is a no-op
+    dr.draft_block(i32(0, wl.block), i32(0, wl.block))
+    torch.cuda.synchronize()
+    assert dr.check() == 0
+    dr.close()
 
 
 @pytest.mark.parametrize("name,seqs", [
