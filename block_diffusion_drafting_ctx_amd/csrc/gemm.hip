@@ -102,7 +102,7 @@ __device__ __forceinline__ uint64_t tile_row_best(const f32x4& v, int n0, int la
 template <int MR>
 struct AsShape {
   static constexpr int MT = 16 * MR;
-  static constexpr int U = 8 / MR;  // k-steps per register stage
+  static constexpr int U = 8;  // k-steps per register stage (16 rows x 512 contiguous bytes of W)
 };
 
 template <typename S, int MR, int SRC, bool LO, int OUT>
@@ -128,23 +128,23 @@ __global__ void __launch_bounds__(512) gemm_as_kernel(const GemmArgs g) {
   };
   const S* wp = tile_row_ptr<S>(g, tile < t1 ? tile : t0, lane, k0);
 
-  // ---- activation slice -> LDS (rows beyond M repeat row M-1; never stored).
-  // A thread issues the loads of C pieces before storing any of them, so the
-  // staging costs one round of memory latency per C pieces, not one per piece.
-  // The first weight stage is fetched right behind the first chunk: a compute
-  // unit returns loads in order, so activations fetched after the weight
-  // stream would wait for it.
+  // ---- activation slice -> LDS.  Only the M real rows are staged: LDS rows
+  // past M feed only the matrix-core outputs of rows past M, which are never
+  // stored.  A thread issues the loads of C pieces before storing any of
+  // them, so the staging costs one round of memory latency per C pieces, not
+  // one per piece.  The first weight stage is fetched right behind the first
+  // chunk: a compute unit returns loads in order, so activations fetched
+  // after the weight stream would wait for it.
   const int pr = g.ksl / 8;  // 8-element pieces per row
-  const int npieces = MT * pr;
-  constexpr int C = SRC == SRC_CONCAT ? 4 : 8;
+  const int npieces = min(MT, g.M) * pr;
+  constexpr int C = 8;
   for (int p0 = 0; p0 < npieces; p0 += C * (int)blockDim.x) {
     Raw8 rh[C], rl[C];
 #pragma unroll
     for (int i = 0; i < C; ++i) {
       const int p = p0 + i * (int)blockDim.x + tid;
       if (p >= npieces) continue;
-      const int row = p / pr, col = (p - row * pr) * 8;
-      const int m = min(row, g.M - 1);
+      const int m = p / pr, col = (p - m * pr) * 8;
       if constexpr (SRC == SRC_SPLIT) {
         const size_t o = (size_t)m * g.lda + k0 + col;
         rh[i].lo = *reinterpret_cast<const u32x4*>(reinterpret_cast<const bf16_t*>(g.a_hi) + o);
