@@ -31,20 +31,12 @@ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 constexpr int kMaxNd = 64;
 constexpr int kVerifyChunk = 8192;  // vocab entries per workgroup of the verify argmax (8 loads per thread)
 constexpr int kCUs = 256;            // compute units of the chip
+constexpr int kMlpHiOnlyRows = 256;  // draft rows from which the MLP products take plain bf16 inputs
 constexpr int kMtTargetWgs = kCUs;   // gemm_mt workgroups to aim for (one per compute unit)
-// Keys per attention split for a batch, in multiples of 16 keys.  Equal
-// contexts: as many splits as keep every (sequence, KV head, split)
-// workgroup in one dispatch round (one 8-wave workgroup per compute unit fits
-// the attention kernel's registers).  At least 2 splits per sequence, so that
-// ragged batches are balanced by the dispatcher (splits past a sequence's
-// keys exit at once).
-int attn_cw(const dflash_config& c, int batch) {
-  const int total = c.max_ctx + c.block;
-  const int splits = std::max(2, kCUs / (batch * c.n_kv_heads));
-  const int cw = (total + splits - 1) / splits;
-  return std::max(16, ((cw + 15) / 16) * 16);
-}
-int attn_splits(const dflash_config& c, int cw) { return (c.max_ctx + c.block + cw - 1) / cw; }
+// Attention workgroups: the batch's key axis is cut into this many ranges,
+// one 8-wave workgroup per compute unit (the attention kernel's registers and
+// LDS allow one), so every range runs in the first dispatch round.
+constexpr int kAttnWgs = kCUs;
 
 const char* validate(const dflash_config* c) {
   if (!c) return "null config";
@@ -59,6 +51,9 @@ const char* validate(const dflash_config* c) {
   if (c->block < 1 || c->block > 64) return "block must be in [1, 64]";
   if (c->n_target_layers < 1 || c->n_target_layers > 8) return "n_target_layers must be in [1, 8]";
   if (c->max_batch < 1 || c->max_ctx < 1 || c->max_fuse_rows < 1) return "bad limits";
+  if (c->max_batch > kAttnMaxBatch) return "max_batch must be <= 1024";
+  if ((int64_t)c->n_kv_heads * c->max_batch * ((int64_t)c->max_ctx + c->block) >= ((int64_t)1 << 31))
+    return "n_kv_heads * max_batch * (max_ctx + block) must be below 2^31";
   if (c->conv_width != 0 && c->conv_width != 3) return "conv_width must be 0 or 3";
   if (c->conv_width == 3 && 16 % c->block) return "the block conv needs block to divide 16";
   if (c->dtype != DFLASH_DTYPE_F32 && c->dtype != DFLASH_DTYPE_BF16) return "unknown dtype";
@@ -141,7 +136,7 @@ struct WsLayout {
   size_t x, ssq, rinv, y, xs_hi, xs_lo, q_hi, q_lo, kb, vb, o_hi, o_lo, act_hi, act_lo, part, lm_best, ver_best,
       part_o, part_ml, rope;
   size_t total;
-  int md, mf, mmax, ssq_parts, attn_max_wgs_rows, ver_chunks, rope_rows;
+  int md, mf, mmax, ssq_parts, ver_chunks, rope_rows;
 };
 
 WsLayout layout(const dflash_config& c) {
@@ -154,17 +149,18 @@ WsLayout layout(const dflash_config& c) {
   L.mf = c.max_batch * c.max_fuse_rows;
   L.mmax = std::max(L.md, L.mf);
   L.ssq_parts = c.hidden / 16;
-  int attn_rows = 0;  // max over batch of batch * splits
-  for (int b = 1; b <= c.max_batch; ++b) attn_rows = std::max(attn_rows, b * attn_splits(c, attn_cw(c, b)));
-  L.attn_max_wgs_rows = attn_rows;
+  // attention piece slots: workgroup + segment index of every piece
+  const size_t attn_slots = (size_t)kAttnWgs + (size_t)c.max_batch * c.n_kv_heads;
   const size_t QR = (size_t)(c.n_q_heads / c.n_kv_heads) * c.block;
   size_t parts = 0;
   parts = std::max(parts, partial_floats(st, SRC_CONCAT, false, L.mf, c.hidden, c.hidden * c.n_target_layers));
   parts = std::max(parts, partial_floats(st, SRC_SPLIT, false, L.mf, 2 * c.n_layers * Nk, c.hidden));
   parts = std::max(parts, partial_floats(st, SRC_SPLIT, true, L.md, Nq + 2 * Nk, c.hidden));
   parts = std::max(parts, partial_floats(st, SRC_SPLIT, true, L.md, c.hidden, Nq));
-  parts = std::max(parts, partial_floats(st, SRC_SPLIT, true, L.md, 2 * c.ffn, c.hidden));
-  parts = std::max(parts, partial_floats(st, SRC_SPLIT, true, L.md, c.hidden, c.ffn));
+  for (bool lo : {true, false}) {  // the MLP products take hi/lo or plain activations
+    parts = std::max(parts, partial_floats(st, SRC_SPLIT, lo, L.md, 2 * c.ffn, c.hidden));
+    parts = std::max(parts, partial_floats(st, SRC_SPLIT, lo, L.md, c.hidden, c.ffn));
+  }
   size_t off = 0;
   auto take = [&](size_t bytes) {
     size_t o = off;
@@ -191,8 +187,8 @@ WsLayout layout(const dflash_config& c) {
   L.lm_best = take((size_t)(c.vocab / 16) * L.md * 8);
   L.ver_chunks = (c.vocab + kVerifyChunk - 1) / kVerifyChunk;
   L.ver_best = take((size_t)c.max_batch * (kMaxNd + 1) * L.ver_chunks * 8);
-  L.part_o = take((size_t)attn_rows * c.n_kv_heads * QR * D * 4);
-  L.part_ml = take((size_t)attn_rows * c.n_kv_heads * QR * 2 * 4);
+  L.part_o = take(attn_slots * QR * D * 4);
+  L.part_ml = take(attn_slots * QR * 2 * 4);
   // RoPE positions reach max_ctx + rows per sequence - 1 (block rows, or fused rows)
   L.rope_rows = c.max_ctx + std::max(c.block, c.max_fuse_rows);
   L.rope = take((size_t)L.rope_rows * (D / 2) * 8);
@@ -504,8 +500,6 @@ dflash_status dflash_draft_block(dflash_ctx* c, int32_t batch, const int32_t* bl
     if (st) return st;
   }
   int ssq_parts = 1;
-  const int cw = attn_cw(cf, batch);
-  const int splits = attn_splits(cf, cw);
   float* rinv = c->at<float>(L.rinv);
   // RMSNorm of the product's activation rows: its main kernel turns the
   // partial sums of squares into row scales for the finish kernel
@@ -517,6 +511,11 @@ dflash_status dflash_draft_block(dflash_ctx* c, int32_t batch, const int32_t* bl
     a.rinv_out = rinv;
     f.rinv = rinv;
   };
+  // The MLP inputs (normalised residual into gate/up, SiLU product into down)
+  // enter their products as a hi/lo pair while the products stream weights
+  // (the pair costs no HBM bytes there); from kMlpHiOnlyRows rows on, where
+  // the products are matrix-core bound, they enter as plain bf16.
+  const bool mlp_lo = M < kMlpHiOnlyRows;
   for (int l = 0; l < cf.n_layers; ++l) {
     {  // RMSNorm -> Q/K/V, RoPE
       StageScope sc(c, DFLASH_STAGE_QKV, s);
@@ -558,8 +557,7 @@ dflash_status dflash_draft_block(dflash_ctx* c, int32_t batch, const int32_t* bl
       a.Hkv = cf.n_kv_heads;
       a.D = D;
       a.max_ctx = cf.max_ctx;
-      a.CW = cw;
-      a.max_splits = splits;
+      a.nwg = kAttnWgs;
       a.part_o = c->at<float>(L.part_o);
       a.part_ml = c->at<float>(L.part_ml);
       a.out_hi = c->at<void>(L.o_hi);
@@ -582,7 +580,7 @@ dflash_status dflash_draft_block(dflash_ctx* c, int32_t batch, const int32_t* bl
       f.block = cf.block;
       f.gnext = c->g_post[l];
       f.out_hi = xs_hi;
-      f.out_lo = xs_lo;
+      f.out_lo = mlp_lo ? xs_lo : nullptr;
       f.ssq_out = ssq;
       f.ld_ssq = L.mmax;
       if ((st = finish(c, FIN_ROWTILE, f, gl, M, H, s))) return st;
@@ -594,13 +592,13 @@ dflash_status dflash_draft_block(dflash_ctx* c, int32_t batch, const int32_t* bl
       GemmLaunch gl{};
       set_segments(a, {{c->w_gate[l], F}, {c->w_up[l], F}});
       a.a_hi = xs_hi;
-      a.a_lo = xs_lo;
+      a.a_lo = mlp_lo ? xs_lo : nullptr;
       a.lda = H;
       FinishArgs f{};
       norm(a, f);
-      if ((st = gemm_partial(c, a, SRC_SPLIT, true, M, 2 * F, H, &gl, s))) return st;
+      if ((st = gemm_partial(c, a, SRC_SPLIT, mlp_lo, M, 2 * F, H, &gl, s))) return st;
       f.out_hi = c->at<void>(L.act_hi);
-      f.out_lo = c->at<void>(L.act_lo);
+      f.out_lo = mlp_lo ? c->at<void>(L.act_lo) : nullptr;
       if ((st = finish(c, FIN_SWIGLU, f, gl, M, 2 * F, s))) return st;
     }
     {  // down projection + residual; hi/lo of x * (next layer's g_in, or g_final)
@@ -609,9 +607,9 @@ dflash_status dflash_draft_block(dflash_ctx* c, int32_t batch, const int32_t* bl
       GemmLaunch gl{};
       set_segments(a, {{c->w_down[l], H}});
       a.a_hi = c->at<void>(L.act_hi);
-      a.a_lo = c->at<void>(L.act_lo);
+      a.a_lo = mlp_lo ? c->at<void>(L.act_lo) : nullptr;
       a.lda = F;
-      if ((st = gemm_partial(c, a, SRC_SPLIT, true, M, H, F, &gl, s))) return st;
+      if ((st = gemm_partial(c, a, SRC_SPLIT, mlp_lo, M, H, F, &gl, s))) return st;
       FinishArgs f{};
       f.x = x;
       f.block = cf.block;

@@ -1,13 +1,31 @@
 // Non-causal grouped-query attention of a drafted block over
-// [cached context ; the block itself], split over the key axis.
+// [cached context ; the block itself], with the key axis of the whole batch
+// cut evenly over the compute units.
 //
-// One workgroup = (sequence b, KV head, key split) with 8 waves.  Its query
-// rows are the G query heads of that KV head times the Bs block rows
-// (QR = G*Bs rows, 16-row tiles); the waves are (query tile, key group)
-// pairs, so with four query tiles two groups of four waves each take half of
-// every 128-key stage and are merged through LDS at the end.  Every context
-// K/V byte is read from HBM once per step, and all of a stage's K/V loads are
-// issued together (one round of memory latency per stage).
+// Work decomposition.  Every (sequence b, KV head h) pair is a segment of
+// T_b + Bs keys (T_b = committed context length, clamped to [0, max_ctx]).
+// The segments are laid end to end, b major and h minor, and the resulting
+// key axis is cut into gridDim.x ranges of Q keys, one per workgroup, so a
+// ragged batch keeps every compute unit busy in a single dispatch round and a
+// single sequence is spread over all of them.  A workgroup walks its range in
+// stages of 192 keys.  The part of one segment that a workgroup owns is a
+// piece: where the range crosses into the next segment the workgroup closes
+// its piece and starts the next one with that segment's queries.  A piece
+// that is a whole segment writes the normalised output; any other piece
+// writes an unnormalised partial (O, running max, running sum) into slot
+// w + s (workgroup w, segment s: distinct for every piece, since a later
+// piece of the same workgroup has a larger segment index and a later piece of
+// the same segment a larger workgroup index), and a second kernel merges the
+// pieces of each split segment in a fixed order (deterministic; no
+// cross-workgroup atomics).
+//
+// Inside a piece: one workgroup of 8 waves; its query rows are the G query
+// heads of the KV head times the Bs block rows (QR = G*Bs rows, 16-row
+// tiles).  The waves are (query tile, key group) pairs: the key groups split
+// the six 32-key units of every stage and are merged through LDS when the
+// piece ends.  Every context K/V byte is read from HBM once per step; a
+// stage's K/V loads are all issued together, one stage ahead of the matrix
+// work.
 //
 // Scores are formed transposed (S^T = K Q^T, 16x16x32 MFMA) so that each lane
 // owns one query row: the online-softmax max and scale are per lane, and the
@@ -17,26 +35,30 @@
 // dimension, which keeps the transposing stores at two-way bank conflicts and
 // the operand reads conflict-free.  Queries and probabilities enter the bf16
 // products as hi/lo pairs (two MFMAs each), keys and values as stored.
-// Splits write unnormalised partials (O, running max, running sum) that a
-// second kernel merges in a fixed order (deterministic; no cross-workgroup
-// atomics, which cost tens of nanoseconds each on this chip).
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
 namespace dfl {
 
-constexpr int kStage = 128;   // keys per LDS stage
-constexpr int kUnit = 32;     // keys per softmax update / PV product
+constexpr int kUnit = 32;               // keys per softmax update / PV product
+constexpr int kUnits = 6;               // units per LDS stage
+constexpr int kStage = kUnit * kUnits;  // keys per LDS stage
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
+constexpr int kMinPieceKeys = 64;       // a workgroup's range is never cut shorter
 
 template <int D>
 struct AttnLds {
-  static constexpr int KS = D + 8;        // K row stride (elements)
-  static constexpr int VW = kStage / 2;   // V^T row length in dwords (key pairs)
+  static constexpr int KS = D + 8;  // K row stride (elements)
+  // V^T row length in dwords: kStage / 2 = 96 key pairs, padded to 128 so the
+  // column swizzle (an XOR of bits 1..4) never leaves the row
+  static constexpr int VW = 128;
   bf16_t k[kStage * KS];
   uint32_t vt[D * VW];
 };
+static_assert(kStage / 2 <= 96, "V^T rows hold at most 96 key pairs");
 
 // Column of key pair kp in V^T row d.  Even, so a pair of key pairs stays
 // adjacent and in order.
@@ -48,34 +70,173 @@ __device__ __forceinline__ void split_out(bf16_t* hi, bf16_t* lo, size_t idx, fl
   lo[idx] = f32_to_bf16_bits(v - bf16_bits_to_f32(h));
 }
 
-// Waves per key group (a power of two covering QT query tiles).
+// Waves per key group (a power of two covering QT query tiles), and the key
+// groups: the largest divisor of the six units of a stage that fits the waves.
 __host__ __device__ inline int attn_qtp(int QT) { return QT <= 1 ? 1 : QT <= 2 ? 2 : QT <= 4 ? 4 : 8; }
+__host__ __device__ constexpr int attn_kg(int qtp) { return qtp >= 8 ? 1 : qtp >= 4 ? 2 : qtp >= 2 ? 3 : 6; }
+
+// Wave-wide inclusive prefix sum.
+__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int t = __shfl_up(v, off);
+    if (lane >= off) v += t;
+  }
+  return v;
+}
+
+// The work plan of a launch over nwg workgroups, built by one wave in LDS
+// (lane l owns sequences l, l + 64, ...; all its loads are issued together;
+// the caller synchronises before reading):
+//   pre[b]  = sum over b' < b of L_b', L_b = T_b + Bs (a segment's keys), b = 0..B
+//   wpre[b] = Hkv * sum over b' < b of n_b', n_b = max(1, floor(L_b * nwg / total))
+// with total = Hkv * pre[B], and *seg_mode.  Segment mode (every segment of
+// sequence b cut into n_b balanced pieces, one workgroup each, the
+// workgroups of sequence b starting at wpre[b]) is taken when those pieces fit
+// the grid and none is more than 5/4 of an equal share of the keys; it keeps
+// every workgroup inside one segment.  Otherwise the flattened key axis is cut
+// into equal ranges.  n_b is formed in fp32 (the same instructions in every
+// kernel that reads the plan, so all of them agree).
+__device__ __forceinline__ int range_keys(int total, int nwg);
+__device__ __forceinline__ void build_plan(const int32_t* ctx_len, int B, int Bs, int Hkv, int max_ctx, int nwg,
+                                           int* pre, int* wpre, int* seg_mode, int lane) {
+  const int nI = (B + 63) >> 6;  // sequences per lane, at most 16
+  int v[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int b = lane + 64 * i;
+    v[i] = i < nI && b < B ? min(max(ctx_len[b], 0), max_ctx) + Bs : 0;
+  }
+  int carry = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    if (i >= nI) break;
+    const int incl = wave_incl_scan(v[i], lane) + carry;
+    if (lane + 64 * i < B) pre[lane + 64 * i + 1] = incl;
+    carry = __shfl(incl, 63);
+  }
+  const int total = Hkv * carry;
+  const float share = (float)nwg / (float)total;
+  int wcarry = 0, longest = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    if (i >= nI) break;
+    const int b = lane + 64 * i;
+    const int n = b < B ? max(1, (int)((float)v[i] * share)) : 0;
+    if (n > 0) longest = max(longest, (v[i] + n - 1) / n);
+    const int incl = Hkv * wave_incl_scan(n, lane) + wcarry;
+    if (b < B) wpre[b + 1] = incl;
+    wcarry = __shfl(incl, 63);
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) longest = max(longest, __shfl_xor(longest, off));
+  if (lane == 0) {
+    pre[0] = 0;
+    wpre[0] = 0;
+    *seg_mode = wcarry <= nwg && 4 * longest <= 5 * range_keys(total, nwg);
+  }
+}
+
+// Keys per workgroup range of the flattened key axis of `total` keys.
+__device__ __forceinline__ int range_keys(int total, int nwg) { return max((total + nwg - 1) / nwg, kMinPieceKeys); }
+
+// Largest b in [0, B) with key(b) <= x, for key nondecreasing over [0, B].
+template <typename F>
+__device__ __forceinline__ int upper_index(int B, int x, F key) {
+  int lo = 0, hi = B;  // key(lo) <= x < key(hi)
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (key(mid) <= x) lo = mid;
+    else hi = mid;
+  }
+  return lo;
+}
 
 // QTP (waves per key group, >= the query tiles) is a template parameter so
 // that a wave's key units unroll completely.
 template <typename S, int D, int QTP>
 __global__ void __launch_bounds__(kThreads) attention_kernel(const AttnArgs a) {
-  constexpr int KG = kWaves / QTP < kStage / kUnit ? kWaves / QTP : kStage / kUnit;  // key groups
-  constexpr int UPG = (kStage / kUnit) / KG;  // 32-key units per key group and stage
+  constexpr int KG = attn_kg(QTP);  // key groups
+  constexpr int UPG = kUnits / KG;  // 32-key units per key group and stage
+  static_assert(KG * QTP <= kWaves && UPG * KG == kUnits, "wave layout");
   extern __shared__ __align__(16) unsigned char lds_raw[];
   AttnLds<D>& L = *reinterpret_cast<AttnLds<D>*>(lds_raw);
+  int* pre = reinterpret_cast<int*>(lds_raw + sizeof(AttnLds<D>));  // [2][kAttnMaxBatch + 1]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int b = blockIdx.z, kvh = blockIdx.y, sp = blockIdx.x;
   const int G = a.Hq / a.Hkv;
   const int QR = G * a.Bs;
   const int QT = (QR + 15) / 16;
   const int qt = wave % QTP, kg = wave / QTP;
   const bool computes = qt < QT && kg < KG;
+  const int Hkv = a.Hkv, Bs = a.Bs;
 
-  // ---- this lane's query row (loads issued before the context length arrives)
+  // ---- this workgroup's piece(s)
+  int* wpre = pre + kAttnMaxBatch + 1;
+  int* mode = wpre + kAttnMaxBatch + 1;
+  if (wave == 0) build_plan(a.ctx_len, a.batch, Bs, Hkv, a.max_ctx, gridDim.x, pre, wpre, mode, lane);
+  __syncthreads();
+  const int total = Hkv * pre[a.batch];
+  const bool seg_mode = *mode != 0;
+  // the piece being computed: segment (b, h) of length seg_len starting at
+  // sstart on the flattened axis; keys [pstart, pend) of it are this workgroup's
+  struct Piece {
+    int b, h, seg_len, sstart, pstart, pend;
+  };
+  Piece p;
+  int g1;  // end of the workgroup's range on the flattened axis
+  if (seg_mode) {
+    const int w = blockIdx.x;
+    if (w >= wpre[a.batch]) return;
+    p.b = __builtin_amdgcn_readfirstlane(upper_index(a.batch, w, [&](int i) { return wpre[i]; }));
+    p.seg_len = __builtin_amdgcn_readfirstlane(pre[p.b + 1] - pre[p.b]);
+    const int nb = (wpre[p.b + 1] - wpre[p.b]) / Hkv;
+    const int idx = w - wpre[p.b];
+    p.h = __builtin_amdgcn_readfirstlane(idx / nb);
+    const int k = idx - p.h * nb;
+    p.sstart = Hkv * pre[p.b] + p.h * p.seg_len;
+    p.pstart = (int)((int64_t)k * p.seg_len / nb);
+    p.pend = (int)((int64_t)(k + 1) * p.seg_len / nb);
+    g1 = p.sstart + p.pend;
+  } else {
+    const int Q = range_keys(total, gridDim.x);
+    const int g0 = blockIdx.x * Q;
+    if (g0 >= total) return;
+    g1 = min(total, g0 + Q);
+    p.b = __builtin_amdgcn_readfirstlane(upper_index(a.batch, g0, [&](int i) { return Hkv * pre[i]; }));
+    p.seg_len = __builtin_amdgcn_readfirstlane(pre[p.b + 1] - pre[p.b]);
+    const int base = Hkv * pre[p.b];
+    p.h = __builtin_amdgcn_readfirstlane((g0 - base) / p.seg_len);
+    p.sstart = base + p.h * p.seg_len;
+    p.pstart = g0 - p.sstart;
+    p.pend = min(p.seg_len, g1 - p.sstart);
+  }
+  int c0 = p.pstart;  // first key of the current stage, in segment coordinates
+  // next stage; false when the range is done
+  auto advance = [&](Piece& q, int& c) -> bool {
+    c += kStage;
+    if (c < q.pend) return true;
+    q.sstart += q.seg_len;
+    if (q.sstart >= g1) return false;
+    if (++q.h == Hkv) {
+      q.h = 0;
+      ++q.b;
+      q.seg_len = __builtin_amdgcn_readfirstlane(pre[q.b + 1] - pre[q.b]);
+    }
+    q.pstart = 0;
+    q.pend = min(q.seg_len, g1 - q.sstart);
+    c = 0;
+    return true;
+  };
+
+  // ---- query rows of the current piece: lane's row r = 16*qt + (lane & 15)
   const int r = 16 * qt + (lane & 15);
   const bool qvalid = computes && r < QR;
   const int rr = qvalid ? r : 0;
-  const int gq = rr / a.Bs, iq = rr - gq * a.Bs;
+  const int gq = rr / Bs, iq = rr - gq * Bs;
   const int HqD = a.Hq * D;
-  const size_t qoff = (size_t)(b * a.Bs + iq) * HqD + (kvh * G + gq) * D;
   bf16x8 qf[D / 32], qr[D / 32];  // query = qf + qr (hi/lo pair)
-  {
+  auto q_load = [&](const Piece& q) {
+    const size_t qoff = (size_t)(q.b * Bs + iq) * HqD + (q.h * G + gq) * D;
     const bf16_t* qh = reinterpret_cast<const bf16_t*>(a.q_hi) + qoff;
     const bf16_t* ql = reinterpret_cast<const bf16_t*>(a.q_lo) + qoff;
 #pragma unroll
@@ -87,81 +248,82 @@ __global__ void __launch_bounds__(kThreads) attention_kernel(const AttnArgs a) {
         qr[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(ql + 32 * s + 8 * (lane >> 4)));
       }
     }
-  }
-
-  // a caller-set length outside [0, max_ctx] is clamped so no access leaves the cache
-  const int T = min(max(a.ctx_len[b], 0), a.max_ctx);
-  const int total = T + a.Bs;
-  const int ns = (total + a.CW - 1) / a.CW;
-  if (sp >= ns) return;
-  const int j0 = sp * a.CW;
-  const int j1 = min(total, j0 + a.CW);
-  const int nstages = (j1 - j0 + kStage - 1) / kStage;
+  };
 
   const S* kc = reinterpret_cast<const S*>(a.kc);
   const S* vc = reinterpret_cast<const S*>(a.vc);
   const S* kb = reinterpret_cast<const S*>(a.kb);
   const S* vb = reinterpret_cast<const S*>(a.vb);
-  const size_t row = (size_t)a.Hkv * D;  // elements between consecutive keys
-  auto key_ptr = [&](const S* cache, const S* blk, int j) {
-    return j < T ? cache + ((size_t)b * a.max_ctx + j) * row + kvh * D
-                 : blk + (size_t)(b * a.Bs + (j - T)) * row + kvh * D;
+  const size_t row = (size_t)Hkv * D;  // elements between consecutive keys
+  // key j of segment (b, h): context key j < T from the cache, block key j - T after it
+  auto key_ptr = [&](const S* cache, const S* blk, const Piece& q, int j) {
+    const int T = q.seg_len - Bs;
+    return j < T ? cache + ((size_t)q.b * a.max_ctx + j) * row + q.h * D
+                 : blk + (size_t)(q.b * Bs + (j - T)) * row + q.h * D;
   };
 
   // ---- staging through registers.  K: (key, 8-dim piece) items, 16 lanes per
-  // key row.  V: (key pair, piece) items; the two half-waves of 16 lanes take
-  // key pairs 16 apart (the bank pattern the V^T swizzle is built for).
+  // key row.  V: (key pair, piece) items in blocks of 32 key pairs; the two
+  // half-blocks of 16 take key pairs 16 apart (the bank pattern the V^T
+  // swizzle is built for).
   constexpr int PIECES = D / 8;
   constexpr int KITEMS = kStage * PIECES;
   constexpr int VITEMS = (kStage / 2) * PIECES;
   constexpr int KPT = KITEMS / kThreads;
-  constexpr int VPT = VITEMS / kThreads;
-  static_assert(KITEMS % kThreads == 0 && VITEMS % kThreads == 0, "stage items must fill the workgroup");
+  constexpr int VPT = (VITEMS + kThreads - 1) / kThreads;
+  static_assert(KITEMS % kThreads == 0 && VITEMS % 64 == 0, "stage items must fill whole waves");
   struct StageRegs {
     Raw8 k[KPT], v[VPT][2];
   };
-  auto v_item = [&](int idx, int& kp, int& p) {
-    p = idx % PIECES;
+  auto v_item = [&](int idx, int& kp, int& pc) {
+    pc = idx % PIECES;
     const int h = (idx / PIECES) & 1, rest = idx / (2 * PIECES);
     kp = (rest & 15) + 16 * h + 32 * (rest >> 4);
   };
-  // Loads are unconditional (keys past the split re-read its last key and are
-  // zeroed at the store): branch-free address selects keep the loads of a
-  // stage in flight together.
-  auto stage_load = [&](StageRegs& R, int c0) {
+  // Loads are unconditional within the stage's items (keys past the piece
+  // re-read its last key and are zeroed at the store): branch-free address
+  // selects keep the loads of a stage in flight together.
+  auto stage_load = [&](StageRegs& R, const Piece& q, int c) {
+    const int jl = q.pend - 1;
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
       const int idx = tid + i * kThreads;
       const int key = idx / PIECES, p8 = (idx % PIECES) * 8;
-      load_raw8<S>(R.k[i], key_ptr(kc, kb, min(c0 + key, j1 - 1)) + p8);
+      load_raw8<S>(R.k[i], key_ptr(kc, kb, q, min(c + key, jl)) + p8);
     }
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
-      int kp, p;
-      v_item(tid + i * kThreads, kp, p);
+      const int idx = tid + i * kThreads;
+      if (idx >= VITEMS) continue;  // whole waves
+      int kp, pc;
+      v_item(idx, kp, pc);
 #pragma unroll
-      for (int t = 0; t < 2; ++t) load_raw8<S>(R.v[i][t], key_ptr(vc, vb, min(c0 + 2 * kp + t, j1 - 1)) + 8 * p);
+      for (int t = 0; t < 2; ++t) load_raw8<S>(R.v[i][t], key_ptr(vc, vb, q, min(c + 2 * kp + t, jl)) + 8 * pc);
     }
   };
-  auto stage_store = [&](const StageRegs& R, int c0) {
+  auto stage_store = [&](const StageRegs& R, const Piece& q, int c) {
+    int t0 = tid;  // opaque: the store addresses are recomputed per stage, not kept live
+    asm volatile("" : "+v"(t0));
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
       const int idx = tid + i * kThreads;
       const int key = idx / PIECES, p8 = (idx % PIECES) * 8;
-      const bf16x8 v = c0 + key < j1 ? raw_to_bf16x8<S>(R.k[i]) : bf16x8{};
+      const bf16x8 v = c + key < q.pend ? raw_to_bf16x8<S>(R.k[i]) : bf16x8{};
       *reinterpret_cast<bf16x8*>(&L.k[key * AttnLds<D>::KS + p8]) = v;
     }
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
-      int kp, p;
-      v_item(tid + i * kThreads, kp, p);
+      const int idx = t0 + i * kThreads;
+      if (idx >= VITEMS) continue;
+      int kp, pc;
+      v_item(idx, kp, pc);
       float v0[8], v1[8];
       raw_to_f32x8<S>(R.v[i][0], v0);
       raw_to_f32x8<S>(R.v[i][1], v1);
-      const bool ok0 = c0 + 2 * kp < j1, ok1 = c0 + 2 * kp + 1 < j1;
+      const bool ok0 = c + 2 * kp < q.pend, ok1 = c + 2 * kp + 1 < q.pend;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const int d = 8 * p + e;
+        const int d = 8 * pc + e;
         const uint32_t lo = ok0 ? (uint32_t)f32_to_bf16_bits(v0[e]) : 0u;
         const uint32_t hi = ok1 ? (uint32_t)f32_to_bf16_bits(v1[e]) : 0u;
         L.vt[d * AttnLds<D>::VW + vt_col(d, kp)] = lo | (hi << 16);
@@ -174,263 +336,313 @@ __global__ void __launch_bounds__(kThreads) attention_kernel(const AttnArgs a) {
 #pragma unroll
   for (int ds = 0; ds < D / 16; ++ds) o[ds] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // Stages are fetched PF ahead through a pair of register sets: with PF = 2
-  // the loads of stage st+2 are issued before the matrix work of stage st and
-  // stage st+1 (fetched a stage earlier) is stored to LDS after it; the widest
-  // wave layout (eight query tiles) and fp32 storage need the registers and
-  // fetch one ahead.
-  constexpr int PF = (QTP >= 8 || sizeof(S) == 4) ? 1 : 2;
-  StageRegs ra, rb;
-  stage_load(ra, j0);
-  if (PF == 2 && nstages > 1) stage_load(rb, j0 + kStage);
-  stage_store(ra, j0);
-  __syncthreads();
-  auto step = [&](StageRegs& fr, StageRegs& nx, int st) {
-    const int c0 = j0 + st * kStage;
-    if (PF == 2 && st + 2 < nstages) stage_load(fr, c0 + 2 * kStage);  // fr's stage st is already in LDS
-    if (PF == 1 && st + 1 < nstages) stage_load(nx, c0 + kStage);
-    if (computes) {
-      // ---- scores S^T[key][q] of all the wave's units (independent MFMA
-      // chains), then one softmax update and one rescale for the stage
-      f32x4 sc[UPG][2];
+  // ---- one stage: for each chunk of up to three of the wave's units, the
+  // scores S^T[key][q] (independent MFMA chains), one softmax update and one
+  // rescale, then O^T += V^T P^T.  The LDS addresses are recomputed from an
+  // opaque copy of the lane index in every stage: hoisted out of the stage loop
+  // they would not fit the registers, and their spill reloads would wait for
+  // the next stage's K/V loads.
+  constexpr int UC = UPG < 3 ? UPG : 3;  // units per softmax update
+  auto compute_units = [&](int c, int j1, int ub) {
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    f32x4 sc[UC][2];
 #pragma unroll
-      for (int uu = 0; uu < UPG; ++uu) {
-        const int u = kg * UPG + uu;
+    for (int uu = 0; uu < UC; ++uu) {
+      const int u = ub + uu;
 #pragma unroll
-        for (int h = 0; h < 2; ++h) sc[uu][h] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (c0 + kUnit * u >= j1) continue;
+      for (int h = 0; h < 2; ++h) sc[uu][h] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (c + kUnit * u >= j1) continue;
 #pragma unroll
-        for (int s = 0; s < D / 32; ++s)
+      for (int s = 0; s < D / 32; ++s)
 #pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            const bf16x8 kf = *reinterpret_cast<const bf16x8*>(
-                &L.k[(kUnit * u + 16 * h + (lane & 15)) * AttnLds<D>::KS + 32 * s + 8 * (lane >> 4)]);
-            sc[uu][h] = mfma16x16x32(kf, qf[s], sc[uu][h]);
-            sc[uu][h] = mfma16x16x32(kf, qr[s], sc[uu][h]);
-          }
+        for (int h = 0; h < 2; ++h) {
+          const bf16x8 kf = *reinterpret_cast<const bf16x8*>(
+              &L.k[(kUnit * u + 16 * h + (ln & 15)) * AttnLds<D>::KS + 32 * s + 8 * (ln >> 4)]);
+          sc[uu][h] = mfma16x16x32(kf, qf[s], sc[uu][h]);
+          sc[uu][h] = mfma16x16x32(kf, qr[s], sc[uu][h]);
+        }
+    }
+    // lane holds keys c + 32*u + 16*h + 4*(lane>>4) + e for query row (lane & 15)
+    float cmax = -INFINITY;
+#pragma unroll
+    for (int uu = 0; uu < UC; ++uu)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (c + kUnit * (ub + uu) + 16 * h + 4 * (lane >> 4) + e >= j1) sc[uu][h][e] = -INFINITY;
+          cmax = fmaxf(cmax, sc[uu][h][e]);
+        }
+    cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
+    cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
+    const float m_new = fmaxf(m_run, cmax);
+    if (m_new == -INFINITY) return;  // no valid key in these units
+    const float alpha = fast_exp2(m_run - m_new);
+    float psum = 0.f;
+#pragma unroll
+    for (int uu = 0; uu < UC; ++uu)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          sc[uu][h][e] = fast_exp2(sc[uu][h][e] - m_new);
+          psum += sc[uu][h][e];
+        }
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+#pragma unroll
+    for (int ds = 0; ds < D / 16; ++ds) o[ds] *= alpha;
+    // O^T[d][q] += V^T[d][keys] P^T[keys][q]; P as a hi/lo pair
+#pragma unroll
+    for (int uu = 0; uu < UC; ++uu) {
+      const int u = ub + uu;
+      if (c + kUnit * u >= j1) continue;
+      bf16x8 ph, pl;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        ph[e] = (__bf16)sc[uu][0][e];
+        ph[4 + e] = (__bf16)sc[uu][1][e];
+        pl[e] = (__bf16)(sc[uu][0][e] - (float)ph[e]);
+        pl[4 + e] = (__bf16)(sc[uu][1][e] - (float)ph[4 + e]);
       }
-      // lane holds keys c0 + 32*u + 16*h + 4*(lane>>4) + e for query row (lane & 15)
-      float cmax = -INFINITY;
+      const int kp0 = (kUnit / 2) * u + 2 * (ln >> 4);  // keys 32*u + 4*(lane>>4) + [0, 4)
 #pragma unroll
-      for (int uu = 0; uu < UPG; ++uu)
+      for (int ds = 0; ds < D / 16; ++ds) {
+        const int d = 16 * ds + (ln & 15);
+        const uint32_t* vrow = &L.vt[d * AttnLds<D>::VW];
+        const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow + vt_col(d, kp0));
+        const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + vt_col(d, kp0 + 8));
+        const bf16x8 vf = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+        o[ds] = mfma16x16x32(vf, ph, o[ds]);
+        o[ds] = mfma16x16x32(vf, pl, o[ds]);
+      }
+    }
+  };
+  // the stage's units that hold keys are split evenly over the key groups
+  auto compute = [&](int c, int j1) {
+    if (!computes) return;
+    const int nu = min(kUnits, (j1 - c + kUnit - 1) / kUnit);
+    const int per = (nu + KG - 1) / KG;
+    const int u0 = kg * per;
+    const int jg = min(j1, c + kUnit * min(nu, u0 + per));  // this group's key limit
+    for (int cb = 0; cb < per; cb += UC) compute_units(c, jg, u0 + cb);
+  };
+
+  // ---- close a piece: merge the key groups of each query tile through LDS
+  // (group 0 keeps the result; the records reuse the stage area, so every wave
+  // must be done reading the stage), then write the output or the partial.
+  // Records are [group-1][tile][d-slice][lane] 16-byte slots, so a wave's LDS
+  // traffic is conflict-free 16-byte accesses.
+  auto close_piece = [&](const Piece& q) {
+    if constexpr (KG > 1) {
+      __syncthreads();
+      f32x4* mo = reinterpret_cast<f32x4*>(lds_raw);                               // [KG-1][QTP][D/16][64]
+      float* mml = reinterpret_cast<float*>(mo + (KG - 1) * QTP * (D / 16) * 64);  // [KG-1][QTP][64][2]
+      if (computes && kg > 0) {
+        const int g = (kg - 1) * QTP + qt;
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
+        for (int ds = 0; ds < D / 16; ++ds) mo[(g * (D / 16) + ds) * 64 + lane] = o[ds];
+        mml[(g * 64 + lane) * 2] = m_run;
+        mml[(g * 64 + lane) * 2 + 1] = l_run;
+      }
+      __syncthreads();
+      if (computes && kg == 0) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            if (c0 + kUnit * (kg * UPG + uu) + 16 * h + 4 * (lane >> 4) + e >= j1) sc[uu][h][e] = -INFINITY;
-            cmax = fmaxf(cmax, sc[uu][h][e]);
-          }
-      cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
-      cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
-      const float m_new = fmaxf(m_run, cmax);
-      if (m_new != -INFINITY) {  // some key of this wave's share of the stage is valid
-        const float alpha = fast_exp2(m_run - m_new);
-        float psum = 0.f;
+        for (int g2 = 1; g2 < KG; ++g2) {
+          const int g = (g2 - 1) * QTP + qt;
+          const float m2 = mml[(g * 64 + lane) * 2], l2 = mml[(g * 64 + lane) * 2 + 1];
+          const float mn = fmaxf(m_run, m2);
+          if (mn == -INFINITY) continue;
+          const float w1 = m_run == -INFINITY ? 0.f : fast_exp2(m_run - mn);
+          const float w2 = m2 == -INFINITY ? 0.f : fast_exp2(m2 - mn);
 #pragma unroll
-        for (int uu = 0; uu < UPG; ++uu)
-#pragma unroll
-          for (int h = 0; h < 2; ++h)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              sc[uu][h][e] = fast_exp2(sc[uu][h][e] - m_new);
-              psum += sc[uu][h][e];
-            }
-        l_run = l_run * alpha + psum;
-        m_run = m_new;
-#pragma unroll
-        for (int ds = 0; ds < D / 16; ++ds) o[ds] *= alpha;
-        // ---- O^T[d][q] += V^T[d][keys] P^T[keys][q]; P as a hi/lo pair
-#pragma unroll
-        for (int uu = 0; uu < UPG; ++uu) {
-          const int u = kg * UPG + uu;
-          if (c0 + kUnit * u >= j1) continue;
-          bf16x8 ph, pl;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            ph[e] = (__bf16)sc[uu][0][e];
-            ph[4 + e] = (__bf16)sc[uu][1][e];
-            pl[e] = (__bf16)(sc[uu][0][e] - (float)ph[e]);
-            pl[4 + e] = (__bf16)(sc[uu][1][e] - (float)ph[4 + e]);
-          }
-          const int kp0 = (kUnit / 2) * u + 2 * (lane >> 4);  // keys 32*u + 4*(lane>>4) + [0, 4)
-#pragma unroll
-          for (int ds = 0; ds < D / 16; ++ds) {
-            const int d = 16 * ds + (lane & 15);
-            const uint32_t* vrow = &L.vt[d * AttnLds<D>::VW];
-            const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow + vt_col(d, kp0));
-            const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + vt_col(d, kp0 + 8));
-            const bf16x8 vf = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
-            o[ds] = mfma16x16x32(vf, ph, o[ds]);
-            o[ds] = mfma16x16x32(vf, pl, o[ds]);
-          }
+          for (int ds = 0; ds < D / 16; ++ds) o[ds] = o[ds] * w1 + mo[(g * (D / 16) + ds) * 64 + lane] * w2;
+          l_run = l_run * w1 + l2 * w2;
+          m_run = mn;
         }
       }
     }
-    if (st + 1 < nstages) {
-      __syncthreads();
-      stage_store(nx, c0 + kStage);
-      __syncthreads();
-    }
-  };
-  if constexpr (PF == 1) {
-    for (int st = 0; st < nstages; ++st) step(ra, ra, st);
-  } else {
-    for (int st = 0; st < nstages; st += 2) {
-      step(ra, rb, st);
-      if (st + 1 < nstages) step(rb, ra, st + 1);
-    }
-  }
-
-  // ---- merge the key groups of each query tile through LDS (group 0 keeps the
-  // result).  Records are [group-1][tile][d-slice][lane] 16-byte slots, so a
-  // wave's LDS traffic is conflict-free 16-byte accesses.
-  if constexpr (KG > 1) {
-    __syncthreads();  // every wave is done reading K / V^T
-    f32x4* mo = reinterpret_cast<f32x4*>(lds_raw);                       // [KG-1][QTP][D/16][64]
-    float* mml = reinterpret_cast<float*>(mo + (KG - 1) * QTP * (D / 16) * 64);  // [KG-1][QTP][64][2]
-    if (computes && kg > 0) {
-      const int g = (kg - 1) * QTP + qt;
-#pragma unroll
-      for (int ds = 0; ds < D / 16; ++ds) mo[(g * (D / 16) + ds) * 64 + lane] = o[ds];
-      mml[(g * 64 + lane) * 2] = m_run;
-      mml[(g * 64 + lane) * 2 + 1] = l_run;
-    }
-    __syncthreads();
     if (computes && kg == 0) {
+      // lane (q = lane & 15) holds O^T rows d = 16*ds + 4*(lane>>4) + e
+      float l_tot = l_run + __shfl_xor(l_run, 16);
+      l_tot += __shfl_xor(l_tot, 32);
+      if (q.pstart == 0 && q.pend == q.seg_len) {  // the whole segment: final output
+        if (qvalid) {
+          bf16_t* out_h = reinterpret_cast<bf16_t*>(a.out_hi);
+          bf16_t* out_l = reinterpret_cast<bf16_t*>(a.out_lo);
+          const size_t qoff = (size_t)(q.b * Bs + iq) * HqD + (q.h * G + gq) * D;
+          const float inv = 1.0f / l_tot;
 #pragma unroll
-      for (int g2 = 1; g2 < KG; ++g2) {
-        const int g = (g2 - 1) * QTP + qt;
-        const float m2 = mml[(g * 64 + lane) * 2], l2 = mml[(g * 64 + lane) * 2 + 1];
-        const float mn = fmaxf(m_run, m2);  // finite: group 0 always has a valid key
-        const float w1 = fast_exp2(m_run - mn);
-        const float w2 = m2 == -INFINITY ? 0.f : fast_exp2(m2 - mn);
+          for (int ds = 0; ds < D / 16; ++ds)
 #pragma unroll
-        for (int ds = 0; ds < D / 16; ++ds) o[ds] = o[ds] * w1 + mo[(g * (D / 16) + ds) * 64 + lane] * w2;
-        l_run = l_run * w1 + l2 * w2;
-        m_run = mn;
+            for (int e = 0; e < 4; ++e)
+              split_out(out_h, out_l, qoff + 16 * ds + 4 * (lane >> 4) + e, o[ds][e] * inv);
+        }
+      } else if (qvalid) {
+        const size_t slot = (size_t)blockIdx.x + q.b * Hkv + q.h;
+        float* po = a.part_o + (slot * QR + r) * D;
+#pragma unroll
+        for (int ds = 0; ds < D / 16; ++ds) *reinterpret_cast<f32x4*>(po + 16 * ds + 4 * (lane >> 4)) = o[ds];
+        if ((lane >> 4) == 0) {
+          a.part_ml[(slot * QR + r) * 2 + 0] = m_run;
+          a.part_ml[(slot * QR + r) * 2 + 1] = l_tot;
+        }
       }
     }
-  }
-  if (!computes || kg != 0) return;
+    m_run = -INFINITY;
+    l_run = 0.f;
+#pragma unroll
+    for (int ds = 0; ds < D / 16; ++ds) o[ds] = f32x4{0.f, 0.f, 0.f, 0.f};
+  };
 
-  // lane (q = lane & 15) holds O^T rows d = 16*ds + 4*(lane>>4) + e
-  float l_tot = l_run + __shfl_xor(l_run, 16);
-  l_tot += __shfl_xor(l_tot, 32);
-
-  if (ns == 1) {
-    if (qvalid) {
-      bf16_t* out_h = reinterpret_cast<bf16_t*>(a.out_hi);
-      bf16_t* out_l = reinterpret_cast<bf16_t*>(a.out_lo);
-      const float inv = 1.0f / l_tot;
-#pragma unroll
-      for (int ds = 0; ds < D / 16; ++ds)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) split_out(out_h, out_l, qoff + 16 * ds + 4 * (lane >> 4) + e, o[ds][e] * inv);
-    }
-    return;
-  }
-  const size_t pbase = ((size_t)(b * a.Hkv + kvh) * a.max_splits);
-  if (qvalid) {
-    float* po = a.part_o + ((pbase + sp) * QR + r) * D;
-#pragma unroll
-    for (int ds = 0; ds < D / 16; ++ds) *reinterpret_cast<f32x4*>(po + 16 * ds + 4 * (lane >> 4)) = o[ds];
-    if ((lane >> 4) == 0) {
-      a.part_ml[((pbase + sp) * QR + r) * 2 + 0] = m_run;
-      a.part_ml[((pbase + sp) * QR + r) * 2 + 1] = l_tot;
-    }
+  // ---- pipeline: the loads of the next stage are issued before the matrix
+  // work of the current one and stored to LDS after it
+  StageRegs R;
+  q_load(p);
+  stage_load(R, p, c0);
+  stage_store(R, p, c0);
+  __syncthreads();
+  while (true) {
+    Piece pn = p;
+    int cn = c0;
+    const bool more = advance(pn, cn);
+    if (more) stage_load(R, pn, cn);
+    compute(c0, p.pend);
+    const bool ends = !more || pn.sstart != p.sstart;
+    if (ends) close_piece(p);
+    if (!more) break;
+    __syncthreads();
+    stage_store(R, pn, cn);
+    __syncthreads();
+    if (ends) q_load(pn);
+    p = pn;
+    c0 = cn;
   }
 }
 
-// Merge of the split partials of one (sequence, KV head).  A wave covers four
-// (query row, 4 dims) items; its 16 lane groups take splits g, g+16, ... so all
-// partial loads are issued together, and the groups are folded by a fixed
-// butterfly (deterministic).  grid: (item groups of 16, Hkv, B), 256 threads.
+// Merge of the partial pieces of one segment (sequence, KV head).  Lanes are
+// (item, group) with SG groups per item (SG from the segment's piece count);
+// an item is one query row and 4 dims.  Group g takes pieces g, g+SG, ...,
+// four loads of each kind issued together, and the groups are folded by a
+// fixed butterfly (deterministic).  grid: (item chunks, B * Hkv), 256 threads.
 template <int D>
 __global__ void __launch_bounds__(256) attention_combine_kernel(const AttnArgs a) {
-  const int b = blockIdx.z, kvh = blockIdx.y;
-  const int T = min(max(a.ctx_len[b], 0), a.max_ctx);
-  const int ns = (T + a.Bs + a.CW - 1) / a.CW;
-  if (ns <= 1) return;  // written directly by the split kernel
+  __shared__ int pre[kAttnMaxBatch + 1], wpre[kAttnMaxBatch + 1], mode;
+  const int s = blockIdx.y, b = s / a.Hkv, h = s - b * a.Hkv;
+  const int tid = threadIdx.x, lane = tid & 63;
+  if (tid < 64) build_plan(a.ctx_len, a.batch, a.Bs, a.Hkv, a.max_ctx, a.nwg, pre, wpre, &mode, lane);
+  __syncthreads();
+  // this segment's pieces: workgroups w0 .. w0 + np - 1 (slots w + s)
+  int w0, np;
+  if (mode) {
+    np = (wpre[b + 1] - wpre[b]) / a.Hkv;
+    w0 = wpre[b] + h * np;
+  } else {
+    const int total = a.Hkv * pre[a.batch];
+    const int Q = range_keys(total, a.nwg);
+    const int seg_len = pre[b + 1] - pre[b];
+    const int sstart = a.Hkv * pre[b] + h * seg_len;
+    w0 = sstart / Q;
+    np = (sstart + seg_len - 1) / Q - w0 + 1;
+  }
+  if (np <= 1) return;  // written directly by the attention kernel
+  const int SG = np <= 4 ? 1 : np <= 16 ? 4 : 16;
+  const int per = 256 / SG;  // items per chunk
   const int G = a.Hq / a.Hkv;
   const int QR = G * a.Bs;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int sg = lane >> 2;
-  const int item = blockIdx.x * 16 + wave * 4 + (lane & 3);
-  const bool valid = item < QR * (D / 4);
-  const int it = valid ? item : 0;
-  const int r = it / (D / 4), d4 = (it - r * (D / 4)) * 4;
-  const size_t pbase = ((size_t)(b * a.Hkv + kvh) * a.max_splits);
-  const float* ml = a.part_ml + (pbase * QR + r) * 2;
-  const float* po = a.part_o + (pbase * QR + r) * D + d4;
-  const size_t sstride_ml = (size_t)QR * 2, sstride_o = (size_t)QR * D;
-
-  float m = -INFINITY, l = 0.f;
-  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int s0 = 0; s0 < ns; s0 += 64) {
-    float mv[4], lv[4];
-    f32x4 ov[4];
+  const int items = QR * (D / 4);
+  const int g = tid % SG, il = tid / SG;
+  const size_t slot0 = (size_t)w0 + s;
+  for (int chunk = blockIdx.x; chunk * per < items; chunk += gridDim.x) {
+    const int item = chunk * per + il;
+    const bool valid = item < items;
+    const int it = valid ? item : 0;
+    const int r = it / (D / 4), d4 = (it - r * (D / 4)) * 4;
+    float m = -INFINITY, l = 0.f;
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int p0 = 0; p0 < np; p0 += 4 * SG) {
+      float mv[4], lv[4];
+      f32x4 ov[4];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int s = s0 + sg + 16 * k;
-      mv[k] = -INFINITY;
-      lv[k] = 0.f;
-      ov[k] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (s < ns) {
-        mv[k] = ml[s * sstride_ml];
-        lv[k] = ml[s * sstride_ml + 1];
-        ov[k] = *reinterpret_cast<const f32x4*>(po + s * sstride_o);
+      for (int k = 0; k < 4; ++k) {
+        const int pc = p0 + g + SG * k;
+        mv[k] = -INFINITY;
+        lv[k] = 0.f;
+        ov[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (pc < np) {
+          const size_t sl = slot0 + pc;
+          mv[k] = a.part_ml[(sl * QR + r) * 2];
+          lv[k] = a.part_ml[(sl * QR + r) * 2 + 1];
+          ov[k] = *reinterpret_cast<const f32x4*>(a.part_o + (sl * QR + r) * D + d4);
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float mn = fmaxf(m, mv[k]);
+        if (mn == -INFINITY) continue;
+        const float w1 = m == -INFINITY ? 0.f : fast_exp2(m - mn);
+        const float w2 = mv[k] == -INFINITY ? 0.f : fast_exp2(mv[k] - mn);
+        acc = acc * w1 + ov[k] * w2;
+        l = l * w1 + lv[k] * w2;
+        m = mn;
       }
     }
+    for (int x = 1; x < SG; x <<= 1) {
+      const float mo = __shfl_xor(m, x), lo = __shfl_xor(l, x);
+      f32x4 ao;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const float mn = fmaxf(m, mv[k]);
-      if (mn == -INFINITY) continue;
+      for (int e = 0; e < 4; ++e) ao[e] = __shfl_xor(acc[e], x);
+      const float mn = fmaxf(m, mo);
       const float w1 = m == -INFINITY ? 0.f : fast_exp2(m - mn);
-      const float w2 = mv[k] == -INFINITY ? 0.f : fast_exp2(mv[k] - mn);
-      acc = acc * w1 + ov[k] * w2;
-      l = l * w1 + lv[k] * w2;
+      const float w2 = mo == -INFINITY ? 0.f : fast_exp2(mo - mn);
+      acc = acc * w1 + ao * w2;
+      l = l * w1 + lo * w2;
       m = mn;
     }
+    if (g != 0 || !valid) continue;
+    const float inv = 1.0f / l;
+    const int gq = r / a.Bs, iq = r - gq * a.Bs;
+    const size_t orow = (size_t)(b * a.Bs + iq) * (a.Hq * D) + (h * G + gq) * D + d4;
+    uint32_t hv[2], lv2[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const float v0 = acc[2 * e] * inv, v1 = acc[2 * e + 1] * inv;
+      const uint32_t h0 = f32_to_bf16_bits(v0), h1 = f32_to_bf16_bits(v1);
+      hv[e] = h0 | (h1 << 16);
+      lv2[e] = (uint32_t)f32_to_bf16_bits(v0 - bf16_bits_to_f32(h0)) |
+               ((uint32_t)f32_to_bf16_bits(v1 - bf16_bits_to_f32(h1)) << 16);
+    }
+    *reinterpret_cast<u32x2*>(reinterpret_cast<bf16_t*>(a.out_hi) + orow) = u32x2{hv[0], hv[1]};
+    *reinterpret_cast<u32x2*>(reinterpret_cast<bf16_t*>(a.out_lo) + orow) = u32x2{lv2[0], lv2[1]};
   }
-#pragma unroll
-  for (int x = 4; x <= 32; x <<= 1) {
-    const float mo = __shfl_xor(m, x), lo = __shfl_xor(l, x);
-    f32x4 ao;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) ao[e] = __shfl_xor(acc[e], x);
-    const float mn = fmaxf(m, mo);
-    const float w1 = m == -INFINITY ? 0.f : fast_exp2(m - mn);
-    const float w2 = mo == -INFINITY ? 0.f : fast_exp2(mo - mn);
-    acc = acc * w1 + ao * w2;
-    l = l * w1 + lo * w2;
-    m = mn;
-  }
-  if (sg != 0 || !valid) return;
-  const float inv = 1.0f / l;
-  const int gq = r / a.Bs, iq = r - gq * a.Bs;
-  const size_t orow = (size_t)(b * a.Bs + iq) * (a.Hq * D) + (kvh * G + gq) * D + d4;
-  bf16_t* out_h = reinterpret_cast<bf16_t*>(a.out_hi);
-  bf16_t* out_l = reinterpret_cast<bf16_t*>(a.out_lo);
-#pragma unroll
-  for (int e = 0; e < 4; ++e) split_out(out_h, out_l, orow + e, acc[e] * inv);
+}
+
+template <int D>
+static size_t attention_lds_bytes() {
+  return sizeof(AttnLds<D>) + (size_t)(2 * (kAttnMaxBatch + 1) + 1) * sizeof(int);
 }
 
 template <typename S, int D>
 static hipError_t launch_attention_d(const AttnArgs& a, hipStream_t stream) {
   const int QR = (a.Hq / a.Hkv) * a.Bs;
-  if (QR > 16 * kWaves || a.CW <= 0 || a.CW % 16) return hipErrorInvalidValue;
-  const size_t lds = sizeof(AttnLds<D>);
+  if (QR > 16 * kWaves || a.nwg <= 0 || a.batch > kAttnMaxBatch) return hipErrorInvalidValue;
+  const size_t lds = attention_lds_bytes<D>();
   const int qtp = attn_qtp((QR + 15) / 16);
   auto k = qtp == 1 ? attention_kernel<S, D, 1>
                     : qtp == 2 ? attention_kernel<S, D, 2> : qtp == 4 ? attention_kernel<S, D, 4> : attention_kernel<S, D, 8>;
   if (lds > 64 * 1024)
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize,
                               (int)lds);
-  hipLaunchKernelGGL(k, dim3(a.max_splits, a.Hkv, a.batch), dim3(kThreads), lds, stream, a);
+  hipLaunchKernelGGL(k, dim3(a.nwg), dim3(kThreads), lds, stream, a);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.max_splits <= 1) return e;
+  if (e != hipSuccess) return e;
+  // merge chunks per segment: enough for the finest grouping (16 items per
+  // chunk) at small batches, about 2048 workgroups in all at large ones
   const int items = QR * (D / 4);
-  hipLaunchKernelGGL(attention_combine_kernel<D>, dim3((items + 15) / 16, a.Hkv, a.batch), dim3(256), 0, stream, a);
+  const int segs = a.batch * a.Hkv;
+  const int gx = std::max(1, std::min((items + 15) / 16, (2048 + segs - 1) / segs));
+  hipLaunchKernelGGL(attention_combine_kernel<D>, dim3(gx, segs), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -116,6 +116,9 @@ struct FinishArgs {
 hipError_t launch_finish(int storage, FinishKind kind, const FinishArgs& f, hipStream_t stream);
 
 // ------------------------------------------------------------------ attention
+// Sequences per attention launch (the per-workgroup prefix table of segment
+// lengths lives in LDS).
+constexpr int kAttnMaxBatch = 1024;
 struct AttnArgs {
   const void* q_hi;  // bf16 hi/lo pair [B*Bs, Hq*D], already scaled by log2(e)/sqrt(D)
   const void* q_lo;
@@ -125,16 +128,15 @@ struct AttnArgs {
   const void* vc;
   const int32_t* ctx_len;
   int Bs, Hq, Hkv, D, max_ctx;
-  int CW;          // keys per split
-  int max_splits;  // grid.x
-  float* part_o;   // [B*Hkv*max_splits, QR, D]   unnormalised split outputs
-  float* part_ml;  // [B*Hkv*max_splits, QR, 2]   split running max and sum
+  int nwg;         // workgroups the batch's key axis is cut over (grid of the split kernel)
+  float* part_o;   // [nwg + B*Hkv slots, QR, D]   unnormalised piece outputs
+  float* part_ml;  // [nwg + B*Hkv slots, QR, 2]   piece running max and sum
   void* out_hi;    // bf16 hi/lo pair [B*Bs, Hq*D]
   void* out_lo;
   int batch;
 };
-// Launches the split attention and, for sequences with more than one split,
-// the merge of the split partials.
+// Launches the split attention and the merge of the pieces of every segment
+// that more than one workgroup touched.
 hipError_t launch_attention(int storage, const AttnArgs& a, hipStream_t stream);
 
 // ------------------------------------------------------------------ small kernels
