@@ -37,6 +37,22 @@ constexpr int kMtTargetWgs = kCUs;   // gemm_mt workgroups to aim for (one per c
 // one 8-wave workgroup per compute unit (the attention kernel's registers and
 // LDS allow one), so every range runs in the first dispatch round.
 constexpr int kAttnWgs = kCUs;
+constexpr int kAttnMinChunk = 64;  // keys
+
+// Small batches (at least two workgroups per segment) take fixed chunks: the
+// cache capacity of every segment cut into as many equal chunks as the grid
+// allows, so a workgroup's keys follow from its index alone.  Larger batches
+// are planned on the device from the context lengths.
+void attn_grid(const dflash_config& c, int batch, AttnArgs* a) {
+  const int segs = batch * c.n_kv_heads;
+  a->fixed_chunk = a->fixed_pieces = 0;
+  a->nwg = kAttnWgs;
+  if (2 * segs > kAttnWgs) return;
+  const int pieces = std::max(1, std::min(kAttnWgs / segs, (c.max_ctx + kAttnMinChunk - 1) / kAttnMinChunk));
+  a->fixed_pieces = pieces;
+  a->fixed_chunk = (c.max_ctx + pieces - 1) / pieces;
+  a->nwg = segs * pieces;
+}
 
 const char* validate(const dflash_config* c) {
   if (!c) return "null config";
@@ -142,7 +158,6 @@ struct WsLayout {
 WsLayout layout(const dflash_config& c) {
   WsLayout L{};
   const int st = c.dtype == DFLASH_DTYPE_BF16 ? ST_BF16 : ST_F32;
-  const size_t S = st == ST_BF16 ? 2 : 4;
   const size_t H = c.hidden, D = c.head_dim, F = c.ffn;
   const int Nq = c.n_q_heads * c.head_dim, Nk = c.n_kv_heads * c.head_dim;
   L.md = c.max_batch * c.block;
@@ -177,8 +192,6 @@ WsLayout layout(const dflash_config& c) {
   L.xs_lo = take((size_t)L.mmax * H * 2);
   L.q_hi = take((size_t)L.md * Nq * 2);
   L.q_lo = take((size_t)L.md * Nq * 2);
-  L.kb = take((size_t)L.md * Nk * S);
-  L.vb = take((size_t)L.md * Nk * S);
   L.o_hi = take((size_t)L.md * Nq * 2);
   L.o_lo = take((size_t)L.md * Nq * 2);
   L.act_hi = take((size_t)L.md * F * 2);
@@ -538,8 +551,9 @@ dflash_status dflash_draft_block(dflash_ctx* c, int32_t batch, const int32_t* bl
       f.q_scale = (float)(1.4426950408889634 / std::sqrt((double)D));
       f.out_hi = c->at<void>(L.q_hi);
       f.out_lo = c->at<void>(L.q_lo);
-      f.kb_out = c->at<void>(L.kb);
-      f.vb_out = c->at<void>(L.vb);
+      f.kv_cache[0] = c->kv_k[l];
+      f.kv_cache[1] = c->kv_v[l];
+      f.err = c->at<uint32_t>(L.err);
       if ((st = finish(c, FIN_QKV, f, gl, M, Nq + 2 * Nk, s))) return st;
     }
     {  // attention over [context ; block]
@@ -547,8 +561,6 @@ dflash_status dflash_draft_block(dflash_ctx* c, int32_t batch, const int32_t* bl
       AttnArgs a{};
       a.q_hi = c->at<void>(L.q_hi);
       a.q_lo = c->at<void>(L.q_lo);
-      a.kb = c->at<void>(L.kb);
-      a.vb = c->at<void>(L.vb);
       a.kc = c->kv_k[l];
       a.vc = c->kv_v[l];
       a.ctx_len = c->ctx_len;
@@ -557,7 +569,7 @@ dflash_status dflash_draft_block(dflash_ctx* c, int32_t batch, const int32_t* bl
       a.Hkv = cf.n_kv_heads;
       a.D = D;
       a.max_ctx = cf.max_ctx;
-      a.nwg = kAttnWgs;
+      attn_grid(cf, batch, &a);
       a.part_o = c->at<float>(L.part_o);
       a.part_ml = c->at<float>(L.part_ml);
       a.out_hi = c->at<void>(L.o_hi);

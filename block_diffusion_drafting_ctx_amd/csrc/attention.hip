@@ -2,29 +2,39 @@
 // [cached context ; the block itself], with the key axis of the whole batch
 // cut evenly over the compute units.
 //
-// Work decomposition.  Every (sequence b, KV head h) pair is a segment of
-// T_b + Bs keys (T_b = committed context length, clamped to [0, max_ctx]).
-// The segments are laid end to end, b major and h minor, and the resulting
-// key axis is cut into gridDim.x ranges of Q keys, one per workgroup, so a
-// ragged batch keeps every compute unit busy in a single dispatch round and a
-// single sequence is spread over all of them.  A workgroup walks its range in
-// stages of 192 keys.  The part of one segment that a workgroup owns is a
-// piece: where the range crosses into the next segment the workgroup closes
-// its piece and starts the next one with that segment's queries.  A piece
-// that is a whole segment writes the normalised output; any other piece
-// writes an unnormalised partial (O, running max, running sum) into slot
-// w + s (workgroup w, segment s: distinct for every piece, since a later
-// piece of the same workgroup has a larger segment index and a later piece of
-// the same segment a larger workgroup index), and a second kernel merges the
-// pieces of each split segment in a fixed order (deterministic; no
-// cross-workgroup atomics).
+// Every key is read from this layer's cache: the block's own K/V rows sit at
+// cache rows T_b + i (staged there by the Q/K/V finish kernel), so key j of
+// (sequence b, KV head h) is cache row j for j < L_b = T_b + Bs, and a key's
+// address never depends on T_b -- only whether it counts does.
+//
+// Work decomposition.  Every (b, h) pair is a segment of L_b keys; the parts
+// of segments the workgroups own are pieces.
+//  * Fixed chunks (small batches; chosen by the host): every segment is cut
+//    at multiples of a chunk size C fixed from the cache capacity, so
+//    workgroup (segment, chunk) knows its keys and queries from its index and
+//    issues its query, K/V and context-length loads together; chunks past L_b
+//    are dropped once the length arrives.
+//  * Planned (large batches): from the context lengths each workgroup builds
+//    the plan in LDS.  Either every segment is cut into a number of balanced
+//    pieces in proportion to its length (one workgroup each), or the segments
+//    are laid end to end (b major, h minor) and the resulting key axis is cut
+//    into gridDim.x equal ranges, where a workgroup closes its piece at a
+//    segment end and starts the next one with that segment's queries.
+// A workgroup walks its range in stages of 192 keys.  A piece that is a whole
+// segment writes the normalised output; any other piece writes an
+// unnormalised partial (O, running max, running sum) into slot w + s
+// (workgroup w, segment s: distinct for every piece, since a later piece of
+// the same workgroup has a larger segment index and a later piece of the same
+// segment a larger workgroup index), and a second kernel merges the pieces of
+// each split segment in a fixed order (deterministic; no cross-workgroup
+// atomics).  All of it runs in one dispatch round.
 //
 // Inside a piece: one workgroup of 8 waves; its query rows are the G query
 // heads of the KV head times the Bs block rows (QR = G*Bs rows, 16-row
 // tiles).  The waves are (query tile, key group) pairs: the key groups split
-// the six 32-key units of every stage and are merged through LDS when the
-// piece ends.  Every context K/V byte is read from HBM once per step; a
-// stage's K/V loads are all issued together, one stage ahead of the matrix
+// the 32-key units of every stage that hold keys, and are merged through LDS
+// when the piece ends.  Every context K/V byte is read from HBM once per step;
+// a stage's K/V loads are all issued together, one stage ahead of the matrix
 // work.
 //
 // Scores are formed transposed (S^T = K Q^T, 16x16x32 MFMA) so that each lane
@@ -110,17 +120,18 @@ __device__ __forceinline__ void build_plan(const int32_t* ctx_len, int B, int Bs
   int carry = 0;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    if (i >= nI) break;
-    const int incl = wave_incl_scan(v[i], lane) + carry;
-    if (lane + 64 * i < B) pre[lane + 64 * i + 1] = incl;
-    carry = __shfl(incl, 63);
+    if (i < nI) {  // wave-uniform
+      const int incl = wave_incl_scan(v[i], lane) + carry;
+      if (lane + 64 * i < B) pre[lane + 64 * i + 1] = incl;
+      carry = __shfl(incl, 63);
+    }
   }
   const int total = Hkv * carry;
   const float share = (float)nwg / (float)total;
   int wcarry = 0, longest = 0;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    if (i >= nI) break;
+    if (i >= nI) continue;  // wave-uniform
     const int b = lane + 64 * i;
     const int n = b < B ? max(1, (int)((float)v[i] * share)) : 0;
     if (n > 0) longest = max(longest, (v[i] + n - 1) / n);
@@ -170,64 +181,11 @@ __global__ void __launch_bounds__(kThreads) attention_kernel(const AttnArgs a) {
   const bool computes = qt < QT && kg < KG;
   const int Hkv = a.Hkv, Bs = a.Bs;
 
-  // ---- this workgroup's piece(s)
-  int* wpre = pre + kAttnMaxBatch + 1;
-  int* mode = wpre + kAttnMaxBatch + 1;
-  if (wave == 0) build_plan(a.ctx_len, a.batch, Bs, Hkv, a.max_ctx, gridDim.x, pre, wpre, mode, lane);
-  __syncthreads();
-  const int total = Hkv * pre[a.batch];
-  const bool seg_mode = *mode != 0;
   // the piece being computed: segment (b, h) of length seg_len starting at
   // sstart on the flattened axis; keys [pstart, pend) of it are this workgroup's
   struct Piece {
     int b, h, seg_len, sstart, pstart, pend;
   };
-  Piece p;
-  int g1;  // end of the workgroup's range on the flattened axis
-  if (seg_mode) {
-    const int w = blockIdx.x;
-    if (w >= wpre[a.batch]) return;
-    p.b = __builtin_amdgcn_readfirstlane(upper_index(a.batch, w, [&](int i) { return wpre[i]; }));
-    p.seg_len = __builtin_amdgcn_readfirstlane(pre[p.b + 1] - pre[p.b]);
-    const int nb = (wpre[p.b + 1] - wpre[p.b]) / Hkv;
-    const int idx = w - wpre[p.b];
-    p.h = __builtin_amdgcn_readfirstlane(idx / nb);
-    const int k = idx - p.h * nb;
-    p.sstart = Hkv * pre[p.b] + p.h * p.seg_len;
-    p.pstart = (int)((int64_t)k * p.seg_len / nb);
-    p.pend = (int)((int64_t)(k + 1) * p.seg_len / nb);
-    g1 = p.sstart + p.pend;
-  } else {
-    const int Q = range_keys(total, gridDim.x);
-    const int g0 = blockIdx.x * Q;
-    if (g0 >= total) return;
-    g1 = min(total, g0 + Q);
-    p.b = __builtin_amdgcn_readfirstlane(upper_index(a.batch, g0, [&](int i) { return Hkv * pre[i]; }));
-    p.seg_len = __builtin_amdgcn_readfirstlane(pre[p.b + 1] - pre[p.b]);
-    const int base = Hkv * pre[p.b];
-    p.h = __builtin_amdgcn_readfirstlane((g0 - base) / p.seg_len);
-    p.sstart = base + p.h * p.seg_len;
-    p.pstart = g0 - p.sstart;
-    p.pend = min(p.seg_len, g1 - p.sstart);
-  }
-  int c0 = p.pstart;  // first key of the current stage, in segment coordinates
-  // next stage; false when the range is done
-  auto advance = [&](Piece& q, int& c) -> bool {
-    c += kStage;
-    if (c < q.pend) return true;
-    q.sstart += q.seg_len;
-    if (q.sstart >= g1) return false;
-    if (++q.h == Hkv) {
-      q.h = 0;
-      ++q.b;
-      q.seg_len = __builtin_amdgcn_readfirstlane(pre[q.b + 1] - pre[q.b]);
-    }
-    q.pstart = 0;
-    q.pend = min(q.seg_len, g1 - q.sstart);
-    c = 0;
-    return true;
-  };
-
   // ---- query rows of the current piece: lane's row r = 16*qt + (lane & 15)
   const int r = 16 * qt + (lane & 15);
   const bool qvalid = computes && r < QR;
@@ -252,14 +210,11 @@ __global__ void __launch_bounds__(kThreads) attention_kernel(const AttnArgs a) {
 
   const S* kc = reinterpret_cast<const S*>(a.kc);
   const S* vc = reinterpret_cast<const S*>(a.vc);
-  const S* kb = reinterpret_cast<const S*>(a.kb);
-  const S* vb = reinterpret_cast<const S*>(a.vb);
   const size_t row = (size_t)Hkv * D;  // elements between consecutive keys
-  // key j of segment (b, h): context key j < T from the cache, block key j - T after it
-  auto key_ptr = [&](const S* cache, const S* blk, const Piece& q, int j) {
-    const int T = q.seg_len - Bs;
-    return j < T ? cache + ((size_t)q.b * a.max_ctx + j) * row + q.h * D
-                 : blk + (size_t)(q.b * Bs + (j - T)) * row + q.h * D;
+  // key j of segment (b, h): cache row j (kept inside the cache; a segment
+  // longer than the cache only arises with a flagged overflow)
+  auto key_ptr = [&](const S* cache, const Piece& q, int j) {
+    return cache + ((size_t)q.b * a.max_ctx + min(j, a.max_ctx - 1)) * row + q.h * D;
   };
 
   // ---- staging through registers.  K: (key, 8-dim piece) items, 16 lanes per
@@ -289,7 +244,7 @@ __global__ void __launch_bounds__(kThreads) attention_kernel(const AttnArgs a) {
     for (int i = 0; i < KPT; ++i) {
       const int idx = tid + i * kThreads;
       const int key = idx / PIECES, p8 = (idx % PIECES) * 8;
-      load_raw8<S>(R.k[i], key_ptr(kc, kb, q, min(c + key, jl)) + p8);
+      load_raw8<S>(R.k[i], key_ptr(kc, q, min(c + key, jl)) + p8);
     }
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
@@ -298,7 +253,7 @@ __global__ void __launch_bounds__(kThreads) attention_kernel(const AttnArgs a) {
       int kp, pc;
       v_item(idx, kp, pc);
 #pragma unroll
-      for (int t = 0; t < 2; ++t) load_raw8<S>(R.v[i][t], key_ptr(vc, vb, q, min(c + 2 * kp + t, jl)) + 8 * pc);
+      for (int t = 0; t < 2; ++t) load_raw8<S>(R.v[i][t], key_ptr(vc, q, min(c + 2 * kp + t, jl)) + 8 * pc);
     }
   };
   auto stage_store = [&](const StageRegs& R, const Piece& q, int c) {
@@ -329,6 +284,84 @@ __global__ void __launch_bounds__(kThreads) attention_kernel(const AttnArgs a) {
         L.vt[d * AttnLds<D>::VW + vt_col(d, kp)] = lo | (hi << 16);
       }
     }
+  };
+
+  // ---- this workgroup's piece(s)
+  Piece p;
+  int g1;                 // end of the workgroup's range on the flattened axis
+  StageRegs R;
+  bool staged = false;    // the first stage's loads are already in flight
+  int* wpre = pre + kAttnMaxBatch + 1;
+  int* mode = wpre + kAttnMaxBatch + 1;
+  if (a.fixed_chunk > 0) {
+    // fixed chunks: segment and chunk from the workgroup index; the queries
+    // and the chunk's first stage (every key of it inside the cache) are
+    // loaded together with the context length
+    const int C = a.fixed_chunk;
+    const int sg = blockIdx.x / a.fixed_pieces, k = blockIdx.x - sg * a.fixed_pieces;
+    p.b = sg / Hkv;
+    p.h = sg - p.b * Hkv;
+    const int craw = a.ctx_len[p.b];
+    p.pstart = k * C;
+    p.sstart = 0;
+    if (p.pstart >= a.max_ctx) return;
+    Piece ps = p;
+    ps.seg_len = a.max_ctx;
+    ps.pend = min(p.pstart + C, a.max_ctx);
+    q_load(ps);
+    stage_load(R, ps, ps.pstart);
+    staged = true;
+    p.seg_len = min(min(max(craw, 0), a.max_ctx) + Bs, a.max_ctx);
+    p.pend = min(p.pstart + C, p.seg_len);
+    if (p.pstart >= p.pend) return;
+    g1 = p.pend;
+  } else {
+    if (wave == 0) build_plan(a.ctx_len, a.batch, Bs, Hkv, a.max_ctx, gridDim.x, pre, wpre, mode, lane);
+    __syncthreads();
+    const int total = Hkv * pre[a.batch];
+    if (*mode != 0) {
+      const int w = blockIdx.x;
+      if (w >= wpre[a.batch]) return;
+      p.b = __builtin_amdgcn_readfirstlane(upper_index(a.batch, w, [&](int i) { return wpre[i]; }));
+      p.seg_len = __builtin_amdgcn_readfirstlane(pre[p.b + 1] - pre[p.b]);
+      const int nb = (wpre[p.b + 1] - wpre[p.b]) / Hkv;
+      const int idx = w - wpre[p.b];
+      p.h = __builtin_amdgcn_readfirstlane(idx / nb);
+      const int k = idx - p.h * nb;
+      p.sstart = Hkv * pre[p.b] + p.h * p.seg_len;
+      p.pstart = (int)((int64_t)k * p.seg_len / nb);
+      p.pend = (int)((int64_t)(k + 1) * p.seg_len / nb);
+      g1 = p.sstart + p.pend;
+    } else {
+      const int Q = range_keys(total, gridDim.x);
+      const int g0 = blockIdx.x * Q;
+      if (g0 >= total) return;
+      g1 = min(total, g0 + Q);
+      p.b = __builtin_amdgcn_readfirstlane(upper_index(a.batch, g0, [&](int i) { return Hkv * pre[i]; }));
+      p.seg_len = __builtin_amdgcn_readfirstlane(pre[p.b + 1] - pre[p.b]);
+      const int base = Hkv * pre[p.b];
+      p.h = __builtin_amdgcn_readfirstlane((g0 - base) / p.seg_len);
+      p.sstart = base + p.h * p.seg_len;
+      p.pstart = g0 - p.sstart;
+      p.pend = min(p.seg_len, g1 - p.sstart);
+    }
+  }
+  int c0 = p.pstart;  // first key of the current stage, in segment coordinates
+  // next stage; false when the range is done
+  auto advance = [&](Piece& q, int& c) -> bool {
+    c += kStage;
+    if (c < q.pend) return true;
+    q.sstart += q.seg_len;
+    if (q.sstart >= g1) return false;
+    if (++q.h == Hkv) {
+      q.h = 0;
+      ++q.b;
+      q.seg_len = __builtin_amdgcn_readfirstlane(pre[q.b + 1] - pre[q.b]);
+    }
+    q.pstart = 0;
+    q.pend = min(q.seg_len, g1 - q.sstart);
+    c = 0;
+    return true;
   };
 
   float m_run = -INFINITY, l_run = 0.f;
@@ -498,9 +531,10 @@ __global__ void __launch_bounds__(kThreads) attention_kernel(const AttnArgs a) {
 
   // ---- pipeline: the loads of the next stage are issued before the matrix
   // work of the current one and stored to LDS after it
-  StageRegs R;
-  q_load(p);
-  stage_load(R, p, c0);
+  if (!staged) {
+    q_load(p);
+    stage_load(R, p, c0);
+  }
   stage_store(R, p, c0);
   __syncthreads();
   while (true) {
@@ -531,23 +565,34 @@ __global__ void __launch_bounds__(256) attention_combine_kernel(const AttnArgs a
   __shared__ int pre[kAttnMaxBatch + 1], wpre[kAttnMaxBatch + 1], mode;
   const int s = blockIdx.y, b = s / a.Hkv, h = s - b * a.Hkv;
   const int tid = threadIdx.x, lane = tid & 63;
-  if (tid < 64) build_plan(a.ctx_len, a.batch, a.Bs, a.Hkv, a.max_ctx, a.nwg, pre, wpre, &mode, lane);
-  __syncthreads();
-  // this segment's pieces: workgroups w0 .. w0 + np - 1 (slots w + s)
-  int w0, np;
-  if (mode) {
-    np = (wpre[b + 1] - wpre[b]) / a.Hkv;
-    w0 = wpre[b] + h * np;
+  // this segment's pieces: workgroups w0 .. w0 + np - 1 (slots w + s); loads
+  // go out for np_load pieces (fixed chunks: every chunk, before the context
+  // length is known; the ones past the segment end are dropped after)
+  int w0, np, np_load;
+  if (a.fixed_chunk > 0) {
+    const int craw = a.ctx_len[b];
+    w0 = s * a.fixed_pieces;
+    np_load = a.fixed_pieces;
+    const int seg_len = min(min(max(craw, 0), a.max_ctx) + a.Bs, a.max_ctx);
+    np = (seg_len + a.fixed_chunk - 1) / a.fixed_chunk;
   } else {
-    const int total = a.Hkv * pre[a.batch];
-    const int Q = range_keys(total, a.nwg);
-    const int seg_len = pre[b + 1] - pre[b];
-    const int sstart = a.Hkv * pre[b] + h * seg_len;
-    w0 = sstart / Q;
-    np = (sstart + seg_len - 1) / Q - w0 + 1;
+    if (tid < 64) build_plan(a.ctx_len, a.batch, a.Bs, a.Hkv, a.max_ctx, a.nwg, pre, wpre, &mode, lane);
+    __syncthreads();
+    if (mode) {
+      np = (wpre[b + 1] - wpre[b]) / a.Hkv;
+      w0 = wpre[b] + h * np;
+    } else {
+      const int total = a.Hkv * pre[a.batch];
+      const int Q = range_keys(total, a.nwg);
+      const int seg_len = pre[b + 1] - pre[b];
+      const int sstart = a.Hkv * pre[b] + h * seg_len;
+      w0 = sstart / Q;
+      np = (sstart + seg_len - 1) / Q - w0 + 1;
+    }
+    np_load = np;
+    if (np <= 1) return;  // written directly by the attention kernel
   }
-  if (np <= 1) return;  // written directly by the attention kernel
-  const int SG = np <= 4 ? 1 : np <= 16 ? 4 : 16;
+  const int SG = np_load <= 4 ? 1 : np_load <= 16 ? 4 : 16;
   const int per = 256 / SG;  // items per chunk
   const int G = a.Hq / a.Hkv;
   const int QR = G * a.Bs;
@@ -561,7 +606,7 @@ __global__ void __launch_bounds__(256) attention_combine_kernel(const AttnArgs a
     const int r = it / (D / 4), d4 = (it - r * (D / 4)) * 4;
     float m = -INFINITY, l = 0.f;
     f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int p0 = 0; p0 < np; p0 += 4 * SG) {
+    for (int p0 = 0; p0 < np_load; p0 += 4 * SG) {
       float mv[4], lv[4];
       f32x4 ov[4];
 #pragma unroll
@@ -570,15 +615,17 @@ __global__ void __launch_bounds__(256) attention_combine_kernel(const AttnArgs a
         mv[k] = -INFINITY;
         lv[k] = 0.f;
         ov[k] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (pc < np) {
+        if (pc < np_load) {
           const size_t sl = slot0 + pc;
           mv[k] = a.part_ml[(sl * QR + r) * 2];
           lv[k] = a.part_ml[(sl * QR + r) * 2 + 1];
           ov[k] = *reinterpret_cast<const f32x4*>(a.part_o + (sl * QR + r) * D + d4);
         }
       }
+      if (np <= 1) return;  // fixed chunks: the segment was one chunk, written by the attention kernel
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
+        if (p0 + g + SG * k >= np) mv[k] = -INFINITY;  // a chunk past the segment: stale
         const float mn = fmaxf(m, mv[k]);
         if (mn == -INFINITY) continue;
         const float w1 = m == -INFINITY ? 0.f : fast_exp2(m - mn);

@@ -680,9 +680,12 @@ __global__ void __launch_bounds__(256) finish_swiglu_kernel(const FinishArgs f) 
               silu_f32(gv) * uv);
 }
 
-// Block Q/K/V: RoPE on Q and K at position ctx_len[b] + i; Q scaled and stored
-// as a hi/lo pair, K and V in storage type.  One thread per rotation pair
-// (row, head of the concatenated [Q | K | V] output, d < D/2).
+// Block Q/K/V: RoPE on Q and K at position T + i (T = ctx_len[b], clamped);
+// Q scaled and stored as a hi/lo pair; K and V staged in this layer's cache at
+// rows T + i (rows past the committed context: the attention reads every key
+// from the cache).  A sequence whose block would pass max_ctx stages nothing
+// and is flagged.  One thread per rotation pair (row, head of the
+// concatenated [Q | K | V] output, d < D/2).
 template <typename S>
 __global__ void __launch_bounds__(256) finish_qkv_kernel(const FinishArgs f) {
   const int D = f.head_dim, half = D >> 1;
@@ -693,14 +696,14 @@ __global__ void __launch_bounds__(256) finish_qkv_kernel(const FinishArgs f) {
   const int hd = rem / half, d = rem - hd * half;
   const int n = hd * D + d;
   const int Nq = f.n_q_heads * D, Nk = f.n_kv_heads * D;
-  const int b = m / f.block;
+  const int b = m / f.block, i = m - b * f.block;
   KPair kp;
   const bool fast = f.KS <= 8;
   if (fast) kpair_issue(f, m, n, n + half, kp);
   const float r = row_scale(f, m);
-  const int ctx = f.ctx_len[b];
   // a caller-set length outside [0, max_ctx] is clamped (the table covers every clamped position)
-  const int pos = min(max(ctx, 0), f.max_ctx) + (m - b * f.block);
+  const int T = min(max(f.ctx_len[b], 0), f.max_ctx);
+  const int pos = T + i;
   const float2 cs = f.rope[(size_t)pos * half + d];
   float lo, hi;
   if (fast) kpair_reduce(f, kp, lo, hi);
@@ -713,16 +716,18 @@ __global__ void __launch_bounds__(256) finish_qkv_kernel(const FinishArgs f) {
     rope_apply(lo, hi, cs);
     split_store(qh, ql, (size_t)m * Nq + n, lo * f.q_scale);
     split_store(qh, ql, (size_t)m * Nq + n + half, hi * f.q_scale);
-  } else if (n < Nq + Nk) {
-    S* ko = reinterpret_cast<S*>(f.kb_out) + (size_t)m * Nk + (n - Nq);
-    rope_apply(lo, hi, cs);
-    store_from_f32<S>(ko, lo);
-    store_from_f32<S>(ko + half, hi);
-  } else {
-    S* vo = reinterpret_cast<S*>(f.vb_out) + (size_t)m * Nk + (n - Nq - Nk);
-    store_from_f32<S>(vo, lo);
-    store_from_f32<S>(vo + half, hi);
+    return;
   }
+  if (T + f.block > f.max_ctx) {
+    if (rem == Nq / 2 && i == 0) atomicOr(f.err, kErrDraftOverflow);
+    return;
+  }
+  const bool is_k = n < Nq + Nk;
+  const int c = is_k ? n - Nq : n - Nq - Nk;  // column within the KV heads
+  if (is_k) rope_apply(lo, hi, cs);
+  S* dst = reinterpret_cast<S*>(f.kv_cache[is_k ? 0 : 1]) + ((size_t)b * f.max_ctx + pos) * Nk + c;
+  store_from_f32<S>(dst, lo);
+  store_from_f32<S>(dst + half, hi);
 }
 
 // Context K/V of every layer (segments K^0, V^0, K^1, V^1, ...): RoPE on K at
@@ -753,7 +758,7 @@ __global__ void __launch_bounds__(256) finish_kv_kernel(const FinishArgs f) {
   if (fast) kpair_reduce(f, kp, lo, hi);
   else ksum2(f, m, n, n + half, lo, hi);
   if (bad) {
-    if (rem == 0 && i == 0) atomicOr(f.err, 1u);
+    if (rem == 0 && i == 0) atomicOr(f.err, kErrFuseOverflow);
     return;
   }
   lo *= r;

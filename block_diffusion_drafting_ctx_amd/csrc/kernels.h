@@ -10,6 +10,12 @@ namespace dfl {
 
 enum StorageType { ST_F32 = 0, ST_BF16 = 1 };
 
+// Device error-word bits (the public header's DFLASH_ERR_*).
+constexpr uint32_t kErrFuseOverflow = 1u << 0;    // ctx_len + t_new > max_ctx in the fusion
+constexpr uint32_t kErrTokenRange = 1u << 1;      // block id outside [0, vocab)
+constexpr uint32_t kErrVerifyOverflow = 1u << 2;  // ctx_len + n_d + 1 > max_ctx in verify
+constexpr uint32_t kErrDraftOverflow = 1u << 3;   // ctx_len + block > max_ctx in the draft
+
 // ------------------------------------------------------------------ GEMM
 // Y[M, N] = A[M, K] . W[N, K]^T.  The N axis concatenates weight segments and
 // is cut into 16-row tiles.  The main kernel writes fp32 partial tiles
@@ -108,9 +114,7 @@ struct FinishArgs {
   int max_ctx;
   int head_dim, n_q_heads, n_kv_heads;
   float q_scale;
-  void* kb_out;  // FIN_QKV [M, Hkv*D] storage type
-  void* vb_out;
-  void* kv_cache[kMaxSeg];  // FIN_KV: one per segment
+  void* kv_cache[kMaxSeg];  // FIN_KV: one per segment; FIN_QKV: this layer's K, V caches
   uint32_t* err;
 };
 hipError_t launch_finish(int storage, FinishKind kind, const FinishArgs& f, hipStream_t stream);
@@ -122,13 +126,13 @@ constexpr int kAttnMaxBatch = 1024;
 struct AttnArgs {
   const void* q_hi;  // bf16 hi/lo pair [B*Bs, Hq*D], already scaled by log2(e)/sqrt(D)
   const void* q_lo;
-  const void* kb;  // storage [B*Bs, Hkv*D] block keys (RoPE applied)
-  const void* vb;
-  const void* kc;  // storage [B, max_ctx, Hkv, D] this layer's cache
-  const void* vc;
+  const void* kc;  // storage [B, max_ctx, Hkv, D] this layer's cache; the block's
+  const void* vc;  //   K/V (RoPE applied) at rows ctx_len[b] + i
   const int32_t* ctx_len;
   int Bs, Hq, Hkv, D, max_ctx;
-  int nwg;         // workgroups the batch's key axis is cut over (grid of the split kernel)
+  int nwg;           // workgroups the batch's key axis is cut over (grid of the split kernel)
+  int fixed_chunk;   // > 0: fixed chunks of this many keys, fixed_pieces per segment
+  int fixed_pieces;  //   (nwg = B * Hkv * fixed_pieces); 0: planned from the lengths
   float* part_o;   // [nwg + B*Hkv slots, QR, D]   unnormalised piece outputs
   float* part_ml;  // [nwg + B*Hkv slots, QR, 2]   piece running max and sum
   void* out_hi;    // bf16 hi/lo pair [B*Bs, Hq*D]

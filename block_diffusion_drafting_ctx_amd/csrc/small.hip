@@ -73,7 +73,7 @@ __global__ void __launch_bounds__(64) verify_commit_kernel(const VerifyArgs a) {
     a.bonus[b] = s_g[n];
     const int t0 = a.ctx_len[b];
     if (t0 < 0 || t0 + R > a.max_ctx) {
-      atomicOr(a.err, 4u);
+      atomicOr(a.err, kErrVerifyOverflow);
     } else {
       a.ctx_len[b] = t0 + n + 1;
     }
@@ -105,7 +105,7 @@ __global__ void __launch_bounds__(256) embed_kernel(const S* embed, const S* gai
   const int m = blockIdx.x, tid = threadIdx.x;
   const int id = ids[m];
   const bool ok = id >= 0 && id < V;
-  if (!ok && tid == 0) atomicOr(err, 2u);
+  if (!ok && tid == 0) atomicOr(err, kErrTokenRange);
   const S* e = embed + (size_t)(ok ? id : 0) * H;
   float s = 0.f;
   for (int k = 8 * tid; k < H; k += 8 * 256) {

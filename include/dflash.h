@@ -72,7 +72,8 @@ enum { DFLASH_DTYPE_F32 = 0, DFLASH_DTYPE_BF16 = 1 };
 enum {
   DFLASH_ERR_FUSE_OVERFLOW = 1u << 0,   /* ctx_len[b] + t_new > max_ctx in fuse_ctx */
   DFLASH_ERR_TOKEN_RANGE = 1u << 1,     /* block id outside [0, vocab) in draft_block */
-  DFLASH_ERR_VERIFY_OVERFLOW = 1u << 2  /* ctx_len[b] + n_d + 1 > max_ctx in verify */
+  DFLASH_ERR_VERIFY_OVERFLOW = 1u << 2, /* ctx_len[b] + n_d + 1 > max_ctx in verify */
+  DFLASH_ERR_DRAFT_OVERFLOW = 1u << 3   /* ctx_len[b] + block > max_ctx in draft_block */
 };
 
 /* Stages, for dflash_stage_time. */
@@ -207,6 +208,11 @@ dflash_status dflash_verify(dflash_ctx* ctx, int32_t batch, const float* target_
  *     with the tie / NaN rule of dflash_verify.
  *  logits_dbg: nullable fp32 [batch, Bs, V]; hidden_dbg: nullable fp32
  *  [batch, Bs, H] final residual stream before the final norm (testing).
+ *  Every layer's block K/V rows are staged in that layer's cache at rows
+ *  ctx_len[b] + i (past the committed context: rows no committed state
+ *  lives in, which the next dflash_fuse_ctx overwrites); a sequence with
+ *  ctx_len[b] + Bs > max_ctx stages nothing, sets DFLASH_ERR_DRAFT_OVERFLOW
+ *  and gets unspecified drafts.
  *  A block id outside [0, V) sets DFLASH_ERR_TOKEN_RANGE and embeds zeros.
  *  batch == 0 is a no-op. */
 dflash_status dflash_draft_block(dflash_ctx* ctx, int32_t batch, const int32_t* block_ids,

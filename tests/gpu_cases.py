@@ -117,6 +117,16 @@ def run_step(wl: gen.Workload, seed: int, device="cuda", seqs: Optional[Sequence
     feat = torch.empty(B, t_new, H, dtype=torch.float32, device=device)
     dr.fuse_ctx([h.to(device) for h in hid], commit=False, feat_dbg=feat)
     ctx_after_fuse = dr.ctx_len.clone()
+    # the fused rows of the sampled sequences as the fusion left them (the
+    # draft later stages its block's keys in the rows past the committed ones)
+    fused_rows = {}
+    if check_oracle:
+        for b in seqs:
+            t0 = int(ctx_after_fuse[b])
+            lo = 0 if prefill else t0
+            for l in range(wl.n_layers):
+                fused_rows[(b, l, "K")] = dr.kv_k[l][b, lo:t0 + t_new].clone()
+                fused_rows[(b, l, "V")] = dr.kv_v[l][b, lo:t0 + t_new].clone()
     d_dev = torch.from_numpy(drafts).to(device)
     n_acc = torch.full((B,), -7, dtype=torch.int32, device=device)
     bonus = torch.full((B,), -7, dtype=torch.int32, device=device)
@@ -169,8 +179,8 @@ def run_step(wl: gen.Workload, seed: int, device="cuda", seqs: Optional[Sequence
         t0 = int(st.ctx_len[j])
         lo = 0 if prefill else t0
         for l in range(wl.n_layers):
-            for name, cache, ref in (("K", dr.kv_k[l], st.k[l]), ("V", dr.kv_v[l], st.v[l])):
-                got = np64(cache[b, lo:t0 + t_new])
+            for name, ref in (("K", st.k[l]), ("V", st.v[l])):
+                got = np64(fused_rows[(b, l, name)])
                 e = rel_l2(got, ref[j, lo:t0 + t_new])
                 res.note(f"cache_{name}_rel_l2", e)
                 assert e <= REL_L2, f"seq {b} layer {l} cache {name} rel L2 {e}"
@@ -254,9 +264,12 @@ def run_error_paths(wl: gen.Workload, seed: int, device="cuda") -> None:
     err = dr.check()
     want = _abi.ERR_FUSE_OVERFLOW | _abi.ERR_VERIFY_OVERFLOW | _abi.ERR_TOKEN_RANGE
     assert err == want, f"error word {err:#x}, expected {want:#x}"
-    # the overflowing sequence: cache untouched, length not advanced
+    # the overflowing sequence: committed rows untouched (rows past ctx_len only
+    # stage the drafted block's keys), length not advanced
+    t1 = int(ctx_lens[1])
     for l in range(wl.n_layers):
-        assert torch.equal(dr.kv_k[l][1], k1_before[l]), f"layer {l}: cache of the overflowing sequence written"
+        assert torch.equal(dr.kv_k[l][1][:t1], k1_before[l][:t1]), \
+            f"layer {l}: committed cache rows of the overflowing sequence written"
     assert int(ctx_after[1]) == int(ctx_lens[1])
     # the healthy sequences: verify bit-exact, sequence 0 matches the oracle
     from oracle import greedy_verify
