@@ -113,14 +113,16 @@ bool plan_gemm(int storage, int src, int out, bool lo, int M, int N, int K, Gemm
     return true;
   }
   // gemm_mt: BM = 64 * MF rows by BN = 32 * NF columns per workgroup; split K
-  // until the grid fills the chip (one 8-wave workgroup per compute unit)
+  // as far as the grid stays within one dispatch round (one 8-wave workgroup
+  // per compute unit): a second, partly filled round would cost a whole
+  // workgroup's time, and every k-slice adds a partial-output round trip
   const int MF = M <= 64 ? 1 : (M <= 128 ? 2 : 4);
   const int BN = 32 * gemm_mt_nf(MF);
   const int nbm = (M + 64 * MF - 1) / (64 * MF);
   const int nbn = (N + BN - 1) / BN;
   int KS = 1;
   if (out == OUT_PARTIAL)
-    while (nbn * nbm * KS < kMtTargetWgs && (K / 32) % (2 * KS) == 0 && K / (2 * KS) >= 256) KS *= 2;
+    while (nbn * nbm * 2 * KS <= kMtTargetWgs && (K / 32) % (2 * KS) == 0 && K / (2 * KS) >= 256) KS *= 2;
   const int units = nbn * KS;
   l->kind = GEMM_MT;
   l->MR = MF;
@@ -525,9 +527,10 @@ dflash_status dflash_draft_block(dflash_ctx* c, int32_t batch, const int32_t* bl
     f.rinv = rinv;
   };
   // The MLP inputs (normalised residual into gate/up, SiLU product into down)
-  // enter their products as a hi/lo pair while the products stream weights
-  // (the pair costs no HBM bytes there); from kMlpHiOnlyRows rows on, where
-  // the products are matrix-core bound, they enter as plain bf16.
+  // and the attention probabilities enter their products as a hi/lo pair
+  // while the products stream weights or wait on memory (the pair costs no
+  // HBM bytes there); from kMlpHiOnlyRows rows on, where the products are
+  // matrix-core bound, they enter as plain bf16.
   const bool mlp_lo = M < kMlpHiOnlyRows;
   for (int l = 0; l < cf.n_layers; ++l) {
     {  // RMSNorm -> Q/K/V, RoPE
@@ -570,6 +573,7 @@ dflash_status dflash_draft_block(dflash_ctx* c, int32_t batch, const int32_t* bl
       a.D = D;
       a.max_ctx = cf.max_ctx;
       attn_grid(cf, batch, &a);
+      a.p_lo = mlp_lo;
       a.part_o = c->at<float>(L.part_o);
       a.part_ml = c->at<float>(L.part_ml);
       a.out_hi = c->at<void>(L.o_hi);

@@ -43,9 +43,11 @@
 // operand.  V is stored transposed in LDS as key pairs (one dword = two keys
 // of one dimension) with an XOR swizzle of the key-pair column by the
 // dimension, which keeps the transposing stores at two-way bank conflicts and
-// the operand reads conflict-free.  Queries and probabilities enter the bf16
-// products as hi/lo pairs (two MFMAs each), keys and values as stored.
+// the operand reads conflict-free.  Queries enter the bf16 products as hi/lo
+// pairs (two MFMAs each), probabilities as a pair or as plain bf16 (p_lo), keys
+// and values as stored.
 #include <algorithm>
+#include <type_traits>
 
 #include "common.h"
 #include "kernels.h"
@@ -164,8 +166,9 @@ __device__ __forceinline__ int upper_index(int B, int x, F key) {
 }
 
 // QTP (waves per key group, >= the query tiles) is a template parameter so
-// that a wave's key units unroll completely.
-template <typename S, int D, int QTP>
+// that a wave's key units unroll completely; PLO: probabilities enter the PV
+// product as a hi/lo pair (else plain bf16).
+template <typename S, int D, int QTP, bool PLO>
 __global__ void __launch_bounds__(kThreads) attention_kernel(const AttnArgs a) {
   constexpr int KG = attn_kg(QTP);  // key groups
   constexpr int UPG = kUnits / KG;  // 32-key units per key group and stage
@@ -436,8 +439,10 @@ __global__ void __launch_bounds__(kThreads) attention_kernel(const AttnArgs a) {
       for (int e = 0; e < 4; ++e) {
         ph[e] = (__bf16)sc[uu][0][e];
         ph[4 + e] = (__bf16)sc[uu][1][e];
-        pl[e] = (__bf16)(sc[uu][0][e] - (float)ph[e]);
-        pl[4 + e] = (__bf16)(sc[uu][1][e] - (float)ph[4 + e]);
+        if constexpr (PLO) {
+          pl[e] = (__bf16)(sc[uu][0][e] - (float)ph[e]);
+          pl[4 + e] = (__bf16)(sc[uu][1][e] - (float)ph[4 + e]);
+        }
       }
       const int kp0 = (kUnit / 2) * u + 2 * (ln >> 4);  // keys 32*u + 4*(lane>>4) + [0, 4)
 #pragma unroll
@@ -448,7 +453,7 @@ __global__ void __launch_bounds__(kThreads) attention_kernel(const AttnArgs a) {
         const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + vt_col(d, kp0 + 8));
         const bf16x8 vf = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
         o[ds] = mfma16x16x32(vf, ph, o[ds]);
-        o[ds] = mfma16x16x32(vf, pl, o[ds]);
+        if constexpr (PLO) o[ds] = mfma16x16x32(vf, pl, o[ds]);
       }
     }
   };
@@ -676,8 +681,13 @@ static hipError_t launch_attention_d(const AttnArgs& a, hipStream_t stream) {
   if (QR > 16 * kWaves || a.nwg <= 0 || a.batch > kAttnMaxBatch) return hipErrorInvalidValue;
   const size_t lds = attention_lds_bytes<D>();
   const int qtp = attn_qtp((QR + 15) / 16);
-  auto k = qtp == 1 ? attention_kernel<S, D, 1>
-                    : qtp == 2 ? attention_kernel<S, D, 2> : qtp == 4 ? attention_kernel<S, D, 4> : attention_kernel<S, D, 8>;
+  auto pick = [&](auto plo) {
+    constexpr bool P = decltype(plo)::value;
+    return qtp == 1 ? attention_kernel<S, D, 1, P>
+                    : qtp == 2 ? attention_kernel<S, D, 2, P> : qtp == 4 ? attention_kernel<S, D, 4, P>
+                                                                      : attention_kernel<S, D, 8, P>;
+  };
+  auto k = a.p_lo ? pick(std::true_type{}) : pick(std::false_type{});
   if (lds > 64 * 1024)
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize,
                               (int)lds);

@@ -133,6 +133,7 @@ struct AttnArgs {
   int nwg;           // workgroups the batch's key axis is cut over (grid of the split kernel)
   int fixed_chunk;   // > 0: fixed chunks of this many keys, fixed_pieces per segment
   int fixed_pieces;  //   (nwg = B * Hkv * fixed_pieces); 0: planned from the lengths
+  int p_lo;          // probabilities as a hi/lo pair in the PV product (else plain bf16)
   float* part_o;   // [nwg + B*Hkv slots, QR, D]   unnormalised piece outputs
   float* part_ml;  // [nwg + B*Hkv slots, QR, 2]   piece running max and sum
   void* out_hi;    // bf16 hi/lo pair [B*Bs, Hq*D]
