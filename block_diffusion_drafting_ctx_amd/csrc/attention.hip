@@ -55,22 +55,22 @@
 namespace dfl {
 
 constexpr int kUnit = 32;               // keys per softmax update / PV product
-constexpr int kUnits = 6;               // units per LDS stage
-constexpr int kStage = kUnit * kUnits;  // keys per LDS stage
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kMinPieceKeys = 64;       // a workgroup's range is never cut shorter
 
-template <int D>
+// LDS stage of NU 32-key units.  NU = 6 (192 keys, fetched one stage ahead)
+// serves chunks that fit one stage; NU = 4 (128 keys, fetched two stages
+// ahead through a second register set) serves longer pieces.
+template <int D, int NU>
 struct AttnLds {
   static constexpr int KS = D + 8;  // K row stride (elements)
-  // V^T row length in dwords: kStage / 2 = 96 key pairs, padded to 128 so the
+  // V^T row length in dwords: 16 NU key pairs, padded to a power of two so the
   // column swizzle (an XOR of bits 1..4) never leaves the row
-  static constexpr int VW = 128;
-  bf16_t k[kStage * KS];
+  static constexpr int VW = 16 * NU <= 64 ? 64 : 128;
+  bf16_t k[kUnit * NU * KS];
   uint32_t vt[D * VW];
 };
-static_assert(kStage / 2 <= 96, "V^T rows hold at most 96 key pairs");
 
 // Column of key pair kp in V^T row d.  Even, so a pair of key pairs stays
 // adjacent and in order.
@@ -83,9 +83,11 @@ __device__ __forceinline__ void split_out(bf16_t* hi, bf16_t* lo, size_t idx, fl
 }
 
 // Waves per key group (a power of two covering QT query tiles), and the key
-// groups: the largest divisor of the six units of a stage that fits the waves.
+// groups: the largest divisor of the NU units of a stage that fits the waves.
 __host__ __device__ inline int attn_qtp(int QT) { return QT <= 1 ? 1 : QT <= 2 ? 2 : QT <= 4 ? 4 : 8; }
-__host__ __device__ constexpr int attn_kg(int qtp) { return qtp >= 8 ? 1 : qtp >= 4 ? 2 : qtp >= 2 ? 3 : 6; }
+__host__ __device__ constexpr int attn_kg(int qtp, int nu) {
+  return nu == 6 ? (qtp >= 8 ? 1 : qtp >= 4 ? 2 : qtp >= 2 ? 3 : 6) : (qtp >= 8 ? 1 : qtp >= 4 ? 2 : 4);
+}
 
 // Wave-wide inclusive prefix sum.
 __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
@@ -168,14 +170,18 @@ __device__ __forceinline__ int upper_index(int B, int x, F key) {
 // QTP (waves per key group, >= the query tiles) is a template parameter so
 // that a wave's key units unroll completely; PLO: probabilities enter the PV
 // product as a hi/lo pair (else plain bf16).
-template <typename S, int D, int QTP, bool PLO>
+template <typename S, int D, int QTP, bool PLO, int NU>
 __global__ void __launch_bounds__(kThreads) attention_kernel(const AttnArgs a) {
-  constexpr int KG = attn_kg(QTP);  // key groups
-  constexpr int UPG = kUnits / KG;  // 32-key units per key group and stage
+  constexpr int kUnits = NU;                // units per LDS stage
+  constexpr int kStage = kUnit * kUnits;    // keys per LDS stage
+  constexpr int PF = NU == 4 ? 2 : 1;       // stages in flight ahead of the matrix work
+  constexpr int KG = attn_kg(QTP, NU);      // key groups
+  constexpr int UPG = kUnits / KG;          // 32-key units per key group and stage
   static_assert(KG * QTP <= kWaves && UPG * KG == kUnits, "wave layout");
+  using Lds = AttnLds<D, NU>;
   extern __shared__ __align__(16) unsigned char lds_raw[];
-  AttnLds<D>& L = *reinterpret_cast<AttnLds<D>*>(lds_raw);
-  int* pre = reinterpret_cast<int*>(lds_raw + sizeof(AttnLds<D>));  // [2][kAttnMaxBatch + 1]
+  Lds& L = *reinterpret_cast<Lds*>(lds_raw);
+  int* pre = reinterpret_cast<int*>(lds_raw + sizeof(Lds));  // [2][kAttnMaxBatch + 1] + 1
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int G = a.Hq / a.Hkv;
   const int QR = G * a.Bs;
@@ -214,12 +220,6 @@ __global__ void __launch_bounds__(kThreads) attention_kernel(const AttnArgs a) {
   const S* kc = reinterpret_cast<const S*>(a.kc);
   const S* vc = reinterpret_cast<const S*>(a.vc);
   const size_t row = (size_t)Hkv * D;  // elements between consecutive keys
-  // key j of segment (b, h): cache row j (kept inside the cache; a segment
-  // longer than the cache only arises with a flagged overflow)
-  auto key_ptr = [&](const S* cache, const Piece& q, int j) {
-    return cache + ((size_t)q.b * a.max_ctx + min(j, a.max_ctx - 1)) * row + q.h * D;
-  };
-
   // ---- staging through registers.  K: (key, 8-dim piece) items, 16 lanes per
   // key row.  V: (key pair, piece) items in blocks of 32 key pairs; the two
   // half-blocks of 16 take key pairs 16 apart (the bank pattern the V^T
@@ -238,16 +238,21 @@ __global__ void __launch_bounds__(kThreads) attention_kernel(const AttnArgs a) {
     const int h = (idx / PIECES) & 1, rest = idx / (2 * PIECES);
     kp = (rest & 15) + 16 * h + 32 * (rest >> 4);
   };
-  // Loads are unconditional within the stage's items (keys past the piece
-  // re-read its last key and are zeroed at the store): branch-free address
-  // selects keep the loads of a stage in flight together.
+  // Loads are unconditional within the stage's items: a key past the piece
+  // (or past the cache) re-reads the piece's last key and is zeroed at the
+  // store.  The stage's base address is wave-uniform and a lane's offset is
+  // min(key, lim) rows with a uniform lim, so the loads of a stage go out
+  // together without branches and with little address arithmetic.
   auto stage_load = [&](StageRegs& R, const Piece& q, int c) {
-    const int jl = q.pend - 1;
+    const int lim = min(a.max_ctx, q.pend) - 1 - c;  // last key of the stage that exists
+    const size_t base = ((size_t)q.b * a.max_ctx + c) * row + q.h * D;
+    const S* kq = kc + base;
+    const S* vq = vc + base;
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
       const int idx = tid + i * kThreads;
       const int key = idx / PIECES, p8 = (idx % PIECES) * 8;
-      load_raw8<S>(R.k[i], key_ptr(kc, q, min(c + key, jl)) + p8);
+      load_raw8<S>(R.k[i], kq + min(key, lim) * (int)row + p8);
     }
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
@@ -256,18 +261,24 @@ __global__ void __launch_bounds__(kThreads) attention_kernel(const AttnArgs a) {
       int kp, pc;
       v_item(idx, kp, pc);
 #pragma unroll
-      for (int t = 0; t < 2; ++t) load_raw8<S>(R.v[i][t], key_ptr(vc, q, min(c + 2 * kp + t, jl)) + 8 * pc);
+      for (int t = 0; t < 2; ++t) load_raw8<S>(R.v[i][t], vq + min(2 * kp + t, lim) * (int)row + 8 * pc);
     }
   };
+  // V^T dwords are key pairs of one dimension: for bf16 storage a byte
+  // permute of the two keys' dwords, for fp32 storage a conversion.  Keys past
+  // the piece are zeroed (only in a piece's last stage).
   auto stage_store = [&](const StageRegs& R, const Piece& q, int c) {
     int t0 = tid;  // opaque: the store addresses are recomputed per stage, not kept live
     asm volatile("" : "+v"(t0));
+    const int nvalid = q.pend - c;  // keys of the stage inside the piece
+    const bool full = nvalid >= kStage;
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
       const int idx = tid + i * kThreads;
       const int key = idx / PIECES, p8 = (idx % PIECES) * 8;
-      const bf16x8 v = c + key < q.pend ? raw_to_bf16x8<S>(R.k[i]) : bf16x8{};
-      *reinterpret_cast<bf16x8*>(&L.k[key * AttnLds<D>::KS + p8]) = v;
+      bf16x8 v = raw_to_bf16x8<S>(R.k[i]);
+      if (!full && key >= nvalid) v = bf16x8{};
+      *reinterpret_cast<bf16x8*>(&L.k[key * Lds::KS + p8]) = v;
     }
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
@@ -275,16 +286,28 @@ __global__ void __launch_bounds__(kThreads) attention_kernel(const AttnArgs a) {
       if (idx >= VITEMS) continue;
       int kp, pc;
       v_item(idx, kp, pc);
-      float v0[8], v1[8];
-      raw_to_f32x8<S>(R.v[i][0], v0);
-      raw_to_f32x8<S>(R.v[i][1], v1);
-      const bool ok0 = c + 2 * kp < q.pend, ok1 = c + 2 * kp + 1 < q.pend;
+      const bool ok0 = full || 2 * kp < nvalid, ok1 = full || 2 * kp + 1 < nvalid;
+      if constexpr (sizeof(S) == 2) {
+        u32x4 k0 = R.v[i][0].lo, k1 = R.v[i][1].lo;
+        if (!ok0) k0 = u32x4{0u, 0u, 0u, 0u};
+        if (!ok1) k1 = u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int d = 8 * pc + e;
-        const uint32_t lo = ok0 ? (uint32_t)f32_to_bf16_bits(v0[e]) : 0u;
-        const uint32_t hi = ok1 ? (uint32_t)f32_to_bf16_bits(v1[e]) : 0u;
-        L.vt[d * AttnLds<D>::VW + vt_col(d, kp)] = lo | (hi << 16);
+        for (int j = 0; j < 4; ++j) {
+          const int d = 8 * pc + 2 * j;
+          L.vt[d * Lds::VW + vt_col(d, kp)] = __builtin_amdgcn_perm(k1[j], k0[j], 0x05040100u);
+          L.vt[(d + 1) * Lds::VW + vt_col(d + 1, kp)] = __builtin_amdgcn_perm(k1[j], k0[j], 0x07060302u);
+        }
+      } else {
+        float v0[8], v1[8];
+        raw_to_f32x8<S>(R.v[i][0], v0);
+        raw_to_f32x8<S>(R.v[i][1], v1);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int d = 8 * pc + e;
+          const uint32_t lo = ok0 ? (uint32_t)f32_to_bf16_bits(v0[e]) : 0u;
+          const uint32_t hi = ok1 ? (uint32_t)f32_to_bf16_bits(v1[e]) : 0u;
+          L.vt[d * Lds::VW + vt_col(d, kp)] = lo | (hi << 16);
+        }
       }
     }
   };
@@ -394,7 +417,7 @@ __global__ void __launch_bounds__(kThreads) attention_kernel(const AttnArgs a) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           const bf16x8 kf = *reinterpret_cast<const bf16x8*>(
-              &L.k[(kUnit * u + 16 * h + (ln & 15)) * AttnLds<D>::KS + 32 * s + 8 * (ln >> 4)]);
+              &L.k[(kUnit * u + 16 * h + (ln & 15)) * Lds::KS + 32 * s + 8 * (ln >> 4)]);
           sc[uu][h] = mfma16x16x32(kf, qf[s], sc[uu][h]);
           sc[uu][h] = mfma16x16x32(kf, qr[s], sc[uu][h]);
         }
@@ -448,7 +471,7 @@ __global__ void __launch_bounds__(kThreads) attention_kernel(const AttnArgs a) {
 #pragma unroll
       for (int ds = 0; ds < D / 16; ++ds) {
         const int d = 16 * ds + (ln & 15);
-        const uint32_t* vrow = &L.vt[d * AttnLds<D>::VW];
+        const uint32_t* vrow = &L.vt[d * Lds::VW];
         const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow + vt_col(d, kp0));
         const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + vt_col(d, kp0 + 8));
         const bf16x8 vf = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
@@ -534,29 +557,57 @@ __global__ void __launch_bounds__(kThreads) attention_kernel(const AttnArgs a) {
     for (int ds = 0; ds < D / 16; ++ds) o[ds] = f32x4{0.f, 0.f, 0.f, 0.f};
   };
 
-  // ---- pipeline: the loads of the next stage are issued before the matrix
-  // work of the current one and stored to LDS after it
+  // ---- pipeline: the loads of the stage PF ahead are issued before the
+  // matrix work of the current one (into the register set whose stage is
+  // already in LDS), the next stage is stored to LDS after it
+  struct Stage {
+    Piece p;
+    int c;
+  };
+  Stage s0{p, c0}, s1 = s0, s2;
+  bool m1 = advance(s1.p, s1.c), m2 = false;
+  if (PF == 2 && m1) {
+    s2 = s1;
+    m2 = advance(s2.p, s2.c);
+  }
+  StageRegs rb;
   if (!staged) {
     q_load(p);
-    stage_load(R, p, c0);
+    stage_load(R, s0.p, s0.c);
   }
-  stage_store(R, p, c0);
+  if (PF == 2 && m1) stage_load(rb, s1.p, s1.c);
+  stage_store(R, s0.p, s0.c);
   __syncthreads();
-  while (true) {
-    Piece pn = p;
-    int cn = c0;
-    const bool more = advance(pn, cn);
-    if (more) stage_load(R, pn, cn);
-    compute(c0, p.pend);
-    const bool ends = !more || pn.sstart != p.sstart;
-    if (ends) close_piece(p);
-    if (!more) break;
+  // one stage: `cur` holds the stage now in LDS (free), `nxt` the next one
+  auto step = [&](StageRegs& cur, StageRegs& nxt) -> bool {
+    if (PF == 2 ? m2 : m1) {
+      if (PF == 2) stage_load(cur, s2.p, s2.c);
+      else stage_load(cur, s1.p, s1.c);
+    }
+    compute(s0.c, s0.p.pend);
+    const bool ends = !m1 || s1.p.sstart != s0.p.sstart;
+    if (ends) close_piece(s0.p);
+    if (!m1) return false;
     __syncthreads();
-    stage_store(R, pn, cn);
+    stage_store(PF == 2 ? nxt : cur, s1.p, s1.c);
     __syncthreads();
-    if (ends) q_load(pn);
-    p = pn;
-    c0 = cn;
+    if (ends) q_load(s1.p);
+    s0 = s1;
+    if (PF == 2) {
+      s1 = s2;
+      m1 = m2;
+      if (m2) m2 = advance(s2.p, s2.c);
+    } else {
+      m1 = advance(s1.p, s1.c);
+    }
+    return true;
+  };
+  if constexpr (PF == 1) {
+    while (step(R, R)) {
+    }
+  } else {
+    while (step(R, rb) && step(rb, R)) {
+    }
   }
 }
 
@@ -670,29 +721,36 @@ __global__ void __launch_bounds__(256) attention_combine_kernel(const AttnArgs a
   }
 }
 
-template <int D>
+template <int D, int NU>
 static size_t attention_lds_bytes() {
-  return sizeof(AttnLds<D>) + (size_t)(2 * (kAttnMaxBatch + 1) + 1) * sizeof(int);
+  return sizeof(AttnLds<D, NU>) + (size_t)(2 * (kAttnMaxBatch + 1) + 1) * sizeof(int);
 }
 
-template <typename S, int D>
-static hipError_t launch_attention_d(const AttnArgs& a, hipStream_t stream) {
-  const int QR = (a.Hq / a.Hkv) * a.Bs;
-  if (QR > 16 * kWaves || a.nwg <= 0 || a.batch > kAttnMaxBatch) return hipErrorInvalidValue;
-  const size_t lds = attention_lds_bytes<D>();
-  const int qtp = attn_qtp((QR + 15) / 16);
+template <typename S, int D, int NU>
+static hipError_t launch_attention_nu(const AttnArgs& a, int qtp, hipStream_t stream) {
+  const size_t lds = attention_lds_bytes<D, NU>();
   auto pick = [&](auto plo) {
     constexpr bool P = decltype(plo)::value;
-    return qtp == 1 ? attention_kernel<S, D, 1, P>
-                    : qtp == 2 ? attention_kernel<S, D, 2, P> : qtp == 4 ? attention_kernel<S, D, 4, P>
-                                                                      : attention_kernel<S, D, 8, P>;
+    return qtp == 1 ? attention_kernel<S, D, 1, P, NU>
+                    : qtp == 2 ? attention_kernel<S, D, 2, P, NU>
+                               : qtp == 4 ? attention_kernel<S, D, 4, P, NU> : attention_kernel<S, D, 8, P, NU>;
   };
   auto k = a.p_lo ? pick(std::true_type{}) : pick(std::false_type{});
   if (lds > 64 * 1024)
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize,
                               (int)lds);
   hipLaunchKernelGGL(k, dim3(a.nwg), dim3(kThreads), lds, stream, a);
-  hipError_t e = hipGetLastError();
+  return hipGetLastError();
+}
+
+template <typename S, int D>
+static hipError_t launch_attention_d(const AttnArgs& a, hipStream_t stream) {
+  const int QR = (a.Hq / a.Hkv) * a.Bs;
+  if (QR > 16 * kWaves || a.nwg <= 0 || a.batch > kAttnMaxBatch) return hipErrorInvalidValue;
+  const int qtp = attn_qtp((QR + 15) / 16);
+  // a fixed chunk that fits one 192-key stage takes the one-stage form
+  const bool one_stage = a.fixed_chunk > 0 && a.fixed_chunk <= 6 * kUnit;
+  hipError_t e = one_stage ? launch_attention_nu<S, D, 6>(a, qtp, stream) : launch_attention_nu<S, D, 4>(a, qtp, stream);
   if (e != hipSuccess) return e;
   // merge chunks per segment: enough for the finest grouping (16 items per
   // chunk) at small batches, about 2048 workgroups in all at large ones
