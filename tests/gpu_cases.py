@@ -217,12 +217,13 @@ def _to(w: dict, device) -> dict:
     return out
 
 
-def run_error_paths(wl: gen.Workload, seed: int, device="cuda") -> None:
+def run_error_paths(wl: gen.Workload, seed: int, device="cuda", draft_overflow: bool = False) -> None:
     """Device-detected faults, forced from the host: a context that would pass
-    max_ctx (fuse and verify skip that sequence's writes and commit) and a
-    block token outside the vocabulary (embedded as zeros).  The other
-    sequences must still match the oracle bit for bit / within the bars, and
-    the sticky error word must name exactly the faults."""
+    max_ctx (fuse and verify skip that sequence's writes and commit; with
+    draft_overflow the drafted block would pass it too, and the draft stages
+    nothing for it) and a block token outside the vocabulary (embedded as
+    zeros).  The other sequences must still match the oracle bit for bit /
+    within the bars, and the sticky error word must name exactly the faults."""
     from block_diffusion_drafting_ctx_amd import Drafter, _abi
 
     B = wl.batch
@@ -232,7 +233,8 @@ def run_error_paths(wl: gen.Workload, seed: int, device="cuda") -> None:
     w = gen.draft_weights(wl, seed, "cpu")
     w_dev = _to(w, device)
     ctx_lens = gen.context_lengths(wl, seed + 1, B)
-    ctx_lens[1] = wl.max_ctx - t_new + 1  # fuse (t_new rows) and verify would pass max_ctx
+    # fuse (t_new rows) and verify would pass max_ctx; with draft_overflow the block (Bs rows) too
+    ctx_lens[1] = wl.max_ctx - (wl.block if draft_overflow else t_new) + 1
     ks, vs = gen.context_kv(wl, np.minimum(ctx_lens, wl.max_ctx), seed + 1, "cpu")
     hid = gen.target_hidden(wl, B, t_new, seed + 2, "cpu")
     drafts = gen.draft_tokens(wl, B, n_d, seed + 3)
@@ -263,6 +265,8 @@ def run_error_paths(wl: gen.Workload, seed: int, device="cuda") -> None:
     torch.cuda.synchronize()
     err = dr.check()
     want = _abi.ERR_FUSE_OVERFLOW | _abi.ERR_VERIFY_OVERFLOW | _abi.ERR_TOKEN_RANGE
+    if draft_overflow:
+        want |= _abi.ERR_DRAFT_OVERFLOW
     assert err == want, f"error word {err:#x}, expected {want:#x}"
     # the overflowing sequence: committed rows untouched (rows past ctx_len only
     # stage the drafted block's keys), length not advanced

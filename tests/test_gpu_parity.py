@@ -66,6 +66,26 @@ def test_device_faults_set_error_bits_and_spare_other_sequences():
     run_error_paths(wl, seed=21)
 
 
+def test_block_past_the_cache_is_flagged_and_spares_other_sequences():
+    # ctx_len = max_ctx - Bs + 1: the fusion, the verify commit and the drafted block all pass max_ctx
+    wl = gen.Workload("tiny-faults-draft", 256, 4, 2, 64, 2, 512, 1024, 8, 3, 3, 10, 60, "bf16", accept_hi=8)
+    run_error_paths(wl, seed=22, draft_overflow=True)
+
+
+def test_many_equal_sequences_one_attention_piece_each():
+    # 128 sequences x 2 KV heads: attention planned on the device, one balanced
+    # piece per segment
+    wl = gen.Workload("tiny-b128-equal", 256, 4, 2, 64, 2, 512, 1024, 8, 3, 128, 100, 100, "bf16", accept_hi=8)
+    run_step(wl, seed=23, seqs=[0, 77, 127], poison=True)
+
+
+def test_many_ragged_sequences_flattened_attention():
+    # 160 ragged sequences: the key axis of the batch cut into equal ranges,
+    # workgroups crossing segment ends
+    wl = gen.Workload("tiny-b160-ragged", 256, 4, 2, 64, 2, 512, 1024, 8, 3, 160, 0, 300, "bf16", accept_hi=8)
+    run_step(wl, seed=24, seqs=[0, 51, 159], poison=True)
+
+
 def test_host_checks_reject_bad_sizes():
     from block_diffusion_drafting_ctx_amd import Drafter, _abi
     from tests.gpu_cases import config_for
