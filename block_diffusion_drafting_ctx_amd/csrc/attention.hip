@@ -579,10 +579,19 @@ __global__ void __launch_bounds__(kThreads) attention_kernel(const AttnArgs a) {
   stage_store(R, s0.p, s0.c);
   __syncthreads();
   // one stage: `cur` holds the stage now in LDS (free), `nxt` the next one
+  // With two stages in flight, the loads of a step go out unconditionally
+  // (with no stage left to fetch, the current one is fetched again, in bounds
+  // and unused) and a piece's query loads are waited for where they are
+  // issued: every path then has the same loads in flight, so the waits the
+  // compiler places before the stores and the matrix work count exactly the
+  // loads they need.  With a varying count it waits for all loads in flight,
+  // the ones of the stage ahead too.  (With one stage in flight the store
+  // waits for the step's own loads anyway.)
   auto step = [&](StageRegs& cur, StageRegs& nxt) -> bool {
-    if (PF == 2 ? m2 : m1) {
-      if (PF == 2) stage_load(cur, s2.p, s2.c);
-      else stage_load(cur, s1.p, s1.c);
+    if constexpr (PF == 2) {
+      stage_load(cur, m2 ? s2.p : s0.p, m2 ? s2.c : s0.c);
+    } else {
+      if (m1) stage_load(cur, s1.p, s1.c);
     }
     compute(s0.c, s0.p.pend);
     const bool ends = !m1 || s1.p.sstart != s0.p.sstart;
@@ -591,7 +600,10 @@ __global__ void __launch_bounds__(kThreads) attention_kernel(const AttnArgs a) {
     __syncthreads();
     stage_store(PF == 2 ? nxt : cur, s1.p, s1.c);
     __syncthreads();
-    if (ends) q_load(s1.p);
+    if (ends) {
+      q_load(s1.p);
+      wait_vm_all();
+    }
     s0 = s1;
     if (PF == 2) {
       s1 = s2;

@@ -155,6 +155,9 @@ __device__ __forceinline__ float wave_sum_f32(float v) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// s_waitcnt vmcnt(0): every vector memory access of the wave has completed.
+__device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 __device__ __forceinline__ float silu_f32(float x) {
   return x / (1.0f + fast_exp2(-x * 1.4426950408889634f));
 }
