@@ -68,8 +68,8 @@ const char* validate(const dflash_config* c) {
   if (c->n_target_layers < 1 || c->n_target_layers > 8) return "n_target_layers must be in [1, 8]";
   if (c->max_batch < 1 || c->max_ctx < 1 || c->max_fuse_rows < 1) return "bad limits";
   if (c->max_batch > kAttnMaxBatch) return "max_batch must be <= 1024";
-  if ((int64_t)c->n_kv_heads * c->max_batch * ((int64_t)c->max_ctx + c->block) >= ((int64_t)1 << 31))
-    return "n_kv_heads * max_batch * (max_ctx + block) must be below 2^31";
+  if ((int64_t)c->n_kv_heads * c->max_batch * ((int64_t)c->max_ctx + c->block + kAttnPieceCost) >= ((int64_t)1 << 31))
+    return "n_kv_heads * max_batch * (max_ctx + block + 256) must be below 2^31";
   if (c->conv_width != 0 && c->conv_width != 3) return "conv_width must be 0 or 3";
   if (c->conv_width == 3 && 16 % c->block) return "the block conv needs block to divide 16";
   if (c->dtype != DFLASH_DTYPE_F32 && c->dtype != DFLASH_DTYPE_BF16) return "unknown dtype";

@@ -155,6 +155,31 @@ __device__ __forceinline__ void build_plan(const int32_t* ctx_len, int B, int Bs
 // Keys per workgroup range of the flattened key axis of `total` keys.
 __device__ __forceinline__ int range_keys(int total, int nwg) { return max((total + nwg - 1) / nwg, kMinPieceKeys); }
 
+// The flattened key axis is cut in a weighted space where every segment
+// carries kPieceCost extra positions in front of its keys: a workgroup's
+// range then pays for each segment it starts (the query reload and the close
+// of a piece cost about as much as streaming this many keys, measured), so
+// workgroups that cross many short segments take fewer keys.  Weighted
+// position of key k of segment (b, h): Hkv*(pre[b] + kPieceCost*b) +
+// h*(L_b + kPieceCost) + kPieceCost + k.
+constexpr int kPieceCost = kAttnPieceCost;
+__device__ __forceinline__ int flat_weight(const int* pre, int b, int Hkv) { return Hkv * (pre[b] + kPieceCost * b); }
+// Key-axis position of weighted position w (positions inside a segment's
+// extra run map to the segment's first key).
+__device__ __forceinline__ int flat_key_of(int w, const int* pre, int B, int Hkv) {
+  int lo = 0, hi = B;  // flat_weight(lo) <= w < flat_weight(hi)
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (flat_weight(pre, mid, Hkv) <= w) lo = mid;
+    else hi = mid;
+  }
+  const int L = pre[lo + 1] - pre[lo];
+  const int off = w - flat_weight(pre, lo, Hkv);
+  const int j = off / (L + kPieceCost);
+  const int k = min(max(off - j * (L + kPieceCost) - kPieceCost, 0), L);
+  return Hkv * pre[lo] + j * L + k;
+}
+
 // Largest b in [0, B) with key(b) <= x, for key nondecreasing over [0, B].
 template <typename F>
 __device__ __forceinline__ int upper_index(int B, int x, F key) {
@@ -344,7 +369,6 @@ __global__ void __launch_bounds__(kThreads) attention_kernel(const AttnArgs a) {
   } else {
     if (wave == 0) build_plan(a.ctx_len, a.batch, Bs, Hkv, a.max_ctx, gridDim.x, pre, wpre, mode, lane);
     __syncthreads();
-    const int total = Hkv * pre[a.batch];
     if (*mode != 0) {
       const int w = blockIdx.x;
       if (w >= wpre[a.batch]) return;
@@ -359,10 +383,13 @@ __global__ void __launch_bounds__(kThreads) attention_kernel(const AttnArgs a) {
       p.pend = (int)((int64_t)(k + 1) * p.seg_len / nb);
       g1 = p.sstart + p.pend;
     } else {
-      const int Q = range_keys(total, gridDim.x);
-      const int g0 = blockIdx.x * Q;
-      if (g0 >= total) return;
-      g1 = min(total, g0 + Q);
+      const int wtot = flat_weight(pre, a.batch, Hkv);
+      const int Q = range_keys(wtot, gridDim.x);
+      const int w0 = blockIdx.x * Q;
+      if (w0 >= wtot) return;
+      const int g0 = __builtin_amdgcn_readfirstlane(flat_key_of(w0, pre, a.batch, Hkv));
+      g1 = __builtin_amdgcn_readfirstlane(flat_key_of(min(wtot, w0 + Q), pre, a.batch, Hkv));
+      if (g0 >= g1) return;  // the range holds no key (inside a segment's extra run)
       p.b = __builtin_amdgcn_readfirstlane(upper_index(a.batch, g0, [&](int i) { return Hkv * pre[i]; }));
       p.seg_len = __builtin_amdgcn_readfirstlane(pre[p.b + 1] - pre[p.b]);
       const int base = Hkv * pre[p.b];
@@ -650,12 +677,12 @@ __global__ void __launch_bounds__(256) attention_combine_kernel(const AttnArgs a
       np = (wpre[b + 1] - wpre[b]) / a.Hkv;
       w0 = wpre[b] + h * np;
     } else {
-      const int total = a.Hkv * pre[a.batch];
-      const int Q = range_keys(total, a.nwg);
+      // the workgroups whose weighted ranges hold a key of this segment
+      const int Q = range_keys(flat_weight(pre, a.batch, a.Hkv), a.nwg);
       const int seg_len = pre[b + 1] - pre[b];
-      const int sstart = a.Hkv * pre[b] + h * seg_len;
-      w0 = sstart / Q;
-      np = (sstart + seg_len - 1) / Q - w0 + 1;
+      const int wk = flat_weight(pre, b, a.Hkv) + h * (seg_len + kPieceCost) + kPieceCost;  // its first key
+      w0 = wk / Q;
+      np = (wk + seg_len - 1) / Q - w0 + 1;
     }
     np_load = np;
     if (np <= 1) return;  // written directly by the attention kernel

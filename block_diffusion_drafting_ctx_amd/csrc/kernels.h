@@ -123,6 +123,9 @@ hipError_t launch_finish(int storage, FinishKind kind, const FinishArgs& f, hipS
 // Sequences per attention launch (the per-workgroup prefix table of segment
 // lengths lives in LDS).
 constexpr int kAttnMaxBatch = 1024;
+// Keys of streaming a flattened-split attention workgroup's plan charges for
+// every segment it starts (positions on the weighted key axis).
+constexpr int kAttnPieceCost = 256;
 struct AttnArgs {
   const void* q_hi;  // bf16 hi/lo pair [B*Bs, Hq*D], already scaled by log2(e)/sqrt(D)
   const void* q_lo;
