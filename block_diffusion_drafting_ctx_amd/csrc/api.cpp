@@ -120,9 +120,11 @@ bool plan_gemm(int storage, int src, int out, bool lo, int M, int N, int K, Gemm
   const int BN = 32 * gemm_mt_nf(MF);
   const int nbm = (M + 64 * MF - 1) / (64 * MF);
   const int nbn = (N + BN - 1) / BN;
+  // (every k-slice keeps an even number of 32-deep stages: the kernel's
+  // pipeline takes them in pairs)
   int KS = 1;
   if (out == OUT_PARTIAL)
-    while (nbn * nbm * 2 * KS <= kMtTargetWgs && (K / 32) % (2 * KS) == 0 && K / (2 * KS) >= 256) KS *= 2;
+    while (nbn * nbm * 2 * KS <= kMtTargetWgs && (K / 32) % (4 * KS) == 0 && K / (2 * KS) >= 256) KS *= 2;
   const int units = nbn * KS;
   l->kind = GEMM_MT;
   l->MR = MF;
