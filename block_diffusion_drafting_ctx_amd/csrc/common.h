@@ -147,6 +147,15 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
   }
   return v;
 }
+// v of lane (lane ^ 1) / (lane ^ 2): DPP quad permutes, register to register
+// (a general shuffle goes through the LDS pipe, ~100 cycles a round).
+__device__ __forceinline__ float quad_xor1(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));  // [1,0,3,2]
+}
+__device__ __forceinline__ float quad_xor2(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));  // [2,3,0,1]
+}
+
 __device__ __forceinline__ float wave_sum_f32(float v) {
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);

@@ -524,78 +524,149 @@ __global__ void __launch_bounds__(1024) argmax_reduce_kernel(const uint64_t* par
 }
 
 // ------------------------------------------------------------------ finish kernels
-// Every finish kernel is elementwise over its outputs and issues all the
-// global loads an output needs at once (one round of memory latency): the
-// k-slice partials of that output, the row scale and the epilogue operands.
+// Every finish kernel is elementwise over its outputs: a thread takes 4
+// consecutive columns of one row (16-byte partial loads) and issues all the
+// global loads those outputs need at once (one round of memory latency): the
+// k-slice partials, the row scale and the epilogue operands.
 
-// Sum of the k-slices of output (m, n) in slice order.
-__device__ __forceinline__ float ksum(const FinishArgs& f, int m, int n) {
-  const int tile = n >> 4, j = n & 15;
-  const size_t stride = (size_t)f.ntiles * f.M * 16;
-  const float* p = f.part + ((size_t)tile * f.M + m) * 16 + j;
-  float v = 0.f;
-  for (int s0 = 0; s0 < f.KS; s0 += 16) {
-    float t[16];
+// k-slice sums of NQ column quads of one row.  Lane j of the SPL lanes that
+// share the quads (KS a multiple of SPL) takes slices j, j + SPL, ... in that
+// order, two per round: a round issues both slices' loads unconditionally,
+// the index clamped to a valid slice and a surplus value dropped on the ALU
+// side.  (Loads behind branches make the compiler copy each result at the
+// merge, waiting for it there, and lose the count of loads in flight, so a
+// later dependent load would wait for all of them.)
+template <int SPL, int NQ>
+struct KSlices {
+  const float* p[NQ];
+  size_t stride;
+  int KS;
+  f32x4 t[NQ][2];
+
+  __device__ __forceinline__ KSlices(const FinishArgs& f, int m, const int (&n)[NQ], int j) {
+    stride = (size_t)f.ntiles * f.M * 16;
+    KS = f.KS;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) t[i] = s0 + i < f.KS ? p[(size_t)(s0 + i) * stride] : 0.f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i)
-      if (s0 + i < f.KS) v += t[i];
+    for (int q = 0; q < NQ; ++q) p[q] = f.part + ((size_t)(n[q] >> 4) * f.M + m) * 16 + (n[q] & 15) + j * stride;
   }
-  return v;
-}
-
-// ksum of two outputs of one row with all loads of both issued together.
-__device__ __forceinline__ void ksum2(const FinishArgs& f, int m, int n0, int n1, float& v0, float& v1) {
-  const size_t stride = (size_t)f.ntiles * f.M * 16;
-  const float* p0 = f.part + ((size_t)(n0 >> 4) * f.M + m) * 16 + (n0 & 15);
-  const float* p1 = f.part + ((size_t)(n1 >> 4) * f.M + m) * 16 + (n1 & 15);
-  v0 = 0.f;
-  v1 = 0.f;
-  for (int s0 = 0; s0 < f.KS; s0 += 8) {
-    float t0[8], t1[8];
+  __device__ __forceinline__ void issue(int s0) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      t0[i] = s0 + i < f.KS ? p0[(size_t)(s0 + i) * stride] : 0.f;
-      t1[i] = s0 + i < f.KS ? p1[(size_t)(s0 + i) * stride] : 0.f;
+    for (int i = 0; i < 2; ++i) {
+      const size_t sl = (size_t)min(s0 + SPL * i, KS - SPL);
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) t[q][i] = *reinterpret_cast<const f32x4*>(p[q] + sl * stride);
     }
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      if (s0 + i < f.KS) {
-        v0 += t0[i];
-        v1 += t1[i];
-      }
   }
-}
-
-// Two-column partial loads for KS <= 8, split into issue and reduce so that
-// independent loads (row scale, context length, RoPE table) can be placed in
-// between.
-struct KPair {
-  float a[8], b[8];
+  __device__ __forceinline__ void add(int s0, f32x4 (&v)[NQ]) const {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const bool in = s0 + SPL * i < KS;
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) v[q] += in ? t[q][i] : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+  // every round after the first (issued and added by the caller)
+  __device__ __forceinline__ void rest(f32x4 (&v)[NQ]) {
+    for (int s0 = 2 * SPL; s0 < KS; s0 += 2 * SPL) {
+      issue(s0);
+      add(s0, v);
+    }
+  }
 };
-__device__ __forceinline__ void kpair_issue(const FinishArgs& f, int m, int n0, int n1, KPair& k) {
-  const size_t stride = (size_t)f.ntiles * f.M * 16;
-  const float* p0 = f.part + ((size_t)(n0 >> 4) * f.M + m) * 16 + (n0 & 15);
-  const float* p1 = f.part + ((size_t)(n1 >> 4) * f.M + m) * 16 + (n1 & 15);
+
+template <int SPL, int NQ>
+__device__ __forceinline__ void ksum(const FinishArgs& f, int m, const int (&n)[NQ], int j, f32x4 (&v)[NQ]) {
+  KSlices<SPL, NQ> k(f, m, n, j);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    k.a[i] = i < f.KS ? p0[(size_t)i * stride] : 0.f;
-    k.b[i] = i < f.KS ? p1[(size_t)i * stride] : 0.f;
-  }
+  for (int q = 0; q < NQ; ++q) v[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+  k.issue(0);
+  k.add(0, v);
+  k.rest(v);
 }
-__device__ __forceinline__ void kpair_reduce(const FinishArgs& f, const KPair& k, float& v0, float& v1) {
-  v0 = 0.f;
-  v1 = 0.f;
+
+// Sum over the SPL adjacent lanes that share a quad (every lane gets it).
+template <int SPL>
+__device__ __forceinline__ void group_sum(f32x4& v) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
-    if (i < f.KS) {
-      v0 += k.a[i];
-      v1 += k.b[i];
-    }
+  for (int e = 0; e < 4; ++e) {
+    if constexpr (SPL >= 2) v[e] += quad_xor1(v[e]);
+    if constexpr (SPL >= 4) v[e] += quad_xor2(v[e]);
+  }
 }
 
 __device__ __forceinline__ float row_scale(const FinishArgs& f, int m) { return f.rinv != nullptr ? f.rinv[m] : 1.0f; }
+
+// E (1, 2 or 4) consecutive bf16 values packed into one 2-, 4- or 8-byte store.
+template <int E>
+__device__ __forceinline__ void store_bits(bf16_t* dst, const bf16_t (&b)[E]) {
+  if constexpr (E == 4) {
+    *reinterpret_cast<u32x2*>(dst) =
+        u32x2{(uint32_t)b[0] | ((uint32_t)b[1] << 16), (uint32_t)b[2] | ((uint32_t)b[3] << 16)};
+  } else if constexpr (E == 2) {
+    *reinterpret_cast<uint32_t*>(dst) = (uint32_t)b[0] | ((uint32_t)b[1] << 16);
+  } else {
+    *dst = b[0];
+  }
+}
+
+// E values as a bf16 hi/lo pair at idx (a multiple of E).
+template <int E>
+__device__ __forceinline__ void split_store(bf16_t* hi, bf16_t* lo, size_t idx, const float (&v)[E]) {
+  bf16_t h[E], l[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    h[e] = f32_to_bf16_bits(v[e]);
+    l[e] = f32_to_bf16_bits(v[e] - bf16_bits_to_f32(h[e]));
+  }
+  store_bits<E>(hi + idx, h);
+  if (lo) store_bits<E>(lo + idx, l);
+}
+
+// E values in the storage type at dst (aligned to E elements).
+template <typename S, int E>
+__device__ __forceinline__ void store_n(S* dst, const float (&v)[E]) {
+  if constexpr (sizeof(S) == 4) {
+    if constexpr (E == 4) *reinterpret_cast<f32x4*>(dst) = f32x4{v[0], v[1], v[2], v[3]};
+    else if constexpr (E == 2) *reinterpret_cast<float2*>(dst) = make_float2(v[0], v[1]);
+    else *dst = v[0];
+  } else {
+    bf16_t b[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) b[e] = f32_to_bf16_bits(v[e]);
+    store_bits<E>(dst, b);
+  }
+}
+
+// E consecutive floats from src (aligned to E elements).
+template <int E>
+__device__ __forceinline__ void load_n(const float* src, float (&v)[E]) {
+  if constexpr (E == 4) {
+    const f32x4 t = *reinterpret_cast<const f32x4*>(src);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = t[e];
+  } else if constexpr (E == 2) {
+    const float2 t = *reinterpret_cast<const float2*>(src);
+    v[0] = t.x;
+    v[1] = t.y;
+  } else {
+    v[0] = *src;
+  }
+}
+
+// Elements j*E .. j*E + E-1 of a quad (lane j of the SPL = 4/E lanes sharing
+// it), picked by selects rather than a dynamic register index.
+template <int E>
+__device__ __forceinline__ void pick(const f32x4& v, int j, float (&o)[E]) {
+  if constexpr (E == 4) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = v[e];
+  } else if constexpr (E == 2) {
+    o[0] = j ? v[2] : v[0];
+    o[1] = j ? v[3] : v[1];
+  } else {
+    o[0] = j == 0 ? v[0] : (j == 1 ? v[1] : (j == 2 ? v[2] : v[3]));
+  }
+}
 
 // Rotation of the pair (lo, hi) by the tabulated angle of (position, pair index).
 __device__ __forceinline__ void rope_apply(float& lo, float& hi, float2 cs) {
@@ -604,160 +675,242 @@ __device__ __forceinline__ void rope_apply(float& lo, float& hi, float2 cs) {
   hi = a * cs.y + b * cs.x;
 }
 
-// y = sum (+ x residual, + width-3 block conv); x / out_f32 = y; hi/lo of
-// y * gnext; sums of squares per (tile, row).  grid: (N/16 tiles, row groups
-// of 16); thread (r, j) = (tid >> 4, tid & 15).  A conv block never crosses a
-// 16-row group (the block divides 16).
-template <typename S>
-__global__ void __launch_bounds__(256) finish_rowtile_kernel(const FinishArgs f) {
-  __shared__ float v0[256];
-  const int tile = blockIdx.x, r = threadIdx.x >> 4, j = threadIdx.x & 15;
-  const int m = 16 * blockIdx.y + r, n = tile * 16 + j;
-  const bool ok = m < f.M;
-  const size_t idx = (size_t)m * f.N + n;
-  // epilogue operands first: their loads fly with the partial loads
-  const float xr = ok && f.x != nullptr ? f.x[idx] : 0.f;
-  const float gnv = load_f32<S>(reinterpret_cast<const S*>(f.gnext) + n);
-  float c0 = 0.f, c1 = 0.f, c2 = 0.f;
-  if (f.conv != nullptr) {
-    const S* cw = reinterpret_cast<const S*>(f.conv);
-    c0 = load_f32<S>(cw + 3 * n);
-    c1 = load_f32<S>(cw + 3 * n + 1);
-    c2 = load_f32<S>(cw + 3 * n + 2);
+// The E tabulated (cos, sin) of pairs d .. d + E-1 at position pos (d a
+// multiple of E).
+template <int E>
+__device__ __forceinline__ void rope_n(const FinishArgs& f, int pos, int d, float2 (&cs)[E]) {
+  const float2* t = f.rope + (size_t)pos * (f.head_dim >> 1) + d;
+  if constexpr (E == 1) {
+    cs[0] = t[0];
+  } else {
+#pragma unroll
+    for (int h = 0; h < E / 2; ++h) {
+      const f32x4 a = reinterpret_cast<const f32x4*>(t)[h];
+      cs[2 * h] = make_float2(a[0], a[1]);
+      cs[2 * h + 1] = make_float2(a[2], a[3]);
+    }
   }
-  float v = 0.f;
-  if (ok) v = ksum(f, m, n) + xr;
-  if (f.conv != nullptr) {
-    v0[threadIdx.x] = v;
-    __syncthreads();
-    const int i = m % f.block;
-    float y = c1 * v;
-    if (i > 0) y += c0 * v0[threadIdx.x - 16];
-    if (i < f.block - 1 && m + 1 < f.M) y += c2 * v0[threadIdx.x + 16];
-    v = v + y;
-  }
-  if (ok) {
-    if (f.x != nullptr) f.x[idx] = v;
-    if (f.out_f32 != nullptr) f.out_f32[idx] = v;
-    split_store(reinterpret_cast<bf16_t*>(f.out_hi), reinterpret_cast<bf16_t*>(f.out_lo), idx, v * gnv);
-  }
-  float sq = ok ? v * v : 0.f;
-  sq += __shfl_xor(sq, 8);
-  sq += __shfl_xor(sq, 4);
-  sq += __shfl_xor(sq, 2);
-  sq += __shfl_xor(sq, 1);
-  if (j == 0 && ok) f.ssq_out[(size_t)tile * f.ld_ssq + m] = sq;
 }
 
-// act[m, c] = silu(rinv * y_gate) * (rinv * y_up) as a hi/lo pair.  One
-// thread per output, ordered (tile, row, column in tile) so the partial reads
-// are contiguous.
+// y = sum (+ x residual, + width-3 block conv); x / out_f32 = y; hi/lo of
+// y * gnext; sums of squares per (tile, row).  grid: (tiles / (4/SPL), row
+// groups of 16); thread t: lane j = t % SPL of the group sharing column quad
+// q = (t / SPL) & 3 of row r = (t / 4SPL) & 15 of tile t / 64SPL, each lane
+// finishing 4/SPL columns.  The conv's neighbour rows come through LDS (a
+// conv block never crosses a 16-row group: the block divides 16).
+template <typename S, int SPL>
+__global__ void __launch_bounds__(256) finish_rowtile_kernel(const FinishArgs f) {
+  constexpr int E = 4 / SPL, TPB = 4 / SPL;  // columns per lane, tiles per workgroup
+  __shared__ float s_y[TPB][16][16];
+  const int t = threadIdx.x, j = t % SPL, q = (t / SPL) & 3, r = (t / (4 * SPL)) & 15, tl = t / (64 * SPL);
+  const int tile = blockIdx.x * TPB + tl;
+  const int m = 16 * blockIdx.y + r, n = tile * 16 + 4 * q, col = 4 * q + j * E;
+  const bool ok = m < f.M && tile < f.ntiles;
+  const size_t idx = (size_t)m * f.N + n + j * E;
+  // epilogue operands of this lane's columns first: their loads fly with the partial loads
+  float xr[E], gn[E], c0[E], c1[E], c2[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) xr[e] = gn[e] = c0[e] = c1[e] = c2[e] = 0.f;
+  if (ok) {
+    if (f.x != nullptr) load_n<E>(f.x + idx, xr);
+    const S* g = reinterpret_cast<const S*>(f.gnext) + n + j * E;
+#pragma unroll
+    for (int e = 0; e < E; ++e) gn[e] = load_f32<S>(g + e);
+    if (f.conv != nullptr) {
+      const S* cw = reinterpret_cast<const S*>(f.conv) + 3 * (n + j * E);
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        c0[e] = load_f32<S>(cw + 3 * e);
+        c1[e] = load_f32<S>(cw + 3 * e + 1);
+        c2[e] = load_f32<S>(cw + 3 * e + 2);
+      }
+    }
+  }
+  // (unconditional loads: a row past M reads row M - 1 and drops it; the grid covers the tiles exactly)
+  f32x4 v4[1];
+  ksum<SPL, 1>(f, min(m, f.M - 1), {n}, j, v4);
+  if (!ok) v4[0] = f32x4{0.f, 0.f, 0.f, 0.f};
+  group_sum<SPL>(v4[0]);
+  float v[E], y[E];
+  pick<E>(v4[0], j, v);
+#pragma unroll
+  for (int e = 0; e < E; ++e) y[e] = v[e] = v[e] + xr[e];
+  if (f.conv != nullptr) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) s_y[tl][r][col + e] = v[e];
+    __syncthreads();
+    const int i = m % f.block;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      float c = c1[e] * v[e];
+      if (i > 0) c += c0[e] * s_y[tl][r - 1][col + e];
+      if (i < f.block - 1 && m + 1 < f.M) c += c2[e] * s_y[tl][r + 1][col + e];
+      y[e] = v[e] + c;
+    }
+  }
+  float sq = 0.f;
+  if (ok) {
+    if (f.x != nullptr) store_n<float, E>(f.x + idx, y);
+    if (f.out_f32 != nullptr) store_n<float, E>(f.out_f32 + idx, y);
+    float sv[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      sv[e] = y[e] * gn[e];
+      sq += y[e] * y[e];
+    }
+    split_store<E>(reinterpret_cast<bf16_t*>(f.out_hi), reinterpret_cast<bf16_t*>(f.out_lo), idx, sv);
+  }
+  // the row's 4 SPL lanes
+  sq += quad_xor1(sq);
+  sq += quad_xor2(sq);
+#pragma unroll
+  for (int o = 4; o < 4 * SPL; o <<= 1) sq += __shfl_xor(sq, o);
+  if (q == 0 && j == 0 && ok) f.ssq_out[(size_t)tile * f.ld_ssq + m] = sq;
+}
+
+// act[m, c] = silu(rinv * y_gate) * (rinv * y_up) as a hi/lo pair.  SPL
+// lanes per 4 outputs, ordered (tile, row, quad) so the partial reads are
+// contiguous; after the lanes' sums are combined each finishes 4/SPL outputs.
+template <int SPL>
 __global__ void __launch_bounds__(256) finish_swiglu_kernel(const FinishArgs f) {
+  constexpr int E = 4 / SPL;
   const int F = f.N >> 1;
-  const int e = blockIdx.x * 256 + threadIdx.x;
-  if (e >= f.M * F) return;
-  const int tile = e / (f.M * 16), rem = e - tile * (f.M * 16);
-  const int m = rem >> 4, c = tile * 16 + (rem & 15);
-  KPair kp;
-  const bool fast = f.KS <= 8;
-  if (fast) kpair_issue(f, m, c, F + c, kp);
+  const int e = blockIdx.x * blockDim.x + threadIdx.x, e4 = e / SPL, j = e % SPL;
+  if (e4 >= f.M * (F >> 2)) return;  // whole lane groups leave together
+  const int tile = e4 / (f.M * 4), rem = e4 - tile * (f.M * 4);
+  const int m = rem >> 2, c = tile * 16 + 4 * (rem & 3);
   const float r = row_scale(f, m);
-  float gv, uv;
-  if (fast) kpair_reduce(f, kp, gv, uv);
-  else ksum2(f, m, c, F + c, gv, uv);
-  gv *= r;
-  uv *= r;
-  split_store(reinterpret_cast<bf16_t*>(f.out_hi), reinterpret_cast<bf16_t*>(f.out_lo), (size_t)m * F + c,
-              silu_f32(gv) * uv);
+  f32x4 gu[2];
+  ksum<SPL, 2>(f, m, {c, F + c}, j, gu);
+  group_sum<SPL>(gu[0]);
+  group_sum<SPL>(gu[1]);
+  float g[E], u[E], a[E];
+  pick<E>(gu[0], j, g);
+  pick<E>(gu[1], j, u);
+#pragma unroll
+  for (int k = 0; k < E; ++k) a[k] = silu_f32(g[k] * r) * (u[k] * r);
+  split_store<E>(reinterpret_cast<bf16_t*>(f.out_hi), reinterpret_cast<bf16_t*>(f.out_lo), (size_t)m * F + c + j * E,
+                 a);
 }
 
 // Block Q/K/V: RoPE on Q and K at position T + i (T = ctx_len[b], clamped);
 // Q scaled and stored as a hi/lo pair; K and V staged in this layer's cache at
 // rows T + i (rows past the committed context: the attention reads every key
 // from the cache).  A sequence whose block would pass max_ctx stages nothing
-// and is flagged.  One thread per rotation pair (row, head of the
-// concatenated [Q | K | V] output, d < D/2).
-template <typename S>
+// and is flagged.  SPL lanes per 4 consecutive rotation pairs (row, head of
+// the concatenated [Q | K | V] output, d .. d + 3 < D/2); each lane finishes
+// 4/SPL of them.
+template <typename S, int SPL>
 __global__ void __launch_bounds__(256) finish_qkv_kernel(const FinishArgs f) {
+  constexpr int E = 4 / SPL;
   const int D = f.head_dim, half = D >> 1;
-  const int pairs = f.N >> 1;
-  const int e = blockIdx.x * 256 + threadIdx.x;
-  if (e >= f.M * pairs) return;
-  const int m = e / pairs, rem = e - m * pairs;
-  const int hd = rem / half, d = rem - hd * half;
-  const int n = hd * D + d;
+  const int quads = f.N >> 3;  // 4-pair groups per row
+  const int e = blockIdx.x * blockDim.x + threadIdx.x, e4 = e / SPL, j = e % SPL;
+  if (e4 >= f.M * quads) return;  // whole lane groups leave together
+  const int m = e4 / quads, rem = e4 - m * quads;
+  const int hd = rem / (half >> 2), d = (rem - hd * (half >> 2)) * 4;
+  const int n = hd * D + d, nj = n + j * E;  // nj: this lane's first pair
   const int Nq = f.n_q_heads * D, Nk = f.n_kv_heads * D;
   const int b = m / f.block, i = m - b * f.block;
-  KPair kp;
-  const bool fast = f.KS <= 8;
-  if (fast) kpair_issue(f, m, n, n + half, kp);
   const float r = row_scale(f, m);
   // a caller-set length outside [0, max_ctx] is clamped (the table covers every clamped position)
   const int T = min(max(f.ctx_len[b], 0), f.max_ctx);
   const int pos = T + i;
-  const float2 cs = f.rope[(size_t)pos * half + d];
-  float lo, hi;
-  if (fast) kpair_reduce(f, kp, lo, hi);
-  else ksum2(f, m, n, n + half, lo, hi);
-  lo *= r;
-  hi *= r;
+  // the first round of partial loads goes out before the table load that
+  // waits for the context length
+  KSlices<SPL, 2> ks(f, m, {n, n + half}, j);
+  ks.issue(0);
+  float2 cs[E];
+  rope_n<E>(f, pos, d + j * E, cs);
+  f32x4 v[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+  ks.add(0, v);
+  ks.rest(v);
+  group_sum<SPL>(v[0]);
+  group_sum<SPL>(v[1]);
+  float lo[E], hi[E];
+  pick<E>(v[0], j, lo);
+  pick<E>(v[1], j, hi);
+#pragma unroll
+  for (int k = 0; k < E; ++k) {
+    lo[k] *= r;
+    hi[k] *= r;
+  }
   if (n < Nq) {
     bf16_t* qh = reinterpret_cast<bf16_t*>(f.out_hi);
     bf16_t* ql = reinterpret_cast<bf16_t*>(f.out_lo);
-    rope_apply(lo, hi, cs);
-    split_store(qh, ql, (size_t)m * Nq + n, lo * f.q_scale);
-    split_store(qh, ql, (size_t)m * Nq + n + half, hi * f.q_scale);
+#pragma unroll
+    for (int k = 0; k < E; ++k) {
+      rope_apply(lo[k], hi[k], cs[k]);
+      lo[k] *= f.q_scale;
+      hi[k] *= f.q_scale;
+    }
+    split_store<E>(qh, ql, (size_t)m * Nq + nj, lo);
+    split_store<E>(qh, ql, (size_t)m * Nq + nj + half, hi);
     return;
   }
   if (T + f.block > f.max_ctx) {
-    if (rem == Nq / 2 && i == 0) atomicOr(f.err, kErrDraftOverflow);
+    if (rem == Nq / 8 && i == 0 && j == 0) atomicOr(f.err, kErrDraftOverflow);
     return;
   }
   const bool is_k = n < Nq + Nk;
-  const int c = is_k ? n - Nq : n - Nq - Nk;  // column within the KV heads
-  if (is_k) rope_apply(lo, hi, cs);
+  const int c = (is_k ? n - Nq : n - Nq - Nk) + j * E;  // column within the KV heads
+  if (is_k) {
+#pragma unroll
+    for (int k = 0; k < E; ++k) rope_apply(lo[k], hi[k], cs[k]);
+  }
   S* dst = reinterpret_cast<S*>(f.kv_cache[is_k ? 0 : 1]) + ((size_t)b * f.max_ctx + pos) * Nk + c;
-  store_from_f32<S>(dst, lo);
-  store_from_f32<S>(dst + half, hi);
+  store_n<S, E>(dst, lo);
+  store_n<S, E>(dst + half, hi);
 }
 
 // Context K/V of every layer (segments K^0, V^0, K^1, V^1, ...): RoPE on K at
 // position ctx_len[b] + i, scatter to cache row ctx_len[b] + i.  A sequence
-// whose rows would pass max_ctx is skipped and flagged.  One thread per
-// rotation pair (row, head of the concatenated output, d < D/2).
-template <typename S>
+// whose rows would pass max_ctx is skipped and flagged.  SPL lanes per 4
+// consecutive rotation pairs (row, head of the concatenated output, d .. d+3);
+// each lane finishes 4/SPL of them.
+template <typename S, int SPL>
 __global__ void __launch_bounds__(256) finish_kv_kernel(const FinishArgs f) {
+  constexpr int E = 4 / SPL;
   const int D = f.head_dim, half = D >> 1, Hkv = f.n_kv_heads;
-  const int pairs = f.N >> 1;
-  const int e = blockIdx.x * 256 + threadIdx.x;
-  if (e >= f.M * pairs) return;
-  const int m = e / pairs, rem = e - m * pairs;
-  const int hd = rem / half, d = rem - hd * half;
+  const int quads = f.N >> 3;
+  const int e = blockIdx.x * blockDim.x + threadIdx.x, e4 = e / SPL, j = e % SPL;
+  if (e4 >= f.M * quads) return;  // whole lane groups leave together
+  const int m = e4 / quads, rem = e4 - m * quads;
+  const int hd = rem / (half >> 2), d = (rem - hd * (half >> 2)) * 4;
   const int seg = hd / Hkv, head = hd - seg * Hkv;
   const int b = m / f.block, i = m - b * f.block;
   const int n = hd * D + d;
-  KPair kp;
-  const bool fast = f.KS <= 8;
-  if (fast) kpair_issue(f, m, n, n + half, kp);
   const float r = row_scale(f, m);
   const int t0 = f.ctx_len[b];
   const bool bad = t0 < 0 || t0 + f.block > f.max_ctx;
   const int pos = bad ? 0 : t0 + i;
-  float2 cs = make_float2(1.f, 0.f);
-  if ((seg & 1) == 0) cs = f.rope[(size_t)pos * half + d];
-  float lo, hi;
-  if (fast) kpair_reduce(f, kp, lo, hi);
-  else ksum2(f, m, n, n + half, lo, hi);
+  KSlices<SPL, 2> ks(f, m, {n, n + half}, j);
+  ks.issue(0);
+  float2 cs[E];
+#pragma unroll
+  for (int k = 0; k < E; ++k) cs[k] = make_float2(1.f, 0.f);
+  if ((seg & 1) == 0) rope_n<E>(f, pos, d + j * E, cs);
+  f32x4 v[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+  ks.add(0, v);
+  ks.rest(v);
+  group_sum<SPL>(v[0]);
+  group_sum<SPL>(v[1]);
   if (bad) {
-    if (rem == 0 && i == 0) atomicOr(f.err, kErrFuseOverflow);
+    if (rem == 0 && i == 0 && j == 0) atomicOr(f.err, kErrFuseOverflow);
     return;
   }
-  lo *= r;
-  hi *= r;
-  if ((seg & 1) == 0) rope_apply(lo, hi, cs);
-  S* dst = reinterpret_cast<S*>(f.kv_cache[seg]) + (((size_t)b * f.max_ctx + pos) * Hkv + head) * D + d;
-  store_from_f32<S>(dst, lo);
-  store_from_f32<S>(dst + half, hi);
+  float lo[E], hi[E];
+  pick<E>(v[0], j, lo);
+  pick<E>(v[1], j, hi);
+#pragma unroll
+  for (int k = 0; k < E; ++k) {
+    lo[k] *= r;
+    hi[k] *= r;
+    if ((seg & 1) == 0) rope_apply(lo[k], hi[k], cs[k]);
+  }
+  S* dst = reinterpret_cast<S*>(f.kv_cache[seg]) + (((size_t)b * f.max_ctx + pos) * Hkv + head) * D + d + j * E;
+  store_n<S, E>(dst, lo);
+  store_n<S, E>(dst + half, hi);
 }
 
 // ------------------------------------------------------------------ launchers
@@ -847,25 +1000,39 @@ hipError_t launch_argmax_reduce(const uint64_t* part, int ntiles, int ld, int M,
   return hipGetLastError();
 }
 
+template <typename S, int SPL>
+static void launch_finish_spl(FinishKind kind, const FinishArgs& f, int blocks, int threads, hipStream_t st) {
+  if (kind == FIN_SWIGLU) hipLaunchKernelGGL(finish_swiglu_kernel<SPL>, dim3(blocks), dim3(threads), 0, st, f);
+  else if (kind == FIN_QKV) hipLaunchKernelGGL((finish_qkv_kernel<S, SPL>), dim3(blocks), dim3(threads), 0, st, f);
+  else hipLaunchKernelGGL((finish_kv_kernel<S, SPL>), dim3(blocks), dim3(threads), 0, st, f);
+}
+
 template <typename S>
 static hipError_t launch_finish_s(FinishKind kind, const FinishArgs& f, hipStream_t st) {
-  const int pair_blocks = (int)(((size_t)f.M * (f.N / 2) + 255) / 256);
-  switch (kind) {
-    case FIN_ROWTILE:
-      hipLaunchKernelGGL(finish_rowtile_kernel<S>, dim3(f.N / 16, (f.M + 15) / 16), dim3(256), 0, st, f);
-      break;
-    case FIN_SWIGLU:
-      hipLaunchKernelGGL(finish_swiglu_kernel, dim3(pair_blocks), dim3(256), 0, st, f);
-      break;
-    case FIN_QKV:
-      hipLaunchKernelGGL(finish_qkv_kernel<S>, dim3(pair_blocks), dim3(256), 0, st, f);
-      break;
-    case FIN_KV:
-      hipLaunchKernelGGL(finish_kv_kernel<S>, dim3(pair_blocks), dim3(256), 0, st, f);
-      break;
-    default:
-      return hipErrorInvalidValue;
+  // 4 outputs (FIN_SWIGLU: of N/2 per row) or 4 rotation pairs per lane
+  // group; groups of 4 or 2 lanes, splitting the k-slices (KS a multiple of
+  // the group), when one lane per quad would leave compute units idle
+  const bool few = kind == FIN_ROWTILE ? (size_t)((f.N / 16 + 3) / 4) * ((f.M + 15) / 16) < (size_t)kCUs
+                                       : ((size_t)f.M * (f.N / 8) + 255) / 256 < (size_t)kCUs;
+  // (a lane takes two slices a round: a group only as wide as keeps both useful)
+  int spl = 1;
+  if (few) spl = f.KS % 4 == 0 && f.KS >= 8 ? 4 : (f.KS % 2 == 0 && f.KS >= 4 ? 2 : 1);
+  if (kind == FIN_ROWTILE) {
+    const dim3 grid((f.N / 16 + 4 / spl - 1) / (4 / spl), (f.M + 15) / 16);
+    if (spl == 4) hipLaunchKernelGGL((finish_rowtile_kernel<S, 4>), grid, dim3(256), 0, st, f);
+    else if (spl == 2) hipLaunchKernelGGL((finish_rowtile_kernel<S, 2>), grid, dim3(256), 0, st, f);
+    else hipLaunchKernelGGL((finish_rowtile_kernel<S, 1>), grid, dim3(256), 0, st, f);
+    return hipGetLastError();
   }
+  if (kind != FIN_SWIGLU && kind != FIN_QKV && kind != FIN_KV) return hipErrorInvalidValue;
+  // (a small grid goes out in one-wave workgroups: the dispatcher then spreads
+  // the waves evenly over the compute units, whose bandwidth bounds it)
+  const size_t quads = (size_t)f.M * (f.N / 8);
+  const int threads = few ? 64 : 256;
+  const int blocks = (int)((quads * spl + threads - 1) / threads);
+  if (spl == 4) launch_finish_spl<S, 4>(kind, f, blocks, threads, st);
+  else if (spl == 2) launch_finish_spl<S, 2>(kind, f, blocks, threads, st);
+  else launch_finish_spl<S, 1>(kind, f, blocks, threads, st);
   return hipGetLastError();
 }
 

@@ -125,6 +125,7 @@ hipError_t launch_finish(int storage, FinishKind kind, const FinishArgs& f, hipS
 constexpr int kAttnMaxBatch = 1024;
 // Keys of streaming a flattened-split attention workgroup's plan charges for
 // every segment it starts (positions on the weighted key axis).
+constexpr int kCUs = 256;  // compute units of the chip
 constexpr int kAttnPieceCost = 256;
 struct AttnArgs {
   const void* q_hi;  // bf16 hi/lo pair [B*Bs, Hq*D], already scaled by log2(e)/sqrt(D)

@@ -86,6 +86,15 @@ def test_many_ragged_sequences_flattened_attention():
     run_step(wl, seed=24, seqs=[0, 51, 159], poison=True)
 
 
+@pytest.mark.parametrize("storage", ["bf16", "f32"])
+def test_batch1_finishes_split_k_slices_over_lanes(storage):
+    # one sequence, hidden 1024: every product runs 4 or 8 k-slices over a grid
+    # smaller than the chip, so the finishes share each output quad among 4 lanes
+    # (the residual finish with the block conv included)
+    wl = gen.Workload("tiny-b1-split", 1024, 8, 2, 128, 2, 2048, 1024, 16, 2, 1, 40, 300, storage, conv_width=3)
+    run_step(wl, seed=25, poison=True)
+
+
 def test_host_checks_reject_bad_sizes():
     from block_diffusion_drafting_ctx_amd import Drafter, _abi
     from tests.gpu_cases import config_for
