@@ -43,6 +43,9 @@ def parse():
     ap.add_argument("--workload", default="qwen3-8b-shape-b1")
     ap.add_argument("--secondary", default="qwen3-8b-shape-b32-ragged",
                     help="comma-separated extra workloads reported under 'secondary' ('' for none)")
+    ap.add_argument("--prefill", default="qwen3-8b-shape-b1:4096:4096",
+                    help="WORKLOAD:ROWS:CHUNK -- also time prompt-scale fusion of ROWS prompt rows per sequence "
+                         "in chunks of CHUNK, reported under 'prefill' ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--stage", default="lmhead", help="kernel stage timed with HIP events for the roofline")
     ap.add_argument("--profile-stages", action="store_true", help="also time every stage (perturbs the step)")
@@ -235,6 +238,47 @@ def time_workload(wl, steps, warmup, stage, profile_stages=False, graph_pass=Tru
     return wb, ms, per_stage
 
 
+def time_prefill(wl, rows, chunk, steps, warmup):
+    """Prompt-scale fusion: `rows` prompt rows of every sequence fused with
+    commit in chunks of `chunk` rows (how a caller fills the draft cache from
+    the target's prompt pass).  Returns ms per prompt and its algorithmic flops."""
+    import torch
+    from block_diffusion_drafting_ctx_amd import Drafter, make_config
+    from harness import gen
+
+    B = wl.batch
+    w = gen.draft_weights(wl, 1, "cuda")
+    max_ctx = ((rows + 2 * (wl.block + 1) + 63) // 64) * 64
+    cfg = make_config(wl.hidden, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.n_layers, wl.ffn, wl.vocab,
+                      wl.block, wl.n_target_layers, B, max_ctx, chunk, wl.conv_width, wl.storage,
+                      wl.rms_eps, wl.rope_theta)
+    dr = Drafter(cfg, w, "cuda")
+    hidden = gen.target_hidden(wl, B, rows, 3, "cuda")
+    parts = [[h[:, r0:min(rows, r0 + chunk)].contiguous() for h in hidden] for r0 in range(0, rows, chunk)]
+    del hidden
+
+    def prompt():
+        dr.ctx_len.zero_()
+        for p in parts:
+            dr.fuse_ctx(p, commit=True)
+
+    for _ in range(warmup):
+        prompt()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        prompt()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    assert dr.check() == 0 and dr.ctx_len.cpu().tolist() == [rows] * B
+    H, Nk = wl.hidden, wl.n_kv_heads * wl.head_dim
+    flops = 2.0 * B * rows * H * (wl.n_target_layers * H + wl.n_layers * 2 * Nk)
+    dr.close()
+    return ms, flops
+
+
 def cpu_baseline(wb):
     """The oracle, as it stands, on one full step of the workload's first sequence."""
     import threadpoolctl
@@ -326,6 +370,18 @@ def main():
         wb = wb2
     if sec:
         out["secondary"] = sec
+    if args.prefill:
+        pname, prows, pchunk = args.prefill.split(":")
+        wl3 = gen.WORKLOADS[pname]
+        del wb
+        torch.cuda.empty_cache()
+        pms, pfl = time_prefill(wl3, int(prows), int(pchunk), max(3, args.steps // 10), 2)
+        out["prefill"] = {"workload": f"{pname}: {wl3.batch} x {int(prows)} prompt rows fused in chunks of {pchunk}",
+                          "prompt_rows_per_s": round(wl3.batch * int(prows) / (pms * 1e-3), 1),
+                          "ms_per_prompt": round(pms, 4),
+                          "mfma_frac": round(pfl / (pms * 1e-3) / (BF16_PEAK_TFLOPS * 1e12), 4)}
+        torch.cuda.empty_cache()
+        wb = None
     if args.copy_calibration_mib:
         n = args.copy_calibration_mib << 20
         src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
@@ -336,7 +392,7 @@ def main():
         out["copy_calibration_bytes"] = n
         del src, dst
     if not args.no_cpu_baseline:
-        wb_c = wb if wb.wl.name == wl.name else None
+        wb_c = wb if wb is not None and wb.wl.name == wl.name else None
         if wb_c is None:
             del wb
             torch.cuda.empty_cache()
