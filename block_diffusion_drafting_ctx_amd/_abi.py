@@ -24,7 +24,8 @@ STAGES = ["fuse_fc", "ctx_kv", "verify", "embed", "qkv", "attn", "oproj", "gateu
 STAGE = {n: i for i, n in enumerate(STAGES)}
 
 EXPORTED = [
-    "dflash_workspace_bytes", "dflash_create", "dflash_fuse_ctx", "dflash_verify", "dflash_draft_block",
+    "dflash_workspace_bytes", "dflash_create", "dflash_reload_weights", "dflash_fuse_ctx", "dflash_verify",
+    "dflash_draft_block",
     "dflash_check", "dflash_clear_errors", "dflash_stats", "dflash_stage_timing", "dflash_stage_time",
     "dflash_destroy", "dflash_last_error", "dflash_version",
 ]
@@ -67,6 +68,7 @@ def lib():
             "dflash_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(Config)]),
             "dflash_create": (i32, [ctypes.POINTER(Config), ctypes.POINTER(Weights), _PP, _PP, vp, vp,
                                     ctypes.c_size_t, ctypes.POINTER(vp)]),
+            "dflash_reload_weights": (i32, [vp, vp]),
             "dflash_fuse_ctx": (i32, [vp, i32, _PP, i32, i32, vp, vp]),
             "dflash_verify": (i32, [vp, i32, vp, vp, i32, i32, vp, vp, vp, vp]),
             "dflash_draft_block": (i32, [vp, i32, vp, vp, vp, vp, vp]),
@@ -259,6 +261,10 @@ def dflash_check(ctx: Context, stream=None) -> int:
     if st not in (DFLASH_OK, DFLASH_EDEVICE):
         _check(st)
     return int(bits.value)
+
+
+def dflash_reload_weights(ctx: Context, stream=None) -> None:
+    _check(lib().dflash_reload_weights(ctx.handle, _stream(stream)))
 
 
 def dflash_clear_errors(ctx: Context, stream=None) -> None:

@@ -154,6 +154,8 @@ struct WsLayout {
   size_t err, stats;
   size_t x, ssq, rinv, y, xs_hi, xs_lo, q_hi, q_lo, kb, vb, o_hi, o_lo, act_hi, act_lo, part, lm_best, ver_best,
       part_o, part_ml, rope;
+  // tiled bf16 copies of the projection matrices, one per product
+  size_t wt_fc, wt_kv, wt_lm, wt_qkv[kMaxSeg / 2], wt_o[kMaxSeg / 2], wt_gu[kMaxSeg / 2], wt_down[kMaxSeg / 2];
   size_t total;
   int md, mf, mmax, ssq_parts, ver_chunks, rope_rows;
 };
@@ -208,6 +210,15 @@ WsLayout layout(const dflash_config& c) {
   // RoPE positions reach max_ctx + rows per sequence - 1 (block rows, or fused rows)
   L.rope_rows = c.max_ctx + std::max(c.block, c.max_fuse_rows);
   L.rope = take((size_t)L.rope_rows * (D / 2) * 8);
+  L.wt_fc = take(H * H * c.n_target_layers * 2);
+  L.wt_kv = take((size_t)2 * c.n_layers * Nk * H * 2);
+  L.wt_lm = take((size_t)c.vocab * H * 2);
+  for (int l = 0; l < c.n_layers; ++l) {
+    L.wt_qkv[l] = take((size_t)(Nq + 2 * Nk) * H * 2);
+    L.wt_o[l] = take(H * Nq * 2);
+    L.wt_gu[l] = take(2 * F * H * 2);
+    L.wt_down[l] = take(H * F * 2);
+  }
   L.total = off;
   return L;
 }
@@ -269,16 +280,31 @@ dflash_status hip_status(hipError_t e, const char* what) {
   return fail(DFLASH_EHIP, std::string(what) + ": " + hipGetErrorString(e));
 }
 
-void set_segments(GemmArgs& a, std::initializer_list<std::pair<const void*, int>> segs) {
-  a.nseg = 0;
-  int start = 0;
-  for (auto& sg : segs) {
-    a.seg_ptr[a.nseg] = sg.first;
-    a.seg_start[a.nseg] = start;
-    start += sg.second;
-    ++a.nseg;
+// Tiled copies of every projection matrix (the products read only these):
+// the segments of a product are laid out tile after tile in its N order.
+dflash_status tile_weights(dflash_ctx* c, hipStream_t s) {
+  const dflash_config& cf = c->cfg;
+  const WsLayout& L = c->L;
+  const int H = cf.hidden, F = cf.ffn, Nq = cf.n_q_heads * cf.head_dim, Nk = cf.n_kv_heads * cf.head_dim;
+  const int st = c->storage();
+  hipError_t e = hipSuccess;
+  auto tile = [&](const void* src, int rows, int K, size_t dst, int row0) {
+    if (e == hipSuccess) e = launch_tile_weights(st, src, rows, K, c->ws + dst, row0 / 16, s);
+  };
+  tile(c->w_fc, H, H * cf.n_target_layers, L.wt_fc, 0);
+  tile(c->w_lm, cf.vocab, H, L.wt_lm, 0);
+  for (int l = 0; l < cf.n_layers; ++l) {
+    tile(c->w_k[l], Nk, H, L.wt_kv, 2 * l * Nk);  // context K^l, V^l: segments 2l, 2l + 1
+    tile(c->w_v[l], Nk, H, L.wt_kv, (2 * l + 1) * Nk);
+    tile(c->w_q[l], Nq, H, L.wt_qkv[l], 0);
+    tile(c->w_k[l], Nk, H, L.wt_qkv[l], Nq);
+    tile(c->w_v[l], Nk, H, L.wt_qkv[l], Nq + Nk);
+    tile(c->w_o[l], H, Nq, L.wt_o[l], 0);
+    tile(c->w_gate[l], F, H, L.wt_gu[l], 0);
+    tile(c->w_up[l], F, H, L.wt_gu[l], F);
+    tile(c->w_down[l], H, F, L.wt_down[l], 0);
   }
-  a.seg_start[a.nseg] = start;
+  return hip_status(e, "weight tiling");
 }
 
 // Main kernel of one product into the partial-tile buffer, then its finish kernel.
@@ -368,13 +394,25 @@ dflash_status dflash_create(const dflash_config* cfg, const dflash_weights* w, v
   hipError_t e = hipMemset(workspace, 0, L.total);
   if (e == hipSuccess)
     e = launch_rope_table(c->at<float2>(L.rope), L.rope_rows, cfg->head_dim, cfg->rope_theta, nullptr);
-  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e == hipSuccess) {
+    if (const dflash_status ts = tile_weights(c, nullptr)) {
+      delete c;
+      return ts;
+    }
+    e = hipDeviceSynchronize();
+  }
   if (e != hipSuccess) {
     delete c;
     return hip_status(e, "workspace clear");
   }
   *out = c;
   return DFLASH_OK;
+}
+
+dflash_status dflash_reload_weights(dflash_ctx* c, void* stream) {
+  g_last_error.clear();
+  if (!c) return fail(DFLASH_EINVAL, "null context");
+  return tile_weights(c, static_cast<hipStream_t>(stream));
 }
 
 dflash_status dflash_fuse_ctx(dflash_ctx* c, int32_t batch, const void* const* hidden, int32_t t_new,
@@ -396,7 +434,7 @@ dflash_status dflash_fuse_ctx(dflash_ctx* c, int32_t batch, const void* const* h
     StageScope sc(c, DFLASH_STAGE_FUSE_FC, s);
     GemmArgs a{};
     GemmLaunch l{};
-    set_segments(a, {{c->w_fc, H}});
+    a.wt = c->at<void>(L.wt_fc);
     for (int j = 0; j < cf.n_target_layers; ++j) a.src[j] = hidden[j];
     a.n_src = cf.n_target_layers;
     a.src_width = H;
@@ -417,16 +455,13 @@ dflash_status dflash_fuse_ctx(dflash_ctx* c, int32_t batch, const void* const* h
     GemmArgs a{};
     GemmLaunch l{};
     FinishArgs f{};
-    a.nseg = 0;
+    a.wt = c->at<void>(L.wt_kv);
     for (int l2 = 0; l2 < cf.n_layers; ++l2) {
       for (int kv = 0; kv < 2; ++kv) {
-        a.seg_ptr[a.nseg] = kv ? c->w_v[l2] : c->w_k[l2];
-        f.kv_cache[a.nseg] = kv ? c->kv_v[l2] : c->kv_k[l2];
-        a.seg_start[a.nseg++] = nkv;
+        f.kv_cache[2 * l2 + kv] = kv ? c->kv_v[l2] : c->kv_k[l2];
         nkv += cf.n_kv_heads * D;
       }
     }
-    a.seg_start[a.nseg] = nkv;
     a.a_hi = c->at<void>(L.xs_hi);
     a.lda = H;
     a.ssq_in = c->at<float>(L.ssq);
@@ -538,7 +573,7 @@ dflash_status dflash_draft_block(dflash_ctx* c, int32_t batch, const int32_t* bl
       StageScope sc(c, DFLASH_STAGE_QKV, s);
       GemmArgs a{};
       GemmLaunch gl{};
-      set_segments(a, {{c->w_q[l], Nq}, {c->w_k[l], Nk}, {c->w_v[l], Nk}});
+      a.wt = c->at<void>(L.wt_qkv[l]);
       a.a_hi = xs_hi;
       a.a_lo = xs_lo;
       a.lda = H;
@@ -586,7 +621,7 @@ dflash_status dflash_draft_block(dflash_ctx* c, int32_t batch, const int32_t* bl
       StageScope sc(c, DFLASH_STAGE_OPROJ, s);
       GemmArgs a{};
       GemmLaunch gl{};
-      set_segments(a, {{c->w_o[l], H}});
+      a.wt = c->at<void>(L.wt_o[l]);
       a.a_hi = c->at<void>(L.o_hi);
       a.a_lo = c->at<void>(L.o_lo);
       a.lda = Nq;
@@ -607,7 +642,7 @@ dflash_status dflash_draft_block(dflash_ctx* c, int32_t batch, const int32_t* bl
       StageScope sc(c, DFLASH_STAGE_GATEUP, s);
       GemmArgs a{};
       GemmLaunch gl{};
-      set_segments(a, {{c->w_gate[l], F}, {c->w_up[l], F}});
+      a.wt = c->at<void>(L.wt_gu[l]);
       a.a_hi = xs_hi;
       a.a_lo = mlp_lo ? xs_lo : nullptr;
       a.lda = H;
@@ -622,7 +657,7 @@ dflash_status dflash_draft_block(dflash_ctx* c, int32_t batch, const int32_t* bl
       StageScope sc(c, DFLASH_STAGE_DOWN, s);
       GemmArgs a{};
       GemmLaunch gl{};
-      set_segments(a, {{c->w_down[l], H}});
+      a.wt = c->at<void>(L.wt_down[l]);
       a.a_hi = c->at<void>(L.act_hi);
       a.a_lo = mlp_lo ? c->at<void>(L.act_lo) : nullptr;
       a.lda = F;
@@ -646,7 +681,7 @@ dflash_status dflash_draft_block(dflash_ctx* c, int32_t batch, const int32_t* bl
     StageScope sc(c, DFLASH_STAGE_LMHEAD, s);
     GemmArgs a{};
     GemmLaunch gl{};
-    set_segments(a, {{c->w_lm, cf.vocab}});
+    a.wt = c->at<void>(L.wt_lm);
     a.a_hi = xs_hi;
     a.lda = H;
     a.best_part = c->at<uint64_t>(L.lm_best);

@@ -34,11 +34,9 @@ constexpr size_t kGemmAsMaxLds = 150 * 1024;    // whole-K activation (LM head; 
 
 struct GemmArgs {
   int M, N, K;
-  // W row segments: global row n in [seg_start[s], seg_start[s+1]) is row
-  // n - seg_start[s] of matrix seg_ptr[s] (all with row length K).
-  int nseg;
-  const void* seg_ptr[kMaxSeg];
-  int seg_start[kMaxSeg + 1];
+  // W [N, K] of the product in tiled bf16 (launch_tile_weights): the block of
+  // rows 16t.. and columns 32s.. is 1 KB at ((t * K/32 + s) * 64) * 8 elements.
+  const void* wt;
   // activations
   const void* a_hi;
   const void* a_lo;
@@ -75,6 +73,13 @@ struct GemmLaunch {
 };
 
 hipError_t launch_gemm(int storage, const GemmArgs& a, const GemmLaunch& l, hipStream_t stream);
+// Weight tiling: rows [0, rows) of the row-major [rows, K] matrix src (storage
+// type) become tiles tile0 .. tile0 + rows/16 - 1 of dst, a tiled bf16 matrix
+// of row length K: the 16 x 32 block (tile t, k-step s) is stored as the 64
+// matrix-core lanes' 16-byte fragments in lane order, lane l holding row
+// 16t + (l & 15), columns 32s + 8(l >> 4) .. + 7.  rows % 16 == 0, K % 32 == 0.
+hipError_t launch_tile_weights(int storage, const void* src, int rows, int K, void* dst, int tile0,
+                               hipStream_t stream);
 // k-slice length gemm_as uses for (M, K) over ntiles 16-row tiles on cus
 // compute units (0: gemm_as does not fit).
 int gemm_as_ksl(int M, int K, bool lo, bool argmax, int ntiles, int cus);

@@ -34,6 +34,9 @@ class Drafter:
         ws = self.workspace[off:off + nbytes]
         self.ctx = _abi.dflash_create(cfg, weights, self.kv_k, self.kv_v, self.ctx_len, ws)
 
+    def reload_weights(self, stream=None):
+        _abi.dflash_reload_weights(self.ctx, stream)
+
     def fuse_ctx(self, hidden, commit: bool, feat_dbg=None, stream=None):
         _abi.dflash_fuse_ctx(self.ctx, hidden, commit, feat_dbg, stream)
 

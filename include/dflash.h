@@ -150,12 +150,23 @@ size_t dflash_workspace_bytes(const dflash_config* cfg);
  *     calls (stream ordered).
  *  workspace: device buffer of dflash_workspace_bytes(cfg) bytes.  It is
  *     cleared here with a synchronous memset and receives the RoPE cos/sin
- *     table (create is not capturable); it belongs to the context until
- *     dflash_destroy and must not be written by the caller.
+ *     table and a bf16 copy of every projection matrix (w_fc, w_q/k/v/o,
+ *     w_gate/up/down, w_lm) in the matrix cores' fragment order: the products
+ *     stream that copy, one contiguous 1 KB block per 16 rows x 32 columns,
+ *     rather than 16 separate row pieces (create is not capturable); it
+ *     belongs to the context until dflash_destroy and must not be written by
+ *     the caller.  The copy takes the values the pointers hold at create:
+ *     after changing those matrices, call dflash_reload_weights.
  * On success *out receives the context. */
 dflash_status dflash_create(const dflash_config* cfg, const dflash_weights* w,
                             void* const* kv_k, void* const* kv_v, int32_t* ctx_len,
                             void* workspace, size_t workspace_bytes, dflash_ctx** out);
+
+/* Re-copy the projection matrices from the pointers given at create into the
+ * workspace's tiled copy (stream ordered, capturable; for a caller that has
+ * changed the weights in place).  Later calls on the stream use the new
+ * values. */
+dflash_status dflash_reload_weights(dflash_ctx* ctx, void* stream);
 
 /* Fuse target hidden states into the context feature and inject it into
  * every layer's K/V.  [P1] "Block-diffusion architecture", feature-injection

@@ -95,6 +95,46 @@ def test_batch1_finishes_split_k_slices_over_lanes(storage):
     run_step(wl, seed=25, poison=True)
 
 
+def test_reload_weights_after_in_place_change():
+    # The products stream the tiled copy made at create.  After the caller
+    # changes matrices in place the old copy stays in use until
+    # dflash_reload_weights; then the draft equals that of a context created
+    # on the changed weights, bit for bit.
+    from block_diffusion_drafting_ctx_amd import Drafter
+    from tests.gpu_cases import config_for
+
+    wl = gen.Workload("tiny-reload", 256, 4, 2, 64, 2, 512, 1024, 8, 3, 2, 10, 20, "bf16")
+    w = gen.draft_weights(wl, 41, "cuda")
+    ctx_lens = gen.context_lengths(wl, 42, 2)
+    ks, vs = gen.context_kv(wl, ctx_lens, 42, "cuda")
+    ids = torch.from_numpy(gen.block_ids(wl, 2, 43)).cuda()
+    cfg = config_for(wl, 2)
+
+    def draft(dr):
+        dr.ctx_len.copy_(torch.from_numpy(ctx_lens).cuda())
+        out = torch.zeros(2, wl.block, dtype=torch.int32, device="cuda")
+        lg = torch.empty(2, wl.block, wl.vocab, dtype=torch.float32, device="cuda")
+        dr.draft_block(ids, out, lg)
+        torch.cuda.synchronize()
+        assert dr.check() == 0
+        return out.clone(), lg.clone()
+
+    dr = Drafter(cfg, w, "cuda", [k.clone() for k in ks], [v.clone() for v in vs])
+    before = draft(dr)
+    w["w_lm"].mul_(-1.0)
+    w["layers"][1]["w_up"].mul_(0.5)
+    stale = draft(dr)
+    dr.reload_weights()
+    after = draft(dr)
+    fresh = Drafter(cfg, w, "cuda", [k.clone() for k in ks], [v.clone() for v in vs])
+    ref = draft(fresh)
+    assert torch.equal(stale[1], before[1])
+    assert torch.equal(after[1], ref[1]) and torch.equal(after[0], ref[0])
+    assert not torch.equal(after[1], before[1])
+    dr.close()
+    fresh.close()
+
+
 def test_host_checks_reject_bad_sizes():
     from block_diffusion_drafting_ctx_amd import Drafter, _abi
     from tests.gpu_cases import config_for
