@@ -116,21 +116,39 @@ bool plan_gemm(int storage, int src, int out, bool lo, int M, int N, int K, Gemm
   // per compute unit): a second, partly filled round would cost a whole
   // workgroup's time, and every k-slice adds a partial-output round trip
   const int MF = M <= 64 ? 1 : (M <= 128 ? 2 : 4);
-  const int BN = 32 * gemm_mt_nf(MF);
   const int nbm = (M + 64 * MF - 1) / (64 * MF);
-  const int nbn = (N + BN - 1) / BN;
   // (every k-slice keeps an even number of 32-deep stages: the kernel's
   // pipeline takes them in pairs)
-  int KS = 1;
-  if (out == OUT_PARTIAL)
-    while (nbn * nbm * 2 * KS <= kMtTargetWgs && (K / 32) % (4 * KS) == 0 && K / (2 * KS) >= 256) KS *= 2;
+  auto split = [&](int nbn) {
+    int KS = 1;
+    if (out == OUT_PARTIAL)
+      while (nbn * nbm * 2 * KS <= kMtTargetWgs && (K / 32) % (4 * KS) == 0 && K / (2 * KS) >= 256) KS *= 2;
+    return KS;
+  };
+  // share of the compute units the grid keeps busy over its dispatch rounds
+  auto fill = [&](int wgs) { return (double)wgs / (double)(((wgs + kCUs - 1) / kCUs) * kCUs); };
+  int NF = MF >= 4 ? 8 : 4;
+  int nbn = (N + 32 * NF - 1) / (32 * NF);
+  int KS = split(nbn);
+  if (MF >= 4 && out == OUT_PARTIAL) {
+    // 192-column blocks when they fill the chip clearly better (gate/up at
+    // 512 rows: 256 workgroups instead of 192); their wave tile reads ~11%
+    // more LDS per matrix-core op
+    const int nbn6 = (N + 191) / 192, KS6 = split(nbn6);
+    if (fill(nbn6 * nbm * KS6) > fill(nbn * nbm * KS) + 0.1) {
+      NF = 6;
+      nbn = nbn6;
+      KS = KS6;
+    }
+  }
   const int units = nbn * KS;
   l->kind = GEMM_MT;
   l->MR = MF;
+  l->NF = NF;
   l->KS = KS;
   l->grid = dim3(((units + 7) / 8) * 8 * nbm);
   l->threads = 512;
-  l->lds = gemm_mt_lds_bytes(MF, lo_eff);
+  l->lds = gemm_mt_lds_bytes(MF, NF, lo_eff);
   l->argmax_tiles = nbn;
   a->nbm = nbm;
   a->nbn = nbn;

@@ -290,28 +290,25 @@ struct MtShape {
   static constexpr int WPT = (BN * 4 + 511) / 512;  // weight pieces per thread
 };
 
-template <int MF, int SRC, bool LO>
+template <int MF, int NF, int SRC, bool LO>
 struct MtRegs {
-  Raw8 w[MtShape<MF, (MF >= 4 ? 8 : 4)>::WPT];
-  Raw8 a[MtShape<MF, 4>::APT];
-  Raw8 l[LO && SRC == SRC_SPLIT ? MtShape<MF, 4>::APT : 1];
+  Raw8 w[MtShape<MF, NF>::WPT];
+  Raw8 a[MtShape<MF, NF>::APT];
+  Raw8 l[LO && SRC == SRC_SPLIT ? MtShape<MF, NF>::APT : 1];
 };
 
-int gemm_mt_nf(int MF) { return MF >= 4 ? 8 : 4; }
-
-size_t gemm_mt_lds_bytes(int MF, bool lo) {
-  const int BM = 64 * MF, BN = 32 * gemm_mt_nf(MF);
+size_t gemm_mt_lds_bytes(int MF, int NF, bool lo) {
+  const int BM = 64 * MF, BN = 32 * NF;
   return (size_t)2 * ((lo ? 2 : 1) * BM + BN) * (32 + 16) * 2;
 }
 
-template <typename S, int MF, int SRC, bool LO, int OUT>
+template <typename S, int MF, int NF, int SRC, bool LO, int OUT>
 __global__ void __launch_bounds__(512) gemm_mt_kernel(const GemmArgs g) {
-  constexpr int NF = MF >= 4 ? 8 : 4;
   using Sh = MtShape<MF, NF>;
   constexpr int BM = Sh::BM, BN = Sh::BN, BK = Sh::BK, LDK = Sh::LDK, APT = Sh::APT, WPT = Sh::WPT;
   constexpr int NA = LO ? 2 : 1;
   constexpr int STAGE = (NA * BM + BN) * LDK;
-  using Regs = MtRegs<MF, SRC, LO>;
+  using Regs = MtRegs<MF, NF, SRC, LO>;
   extern __shared__ __align__(16) bf16_t sm[];  // [2][NA*BM + BN][LDK]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave & 3, wn = wave >> 2;
@@ -328,14 +325,18 @@ __global__ void __launch_bounds__(512) gemm_mt_kernel(const GemmArgs g) {
   // ---- per-thread load sources (fixed rows, k advances).  Weight piece q =
   // tid + 512 i is lane q & 63 of tile q >> 6 of the block: 64 threads read
   // one tile's 1 KB k-step block; past N the last tile is re-read (unused).
+  // When BN * 4 is not a multiple of 512 (NF = 6) a thread with no piece i
+  // repeats its piece 0 (same source, same LDS slot), so the loads stay
+  // unconditional.
+  auto wq = [&](int i) { return tid + i * 512 < BN * 4 ? tid + i * 512 : tid; };
   const bf16_t* wsrc[WPT];
   const int nks = g.K >> 5, ntl = g.N >> 4;
 #pragma unroll
   for (int i = 0; i < WPT; ++i) {
-    const int q = tid + i * 512, t = min(n0 / 16 + (q >> 6), ntl - 1);
+    const int q = wq(i), t = min(n0 / 16 + (q >> 6), ntl - 1);
     wsrc[i] = reinterpret_cast<const bf16_t*>(g.wt) + (((size_t)t * nks + kbeg / 32) * 64 + (q & 63)) * 8;
   }
-  auto wrow = [&](int i) { return (((tid + i * 512) >> 6) << 4) + (tid & 15); };  // block row of weight piece i
+  auto wrow = [&](int i) { return ((wq(i) >> 6) << 4) + (tid & 15); };  // block row of weight piece i
   const int wcol = ((tid >> 4) & 3) * 8;                                             // and its column in the stage
   auto prow = [&](int i) { return (tid + i * 512) >> 2; };  // row of a thread's i-th activation piece
   const int pc = (tid & 3) * 8;                             // its column within the stage
@@ -985,9 +986,9 @@ static hipError_t launch_as(const GemmArgs& a, const GemmLaunch& l, hipStream_t 
   hipLaunchKernelGGL(k, l.grid, dim3(l.threads), l.lds, st, a);
   return hipGetLastError();
 }
-template <typename S, int MF, int SRC, bool LO, int OUT>
+template <typename S, int MF, int NF, int SRC, bool LO, int OUT>
 static hipError_t launch_mt(const GemmArgs& a, const GemmLaunch& l, hipStream_t st) {
-  auto k = gemm_mt_kernel<S, MF, SRC, LO, OUT>;
+  auto k = gemm_mt_kernel<S, MF, NF, SRC, LO, OUT>;
   allow_lds(k, l.lds);
   hipLaunchKernelGGL(k, l.grid, dim3(l.threads), l.lds, st, a);
   return hipGetLastError();
@@ -1001,9 +1002,12 @@ static hipError_t dispatch_mr(const GemmArgs& a, const GemmLaunch& l, hipStream_
     return hipErrorInvalidValue;
   }
   switch (l.MR) {  // GEMM_MT: MR = MF
-    case 1: return launch_mt<S, 1, SRC, LO, OUT>(a, l, st);
-    case 2: return launch_mt<S, 2, SRC, LO, OUT>(a, l, st);
-    case 4: return launch_mt<S, 4, SRC, LO, OUT>(a, l, st);
+    case 1: return launch_mt<S, 1, 4, SRC, LO, OUT>(a, l, st);
+    case 2: return launch_mt<S, 2, 4, SRC, LO, OUT>(a, l, st);
+    case 4:
+      if constexpr (OUT == OUT_PARTIAL)
+        if (l.NF == 6) return launch_mt<S, 4, 6, SRC, LO, OUT>(a, l, st);
+      return launch_mt<S, 4, 8, SRC, LO, OUT>(a, l, st);
   }
   return hipErrorInvalidValue;
 }

@@ -65,6 +65,7 @@ struct GemmLaunch {
   int kind;   // GemmKind
   int src, out, lo;
   int MR;
+  int NF;  // GEMM_MT: 16-column fragments per wave (block width 32 * NF)
   dim3 grid;
   int threads;
   size_t lds;
@@ -84,10 +85,10 @@ hipError_t launch_tile_weights(int storage, const void* src, int rows, int K, vo
 // compute units (0: gemm_as does not fit).
 int gemm_as_ksl(int M, int K, bool lo, bool argmax, int ntiles, int cus);
 size_t gemm_as_lds(int M, int ksl, bool lo);
-// gemm_mt block: BM = 64 * MF rows by BN = 32 * gemm_mt_nf(MF) columns;
-// LDS bytes of its stage ring (lo: hi/lo activation pair).
-int gemm_mt_nf(int MF);
-size_t gemm_mt_lds_bytes(int MF, bool lo);
+// gemm_mt block: BM = 64 * MF rows by BN = 32 * NF columns (NF = 4 for
+// MF < 4; 8, or 6 for split-K outputs, at MF = 4); LDS bytes of its stage
+// ring (lo: hi/lo activation pair).
+size_t gemm_mt_lds_bytes(int MF, int NF, bool lo);
 // ids[m] = index of the largest key over part[t][m], t < ntiles.
 hipError_t launch_argmax_reduce(const uint64_t* part, int ntiles, int ld, int M, int32_t* ids, hipStream_t stream);
 
