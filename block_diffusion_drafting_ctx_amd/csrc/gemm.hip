@@ -1,9 +1,10 @@
 // Weight-streaming matrix-core GEMMs for the skinny products of the drafting
 // hot path, Y[M, N] = A[M, K] . W[N, K]^T, and the kernels that finish them.
 //
-// The N axis is the concatenation of one or more weight matrices ("segments",
-// e.g. W_q | W_k | W_v, or W_gate | W_up, or every layer's W_k | W_v) and is
-// cut into tiles of 16 weight rows.  A main kernel produces fp32 partial
+// The N axis is the concatenation of one or more weight matrices (e.g. W_q |
+// W_k | W_v, or W_gate | W_up, or every layer's W_k | W_v), read from the
+// context's tiled bf16 copy of them (launch_tile_weights), and is cut into
+// tiles of 16 weight rows.  A main kernel produces fp32 partial
 // tiles part[k-slice][tile][m][16]; a finish kernel sums the k-slices in a
 // fixed order (deterministic) and applies the epilogue of the stage.  Only
 // the LM head folds its epilogue (a running argmax) into the main kernel.
@@ -30,13 +31,6 @@
 namespace dfl {
 
 // ------------------------------------------------------------------ helpers
-// v -> (hi, lo) bf16 pair with v ~= hi + lo (lo may be null: hi only).
-__device__ __forceinline__ void split_store(bf16_t* hi, bf16_t* lo, size_t idx, float v) {
-  const bf16_t h = f32_to_bf16_bits(v);
-  hi[idx] = h;
-  if (lo) lo[idx] = f32_to_bf16_bits(v - bf16_bits_to_f32(h));
-}
-
 // Tiled-weight pointer of lane `lane` of 16-row tile t at column k (k a
 // multiple of 32): the lane's 8 columns of row 16t + (lane & 15); the next
 // 32 columns of the tile follow 512 elements on.
@@ -109,8 +103,7 @@ __global__ void __launch_bounds__(512) gemm_as_kernel(const GemmArgs g) {
   extern __shared__ __align__(16) bf16_t sa[];  // [LO ? 2 : 1][MT][ksl + 8]
   const int LDSW = g.ksl + 8;
   const int tid = threadIdx.x, lane = tid & 63, nw = blockDim.x >> 6;
-  // wave-uniform: keeps the tile -> weight-segment lookup on the scalar unit
-  // (a vector load of the segment table would drain the weight stream)
+  // wave-uniform: keeps the tile addressing on the scalar unit
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ks = blockIdx.y, k0 = ks * g.ksl;
   const int ntiles = g.N >> 4;

@@ -17,8 +17,8 @@ constexpr uint32_t kErrVerifyOverflow = 1u << 2;  // ctx_len + n_d + 1 > max_ctx
 constexpr uint32_t kErrDraftOverflow = 1u << 3;   // ctx_len + block > max_ctx in the draft
 
 // ------------------------------------------------------------------ GEMM
-// Y[M, N] = A[M, K] . W[N, K]^T.  The N axis concatenates weight segments and
-// is cut into 16-row tiles.  The main kernel writes fp32 partial tiles
+// Y[M, N] = A[M, K] . W[N, K]^T.  The N axis concatenates weight matrices
+// (one tiled bf16 buffer per product) and is cut into 16-row tiles.  The main kernel writes fp32 partial tiles
 // part[k-slice][tile][m][16] (OUT_PARTIAL) that a finish kernel sums and
 // post-processes, or per-tile argmax keys (OUT_ARGMAX, one k-slice).
 enum SrcKind {
@@ -28,7 +28,7 @@ enum SrcKind {
 enum OutKind { OUT_PARTIAL = 0, OUT_ARGMAX = 1 };
 enum GemmKind { GEMM_AS = 0, GEMM_MT = 1 };
 
-constexpr int kMaxSeg = 16;
+constexpr int kMaxSeg = 16;  // context K/V caches one product writes (2 per layer)
 constexpr size_t kGemmAsSliceLds = 100 * 1024;  // split-K activation slice of a gemm_as workgroup
 constexpr size_t kGemmAsMaxLds = 150 * 1024;    // whole-K activation (LM head; one workgroup per CU)
 
