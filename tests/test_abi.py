@@ -75,7 +75,17 @@ def test_calls_reject_null_context(lib):
     assert lib.dflash_fuse_ctx(None, 1, None, 1, 0, None, None) == _abi.DFLASH_EINVAL
     assert lib.dflash_verify(None, 1, None, None, 1, 1, None, None, None, None) == _abi.DFLASH_EINVAL
     assert lib.dflash_draft_block(None, 1, None, None, None, None, None) == _abi.DFLASH_EINVAL
+    assert lib.dflash_reload_weights(None, None) == _abi.DFLASH_EINVAL
     lib.dflash_destroy(None)
+
+
+def test_workspace_holds_the_tiled_weight_copy(lib):
+    # the bf16 copy of every projection matrix lives in the workspace: at the
+    # 8B shape that is W_fc + every layer's Q/K/V/O/gate/up/down + W_lm
+    H, F, V, L, T = 4096, 12288, 151936, 5, 5
+    Nq, Nk = 32 * 128, 8 * 128
+    weights = 2 * (H * T * H + V * H + L * ((Nq + 2 * Nk) * H + H * Nq + 2 * F * H + H * F) + L * 2 * Nk * H)
+    assert _abi.dflash_workspace_bytes(_cfg()) >= weights
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
