@@ -66,10 +66,12 @@ class StepResult:
 
 def run_step(wl: gen.Workload, seed: int, device="cuda", seqs: Optional[Sequence[int]] = None,
              prefill: bool = False, poison: bool = False, n_d: Optional[int] = None,
-             check_oracle: bool = True, accept: Optional[Sequence[int]] = None) -> StepResult:
+             check_oracle: bool = True, accept: Optional[Sequence[int]] = None,
+             max_batch: Optional[int] = None) -> StepResult:
     """Run one step on the library and compare with the oracle on `seqs`.
 
-    `accept` overrides the planted acceptance lengths (one per sequence)."""
+    `accept` overrides the planted acceptance lengths (one per sequence);
+    `max_batch` sizes the context for more sequences than the call passes."""
     from block_diffusion_drafting_ctx_amd import Drafter
 
     res = StepResult()
@@ -105,10 +107,20 @@ def run_step(wl: gen.Workload, seed: int, device="cuda", seqs: Optional[Sequence
             st = DraftState(k=[np64(t[seqs]) for t in ks], v=[np64(t[seqs]) for t in vs],
                             ctx_len=ctx_lens[seqs].astype(np.int64).copy())
 
-    cfg = config_for(wl, B, max(t_new, wl.ctx_hi if prefill else 0))
-    kv_dev = None if ks is None else ([t.to(device) for t in ks], [t.to(device) for t in vs])
+    cfg = config_for(wl, max_batch or B, max(t_new, wl.ctx_hi if prefill else 0))
+    mb = max_batch or B
+
+    def cache(t):  # [B, ...] -> the context's [max_batch, ...] layout (extra sequences zero)
+        t = t.to(device)
+        if mb == B:
+            return t
+        full = torch.zeros((mb,) + tuple(t.shape[1:]), dtype=t.dtype, device=device)
+        full[:B] = t
+        return full
+
+    kv_dev = None if ks is None else ([cache(t) for t in ks], [cache(t) for t in vs])
     dr = Drafter(cfg, w_dev, device, *(kv_dev or (None, None)))
-    dr.ctx_len.copy_(torch.from_numpy(ctx_lens))
+    dr.ctx_len[:B].copy_(torch.from_numpy(ctx_lens))
     M_f = B * t_new
     H = wl.hidden
     if prefill:

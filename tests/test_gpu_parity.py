@@ -30,6 +30,13 @@ def test_tiny_ragged_batch_bf16_multi_split():
     run_step(wl, seed=13, poison=True)
 
 
+def test_context_sized_for_more_sequences_than_the_call():
+    # a context created for 12 sequences driven with 5: workspace, partial
+    # buffers and the attention plan are laid out for the larger batch
+    wl = gen.Workload("tiny-ragged-under", 256, 4, 2, 64, 2, 512, 1024, 8, 3, 5, 0, 700, "bf16", accept_hi=8)
+    run_step(wl, seed=27, poison=True, max_batch=12)
+
+
 def test_tiny_conv_block16():
     wl = gen.Workload("tiny-conv", 256, 8, 2, 64, 2, 384, 2048, 16, 2, 3, 40, 300, "bf16", conv_width=3)
     run_step(wl, seed=14, poison=True)
