@@ -53,11 +53,15 @@ __global__ void __launch_bounds__(256) verify_argmax_kernel(const VerifyArgs a) 
 // bonus g_n, committed tokens, context-length advance (rollback of the rest)
 // and the step counters.
 __global__ void __launch_bounds__(64) verify_commit_kernel(const VerifyArgs a) {
-  __shared__ int s_g[65];
+  __shared__ int s_g[65], s_d[64];
   __shared__ int s_n;
   const int b = blockIdx.x, tid = threadIdx.x;
   const int R = a.n_d + 1;
+  const int32_t* d = a.draft + (size_t)b * a.draft_stride;
   for (int i = tid; i < R; i += 64) {
+    // the draft ids are loaded alongside the keys, so the comparison below
+    // runs from LDS instead of one dependent global load per accepted token
+    if (i < a.n_d) s_d[i] = d[i];
     const uint64_t* pr = a.part + ((size_t)b * R + i) * a.nchunks;
     uint64_t best = 0;
     for (int c = 0; c < a.nchunks; ++c) best = pr[c] > best ? pr[c] : best;
@@ -65,9 +69,8 @@ __global__ void __launch_bounds__(64) verify_commit_kernel(const VerifyArgs a) {
   }
   __syncthreads();
   if (tid == 0) {
-    const int32_t* d = a.draft + (size_t)b * a.draft_stride;
     int n = 0;
-    while (n < a.n_d && d[n] == s_g[n]) ++n;
+    while (n < a.n_d && s_d[n] == s_g[n]) ++n;
     s_n = n;
     a.n_accept[b] = n;
     a.bonus[b] = s_g[n];
