@@ -50,6 +50,11 @@ Parity status of each function (what pins it, in ``tests/test_oracle_*``):
 * ``argmax_lowest`` / ``greedy_verify`` -- pinned: ``numpy.argmax`` on finite
                             data, planted ties and NaNs, full / zero acceptance,
                             and the lossless invariant on a tiny random target.
+* ``sample_verify``      -- pinned: the emitted token's distribution,
+                            integrated over a grid of uniforms, equals the
+                            target's softmax (the lossless property); the
+                            low-temperature limit equals ``greedy_verify``;
+                            full acceptance draws the bonus by inverse CDF.
 * ``AcceptanceStats``    -- pinned: the pages' printed (rate, mean length)
                             pairs (``tests/golden/acceptance_stats.txt``).
 * real-model acceptance behaviour -- parity unpinned (needs trained weights).
@@ -72,6 +77,6 @@ from .draft import (  # noqa: F401
     fuse_ctx,
     draft_block,
 )
-from .verify import argmax_lowest, greedy_verify, verify_step, AcceptanceStats  # noqa: F401
+from .verify import argmax_lowest, greedy_verify, inverse_cdf, sample_verify, verify_step, AcceptanceStats  # noqa: F401
 from .tiny_target import TinyTarget  # noqa: F401
 from .spec_loop import greedy_generate, speculative_generate  # noqa: F401

@@ -57,6 +57,50 @@ def greedy_verify(logits: np.ndarray, draft: np.ndarray, n_d: int) -> Tuple[int,
     return n, g[n], g[: n + 1]
 
 
+def inverse_cdf(p: np.ndarray, u: float) -> int:
+    """Smallest index v with p[0] + ... + p[v] > u * sum(p) (u in [0, 1));
+    the last index holding mass when rounding leaves u * sum(p) at the top."""
+    c = np.cumsum(np.asarray(p, dtype=np.float64))
+    v = int(np.searchsorted(c, u * c[-1], side="right"))
+    if v >= len(c):
+        v = int(np.flatnonzero(np.asarray(p) > 0)[-1])
+    return v
+
+
+def sample_verify(logits: np.ndarray, draft: np.ndarray, n_d: int, temperature: float,
+                  uniforms: np.ndarray) -> Tuple[int, int, List[int]]:
+    """Verification when the target samples at temperature T > 0.
+
+    The pages measure this mode (a "thinking" setting that samples) but state
+    no rule; the reading here is the standard lossless speculative-sampling
+    rule for a drafter whose proposal is a single token (its distribution is
+    all on the drafted token): with p_i = softmax(logits[i] / T), draft d_i
+    is accepted when uniforms[i, 0] < p_i(d_i); at the first rejected row i
+    the emitted token is drawn from p_i with d_i removed (renormalised) by
+    the inverse CDF at uniforms[i, 1]; when every draft is accepted, the
+    bonus token is drawn from p_{n_d} at uniforms[n_d, 1].  Each emitted
+    token then has exactly the target's sampling distribution.
+
+    Returns (n, token, out): n accepted drafts, the drawn token, and the n + 1
+    committed tokens [d_0 .. d_{n-1}, token].
+    """
+    x = np.asarray(logits, dtype=np.float64) / float(temperature)
+    u = np.asarray(uniforms, dtype=np.float64)
+    for i in range(n_d):
+        p = np.exp(x[i] - np.max(x[i]))
+        p /= p.sum()
+        d = int(draft[i])
+        if u[i, 0] < p[d]:
+            continue
+        r = p.copy()
+        r[d] = 0.0
+        tok = inverse_cdf(r, u[i, 1])
+        return i, tok, [int(t) for t in draft[:i]] + [tok]
+    p = np.exp(x[n_d] - np.max(x[n_d]))
+    tok = inverse_cdf(p, u[n_d, 1])
+    return n_d, tok, [int(t) for t in draft[:n_d]] + [tok]
+
+
 @dataclass
 class AcceptanceStats:
     """Counters over verify steps, one step per sequence per verify call.

@@ -1,0 +1,58 @@
+"""Pins of the sampling-mode verification rule (oracle.sample_verify).
+
+Reading: the standard lossless speculative-sampling rule for a drafter that
+proposes single tokens.  The pins check what that rule must guarantee rather
+than retyping it: the emitted token's distribution is the target's softmax
+whatever the draft; the low-temperature limit is greedy verification.
+"""
+
+import numpy as np
+import pytest
+
+from oracle import greedy_verify, inverse_cdf, sample_verify
+
+
+def softmax(x, T):
+    z = np.asarray(x, dtype=np.float64) / T
+    e = np.exp(z - z.max())
+    return e / e.sum()
+
+
+@pytest.mark.parametrize("T", [0.5, 1.0, 2.0])
+@pytest.mark.parametrize("draft_tok", [0, 2, 4])
+def test_first_emitted_token_has_the_target_distribution(T, draft_tok):
+    # integrate the rule over a midpoint grid of (accept, sample) uniforms:
+    # P(first emitted token = v) must be softmax(x_0 / T)[v] for any draft
+    rng = np.random.default_rng(3)
+    logits = rng.normal(size=(2, 5)) * 1.5
+    G = 250
+    grid = (np.arange(G) + 0.5) / G
+    counts = np.zeros(5)
+    for ua in grid:
+        for us in grid:
+            u = np.array([[ua, us], [0.5, 0.5]])
+            _, _, out = sample_verify(logits, np.array([draft_tok]), 1, T, u)
+            counts[out[0]] += 1
+    np.testing.assert_allclose(counts / G**2, softmax(logits[0], T), atol=4.0 / G)
+
+
+def test_low_temperature_is_greedy_verification():
+    rng = np.random.default_rng(4)
+    logits = rng.normal(size=(5, 64)) * 3.0
+    g = [int(np.argmax(r)) for r in logits]
+    for draft in (np.array(g[:4]), np.array([g[0], g[1], (g[2] + 1) % 64, g[3]]), np.array([(g[0] + 7) % 64] * 4)):
+        u = rng.uniform(size=(5, 2)) * 0.98 + 0.01
+        assert sample_verify(logits, draft, 4, 1e-4, u) == greedy_verify(logits, draft, 4)
+
+
+def test_full_acceptance_draws_the_bonus_by_inverse_cdf():
+    rng = np.random.default_rng(5)
+    logits = rng.normal(size=(4, 32))
+    draft = np.array([3, 9, 17])
+    u = np.zeros((4, 2))
+    u[3, 1] = 0.637
+    n, tok, out = sample_verify(logits, draft, 3, 0.8, u)
+    p = softmax(logits[3], 0.8)
+    assert n == 3 and out == [3, 9, 17, tok]
+    assert tok == int(np.searchsorted(np.cumsum(p), 0.637))
+    assert inverse_cdf(p, 0.0) == int(np.flatnonzero(p > 0)[0])
