@@ -544,6 +544,43 @@ dflash_status dflash_verify(dflash_ctx* c, int32_t batch, const float* logits, c
   return hip_status(launch_verify(a, s), "verify launch");
 }
 
+dflash_status dflash_verify_sample(dflash_ctx* c, int32_t batch, const float* logits, const int32_t* draft_ids,
+                                   int32_t draft_stride, int32_t n_d, float temperature, const float* uniforms,
+                                   int32_t* n_accept, int32_t* bonus, int32_t* out_tokens, void* stream) {
+  g_last_error.clear();
+  if (!c) return fail(DFLASH_EINVAL, "null context");
+  const dflash_config& cf = c->cfg;
+  if (batch < 0 || batch > cf.max_batch) return fail(DFLASH_EINVAL, "batch out of range");
+  if (n_d < 0 || n_d > kMaxNd) return fail(DFLASH_EINVAL, "n_d out of range [0, 64]");
+  if (!(temperature > 0.f) || !(temperature < 1e30f)) return fail(DFLASH_EINVAL, "temperature must be finite and > 0");
+  if (batch == 0) return DFLASH_OK;
+  if (!logits || !uniforms || !n_accept || !bonus || !out_tokens || (n_d > 0 && !draft_ids))
+    return fail(DFLASH_EINVAL, "null argument");
+  if (n_d > 0 && draft_stride < n_d) return fail(DFLASH_EINVAL, "draft_stride < n_d");
+  VerifyArgs a{};
+  a.logits = logits;
+  a.draft = draft_ids;
+  a.draft_stride = draft_stride;
+  a.n_d = n_d;
+  a.batch = batch;
+  a.V = cf.vocab;
+  a.max_ctx = cf.max_ctx;
+  a.chunk = kVerifyChunk;
+  a.nchunks = c->L.ver_chunks;
+  a.part = c->at<uint64_t>(c->L.ver_best);
+  a.n_accept = n_accept;
+  a.bonus = bonus;
+  a.out_tokens = out_tokens;
+  a.ctx_len = c->ctx_len;
+  a.stats = c->at<unsigned long long>(c->L.stats);
+  a.err = c->at<uint32_t>(c->L.err);
+  a.inv_temp = 1.0f / temperature;
+  a.uniforms = uniforms;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  StageScope sc(c, DFLASH_STAGE_VERIFY, s);
+  return hip_status(launch_verify_sample(a, s), "verify launch");
+}
+
 dflash_status dflash_draft_block(dflash_ctx* c, int32_t batch, const int32_t* block_ids, int32_t* draft_ids,
                                  float* logits_dbg, float* hidden_dbg, void* stream) {
   g_last_error.clear();

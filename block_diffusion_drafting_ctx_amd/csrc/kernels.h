@@ -168,10 +168,18 @@ struct VerifyArgs {
   int32_t* ctx_len;
   unsigned long long* stats;  // {steps, accepted, drafted}
   uint32_t* err;
+  // sampling mode
+  float inv_temp;         // 1 / T
+  const float* uniforms;  // [batch, n_d+1, 2]: (accept test, inverse-CDF draw) per row
 };
 // Two launches: the streaming argmax over the target logits, then the
 // per-sequence accepted prefix, bonus token, commit and counters.
 hipError_t launch_verify(const VerifyArgs& a, hipStream_t stream);
+// Sampling mode, two launches: per (row, vocab chunk) the maximum and
+// exp-sum of logits / T (kept in the key slots), then per sequence the
+// accept tests, the inverse-CDF draw of the emitted token, commit, counters.
+// a.chunk must be 4 * 256 * 8 (one 16-byte load round per thread).
+hipError_t launch_verify_sample(const VerifyArgs& a, hipStream_t stream);
 
 hipError_t launch_embed(int storage, const void* embed, const void* gain, const int32_t* ids, int M, int H, int V,
                         float* x, void* xs_hi, void* xs_lo, float* ssq, uint32_t* err, hipStream_t stream);

@@ -97,6 +97,191 @@ hipError_t launch_verify(const VerifyArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------- verify, sampling mode
+// Pass 1, grid (vocab chunks, rows), 256 threads: the chunk's logits z = x / T
+// (one round of 8 16-byte loads a thread covers the 8192-entry chunk), its
+// maximum m and s = sum exp(z - m), both reduced in a fixed order, stored as
+// a float pair in the (row, chunk) key slot.
+__global__ void __launch_bounds__(256) verify_stats_kernel(const VerifyArgs a) {
+  __shared__ float s_red[4];
+  constexpr int PER = 8;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int row = blockIdx.y;
+  const int v0 = blockIdx.x * a.chunk;
+  const int v1 = min(a.V, v0 + a.chunk);
+  const float* p = a.logits + (size_t)row * a.V;
+  float z[PER][4];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int v = v0 + 4 * (tid + 256 * i);  // V is a multiple of 64: a piece never straddles v1
+    f32x4 x = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    if (v < v1) x = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p + v));
+#pragma unroll
+    for (int e = 0; e < 4; ++e) z[i][e] = v < v1 ? x[e] * a.inv_temp : -INFINITY;
+  }
+  float m = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < PER; ++i)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) m = fmaxf(m, z[i][e]);
+  for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+  if (lane == 0) s_red[wave] = m;
+  __syncthreads();
+  m = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+  __syncthreads();
+  float sum = 0.f;
+#pragma unroll
+  for (int i = 0; i < PER; ++i)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sum += z[i][e] == -INFINITY ? 0.f : __expf(z[i][e] - m);
+  sum = wave_sum_f32(sum);
+  if (lane == 0) s_red[wave] = sum;
+  __syncthreads();
+  if (tid == 0) {
+    const float2 ms = make_float2(m, ((s_red[0] + s_red[1]) + s_red[2]) + s_red[3]);
+    a.part[(size_t)row * a.nchunks + blockIdx.x] = __builtin_bit_cast(uint64_t, ms);
+  }
+}
+
+// Pass 2, one 256-thread workgroup per sequence.  Rows i < n_d accept draft
+// d_i while u[i][0] < p_i(d_i), p_i = softmax(x_i / T); the token emitted at
+// row n (the first rejection, with d_n removed from the distribution, or the
+// bonus row n_d) is the inverse CDF of p_n at u[n][1], over the vocabulary in
+// index order: whole chunks first from the pass-1 sums, then a prefix scan
+// inside the chunk that holds it.
+__global__ void __launch_bounds__(256) verify_sample_commit_kernel(const VerifyArgs a) {
+  __shared__ float s_M[65], s_S[65], s_pd[64], s_pre[256];
+  __shared__ int s_n, s_ex, s_chunk, s_tok;
+  __shared__ float s_t;
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const int R = a.n_d + 1;
+  const int32_t* d = a.draft + (size_t)b * a.draft_stride;
+  const float* u = a.uniforms + (size_t)b * R * 2;
+  for (int i = tid; i < R; i += 256) {
+    const uint64_t* pr = a.part + ((size_t)b * R + i) * a.nchunks;
+    float M = -INFINITY;
+    for (int c = 0; c < a.nchunks; ++c) M = fmaxf(M, __builtin_bit_cast(float2, pr[c]).x);
+    float S = 0.f;
+    for (int c = 0; c < a.nchunks; ++c) {
+      const float2 ms = __builtin_bit_cast(float2, pr[c]);
+      S += ms.y * __expf(ms.x - M);
+    }
+    s_M[i] = M;
+    s_S[i] = S;
+    if (i < a.n_d) {  // a draft id outside the vocabulary is never accepted
+      const int di = d[i];
+      s_pd[i] = di >= 0 && di < a.V ? __expf(a.logits[((size_t)b * R + i) * a.V + di] * a.inv_temp - M) / S : 0.f;
+    }
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int n = 0;
+    while (n < a.n_d && u[2 * n] < s_pd[n]) ++n;
+    const int j = n;
+    const int ex = n < a.n_d && d[n] >= 0 && d[n] < a.V ? d[n] : -1;  // the rejected draft leaves the draw
+    const float* xj = a.logits + ((size_t)b * R + j) * a.V;
+    const float wex = ex >= 0 ? __expf(xj[ex] * a.inv_temp - s_M[j]) : 0.f;
+    float t = u[2 * j + 1] * (s_S[j] - wex);
+    const uint64_t* pr = a.part + ((size_t)b * R + j) * a.nchunks;
+    int chunk = -1, last = 0;
+    for (int c = 0; c < a.nchunks; ++c) {
+      const float2 ms = __builtin_bit_cast(float2, pr[c]);
+      float w = ms.y * __expf(ms.x - s_M[j]);
+      if (ex >= c * a.chunk && ex < (c + 1) * a.chunk) w -= wex;
+      if (w > 0.f) last = c;
+      if (t < w) {
+        chunk = c;
+        break;
+      }
+      t -= w;
+    }
+    if (chunk < 0) {  // rounding left the target at the top: the last chunk holding mass
+      chunk = last;
+      t = INFINITY;
+    }
+    s_n = n;
+    s_ex = ex;
+    s_chunk = chunk;
+    s_t = t;
+    s_tok = -1;
+  }
+  __syncthreads();
+  // inside the chunk: thread tid takes 32 consecutive entries
+  const int j = s_n, ex = s_ex;
+  const float* xj = a.logits + ((size_t)b * R + j) * a.V;
+  const float Mj = s_M[j];
+  const int v0 = s_chunk * a.chunk + 32 * tid;
+  float e[32];
+  float mine = 0.f;
+#pragma unroll
+  for (int k = 0; k < 32; ++k) {
+    const int v = v0 + k;
+    e[k] = (v < a.V && v < (s_chunk + 1) * a.chunk && v != ex) ? __expf(xj[v] * a.inv_temp - Mj) : 0.f;
+    mine += e[k];
+  }
+  s_pre[tid] = mine;
+  __syncthreads();
+  if (tid == 0) {  // exclusive prefix over the threads, in order
+    float run = 0.f;
+    for (int k = 0; k < 256; ++k) {
+      const float x = s_pre[k];
+      s_pre[k] = run;
+      run += x;
+    }
+  }
+  __syncthreads();
+  const float t = s_t, lo = s_pre[tid];
+  if (t >= lo && t < lo + mine) {
+    float run = lo;
+    int tok = -1;
+    for (int k = 0; k < 32 && tok < 0; ++k) {
+      run += e[k];
+      if (t < run && e[k] > 0.f) tok = v0 + k;
+    }
+    if (tok >= 0) s_tok = tok;
+  }
+  __syncthreads();
+  if (s_tok < 0) {  // rounding: the last entry of the chunk holding mass
+    int best = -1;
+#pragma unroll
+    for (int k = 0; k < 32; ++k)
+      if (e[k] > 0.f) best = v0 + k;
+    const unsigned long long key = best < 0 ? 0ull : (unsigned long long)(best + 1);
+    __shared__ unsigned long long s_last;
+    if (tid == 0) s_last = 0ull;
+    __syncthreads();
+    atomicMax(&s_last, key);
+    __syncthreads();
+    if (tid == 0) s_tok = (int)s_last - 1;
+    __syncthreads();
+  }
+  if (tid == 0) {
+    const int n = s_n, tok = s_tok;
+    a.n_accept[b] = n;
+    a.bonus[b] = tok;
+    const int t0 = a.ctx_len[b];
+    if (t0 < 0 || t0 + R > a.max_ctx) {
+      atomicOr(a.err, kErrVerifyOverflow);
+    } else {
+      a.ctx_len[b] = t0 + n + 1;
+    }
+    atomicAdd(&a.stats[0], 1ull);
+    atomicAdd(&a.stats[1], (unsigned long long)n);
+    atomicAdd(&a.stats[2], (unsigned long long)a.n_d);
+  }
+  for (int i = tid; i < R; i += 256)
+    a.out_tokens[(size_t)b * R + i] = i < s_n ? d[i] : (i == s_n ? s_tok : -1);
+}
+
+hipError_t launch_verify_sample(const VerifyArgs& a, hipStream_t stream) {
+  if (a.chunk != 4 * 256 * 8) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(verify_stats_kernel, dim3(a.nchunks, a.batch * (a.n_d + 1)), dim3(256), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(verify_sample_commit_kernel, dim3(a.batch), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------- embedding
 // x[m] = E[ids[m]] as fp32, the hi/lo pair of x * gain (the first layer's
 // RMSNorm gain) and the row's sum of squares (one partial per row).

@@ -43,6 +43,11 @@ class Drafter:
     def verify(self, logits, draft_ids, draft_stride, n_d, n_accept, bonus, out_tokens, stream=None):
         _abi.dflash_verify(self.ctx, logits, draft_ids, draft_stride, n_d, n_accept, bonus, out_tokens, stream)
 
+    def verify_sample(self, logits, draft_ids, draft_stride, n_d, temperature, uniforms, n_accept, bonus,
+                      out_tokens, stream=None):
+        _abi.dflash_verify_sample(self.ctx, logits, draft_ids, draft_stride, n_d, temperature, uniforms, n_accept,
+                                  bonus, out_tokens, stream)
+
     def draft_block(self, block_ids, draft_ids, logits_dbg=None, hidden_dbg=None, stream=None):
         _abi.dflash_draft_block(self.ctx, block_ids, draft_ids, logits_dbg, hidden_dbg, stream)
 

@@ -1,0 +1,102 @@
+"""GPU parity of sampling-mode verification (dflash_verify_sample) with the oracle.
+
+The library decides in fp32 and the oracle in float64, so a decision can only
+differ where a uniform lies within rounding of its boundary: the accept test
+u < p(d) or a step of the inverse CDF.  Sequences with a margin below 1e-5 are
+reported as ambiguous and not compared; the seeded inputs keep them rare, and
+every other sequence must match exactly (accepted count, drawn token,
+committed tokens, context length).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from harness import gen
+from oracle import sample_verify
+from tests.gpu_cases import _to, config_for, log
+
+pytestmark = pytest.mark.gpu
+
+MARGIN = 1e-5
+
+
+def margins(logits, draft, n_d, T, u):
+    """Smallest distance of a deciding uniform to its boundary (float64)."""
+    x = np.asarray(logits, np.float64) / T
+    worst = np.inf
+    for i in range(n_d + 1):
+        p = np.exp(x[i] - x[i].max())
+        p /= p.sum()
+        if i < n_d:
+            worst = min(worst, abs(u[i, 0] - p[int(draft[i])]))
+            if u[i, 0] < p[int(draft[i])]:
+                continue
+            p[int(draft[i])] = 0.0
+            p /= p.sum()
+        c = np.cumsum(p)
+        worst = min(worst, float(np.min(np.abs(c - u[i, 1]))))
+        break
+    return worst
+
+
+# (the full vocabulary takes peaky logits, sigma 6: with sigma 2 a draw over
+# 151936 tokens falls within 1e-5 of a CDF step most of the time, where the
+# fp32 and float64 sums may pick neighbouring tokens)
+@pytest.mark.parametrize("vocab,batch,n_d,T,sigma", [(1024, 8, 8, 0.7, 2.0), (151936, 10, 16, 1.0, 6.0)])
+def test_sample_verify_matches_oracle(vocab, batch, n_d, T, sigma):
+    wl = gen.Workload("sv", 256, 4, 2, 64, 2, 512, vocab, n_d, 3, batch, 10, 60, "bf16")
+    log(f"[case] sample verify V={vocab} B={batch} n_d={n_d} T={T}")
+    from block_diffusion_drafting_ctx_amd import Drafter
+
+    dr = Drafter(config_for(wl, batch), _to(gen.draft_weights(wl, 41, "cpu"), "cuda"), "cuda")
+    rng = np.random.default_rng(33)
+    logits = (rng.normal(size=(batch, n_d + 1, vocab)) * sigma).astype(np.float32)
+    drafts = rng.integers(0, vocab, size=(batch, n_d)).astype(np.int32)
+    for b in range(batch):  # planted: a prefix of likely accepts (draft = row max + 3), of varying length
+        for i in range(int(rng.integers(0, n_d + 1))):
+            logits[b, i, drafts[b, i]] = logits[b, i].max() + 3.0
+    u = rng.uniform(size=(batch, n_d + 1, 2)).astype(np.float32)
+    ctx = gen.context_lengths(wl, 34, batch)
+    dr.ctx_len.copy_(torch.from_numpy(ctx))
+    n_acc = torch.full((batch,), -7, dtype=torch.int32, device="cuda")
+    tok = torch.full((batch,), -7, dtype=torch.int32, device="cuda")
+    out = torch.full((batch, n_d + 1), -7, dtype=torch.int32, device="cuda")
+    dr.verify_sample(torch.from_numpy(logits).cuda(), torch.from_numpy(drafts).cuda(), n_d, n_d, T,
+                     torch.from_numpy(u).cuda(), n_acc, tok, out)
+    torch.cuda.synchronize()
+    assert dr.check() == 0
+    n_acc, tok, out, cl = n_acc.cpu().numpy(), tok.cpu().numpy(), out.cpu().numpy(), dr.ctx_len.cpu().numpy()
+    compared = ambiguous = 0
+    total_acc = 0
+    for b in range(batch):
+        ub = u[b].astype(np.float64)
+        if margins(logits[b], drafts[b], n_d, T, ub) < MARGIN:
+            ambiguous += 1
+            continue
+        n, t, toks = sample_verify(logits[b], drafts[b], n_d, T, ub)
+        assert int(n_acc[b]) == n, f"seq {b}: accepted {n_acc[b]} != {n}"
+        assert int(tok[b]) == t, f"seq {b}: drawn {tok[b]} != {t}"
+        assert list(out[b, : n + 1]) == toks and np.all(out[b, n + 1:] == -1), f"seq {b}: out tokens"
+        assert int(cl[b]) == int(ctx[b]) + n + 1
+        compared += 1
+        total_acc += n
+    log(f"[case] sample verify: {compared} compared, {ambiguous} ambiguous, accepted {total_acc}")
+    assert compared >= batch - 1 and compared >= 4
+    steps, accepted, drafted = dr.stats()
+    assert (steps, drafted) == (batch, batch * n_d) and accepted == int(n_acc.sum())
+    dr.close()
+
+
+def test_sample_verify_rejects_bad_temperature():
+    from block_diffusion_drafting_ctx_amd import Drafter, _abi
+
+    wl = gen.Workload("sv-bad", 256, 4, 2, 64, 2, 512, 1024, 8, 3, 1, 10, 20, "bf16")
+    dr = Drafter(config_for(wl, 1), _to(gen.draft_weights(wl, 42, "cpu"), "cuda"), "cuda")
+    z = lambda *s: torch.zeros(*s, dtype=torch.int32, device="cuda")  # noqa: E731
+    lg = torch.zeros(1, 9, 1024, dtype=torch.float32, device="cuda")
+    uu = torch.zeros(1, 9, 2, dtype=torch.float32, device="cuda")
+    for T in (0.0, -1.0, float("inf"), float("nan")):
+        with pytest.raises(_abi.DFlashError):
+            dr.verify_sample(lg, z(1, 8), 8, 8, T, uu, z(1), z(1), z(1, 9))
+    dr.close()
