@@ -47,6 +47,8 @@ def parse():
                     help="WORKLOAD:ROWS:CHUNK -- also time prompt-scale fusion of ROWS prompt rows per sequence "
                          "in chunks of CHUNK, reported under 'prefill' ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-verify-modes", dest="verify_modes", action="store_false",
+                    help="skip timing greedy vs sampling-mode verification (reported under 'verify_modes')")
     ap.add_argument("--stage", default="lmhead", help="kernel stage timed with HIP events for the roofline")
     ap.add_argument("--profile-stages", action="store_true", help="also time every stage (perturbs the step)")
     ap.add_argument("--eager", action="store_true",
@@ -279,6 +281,39 @@ def time_prefill(wl, rows, chunk, steps, warmup):
     return ms, flops
 
 
+def time_verify_modes(wb, calls, temperature=1.0):
+    """Greedy and sampling-mode verification of the workbench's resident target
+    logits, `calls` launches of each (each after the same context-length reset),
+    timed by the library's HIP events around the verify stage.  Returns
+    {mode: mean ms per launch} and the logits bytes one launch reads."""
+    import torch
+    from block_diffusion_drafting_ctx_amd import _abi
+
+    wl, dr = wb.wl, wb.dr
+    g = torch.Generator(device="cuda").manual_seed(11)
+    u = torch.rand(wl.batch, wl.n_d + 1, 2, generator=g, device="cuda")
+    runs = {
+        "greedy": lambda: dr.verify(wb.logits, wb.verify_ids, wl.block, wl.n_d, wb.n_acc, wb.bonus, wb.out_tok),
+        "sample": lambda: dr.verify_sample(wb.logits, wb.verify_ids, wl.block, wl.n_d, temperature, u, wb.n_acc,
+                                           wb.bonus, wb.out_tok),
+    }
+    out = {}
+    for mode, run in runs.items():
+        for _ in range(3):
+            dr.ctx_len.copy_(wb.ctx0)
+            run()
+        torch.cuda.synchronize()
+        _abi.dflash_stage_timing(dr.ctx, "verify", True)
+        for _ in range(calls):
+            dr.ctx_len.copy_(wb.ctx0)
+            run()
+        torch.cuda.synchronize()
+        out[mode] = _abi.dflash_stage_time(dr.ctx, "verify")[0]
+        _abi.dflash_stage_timing(dr.ctx, "verify", False)
+    assert dr.check() == 0
+    return out, wl.batch * (wl.n_d + 1) * wl.vocab * 4
+
+
 def cpu_baseline(wb, min_seconds=10.0, max_steps=60):
     """The oracle, as it stands, on full steps of the workload's first sequence.
 
@@ -361,6 +396,9 @@ def main():
         out["ms_per_step_graph"] = round(wb.ms_graph, 4)
     if args.profile_stages:
         out["stages_ms"] = {k: round(v[0], 5) for k, v in per_stage.items()}
+    vm = {}
+    if args.verify_modes:
+        vm[wl.name] = time_verify_modes(wb, max(20, args.steps))
     sec = []
     for name in [s for s in args.secondary.split(",") if s]:
         wl2 = gen.WORKLOADS[name]
@@ -377,9 +415,17 @@ def main():
                     "step_mfma_frac": round(tf2 / (ms2 * 1e-3) / (BF16_PEAK_TFLOPS * 1e12), 4),
                     "step_hbm_frac": round(tb2 / (ms2 * 1e-3) / (HBM_PEAK_GBS * 1e9), 4),
                     "lmhead_tflops": round(sf2["lmhead"] / (m2 * 1e-3) / 1e12, 1)})
+        if args.verify_modes:
+            vm[name] = time_verify_modes(wb2, max(20, args.steps))
         wb = wb2
     if sec:
         out["secondary"] = sec
+    if vm:
+        out["verify_modes"] = [
+            {"workload": name, "temperature": 1.0,
+             **{f"{m}_ms": round(t, 5) for m, t in times.items()},
+             **{f"{m}_hbm_frac": round(nb / (t * 1e-3) / (HBM_PEAK_GBS * 1e9), 4) for m, t in times.items()}}
+            for name, (times, nb) in vm.items()]
     if args.prefill:
         pname, prows, pchunk = args.prefill.split(":")
         wl3 = gen.WORKLOADS[pname]

@@ -148,89 +148,133 @@ __global__ void __launch_bounds__(256) verify_stats_kernel(const VerifyArgs a) {
 // row n (the first rejection, with d_n removed from the distribution, or the
 // bonus row n_d) is the inverse CDF of p_n at u[n][1], over the vocabulary in
 // index order: whole chunks first from the pass-1 sums, then a prefix scan
-// inside the chunk that holds it.
+// inside the chunk that holds it.  Every step is wave-parallel: the reads that
+// do not depend on one another are issued together, each row's sums are a
+// wave reduction, the accepted prefix is a ballot and both prefix sums are
+// wave scans.
+constexpr int kSamplePartLds = 2560;  // (row, chunk) partials staged in LDS, e.g. 65 rows x 39 chunks
+
+__device__ __forceinline__ float wave_max_f32(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m));
+  return v;
+}
+// inclusive prefix sum over the lanes of a wave, in lane order
+__device__ __forceinline__ float wave_scan_f32(float v, int lane) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const float y = __shfl_up(v, o);
+    if (lane >= o) v += y;
+  }
+  return v;
+}
+// mass of a (max, exp-sum) partial relative to the row maximum M; an empty
+// or all -inf chunk carries none
+__device__ __forceinline__ float part_mass(float2 ms, float M) { return ms.y > 0.f ? ms.y * __expf(ms.x - M) : 0.f; }
+
 __global__ void __launch_bounds__(256) verify_sample_commit_kernel(const VerifyArgs a) {
-  __shared__ float s_M[65], s_S[65], s_pd[64], s_pre[256];
-  __shared__ int s_n, s_ex, s_chunk, s_tok;
+  __shared__ float2 s_part[kSamplePartLds];
+  __shared__ float s_M[65], s_S[65], s_xd[64], s_pd[64], s_u[130], s_wsum[4];
+  __shared__ int s_d[64], s_n, s_ex, s_chunk, s_tok;
   __shared__ float s_t;
-  const int b = blockIdx.x, tid = threadIdx.x;
-  const int R = a.n_d + 1;
+  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int R = a.n_d + 1, NC = a.nchunks;
   const int32_t* d = a.draft + (size_t)b * a.draft_stride;
-  const float* u = a.uniforms + (size_t)b * R * 2;
-  for (int i = tid; i < R; i += 256) {
-    const uint64_t* pr = a.part + ((size_t)b * R + i) * a.nchunks;
+  const float2* gpart = reinterpret_cast<const float2*>(a.part) + (size_t)b * R * NC;
+  const bool staged = R * NC <= kSamplePartLds;
+  // independent reads, all in flight at once: the partials, the uniforms,
+  // the draft ids and the logit of each draft (-inf outside the vocabulary:
+  // such a draft is never accepted)
+  if (staged)
+    for (int k = tid; k < R * NC; k += 256) s_part[k] = gpart[k];
+  if (tid < 2 * R) s_u[tid] = a.uniforms[(size_t)b * R * 2 + tid];
+  if (tid < a.n_d) {
+    const int di = d[tid];
+    s_d[tid] = di;
+    s_xd[tid] = di >= 0 && di < a.V ? a.logits[((size_t)b * R + tid) * a.V + di] * a.inv_temp : -INFINITY;
+  }
+  __syncthreads();
+  const float2* part = staged ? s_part : gpart;
+  for (int i = wave; i < R; i += 4) {  // row i: maximum M and sum S of exp(x / T - M)
+    const float2* pr = part + i * NC;
     float M = -INFINITY;
-    for (int c = 0; c < a.nchunks; ++c) M = fmaxf(M, __builtin_bit_cast(float2, pr[c]).x);
+    for (int c = lane; c < NC; c += 64) M = fmaxf(M, pr[c].x);
+    M = wave_max_f32(M);
     float S = 0.f;
-    for (int c = 0; c < a.nchunks; ++c) {
-      const float2 ms = __builtin_bit_cast(float2, pr[c]);
-      S += ms.y * __expf(ms.x - M);
-    }
-    s_M[i] = M;
-    s_S[i] = S;
-    if (i < a.n_d) {  // a draft id outside the vocabulary is never accepted
-      const int di = d[i];
-      s_pd[i] = di >= 0 && di < a.V ? __expf(a.logits[((size_t)b * R + i) * a.V + di] * a.inv_temp - M) / S : 0.f;
+    for (int c = lane; c < NC; c += 64) S += part_mass(pr[c], M);
+    S = wave_sum_f32(S);
+    if (lane == 0) {
+      s_M[i] = M;
+      s_S[i] = S;
+      if (i < a.n_d) s_pd[i] = __expf(s_xd[i] - M) / S;
     }
   }
   __syncthreads();
-  if (tid == 0) {
-    int n = 0;
-    while (n < a.n_d && u[2 * n] < s_pd[n]) ++n;
-    const int j = n;
-    const int ex = n < a.n_d && d[n] >= 0 && d[n] < a.V ? d[n] : -1;  // the rejected draft leaves the draw
-    const float* xj = a.logits + ((size_t)b * R + j) * a.V;
-    const float wex = ex >= 0 ? __expf(xj[ex] * a.inv_temp - s_M[j]) : 0.f;
-    float t = u[2 * j + 1] * (s_S[j] - wex);
-    const uint64_t* pr = a.part + ((size_t)b * R + j) * a.nchunks;
+  if (wave == 0) {
+    const bool acc = lane < a.n_d && s_u[2 * lane] < s_pd[lane];
+    const uint64_t rej = ~__ballot(acc);
+    const int n = min(a.n_d, rej ? (int)__builtin_ctzll(rej) : 64);
+    const int ex = n < a.n_d && s_d[n] >= 0 && s_d[n] < a.V ? s_d[n] : -1;  // the rejected draft leaves the draw
+    const float M = s_M[n];
+    const float wex = ex >= 0 ? __expf(s_xd[n] - M) : 0.f;
+    const float t = s_u[2 * n + 1] * (s_S[n] - wex);
+    const float2* pr = part + n * NC;
+    // the first chunk whose inclusive prefix of mass exceeds t
     int chunk = -1, last = 0;
-    for (int c = 0; c < a.nchunks; ++c) {
-      const float2 ms = __builtin_bit_cast(float2, pr[c]);
-      float w = ms.y * __expf(ms.x - s_M[j]);
-      if (ex >= c * a.chunk && ex < (c + 1) * a.chunk) w -= wex;
-      if (w > 0.f) last = c;
-      if (t < w) {
-        chunk = c;
+    float rest = INFINITY, carry = 0.f;
+    for (int c0 = 0; c0 < NC; c0 += 64) {
+      const int c = c0 + lane;
+      float w = 0.f;
+      if (c < NC) {
+        w = part_mass(pr[c], M);
+        if (ex >= c * a.chunk && ex < (c + 1) * a.chunk) w -= wex;
+      }
+      const float incl = carry + wave_scan_f32(w, lane);
+      const uint64_t pos = __ballot(c < NC && w > 0.f);
+      if (pos) last = c0 + 63 - (int)__builtin_clzll(pos);
+      const uint64_t hit = __ballot(c < NC && t < incl);
+      if (hit) {
+        const int src = (int)__builtin_ctzll(hit);
+        chunk = c0 + src;
+        rest = t - __shfl(incl - w, src);
         break;
       }
-      t -= w;
+      carry = __shfl(incl, 63);
     }
-    if (chunk < 0) {  // rounding left the target at the top: the last chunk holding mass
-      chunk = last;
-      t = INFINITY;
+    if (chunk < 0) chunk = last;  // rounding left t at the top: the last chunk holding mass, rest = inf
+    if (lane == 0) {
+      s_n = n;
+      s_ex = ex;
+      s_chunk = chunk;
+      s_t = rest;
+      s_tok = -1;
     }
-    s_n = n;
-    s_ex = ex;
-    s_chunk = chunk;
-    s_t = t;
-    s_tok = -1;
   }
   __syncthreads();
-  // inside the chunk: thread tid takes 32 consecutive entries
+  // inside the chunk: thread tid takes 32 consecutive entries (V and the
+  // chunk are multiples of 64, so a thread's run is wholly in or out)
   const int j = s_n, ex = s_ex;
   const float* xj = a.logits + ((size_t)b * R + j) * a.V;
   const float Mj = s_M[j];
   const int v0 = s_chunk * a.chunk + 32 * tid;
+  const bool in = v0 < min(a.V, (s_chunk + 1) * a.chunk);
   float e[32];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    f32x4 x = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    if (in) x = *reinterpret_cast<const f32x4*>(xj + v0 + 4 * q);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) e[4 * q + r] = v0 + 4 * q + r != ex ? __expf(x[r] * a.inv_temp - Mj) : 0.f;
+  }
   float mine = 0.f;
 #pragma unroll
-  for (int k = 0; k < 32; ++k) {
-    const int v = v0 + k;
-    e[k] = (v < a.V && v < (s_chunk + 1) * a.chunk && v != ex) ? __expf(xj[v] * a.inv_temp - Mj) : 0.f;
-    mine += e[k];
-  }
-  s_pre[tid] = mine;
+  for (int k = 0; k < 32; ++k) mine += e[k];
+  const float incl = wave_scan_f32(mine, lane);
+  if (lane == 63) s_wsum[wave] = incl;
   __syncthreads();
-  if (tid == 0) {  // exclusive prefix over the threads, in order
-    float run = 0.f;
-    for (int k = 0; k < 256; ++k) {
-      const float x = s_pre[k];
-      s_pre[k] = run;
-      run += x;
-    }
-  }
-  __syncthreads();
-  const float t = s_t, lo = s_pre[tid];
+  float lo = incl - mine;
+  for (int w = 0; w < wave; ++w) lo += s_wsum[w];
+  const float t = s_t;
   if (t >= lo && t < lo + mine) {
     float run = lo;
     int tok = -1;
