@@ -79,7 +79,9 @@ def sample_verify(logits: np.ndarray, draft: np.ndarray, n_d: int, temperature: 
     the emitted token is drawn from p_i with d_i removed (renormalised) by
     the inverse CDF at uniforms[i, 1]; when every draft is accepted, the
     bonus token is drawn from p_{n_d} at uniforms[n_d, 1].  Each emitted
-    token then has exactly the target's sampling distribution.
+    token then has exactly the target's sampling distribution.  A draft id
+    outside the vocabulary has p = 0: it is rejected, and since the target
+    has no mass there, the draw is from p_i unchanged.
 
     Returns (n, token, out): n accepted drafts, the drawn token, and the n + 1
     committed tokens [d_0 .. d_{n-1}, token].
@@ -90,10 +92,12 @@ def sample_verify(logits: np.ndarray, draft: np.ndarray, n_d: int, temperature: 
         p = np.exp(x[i] - np.max(x[i]))
         p /= p.sum()
         d = int(draft[i])
-        if u[i, 0] < p[d]:
+        inside = 0 <= d < len(p)  # an id outside the vocabulary has no target mass
+        if u[i, 0] < (p[d] if inside else 0.0):
             continue
         r = p.copy()
-        r[d] = 0.0
+        if inside:
+            r[d] = 0.0
         tok = inverse_cdf(r, u[i, 1])
         return i, tok, [int(t) for t in draft[:i]] + [tok]
     p = np.exp(x[n_d] - np.max(x[n_d]))

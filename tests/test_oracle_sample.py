@@ -56,3 +56,21 @@ def test_full_acceptance_draws_the_bonus_by_inverse_cdf():
     assert n == 3 and out == [3, 9, 17, tok]
     assert tok == int(np.searchsorted(np.cumsum(p), 0.637))
     assert inverse_cdf(p, 0.0) == int(np.flatnonzero(p > 0)[0])
+
+
+def test_draft_outside_the_vocabulary_is_rejected_and_removes_nothing():
+    # (p - delta_d)+ = p when d has no target mass: rejected even at a tiny
+    # uniform, and the draw is the plain inverse CDF of p (the last token
+    # carries most of the mass, so an id read modulo the vocabulary, -1 or
+    # -40, would be accepted or would move this draw)
+    rng = np.random.default_rng(6)
+    logits = rng.normal(size=(3, 40))
+    logits[0, 39] = 6.0
+    logits[0, 0] = 5.0
+    p = softmax(logits[0], 1.3)
+    for bad in (-1, -40, 40, 1000):
+        draft = np.array([bad, 5])
+        u = np.array([[0.001, 0.99], [0.0, 0.0], [0.0, 0.0]])
+        n, tok, out = sample_verify(logits, draft, 2, 1.3, u)
+        assert n == 0 and out == [tok]
+        assert tok == int(np.searchsorted(np.cumsum(p), 0.99)) == 39
