@@ -29,10 +29,14 @@ def margins(logits, draft, n_d, T, u):
         p = np.exp(x[i] - x[i].max())
         p /= p.sum()
         if i < n_d:
-            worst = min(worst, abs(u[i, 0] - p[int(draft[i])]))
-            if u[i, 0] < p[int(draft[i])]:
+            d = int(draft[i])
+            inside = 0 <= d < p.size
+            pd = p[d] if inside else 0.0
+            worst = min(worst, abs(u[i, 0] - pd))
+            if u[i, 0] < pd:
                 continue
-            p[int(draft[i])] = 0.0
+            if inside:
+                p[d] = 0.0
             p /= p.sum()
         c = np.cumsum(p)
         worst = min(worst, float(np.min(np.abs(c - u[i, 1]))))
@@ -40,29 +44,40 @@ def margins(logits, draft, n_d, T, u):
     return worst
 
 
-# (the full vocabulary takes peaky logits, sigma 6: with sigma 2 a draw over
-# 151936 tokens falls within 1e-5 of a CDF step most of the time, where the
-# fp32 and float64 sums may pick neighbouring tokens)
-@pytest.mark.parametrize("vocab,batch,n_d,T,sigma", [(1024, 8, 8, 0.7, 2.0), (151936, 10, 16, 1.0, 6.0)])
-def test_sample_verify_matches_oracle(vocab, batch, n_d, T, sigma):
-    wl = gen.Workload("sv", 256, 4, 2, 64, 2, 512, vocab, n_d, 3, batch, 10, 60, "bf16")
-    log(f"[case] sample verify V={vocab} B={batch} n_d={n_d} T={T}")
+def check_against_oracle(vocab, batch, n_d, T, sigma, plant="prefix", bad_ids=False, seed=33):
+    """Seeded logits [batch, n_d+1, vocab] ~ N(0, sigma^2), drafts and uniforms;
+    plant: 'prefix' makes a random-length prefix of drafts likely (row max + 3),
+    'all' makes every draft near-certain (row max + 30, accept uniforms < 0.9);
+    bad_ids puts ids outside the vocabulary (negative and >= vocab) into the
+    drafts.  Every sequence off a rounding boundary must match the oracle."""
+    stride = max(1, n_d)
+    block = max(16, n_d)
+    wl = gen.Workload("sv", 256, 4, 2, 64, 2, 512, vocab, block, 3, batch, 10, 60, "bf16")
+    log(f"[case] sample verify V={vocab} B={batch} n_d={n_d} T={T} plant={plant} bad_ids={bad_ids}")
     from block_diffusion_drafting_ctx_amd import Drafter
 
     dr = Drafter(config_for(wl, batch), _to(gen.draft_weights(wl, 41, "cpu"), "cuda"), "cuda")
-    rng = np.random.default_rng(33)
+    rng = np.random.default_rng(seed)
     logits = (rng.normal(size=(batch, n_d + 1, vocab)) * sigma).astype(np.float32)
-    drafts = rng.integers(0, vocab, size=(batch, n_d)).astype(np.int32)
-    for b in range(batch):  # planted: a prefix of likely accepts (draft = row max + 3), of varying length
-        for i in range(int(rng.integers(0, n_d + 1))):
-            logits[b, i, drafts[b, i]] = logits[b, i].max() + 3.0
+    drafts = rng.integers(0, vocab, size=(batch, stride)).astype(np.int32)
     u = rng.uniform(size=(batch, n_d + 1, 2)).astype(np.float32)
+    for b in range(batch):
+        if plant == "all":
+            for i in range(n_d):
+                logits[b, i, drafts[b, i]] = logits[b, i].max() + 30.0
+            u[b, :n_d, 0] *= 0.9
+        else:
+            for i in range(int(rng.integers(0, n_d + 1))):
+                logits[b, i, drafts[b, i]] = logits[b, i].max() + 3.0
+        if bad_ids and n_d:
+            for i in rng.choice(n_d, size=min(n_d, 3), replace=False):
+                drafts[b, i] = int(rng.choice([-1, -7, vocab, vocab + 12345]))
     ctx = gen.context_lengths(wl, 34, batch)
     dr.ctx_len.copy_(torch.from_numpy(ctx))
     n_acc = torch.full((batch,), -7, dtype=torch.int32, device="cuda")
     tok = torch.full((batch,), -7, dtype=torch.int32, device="cuda")
     out = torch.full((batch, n_d + 1), -7, dtype=torch.int32, device="cuda")
-    dr.verify_sample(torch.from_numpy(logits).cuda(), torch.from_numpy(drafts).cuda(), n_d, n_d, T,
+    dr.verify_sample(torch.from_numpy(logits).cuda(), torch.from_numpy(drafts).cuda(), stride, n_d, T,
                      torch.from_numpy(u).cuda(), n_acc, tok, out)
     torch.cuda.synchronize()
     assert dr.check() == 0
@@ -82,10 +97,37 @@ def test_sample_verify_matches_oracle(vocab, batch, n_d, T, sigma):
         compared += 1
         total_acc += n
     log(f"[case] sample verify: {compared} compared, {ambiguous} ambiguous, accepted {total_acc}")
-    assert compared >= batch - 1 and compared >= 4
+    assert compared >= batch - 1 and compared >= min(batch, 2)
     steps, accepted, drafted = dr.stats()
     assert (steps, drafted) == (batch, batch * n_d) and accepted == int(n_acc.sum())
     dr.close()
+    return int(n_acc.sum())  # over every sequence, ambiguous draws included
+
+
+# (the full vocabulary takes peaky logits, sigma 6: with sigma 2 a draw over
+# 151936 tokens falls within 1e-5 of a CDF step most of the time, where the
+# fp32 and float64 sums may pick neighbouring tokens)
+@pytest.mark.parametrize("vocab,batch,n_d,T,sigma", [(1024, 8, 8, 0.7, 2.0), (151936, 10, 16, 1.0, 6.0)])
+def test_sample_verify_matches_oracle(vocab, batch, n_d, T, sigma):
+    check_against_oracle(vocab, batch, n_d, T, sigma)
+
+
+def test_sample_verify_no_drafts_draws_the_bonus():
+    assert check_against_oracle(1024, 6, 0, 1.0, 2.0) == 0
+
+
+def test_sample_verify_all_64_accepted():
+    assert check_against_oracle(4096, 3, 64, 0.9, 2.0, plant="all") == 3 * 64
+
+
+def test_sample_verify_drafts_outside_the_vocabulary():
+    check_against_oracle(1024, 8, 8, 1.0, 2.0, bad_ids=True)
+
+
+def test_sample_verify_partials_beyond_lds():
+    # 65 rows x 40 vocabulary chunks of partials exceed the LDS staging: the
+    # per-sequence pass reads them from global memory
+    check_against_oracle(327680, 3, 64, 1.0, 8.0)
 
 
 def test_sample_verify_rejects_bad_temperature():
