@@ -206,12 +206,13 @@ dflash_status dflash_verify(dflash_ctx* ctx, int32_t batch, const float* target_
                             int32_t* n_accept, int32_t* bonus, int32_t* out_tokens, void* stream);
 
 /* Verification when the target samples at temperature T > 0.  The pages
- * measure a sampling mode but give no rule ([P1] Speed benchmarks, the
- * thinking setting); the rule here is the standard lossless
+ * measure a sampling mode but give no rule ([P1] Real-world integration,
+ * the thinking setting); the rule here is the standard lossless
  * speculative-sampling rule for a drafter whose proposal is one token: with
  * p_i = softmax(target_logits[b][i] / T), draft d_i is accepted while
  * u[b][i][0] < p_i(d_i) (an id outside the vocabulary never is); the token
- * emitted at the first rejected row n is drawn from p_n with d_n removed, or
+ * emitted at the first rejected row n is drawn from p_n with d_n removed
+ * (nothing is removed for an id outside the vocabulary), or
  * at row n_d (all accepted) from p_{n_d}, as the inverse CDF over the
  * vocabulary in index order at u[b][n][1].  Every emitted token then has the
  * target's sampling distribution.
@@ -221,7 +222,8 @@ dflash_status dflash_verify(dflash_ctx* ctx, int32_t batch, const float* target_
  *  out_tokens[b] = [d_0 .. d_{n-1}, drawn, -1 ...], ctx_len[b] += n + 1 and
  *  the counters advance; ctx_len[b] + n_d + 1 > max_ctx sets
  *  DFLASH_ERR_VERIFY_OVERFLOW and commits nothing.
- *  temperature must be finite and > 0 (T = 0 is dflash_verify). */
+ *  temperature must be finite and > 0, else DFLASH_EINVAL and nothing is
+ *  launched (T = 0 is dflash_verify). */
 dflash_status dflash_verify_sample(dflash_ctx* ctx, int32_t batch, const float* target_logits,
                                    const int32_t* draft_ids, int32_t draft_stride, int32_t n_d,
                                    float temperature, const float* uniforms, int32_t* n_accept,

@@ -71,7 +71,7 @@ def sample_verify(logits: np.ndarray, draft: np.ndarray, n_d: int, temperature: 
                   uniforms: np.ndarray) -> Tuple[int, int, List[int]]:
     """Verification when the target samples at temperature T > 0.
 
-    The pages measure this mode (a "thinking" setting that samples) but state
+    The pages measure this mode ([P1] Real-world integration: a "thinking" setting that samples) but state
     no rule; the reading here is the standard lossless speculative-sampling
     rule for a drafter whose proposal is a single token (its distribution is
     all on the drafted token): with p_i = softmax(logits[i] / T), draft d_i
