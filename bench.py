@@ -358,7 +358,7 @@ def cpu_baseline(wb, min_seconds=10.0, max_steps=60):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        print(json.dumps({"error": "the path runs on one GPU; --gpus must be 1"}))
         sys.exit(2)
     import torch
     from harness import gen

@@ -61,7 +61,7 @@ typedef struct dflash_ctx dflash_ctx; /* opaque, owned by the library */
 typedef enum {
   DFLASH_OK = 0,
   DFLASH_EINVAL = -1,      /* bad argument (host-checked) */
-  DFLASH_EUNSUPPORTED = -2, /* shape or dtype this build does not implement */
+  DFLASH_EUNSUPPORTED = -2, /* shape or dtype the library does not implement */
   DFLASH_EHIP = -3,        /* a HIP runtime call or kernel launch failed */
   DFLASH_EDEVICE = -4      /* dflash_check: the device error word is non-zero */
 } dflash_status;
