@@ -8,12 +8,14 @@ dflash_verify against planted target logits, and dflash_draft_block of one
 block per sequence -- every stage of the hot path, on inputs already resident
 in HBM.  value = batch * block / step time.
 
-Also reported: the dominant kernel's achieved HBM bandwidth against the
-MI355X peak (algorithmic bytes per launch / mean launch time from HIP events
-recorded around every launch of that kernel inside the timed region), and the
-float64 numpy oracle timed on the host cores on a bounded sample of the same
-step.  A secondary line of the same JSON object covers the batch-32 ragged
-workload.
+Also reported: the achieved HBM bandwidth of the kernel that takes most of
+the batch-1 step -- the weight-streaming main kernel of the layer products
+(Q/K/V, O, gate/up, down; their algorithmic bytes over their launch times
+from HIP events recorded around every such launch inside the timed region)
+-- against the MI355X peak; a per-stage table from a separate pass with
+events around every stage; and the float64 numpy oracle timed on the host
+cores on a bounded sample of the same step.  Secondary lines of the same JSON
+object cover the batch-32 ragged, 32k-context and 27B-shaped workloads.
 """
 
 from __future__ import annotations
@@ -41,7 +43,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="qwen3-8b-shape-b1")
-    ap.add_argument("--secondary", default="qwen3-8b-shape-b32-ragged",
+    ap.add_argument("--secondary", default="qwen3-8b-shape-b32-ragged,long-ctx-32k-b4,dflash2-27b-shape-conv-b8",
                     help="comma-separated extra workloads reported under 'secondary' ('' for none)")
     ap.add_argument("--prefill", default="qwen3-8b-shape-b1:4096:4096",
                     help="WORKLOAD:ROWS:CHUNK -- also time prompt-scale fusion of ROWS prompt rows per sequence "
@@ -49,8 +51,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-verify-modes", dest="verify_modes", action="store_false",
                     help="skip timing greedy vs sampling-mode verification (reported under 'verify_modes')")
-    ap.add_argument("--stage", default="lmhead", help="kernel stage timed with HIP events for the roofline")
-    ap.add_argument("--profile-stages", action="store_true", help="also time every stage (perturbs the step)")
+    ap.add_argument("--stage", default="layer_gemm", help="kernel stage timed with HIP events for the roofline")
+    ap.add_argument("--no-stage-table", dest="stage_table", action="store_false",
+                    help="skip the separate pass that times every stage with HIP events")
     ap.add_argument("--eager", action="store_true",
                     help="eager launches only (skip the timed HIP-graph replay pass)")
     ap.add_argument("--graph", action="store_true",
@@ -85,6 +88,19 @@ def stage_bytes(wl, batch, ctx_lens):
     return b
 
 
+def layer_gemm_bytes(wl, batch):
+    """Algorithmic bytes of one step's layer-product main kernels: weights once,
+    the activation rows read once, the fp32 product written once."""
+    S = 2 if wl.storage == "bf16" else 4
+    H, F = wl.hidden, wl.ffn
+    Nq, Nk = wl.n_q_heads * wl.head_dim, wl.n_kv_heads * wl.head_dim
+    Md = batch * wl.block
+    act = 4
+    per_layer = ((Nq + 2 * Nk) * H + H * Nq + 2 * F * H + H * F) * S \
+        + Md * (H + Nq + H + F) * act + Md * ((Nq + 2 * Nk) + H + 2 * F + H) * 4
+    return wl.n_layers * per_layer, 4 * wl.n_layers
+
+
 def stage_flops(wl, batch, ctx_lens):
     H, D, F, V = wl.hidden, wl.head_dim, wl.ffn, wl.vocab
     Nq, Nk = wl.n_q_heads * D, wl.n_kv_heads * D
@@ -99,17 +115,60 @@ def stage_flops(wl, batch, ctx_lens):
         "gateup": 4.0 * Md * H * F,
         "down": 2.0 * Md * F * H,
         "lmhead": 2.0 * Md * H * V,
+        "layer_gemm": 2.0 * Md * H * (Nq + 2 * Nk + 3 * F) + 2.0 * Md * Nq * H,
     }
 
 
-PER_LAYER = ("qkv", "attn", "oproj", "gateup", "down")
+PER_LAYER = ("qkv", "attn", "oproj", "gateup", "down", "layer_gemm")
+STEP_STAGES = ("fuse_fc", "ctx_kv", "verify", "embed", "qkv", "attn", "oproj", "gateup", "down", "lmhead")
 
 
 def step_totals(wl, batch, ctx_lens):
     sb, sf = stage_bytes(wl, batch, ctx_lens), stage_flops(wl, batch, ctx_lens)
-    tb = sum(v * (wl.n_layers if k in PER_LAYER else 1) for k, v in sb.items())
-    tf = sum(v * (wl.n_layers if k in PER_LAYER else 1) for k, v in sf.items())
+    tb = sum(v * (wl.n_layers if k in PER_LAYER else 1) for k, v in sb.items() if k in STEP_STAGES)
+    tf = sum(v * (wl.n_layers if k in PER_LAYER else 1) for k, v in sf.items() if k in STEP_STAGES)
     return tb, tf
+
+
+def stage_launch_bytes(wl, batch, ctx_lens, stage):
+    """Algorithmic bytes of one launch of a timed stage (the layer products:
+    their mean over the four products of a layer)."""
+    if stage == "layer_gemm":
+        tot, launches = layer_gemm_bytes(wl, batch)
+        return tot / launches
+    return stage_bytes(wl, batch, ctx_lens)[stage]
+
+
+def stage_table(wb, steps):
+    """Every stage timed with HIP events around its launches over `steps` more
+    steps (a separate pass: the events perturb the step).  Per stage: mean
+    launch ms, launches per step, algorithmic GB/s and TFLOP/s, and the
+    fractions of the HBM and bf16 peaks."""
+    import torch
+    from block_diffusion_drafting_ctx_amd import _abi
+
+    wl = wb.wl
+    for s in _abi.STAGES:
+        _abi.dflash_stage_timing(wb.dr.ctx, s, True)
+    for _ in range(steps):
+        wb.step()
+    torch.cuda.synchronize()
+    sf = stage_flops(wl, wl.batch, wb.ctx_lens)
+    out = {}
+    for s in _abi.STAGES:
+        mean_ms, n = _abi.dflash_stage_time(wb.dr.ctx, s)
+        _abi.dflash_stage_timing(wb.dr.ctx, s, False)
+        if n == 0:
+            continue
+        nb = stage_launch_bytes(wl, wl.batch, wb.ctx_lens, s)
+        fl = sf.get(s, 0.0) / (4 if s == "layer_gemm" else 1)  # (its flops are per layer: 4 launches)
+        gbs = nb / (mean_ms * 1e-3) / 1e9
+        tfs = fl / (mean_ms * 1e-3) / 1e12
+        out[s] = {"mean_ms": round(mean_ms, 5), "per_step": round(n / steps, 2), "gb_s": round(gbs, 1),
+                  "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "tflop_s": round(tfs, 1),
+                  "mfma_frac": round(tfs / BF16_PEAK_TFLOPS, 4)}
+    assert wb.dr.check() == 0
+    return out
 
 
 def source_hash() -> str:
@@ -176,7 +235,7 @@ class Workbench:
         self.dr.draft_block(self.block_ids, self.draft_ids)
 
 
-def time_workload(wl, steps, warmup, stage, profile_stages=False, graph_pass=True, graph_headline=False):
+def time_workload(wl, steps, warmup, stage, graph_pass=True, graph_headline=False):
     """Time `steps` steps; returns (workbench, ms per step, {stage: (mean launch ms, launches)}).
 
     The headline pass enqueues the step's kernels one by one on the stream
@@ -197,7 +256,7 @@ def time_workload(wl, steps, warmup, stage, profile_stages=False, graph_pass=Tru
     err = wb.dr.check()
     if err:
         raise RuntimeError(f"device error word {err:#x}")
-    stages = list(_abi.STAGES) if profile_stages else [stage]
+    stages = [stage]
 
     def timed(run):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -337,7 +396,19 @@ def cpu_baseline(wb, min_seconds=10.0, max_steps=60):
     drafts = wb.verify_ids[b:b + 1].cpu().numpy().reshape(-1)
     ids = wb.block_ids[b:b + 1].cpu().numpy()
     info = threadpoolctl.threadpool_info()
-    threads = max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [1])
+    blas = [i for i in info if i.get("user_api") == "blas"]
+    threads = max([i.get("num_threads", 1) for i in blas] or [1])
+    blas_desc = ", ".join(f"{i.get('internal_api')} {i.get('version')} ({i.get('num_threads')} threads)"
+                          for i in blas) or "none found"
+    cpu_model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     total, steps = 0.0, 0
     while total < min_seconds and steps < max_steps:
         st = DraftState(k=[x.copy() for x in base.k], v=[x.copy() for x in base.v], ctx_len=base.ctx_len.copy())
@@ -348,17 +419,41 @@ def cpu_baseline(wb, min_seconds=10.0, max_steps=60):
         total += time.perf_counter() - t0
         steps += 1
     return {"value": round(steps * wl.block / total, 3), "unit": "block-tokens/s", "cores": int(threads),
-            "kind": "oracle",
+            "kind": "oracle", "precision": "float64 (the oracle's own arithmetic, not tuned)",
+            "cpu_model": cpu_model, "blas": blas_desc, "host_cpus": os.cpu_count(),
             "sample": f"{steps} full steps of sequence 0 of {wl.name}, each from the same state (fuse {wl.t_new} "
                       f"rows, verify, draft of one {wl.block}-row block through {wl.n_layers} layers and the full "
                       f"vocabulary), float64 numpy",
             "seconds": round(total, 3)}
 
 
+def secondary_line(wl, args):
+    """One secondary workload: its step time, the step's roofline fractions,
+    the LM head's and attention's rates, and its stage table."""
+    import torch
+
+    wb, ms, ps = time_workload(wl, max(5, args.steps // 2), args.warmup, "lmhead",
+                               graph_pass=not args.eager, graph_headline=args.graph)
+    tb, tf = step_totals(wl, wl.batch, wb.ctx_lens)
+    sf = stage_flops(wl, wl.batch, wb.ctx_lens)
+    line = {"workload": wl.name, "batch": wl.batch, "context": int(np.max(wb.ctx_lens)),
+            "value": round(wl.batch * wl.block / (ms * 1e-3), 1), "ms_per_step": round(ms, 4),
+            "ms_per_step_graph": None if wb.ms_graph is None else round(wb.ms_graph, 4),
+            "step_mfma_frac": round(tf / (ms * 1e-3) / (BF16_PEAK_TFLOPS * 1e12), 4),
+            "step_hbm_frac": round(tb / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9), 4),
+            "lmhead_tflops": round(sf["lmhead"] / (ps["lmhead"][0] * 1e-3) / 1e12, 1)}
+    if args.stage_table:
+        tab = stage_table(wb, max(5, args.steps // 4))
+        line["attn_hbm_frac"] = tab["attn"]["hbm_frac"]
+        line["stages"] = tab
+    return wb, line
+
+
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "the path runs on one GPU; --gpus must be 1"}))
+        print(json.dumps({"error": "this benchmark runs on one GPU only; pass --gpus 1 "
+                                   "(the sharded design is described, not built)"}))
         sys.exit(2)
     import torch
     from harness import gen
@@ -366,14 +461,17 @@ def main():
     if not torch.cuda.is_available():
         raise RuntimeError("bench.py needs a GPU")
     wl = gen.WORKLOADS[args.workload]
-    wb, ms, per_stage = time_workload(wl, args.steps, args.warmup, args.stage, args.profile_stages,
+    wb, ms, per_stage = time_workload(wl, args.steps, args.warmup, args.stage,
                                       graph_pass=not args.eager, graph_headline=args.graph)
     B = wl.batch
     value = B * wl.block / (ms * 1e-3)
     tb, tf = step_totals(wl, B, wb.ctx_lens)
-    sb = stage_bytes(wl, B, wb.ctx_lens)
     mean_ms, n = per_stage[args.stage]
-    achieved = sb[args.stage] / (mean_ms * 1e-3) / 1e9
+    nb = stage_launch_bytes(wl, B, wb.ctx_lens, args.stage)
+    achieved = nb / (mean_ms * 1e-3) / 1e9
+    kernel_desc = {"layer_gemm": "weight-streaming main kernel of the layer products (Q/K/V, O, gate/up, down; "
+                                 "finish kernels excluded)",
+                   "lmhead": "LM head with per-tile argmax"}.get(args.stage, args.stage)
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "block-tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
@@ -383,10 +481,10 @@ def main():
                    "layers": wl.n_layers, "hidden": wl.hidden, "vocab": wl.vocab,
                    "launch": "hip-graph replay of the whole step" if args.graph else
                    "eager (the step's kernels enqueued one by one, no host sync inside the timed region)"},
-        "roofline": {"bound": "hbm", "kernel": args.stage, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+        "roofline": {"bound": "hbm", "kernel": args.stage, "kernel_desc": kernel_desc, "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic_from_profiles(args.stage, wl.name),
-                     "algorithmic_bytes_per_launch": int(sb[args.stage]), "mean_launch_ms": round(mean_ms, 5),
+                     "algorithmic_bytes_per_launch": int(nb), "mean_launch_ms": round(mean_ms, 5),
                      "launches": n},
         "step_roofline": {"algorithmic_bytes": int(tb), "algorithmic_flops": int(tf),
                           "hbm_frac": round(tb / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9), 4),
@@ -394,8 +492,8 @@ def main():
     }
     if wb.ms_graph is not None:
         out["ms_per_step_graph"] = round(wb.ms_graph, 4)
-    if args.profile_stages:
-        out["stages_ms"] = {k: round(v[0], 5) for k, v in per_stage.items()}
+    if args.stage_table:
+        out["stages"] = stage_table(wb, max(10, args.steps // 2))
     vm = {}
     if args.verify_modes:
         vm[wl.name] = time_verify_modes(wb, max(20, args.steps))
@@ -404,33 +502,25 @@ def main():
         wl2 = gen.WORKLOADS[name]
         del wb
         torch.cuda.empty_cache()
-        wb2, ms2, ps2 = time_workload(wl2, max(5, args.steps // 2), args.warmup, args.stage,
-                                      graph_pass=not args.eager, graph_headline=args.graph)
-        tb2, tf2 = step_totals(wl2, wl2.batch, wb2.ctx_lens)
-        sf2 = stage_flops(wl2, wl2.batch, wb2.ctx_lens)
-        m2 = ps2[args.stage][0]
-        sec.append({"workload": name, "value": round(wl2.batch * wl2.block / (ms2 * 1e-3), 1),
-                    "ms_per_step": round(ms2, 4),
-                    "ms_per_step_graph": None if wb2.ms_graph is None else round(wb2.ms_graph, 4),
-                    "step_mfma_frac": round(tf2 / (ms2 * 1e-3) / (BF16_PEAK_TFLOPS * 1e12), 4),
-                    "step_hbm_frac": round(tb2 / (ms2 * 1e-3) / (HBM_PEAK_GBS * 1e9), 4),
-                    "lmhead_tflops": round(sf2["lmhead"] / (m2 * 1e-3) / 1e12, 1)})
-        if args.verify_modes:
-            vm[name] = time_verify_modes(wb2, max(20, args.steps))
-        wb = wb2
+        print(f"[bench] secondary {name}", file=sys.stderr, flush=True)
+        wb, line = secondary_line(wl2, args)
+        sec.append(line)
+        if args.verify_modes and wl2.batch > 1 and name.startswith("qwen3"):
+            vm[name] = time_verify_modes(wb, max(20, args.steps))
     if sec:
         out["secondary"] = sec
     if vm:
         out["verify_modes"] = [
             {"workload": name, "temperature": 1.0,
              **{f"{m}_ms": round(t, 5) for m, t in times.items()},
-             **{f"{m}_hbm_frac": round(nb / (t * 1e-3) / (HBM_PEAK_GBS * 1e9), 4) for m, t in times.items()}}
-            for name, (times, nb) in vm.items()]
+             **{f"{m}_hbm_frac": round(nb_ / (t * 1e-3) / (HBM_PEAK_GBS * 1e9), 4) for m, t in times.items()}}
+            for name, (times, nb_) in vm.items()]
     if args.prefill:
         pname, prows, pchunk = args.prefill.split(":")
         wl3 = gen.WORKLOADS[pname]
         del wb
         torch.cuda.empty_cache()
+        print("[bench] prompt fusion", file=sys.stderr, flush=True)
         pms, pfl = time_prefill(wl3, int(prows), int(pchunk), max(3, args.steps // 10), 2)
         out["prefill"] = {"workload": f"{pname}: {wl3.batch} x {int(prows)} prompt rows fused in chunks of {pchunk}",
                           "prompt_rows_per_s": round(wl3.batch * int(prows) / (pms * 1e-3), 1),
@@ -453,6 +543,7 @@ def main():
             del wb
             torch.cuda.empty_cache()
             wb_c = Workbench(wl)
+        print("[bench] cpu baseline", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(wb_c)
     print(json.dumps(out), flush=True)
 

@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(_HERE, "libdflash.so")
 DFLASH_OK, DFLASH_EINVAL, DFLASH_EUNSUPPORTED, DFLASH_EHIP, DFLASH_EDEVICE = 0, -1, -2, -3, -4
 DTYPE_F32, DTYPE_BF16 = 0, 1
 ERR_FUSE_OVERFLOW, ERR_TOKEN_RANGE, ERR_VERIFY_OVERFLOW, ERR_DRAFT_OVERFLOW = 1, 2, 4, 8
-STAGES = ["fuse_fc", "ctx_kv", "verify", "embed", "qkv", "attn", "oproj", "gateup", "down", "lmhead"]
+STAGES = ["fuse_fc", "ctx_kv", "verify", "embed", "qkv", "attn", "oproj", "gateup", "down", "lmhead", "layer_gemm"]
 STAGE = {n: i for i, n in enumerate(STAGES)}
 
 EXPORTED = [

@@ -417,7 +417,7 @@ dflash_status dflash_create(const dflash_config* cfg, const dflash_weights* w, v
       delete c;
       return ts;
     }
-    e = hipDeviceSynchronize();
+    e = hipStreamSynchronize(nullptr);  // the clear, the table and the tiled copy ran on the null stream
   }
   if (e != hipSuccess) {
     delete c;
@@ -552,7 +552,9 @@ dflash_status dflash_verify_sample(dflash_ctx* c, int32_t batch, const float* lo
   const dflash_config& cf = c->cfg;
   if (batch < 0 || batch > cf.max_batch) return fail(DFLASH_EINVAL, "batch out of range");
   if (n_d < 0 || n_d > kMaxNd) return fail(DFLASH_EINVAL, "n_d out of range [0, 64]");
-  if (!(temperature > 0.f) || !(temperature < 1e30f)) return fail(DFLASH_EINVAL, "temperature must be finite and > 0");
+  // 1/T must be finite too: a subnormal T would scale every logit to +-inf
+  if (!(temperature > 0.f) || !(temperature < 1e30f) || !std::isfinite(1.0f / temperature))
+    return fail(DFLASH_EINVAL, "temperature must be finite and > 0, with a finite reciprocal");
   if (batch == 0) return DFLASH_OK;
   if (!logits || !uniforms || !n_accept || !bonus || !out_tokens || (n_d > 0 && !draft_ids))
     return fail(DFLASH_EINVAL, "null argument");
@@ -623,6 +625,11 @@ dflash_status dflash_draft_block(dflash_ctx* c, int32_t batch, const int32_t* bl
   // HBM bytes there); from kMlpHiOnlyRows rows on, where the products are
   // matrix-core bound, they enter as plain bf16.
   const bool mlp_lo = M < kMlpHiOnlyRows;
+  // the main kernel of a layer product, timed on its own under DFLASH_STAGE_LAYER_GEMM
+  auto layer_gemm = [&](GemmArgs& a, bool lo, int N, int K, GemmLaunch* gl) {
+    StageScope sc(c, DFLASH_STAGE_LAYER_GEMM, s);
+    return gemm_partial(c, a, SRC_SPLIT, lo, M, N, K, gl, s);
+  };
   for (int l = 0; l < cf.n_layers; ++l) {
     {  // RMSNorm -> Q/K/V, RoPE
       StageScope sc(c, DFLASH_STAGE_QKV, s);
@@ -634,7 +641,7 @@ dflash_status dflash_draft_block(dflash_ctx* c, int32_t batch, const int32_t* bl
       a.lda = H;
       FinishArgs f{};
       norm(a, f);
-      if ((st = gemm_partial(c, a, SRC_SPLIT, true, M, Nq + 2 * Nk, H, &gl, s))) return st;
+      if ((st = layer_gemm(a, true, Nq + 2 * Nk, H, &gl))) return st;
       f.rope = c->at<float2>(L.rope);
       f.max_ctx = cf.max_ctx;
       f.block = cf.block;
@@ -680,7 +687,7 @@ dflash_status dflash_draft_block(dflash_ctx* c, int32_t batch, const int32_t* bl
       a.a_hi = c->at<void>(L.o_hi);
       a.a_lo = c->at<void>(L.o_lo);
       a.lda = Nq;
-      if ((st = gemm_partial(c, a, SRC_SPLIT, true, M, H, Nq, &gl, s))) return st;
+      if ((st = layer_gemm(a, true, H, Nq, &gl))) return st;
       FinishArgs f{};
       f.x = x;
       f.conv = c->conv[l];
@@ -703,7 +710,7 @@ dflash_status dflash_draft_block(dflash_ctx* c, int32_t batch, const int32_t* bl
       a.lda = H;
       FinishArgs f{};
       norm(a, f);
-      if ((st = gemm_partial(c, a, SRC_SPLIT, mlp_lo, M, 2 * F, H, &gl, s))) return st;
+      if ((st = layer_gemm(a, mlp_lo, 2 * F, H, &gl))) return st;
       f.out_hi = c->at<void>(L.act_hi);
       f.out_lo = mlp_lo ? c->at<void>(L.act_lo) : nullptr;
       if ((st = finish(c, FIN_SWIGLU, f, gl, M, 2 * F, s))) return st;
@@ -716,7 +723,7 @@ dflash_status dflash_draft_block(dflash_ctx* c, int32_t batch, const int32_t* bl
       a.a_hi = c->at<void>(L.act_hi);
       a.a_lo = mlp_lo ? c->at<void>(L.act_lo) : nullptr;
       a.lda = F;
-      if ((st = gemm_partial(c, a, SRC_SPLIT, mlp_lo, M, H, F, &gl, s))) return st;
+      if ((st = layer_gemm(a, mlp_lo, H, F, &gl))) return st;
       FinishArgs f{};
       f.x = x;
       f.block = cf.block;

@@ -720,9 +720,10 @@ __global__ void __launch_bounds__(256) attention_combine_kernel(const AttnArgs a
       if (np <= 1) return;  // fixed chunks: the segment was one chunk, written by the attention kernel
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        if (p0 + g + SG * k >= np) mv[k] = -INFINITY;  // a chunk past the segment: stale
+        // a chunk past the segment holds a stale slot (any values, NaN
+        // included, from an earlier call): skipped, never weighted by zero
+        if (p0 + g + SG * k >= np || mv[k] == -INFINITY) continue;
         const float mn = fmaxf(m, mv[k]);
-        if (mn == -INFINITY) continue;
         const float w1 = m == -INFINITY ? 0.f : fast_exp2(m - mn);
         const float w2 = mv[k] == -INFINITY ? 0.f : fast_exp2(mv[k] - mn);
         acc = acc * w1 + ov[k] * w2;
@@ -775,9 +776,7 @@ static hipError_t launch_attention_nu(const AttnArgs& a, int qtp, hipStream_t st
                                : qtp == 4 ? attention_kernel<S, D, 4, P, NU> : attention_kernel<S, D, 8, P, NU>;
   };
   auto k = a.p_lo ? pick(std::true_type{}) : pick(std::false_type{});
-  if (lds > 64 * 1024)
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize,
-                              (int)lds);
+  (void)allow_dynamic_lds(reinterpret_cast<const void*>(k), lds);
   hipLaunchKernelGGL(k, dim3(a.nwg), dim3(kThreads), lds, stream, a);
   return hipGetLastError();
 }

@@ -967,9 +967,7 @@ size_t gemm_as_lds(int M, int ksl, bool lo) {
 
 template <typename Kern>
 static void allow_lds(Kern kernel, size_t bytes) {
-  if (bytes > 64 * 1024)
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
-                              (int)bytes);
+  (void)allow_dynamic_lds(reinterpret_cast<const void*>(kernel), bytes);
 }
 
 template <typename S, int MR, int SRC, bool LO, int OUT>

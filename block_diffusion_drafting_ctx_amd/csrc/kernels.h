@@ -191,4 +191,9 @@ hipError_t launch_feature_dbg(int storage, const float* y, const float* ssq, int
                               const void* gain, float eps, int M, int H, float* out, hipStream_t stream);
 hipError_t launch_clear_u32(uint32_t* p, int n, hipStream_t stream);
 
+// Raises the dynamic-LDS limit of `kernel` on the current device to `bytes`
+// (needed above 64 KB).  The runtime call is made once per (device, kernel)
+// and larger size; later calls are a table lookup.
+hipError_t allow_dynamic_lds(const void* kernel, size_t bytes);
+
 }  // namespace dfl

@@ -2,6 +2,10 @@
 // context commit and small helpers.  Cross-workgroup results always go
 // through plain stores and a following kernel: a fence-and-ticket handoff
 // costs tens of nanoseconds per workgroup on this chip.
+#include <map>
+#include <mutex>
+#include <utility>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -101,7 +105,8 @@ hipError_t launch_verify(const VerifyArgs& a, hipStream_t stream) {
 // Pass 1, grid (vocab chunks, rows), 256 threads: the chunk's logits z = x / T
 // (one round of 8 16-byte loads a thread covers the 8192-entry chunk), its
 // maximum m and s = sum exp(z - m), both reduced in a fixed order, stored as
-// a float pair in the (row, chunk) key slot.
+// a float pair in the (row, chunk) key slot.  A NaN logit carries no mass
+// (it is read as -inf).
 __global__ void __launch_bounds__(256) verify_stats_kernel(const VerifyArgs a) {
   __shared__ float s_red[4];
   constexpr int PER = 8;
@@ -117,7 +122,7 @@ __global__ void __launch_bounds__(256) verify_stats_kernel(const VerifyArgs a) {
     f32x4 x = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
     if (v < v1) x = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p + v));
 #pragma unroll
-    for (int e = 0; e < 4; ++e) z[i][e] = v < v1 ? x[e] * a.inv_temp : -INFINITY;
+    for (int e = 0; e < 4; ++e) z[i][e] = v < v1 && x[e] == x[e] ? x[e] * a.inv_temp : -INFINITY;
   }
   float m = -INFINITY;
 #pragma unroll
@@ -183,15 +188,16 @@ __global__ void __launch_bounds__(256) verify_sample_commit_kernel(const VerifyA
   const float2* gpart = reinterpret_cast<const float2*>(a.part) + (size_t)b * R * NC;
   const bool staged = R * NC <= kSamplePartLds;
   // independent reads, all in flight at once: the partials, the uniforms,
-  // the draft ids and the logit of each draft (-inf outside the vocabulary:
-  // such a draft is never accepted)
+  // the draft ids and the logit of each draft (-inf outside the vocabulary
+  // or at a NaN logit: such a draft is never accepted)
   if (staged)
     for (int k = tid; k < R * NC; k += 256) s_part[k] = gpart[k];
   if (tid < 2 * R) s_u[tid] = a.uniforms[(size_t)b * R * 2 + tid];
   if (tid < a.n_d) {
     const int di = d[tid];
     s_d[tid] = di;
-    s_xd[tid] = di >= 0 && di < a.V ? a.logits[((size_t)b * R + tid) * a.V + di] * a.inv_temp : -INFINITY;
+    const float xd = di >= 0 && di < a.V ? a.logits[((size_t)b * R + tid) * a.V + di] : -INFINITY;
+    s_xd[tid] = xd == xd ? xd * a.inv_temp : -INFINITY;
   }
   __syncthreads();
   const float2* part = staged ? s_part : gpart;
@@ -264,7 +270,8 @@ __global__ void __launch_bounds__(256) verify_sample_commit_kernel(const VerifyA
     f32x4 x = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
     if (in) x = *reinterpret_cast<const f32x4*>(xj + v0 + 4 * q);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) e[4 * q + r] = v0 + 4 * q + r != ex ? __expf(x[r] * a.inv_temp - Mj) : 0.f;
+    for (int r = 0; r < 4; ++r)
+      e[4 * q + r] = v0 + 4 * q + r != ex && x[r] == x[r] ? __expf(x[r] * a.inv_temp - Mj) : 0.f;
   }
   float mine = 0.f;
 #pragma unroll
@@ -454,6 +461,22 @@ __global__ void clear_u32_kernel(uint32_t* p, int n) {
 hipError_t launch_clear_u32(uint32_t* p, int n, hipStream_t stream) {
   hipLaunchKernelGGL(clear_u32_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, p, n);
   return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- launch attributes
+hipError_t allow_dynamic_lds(const void* kernel, size_t bytes) {
+  if (bytes <= 64 * 1024) return hipSuccess;
+  static std::mutex mu;
+  static std::map<std::pair<int, const void*>, size_t> done;  // (device, kernel) -> limit set
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(mu);
+  size_t& have = done[{dev, kernel}];
+  if (have >= bytes) return hipSuccess;
+  e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  if (e == hipSuccess) have = bytes;
+  return e;
 }
 
 }  // namespace dfl

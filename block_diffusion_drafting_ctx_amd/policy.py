@@ -2,15 +2,22 @@
 
 [P2] "DFlash-2: z-lab boosts speculative-decoding throughput", section
 Optimising for maximum speed (the tuning strategy): start with a draft
-maximum of 4 or 6; when the mean length stays below 2, stop
-using the drafter for that model; when the mean length stays at least 1 above
-the current maximum, raise the maximum to the smallest integer above the
-observed mean; otherwise keep it.
+maximum of 4 or 6; when the mean length stays below 2, stop using the
+drafter for that model; when the mean length stays high against the current
+maximum, raise the maximum to the smallest integer above the observed mean
+(the page's example: a mean of 7.5 gives 8); otherwise keep it.
 
 Readings (the pages leave these open):
 - The mean length is the tokens committed per verify step, 1 + accepted /
   steps, the bonus token included: the pages report 4.12 at a maximum of 4,
-  which only that count allows.
+  which only that count allows.  It therefore never exceeds maximum + 1.
+- The raise trigger.  Taken literally ("at least 1 above the maximum") it
+  could fire only at 100% acceptance and would always raise by exactly 2, so
+  the page's own 7.5 -> 8 example could never occur.  The reading here is
+  that the mean has reached the maximum (mean >= n_max: the drafts alone
+  average at least n_max - 1 accepted, the bonus token being the "1"); then
+  the 7.5 -> 8 example is the case n_max = 7 at 93% acceptance, and the
+  page's 4.12 at a maximum of 4 raises the maximum to 5.
 - "Stays" means over `patience` consecutive evaluation windows, a window
   being the verify steps between two calls of `update`.
 - The raised maximum is capped by what the block layout can verify (block - 1
@@ -38,7 +45,7 @@ class DraftLengthPolicy:
         self.patience = patience
         self.min_mean = min_mean
         self.enabled = True
-        self._prev = (0, 0)
+        self._prev = (0, 0, 0)
         self._low = 0
         self._high = 0
         self._target = 0
@@ -48,16 +55,18 @@ class DraftLengthPolicy:
         return 1.0 + accepted / steps
 
     def update(self, counters: Sequence[int]) -> int:
-        steps, accepted = int(counters[0]), int(counters[1])
-        d_steps, d_acc = steps - self._prev[0], accepted - self._prev[1]
-        if d_steps < 0 or d_acc < 0:
+        steps, accepted, drafted = int(counters[0]), int(counters[1]), int(counters[2])
+        d_steps, d_acc, d_dr = steps - self._prev[0], accepted - self._prev[1], drafted - self._prev[2]
+        if d_steps < 0 or d_acc < 0 or d_dr < 0:
             raise ValueError("counters went backwards (cleared context?)")
-        self._prev = (steps, accepted)
+        if d_acc > d_dr:
+            raise ValueError("more drafts accepted than drafted: not verify counters")
+        self._prev = (steps, accepted, drafted)
         if not self.enabled or d_steps == 0:
             return self.n_max if self.enabled else 0
         mean = self.window_mean(d_steps, d_acc)
         self._low = self._low + 1 if mean < self.min_mean else 0
-        if mean >= self.n_max + 1:
+        if mean >= self.n_max:
             self._high += 1
             self._target = max(self._target, math.floor(mean) + 1)
         else:

@@ -88,7 +88,9 @@ enum {
   DFLASH_STAGE_GATEUP = 7,   /* RMSNorm -> gate/up projection, SiLU product */
   DFLASH_STAGE_DOWN = 8,     /* down projection + residual */
   DFLASH_STAGE_LMHEAD = 9,   /* final RMSNorm -> LM head with per-tile argmax (the LM-head kernel alone) */
-  DFLASH_N_STAGES = 10
+  DFLASH_STAGE_LAYER_GEMM = 10, /* the weight-streaming main kernel of every layer product (Q/K/V, O,
+                                   gate/up, down) alone, without its finish kernel; overlaps stages 4-8 */
+  DFLASH_N_STAGES = 11
 };
 
 /* Draft model shape and limits.  Requirements (else DFLASH_EUNSUPPORTED):
@@ -222,8 +224,12 @@ dflash_status dflash_verify(dflash_ctx* ctx, int32_t batch, const float* target_
  *  out_tokens[b] = [d_0 .. d_{n-1}, drawn, -1 ...], ctx_len[b] += n + 1 and
  *  the counters advance; ctx_len[b] + n_d + 1 > max_ctx sets
  *  DFLASH_ERR_VERIFY_OVERFLOW and commits nothing.
- *  temperature must be finite and > 0, else DFLASH_EINVAL and nothing is
- *  launched (T = 0 is dflash_verify). */
+ *  A NaN logit carries no mass (read as -inf): a draft there is rejected
+ *  and no draw lands on it.  Each row needs a finite logit; +inf logits are
+ *  outside this definition.
+ *  temperature must be finite and > 0 with a finite 1/T (a subnormal T is
+ *  rejected), else DFLASH_EINVAL and nothing is launched (T = 0 is
+ *  dflash_verify). */
 dflash_status dflash_verify_sample(dflash_ctx* ctx, int32_t batch, const float* target_logits,
                                    const int32_t* draft_ids, int32_t draft_stride, int32_t n_d,
                                    float temperature, const float* uniforms, int32_t* n_accept,

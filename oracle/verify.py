@@ -81,12 +81,17 @@ def sample_verify(logits: np.ndarray, draft: np.ndarray, n_d: int, temperature: 
     bonus token is drawn from p_{n_d} at uniforms[n_d, 1].  Each emitted
     token then has exactly the target's sampling distribution.  A draft id
     outside the vocabulary has p = 0: it is rejected, and since the target
-    has no mass there, the draw is from p_i unchanged.
+    has no mass there, the draw is from p_i unchanged.  A NaN logit is read
+    as carrying no mass (as -inf would): a draft there is rejected and the
+    draws never land on it (the pages say nothing about NaN; this keeps one
+    bad entry from voiding the whole row).  A row needs one non-NaN, finite
+    logit; +inf entries are outside this definition.
 
     Returns (n, token, out): n accepted drafts, the drawn token, and the n + 1
     committed tokens [d_0 .. d_{n-1}, token].
     """
     x = np.asarray(logits, dtype=np.float64) / float(temperature)
+    x = np.where(np.isnan(x), -np.inf, x)  # no mass on NaN entries
     u = np.asarray(uniforms, dtype=np.float64)
     for i in range(n_d):
         p = np.exp(x[i] - np.max(x[i]))

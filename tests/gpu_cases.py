@@ -6,9 +6,16 @@ generator's tensors before the library touches them, so no oracle input and
 no expected value comes from the HIP path.
 
 Bars (floating point: bf16 operands, fp32 accumulation on the GPU):
-  context feature, cache rows, final hidden state: relative L2 <= 1e-2;
-  logits: max |diff| <= 5e-2 * std(oracle logits);
-  draft ids: equal wherever the oracle's top-1 minus top-2 margin > 0.1;
+  context feature, cache rows: relative L2 <= 1e-2;
+  final hidden state: relative L2 <= 1e-2 over the block and for every row;
+  logits: NaN in the same entries as the oracle, max |diff| <= 5e-2 *
+  std(oracle logits) over the others;
+  draft ids: equal wherever the oracle's top-1 minus top-2 margin > 0.1
+  (the margin to the next smaller distinct value, NaN ignored, so an exact
+  tie of the top value is decided by the lowest-index rule); on the other
+  rows the drafted id must be a non-NaN entry whose oracle logit is within
+  2 * 5e-2 * std of the row maximum (a near-top token); optionally a floor on
+  the share of rows compared exactly;
   verify (accepted length, bonus, committed tokens, context lengths,
   counters): bit-exact.
 """
@@ -38,8 +45,20 @@ def rel_l2(a, b) -> float:
 
 
 def top2_margin(logits: np.ndarray) -> np.ndarray:
-    part = np.partition(logits, -2, axis=-1)
-    return part[..., -1] - part[..., -2]
+    """Per row: largest value minus the largest value below it (NaN ignored;
+    inf when the row holds a single distinct value)."""
+    x = np.asarray(logits, dtype=np.float64)
+    flat = x.reshape(-1, x.shape[-1])
+    out = np.empty(flat.shape[0])
+    for r, row in enumerate(flat):
+        v = row[~np.isnan(row)]
+        if v.size == 0:
+            out[r] = np.inf
+            continue
+        m1 = v.max()
+        below = v[v < m1]
+        out[r] = m1 - below.max() if below.size else np.inf
+    return out.reshape(x.shape[:-1])
 
 
 def log(msg: str) -> None:
@@ -67,11 +86,15 @@ class StepResult:
 def run_step(wl: gen.Workload, seed: int, device="cuda", seqs: Optional[Sequence[int]] = None,
              prefill: bool = False, poison: bool = False, n_d: Optional[int] = None,
              check_oracle: bool = True, accept: Optional[Sequence[int]] = None,
-             max_batch: Optional[int] = None) -> StepResult:
+             max_batch: Optional[int] = None, mutate=None, min_sure: float = 0.0) -> StepResult:
     """Run one step on the library and compare with the oracle on `seqs`.
 
     `accept` overrides the planted acceptance lengths (one per sequence);
-    `max_batch` sizes the context for more sequences than the call passes."""
+    `max_batch` sizes the context for more sequences than the call passes;
+    `mutate(w)` edits the generated weights in place before either side
+    sees them; `min_sure` is the least share of the compared draft rows whose
+    oracle margin must exceed the bar (so that the exact comparison is not
+    vacuous)."""
     from block_diffusion_drafting_ctx_amd import Drafter
 
     res = StepResult()
@@ -82,6 +105,8 @@ def run_step(wl: gen.Workload, seed: int, device="cuda", seqs: Optional[Sequence
     log(f"[case] {wl.name} B={B} seed={seed} prefill={prefill} poison={poison} n_d={n_d} seqs={seqs}")
     gdev = device if wl.hidden >= 1024 else "cpu"  # big inputs are drawn on the GPU
     w = gen.draft_weights(wl, seed, gdev)
+    if mutate is not None:
+        mutate(w)
     w_dev = _to(w, device)
     if prefill:
         ctx_lens = np.zeros(B, dtype=np.int32)
@@ -204,18 +229,35 @@ def run_step(wl: gen.Workload, seed: int, device="cuda", seqs: Optional[Sequence
     h_gpu = hid_dbg.cpu().numpy()[seqs]
     l_gpu = lg_dbg.cpu().numpy()[seqs]
     i_gpu = draft_ids.cpu().numpy()[seqs]
+    n_sure = n_rows = 0
     for j, b in enumerate(seqs):
         e = rel_l2(h_gpu[j], h_or[j])
         res.note("hidden_rel_l2", e)
         assert e <= REL_L2, f"seq {b} final hidden rel L2 {e}"
-        tol = LOGIT_TOL * float(np.std(l_or[j]))
-        dmax = float(np.max(np.abs(l_gpu[j] - l_or[j])))
-        res.note("logit_maxdiff_over_std", dmax / float(np.std(l_or[j])))
+        for i in range(wl.block):
+            e = rel_l2(h_gpu[j][i], h_or[j][i])
+            res.note("hidden_row_rel_l2", e)
+            assert e <= REL_L2, f"seq {b} row {i} final hidden rel L2 {e}"
+        nan_or = np.isnan(l_or[j])
+        assert np.array_equal(np.isnan(l_gpu[j]), nan_or), f"seq {b}: NaN logits differ from the oracle's"
+        std = float(np.std(l_or[j][~nan_or]))
+        tol = LOGIT_TOL * std
+        dmax = float(np.max(np.abs(l_gpu[j][~nan_or] - l_or[j][~nan_or])))
+        res.note("logit_maxdiff_over_std", dmax / std)
         assert dmax <= tol, f"seq {b} logits max diff {dmax} > {tol}"
         marg = top2_margin(l_or[j])
         sure = marg > MARGIN
         assert np.all(i_gpu[j][sure] == d_or[j][sure]), f"seq {b} draft ids differ where margin > {MARGIN}"
+        for i in np.flatnonzero(~sure):  # low margin: a near-top, non-NaN token
+            g = int(i_gpu[j][i])
+            assert 0 <= g < wl.vocab and not nan_or[i, g], f"seq {b} row {i}: drafted id {g} invalid or NaN"
+            top = float(np.nanmax(l_or[j][i]))
+            assert l_or[j][i, g] >= top - 2 * tol, \
+                f"seq {b} row {i}: drafted id {g} at {l_or[j][i, g]:.4f}, row max {top:.4f}"
         res.note("rows_with_margin", float(sure.sum()))
+        n_sure += int(sure.sum())
+        n_rows += wl.block
+    assert n_sure >= min_sure * n_rows, f"only {n_sure} of {n_rows} draft rows have margin > {MARGIN}"
     res.checks.append("oracle parity")
     log(f"[case] {wl.name}: parity ok {res.worst}")
     dr.close()

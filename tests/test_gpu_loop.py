@@ -4,8 +4,10 @@ The oracle's loop (prefill, draft a block, target forward over [bonus, drafts],
 speculative fusion, verify, roll back) runs with the library as the drafter
 and the oracle's float64 tiny causal target as the target.  Verification is
 lossless whatever the drafts are, so the emitted tokens must equal the
-target's own greedy stream exactly -- with the library's random-weight drafts
-and with drafts forced to the target's future tokens (full acceptance).  The
+target's own greedy stream exactly -- with the library's random-weight drafts,
+with a broken drafter whose output projections are all NaN (every draft is
+garbage: NaN logits draft token 0 by the argmax rule), and with drafts forced
+to the target's future tokens (full acceptance).  The
 library's counters must match the loop's accepted lengths, and the draft-length
 policy reads them.
 """
@@ -31,16 +33,21 @@ PROMPT = [5, 17, 901, 33, 250, 7, 64, 1000, 3, 12]
 class LibraryDrafter:
     """One sequence through the C-ABI library (fp32 storage)."""
 
-    def __init__(self, wl, seed: int, future: Sequence[int] = (), layout: str = "anchor"):
+    def __init__(self, wl, seed: int, future: Sequence[int] = (), layout: str = "anchor", nan_weights=False):
         from block_diffusion_drafting_ctx_amd import Drafter
 
-        self.w = _to(gen.draft_weights(wl, seed=seed), "cuda")
+        w = gen.draft_weights(wl, seed=seed)
+        if nan_weights:
+            for lw in w["layers"]:
+                lw["w_o"].fill_(float("nan"))
+        self.w = _to(w, "cuda")
         self.dr = Drafter(config_for(wl, 1, max_fuse_rows=64), self.w, "cuda")
         self.wl = wl
         self.future = list(future)
         self.layout = layout
         self.emitted = 1
         self.accepted: List[int] = []
+        self.drafts_seen: List[np.ndarray] = []
 
     def _rows(self, feats):
         return [torch.as_tensor(np.asarray(f), dtype=torch.float32, device="cuda")[None].contiguous() for f in feats]
@@ -53,6 +60,7 @@ class LibraryDrafter:
         out = torch.zeros(1, self.wl.block, dtype=torch.int32, device="cuda")
         self.dr.draft_block(bid, out)
         d = out[0].cpu().numpy()
+        self.drafts_seen.append(d.copy())
         if self.future:
             first = 1 if self.layout == "anchor" else 0
             for i in range(first, len(d)):
@@ -89,17 +97,20 @@ def target_and_greedy():
 
 
 @pytest.mark.parametrize("layout", ["anchor", "shifted"])
-@pytest.mark.parametrize("kind", ["random", "forced"])
+@pytest.mark.parametrize("kind", ["random", "nan", "forced"])
 def test_library_loop_output_equals_greedy(target_and_greedy, layout, kind):
     tgt, greedy = target_and_greedy
     log(f"[case] loop layout={layout} drafts={kind}")
-    dr = LibraryDrafter(WL, seed=21, future=greedy if kind == "forced" else (), layout=layout)
+    dr = LibraryDrafter(WL, seed=21, future=greedy if kind == "forced" else (), layout=layout,
+                        nan_weights=kind == "nan")
     out, acc = speculative_generate(tgt, dr, PROMPT, N_TOK, WL.block, WL.mask_id, layout)
     assert out == greedy
     n_d = WL.block - 1 if layout == "anchor" else WL.block
     assert acc == dr.accepted and all(0 <= n <= n_d for n in acc)
     if kind == "forced":
         assert all(n == n_d for n in acc[:-1])
+    if kind == "nan":  # all-NaN logits: the argmax rule drafts index 0 everywhere
+        assert all(np.all(d == 0) for d in dr.drafts_seen)
     steps, accepted, drafted = dr.dr.stats()
     assert (steps, accepted, drafted) == (len(acc), sum(acc), len(acc) * n_d)
     # the tuning rule over the same counters: random drafts are rarely

@@ -175,6 +175,8 @@ def test_host_checks_reject_bad_sizes():
     ("dflash2-27b-shape-conv-b8", [0, 7]),
 ])
 def test_full_size(name, seqs):
+    # at these widths about 70% of the draft rows clear the 0.1 margin; a
+    # quarter is the floor below which the exact comparison would say little
     wl = gen.WORKLOADS[name]
-    run_step(wl, seed=20, seqs=seqs, poison=True)
+    run_step(wl, seed=20, seqs=seqs, poison=True, min_sure=0.25)
     torch.cuda.empty_cache()

@@ -24,6 +24,7 @@ MARGIN = 1e-5
 def margins(logits, draft, n_d, T, u):
     """Smallest distance of a deciding uniform to its boundary (float64)."""
     x = np.asarray(logits, np.float64) / T
+    x = np.where(np.isnan(x), -np.inf, x)
     worst = np.inf
     for i in range(n_d + 1):
         p = np.exp(x[i] - x[i].max())
@@ -44,16 +45,19 @@ def margins(logits, draft, n_d, T, u):
     return worst
 
 
-def check_against_oracle(vocab, batch, n_d, T, sigma, plant="prefix", bad_ids=False, seed=33):
+def check_against_oracle(vocab, batch, n_d, T, sigma, plant="prefix", bad_ids=False, seed=33, nan_entries=False):
     """Seeded logits [batch, n_d+1, vocab] ~ N(0, sigma^2), drafts and uniforms;
     plant: 'prefix' makes a random-length prefix of drafts likely (row max + 3),
     'all' makes every draft near-certain (row max + 30, accept uniforms < 0.9);
     bad_ids puts ids outside the vocabulary (negative and >= vocab) into the
-    drafts.  Every sequence off a rounding boundary must match the oracle."""
+    drafts; nan_entries puts NaN logits at random entries of every row and
+    under some drafts (no mass there: such a draft is rejected).  Every
+    sequence off a rounding boundary must match the oracle."""
     stride = max(1, n_d)
     block = max(16, n_d)
     wl = gen.Workload("sv", 256, 4, 2, 64, 2, 512, vocab, block, 3, batch, 10, 60, "bf16")
-    log(f"[case] sample verify V={vocab} B={batch} n_d={n_d} T={T} plant={plant} bad_ids={bad_ids}")
+    log(f"[case] sample verify V={vocab} B={batch} n_d={n_d} T={T} plant={plant} bad_ids={bad_ids} "
+        f"nan={nan_entries}")
     from block_diffusion_drafting_ctx_amd import Drafter
 
     dr = Drafter(config_for(wl, batch), _to(gen.draft_weights(wl, 41, "cpu"), "cuda"), "cuda")
@@ -69,6 +73,11 @@ def check_against_oracle(vocab, batch, n_d, T, sigma, plant="prefix", bad_ids=Fa
         else:
             for i in range(int(rng.integers(0, n_d + 1))):
                 logits[b, i, drafts[b, i]] = logits[b, i].max() + 3.0
+        if nan_entries:
+            for i in range(n_d + 1):
+                logits[b, i, rng.choice(vocab, size=vocab // 16, replace=False)] = np.nan
+            for i in range(0, n_d, 3):
+                logits[b, i, drafts[b, i]] = np.nan
         if bad_ids and n_d:
             for i in rng.choice(n_d, size=min(n_d, 3), replace=False):
                 drafts[b, i] = int(rng.choice([-1, -7, vocab, vocab + 12345]))
@@ -124,6 +133,11 @@ def test_sample_verify_drafts_outside_the_vocabulary():
     check_against_oracle(1024, 8, 8, 1.0, 2.0, bad_ids=True)
 
 
+@pytest.mark.parametrize("vocab", [1024, 151936])
+def test_sample_verify_nan_entries_carry_no_mass(vocab):
+    check_against_oracle(vocab, 8, 8, 1.0, 2.0 if vocab == 1024 else 6.0, nan_entries=True)
+
+
 def test_sample_verify_partials_beyond_lds():
     # 65 rows x 40 vocabulary chunks of partials exceed the LDS staging: the
     # per-sequence pass reads them from global memory
@@ -138,7 +152,8 @@ def test_sample_verify_rejects_bad_temperature():
     z = lambda *s: torch.zeros(*s, dtype=torch.int32, device="cuda")  # noqa: E731
     lg = torch.zeros(1, 9, 1024, dtype=torch.float32, device="cuda")
     uu = torch.zeros(1, 9, 2, dtype=torch.float32, device="cuda")
-    for T in (0.0, -1.0, float("inf"), float("nan")):
+    # (1e-39 and 1e-45 are fp32 subnormals whose reciprocal overflows)
+    for T in (0.0, -1.0, float("inf"), float("nan"), 1e-39, 1e-45):
         with pytest.raises(_abi.DFlashError):
             dr.verify_sample(lg, z(1, 8), 8, 8, T, uu, z(1), z(1), z(1, 9))
     dr.close()

@@ -74,3 +74,28 @@ def test_draft_outside_the_vocabulary_is_rejected_and_removes_nothing():
         n, tok, out = sample_verify(logits, draft, 2, 1.3, u)
         assert n == 0 and out == [tok]
         assert tok == int(np.searchsorted(np.cumsum(p), 0.99)) == 39
+
+
+@pytest.mark.parametrize("draft_tok", [1, 3])
+def test_nan_entries_carry_no_mass(draft_tok):
+    # entries 1 and 4 are NaN: over a grid of uniforms the emitted token has
+    # the softmax distribution of the finite entries alone, a draft on a NaN
+    # entry is never accepted, and no draw lands on a NaN entry
+    rng = np.random.default_rng(8)
+    logits = rng.normal(size=(2, 6)) * 1.2
+    logits[0, [1, 4]] = np.nan
+    finite = [0, 2, 3, 5]
+    want = np.zeros(6)
+    want[finite] = softmax(logits[0, finite], 0.9)
+    G = 200
+    grid = (np.arange(G) + 0.5) / G
+    counts = np.zeros(6)
+    for ua in grid:
+        for us in grid:
+            u = np.array([[ua, us], [0.5, 0.5]])
+            n, _, out = sample_verify(logits, np.array([draft_tok]), 1, 0.9, u)
+            if draft_tok == 1:
+                assert n == 0
+            counts[out[0]] += 1
+    assert counts[1] == 0 and counts[4] == 0
+    np.testing.assert_allclose(counts / G**2, want, atol=4.0 / G)

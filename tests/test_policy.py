@@ -2,7 +2,8 @@
 
 [P2] "DFlash-2: z-lab boosts speculative-decoding throughput", section
 Optimising for maximum speed: a mean length of 7.5 moves the maximum to 8;
-4.12 at a maximum of 4 keeps it; a mean below 2 drops the drafter.
+a mean below 2 drops the drafter.  Every window below is a set of counters
+verify can produce: accepted <= drafted = steps * n_max.
 """
 
 import pytest
@@ -10,25 +11,36 @@ import pytest
 from block_diffusion_drafting_ctx_amd.policy import DraftLengthPolicy
 
 
-def feed(policy, windows):
-    """windows: (steps, accepted) per window; returns the decisions."""
-    steps = acc = 0
+def feed(policy, windows, n_max_of=None):
+    """windows: (steps, accepted) per window at the policy's current maximum;
+    returns the decisions.  Drafted counts follow the maximum in force."""
+    steps = acc = drafted = 0
     out = []
     for s, a in windows:
+        assert a <= s * policy.n_max, "not a window verify can produce"
         steps += s
         acc += a
-        out.append(policy.update([steps, acc, 0]))
+        drafted += s * policy.n_max
+        out.append(policy.update([steps, acc, drafted]))
     return out
 
 
 def test_pages_example_mean_7_5_raises_to_8():
-    p = DraftLengthPolicy(n_max=6, patience=3)
-    assert feed(p, [(10, 65)] * 3) == [6, 6, 8]  # mean 1 + 6.5 = 7.5 >= 6 + 1
+    # at a maximum of 7, 65 of 70 drafts accepted over 10 steps: mean 7.5
+    p = DraftLengthPolicy(n_max=7, patience=3)
+    assert feed(p, [(10, 65)] * 3) == [7, 7, 8]
 
 
-def test_mean_4_12_at_maximum_4_keeps_it():
+def test_mean_4_12_at_maximum_4_raises_to_5():
+    # the page's third coding stage: 78.06% of 4 drafts, mean 4.12 (>= 4)
     p = DraftLengthPolicy(n_max=4, patience=2)
-    assert feed(p, [(100, 312)] * 5) == [4] * 5  # mean 4.12 < 5
+    assert feed(p, [(100, 312)] * 2) == [4, 5]
+
+
+def test_mean_4_49_at_maximum_6_keeps_it():
+    # 58.13% of 6 drafts, mean 4.49: between 2 and the maximum
+    p = DraftLengthPolicy(n_max=6, patience=1)
+    assert feed(p, [(100, 349)] * 4) == [6] * 4
 
 
 def test_low_mean_drops_the_drafter_and_it_stays_dropped():
@@ -45,14 +57,16 @@ def test_only_consistent_windows_count():
 
 def test_raise_is_capped_by_the_layout():
     p = DraftLengthPolicy(n_max=6, cap=7, patience=1)
-    assert feed(p, [(4, 28)]) == [7]  # mean 8 -> 9, capped at 7
+    assert feed(p, [(4, 24)]) == [7]  # mean 7 -> 8, capped at 7
 
 
 def test_empty_window_keeps_and_bad_counters_raise():
     p = DraftLengthPolicy(n_max=4)
     assert p.update([0, 0, 0]) == 4
     p.update([10, 20, 40])
-    with pytest.raises(ValueError):
+    with pytest.raises(ValueError):  # backwards
         p.update([5, 20, 40])
+    with pytest.raises(ValueError):  # accepted above drafted
+        DraftLengthPolicy(n_max=4).update([10, 65, 40])
     with pytest.raises(ValueError):
         DraftLengthPolicy(n_max=0)
