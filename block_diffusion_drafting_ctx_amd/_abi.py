@@ -25,7 +25,7 @@ STAGE = {n: i for i, n in enumerate(STAGES)}
 
 EXPORTED = [
     "dflash_workspace_bytes", "dflash_create", "dflash_reload_weights", "dflash_fuse_ctx", "dflash_verify",
-    "dflash_verify_sample", "dflash_draft_block",
+    "dflash_verify_sample", "dflash_verify_static", "dflash_draft_block",
     "dflash_check", "dflash_clear_errors", "dflash_stats", "dflash_stage_timing", "dflash_stage_time",
     "dflash_destroy", "dflash_last_error", "dflash_version",
 ]
@@ -72,6 +72,7 @@ def lib():
             "dflash_fuse_ctx": (i32, [vp, i32, _PP, i32, i32, vp, vp]),
             "dflash_verify": (i32, [vp, i32, vp, vp, i32, i32, vp, vp, vp, vp]),
             "dflash_verify_sample": (i32, [vp, i32, vp, vp, i32, i32, ctypes.c_float, vp, vp, vp, vp, vp]),
+            "dflash_verify_static": (i32, [i32, i32, vp, vp, i32, i32, vp, i32, vp, vp, vp, vp, vp, vp]),
             "dflash_draft_block": (i32, [vp, i32, vp, vp, vp, vp, vp]),
             "dflash_check": (i32, [vp, ctypes.POINTER(ctypes.c_uint32), vp]),
             "dflash_clear_errors": (i32, [vp, vp]),
@@ -261,6 +262,33 @@ def dflash_verify_sample(ctx: Context, target_logits: torch.Tensor, draft_ids: t
                                       _ptr(uniforms, torch.float32, b * (n_d + 1) * 2, "uniforms"),
                                       _ptr(n_accept, torch.int32, b, "n_accept"), _ptr(bonus, torch.int32, b, "bonus"),
                                       _ptr(out_tokens, torch.int32, b * (n_d + 1), "out_tokens"), _stream(stream)))
+
+
+def dflash_verify_static(target_logits: torch.Tensor, draft_ids: torch.Tensor, draft_stride: int, n_d: int,
+                         ctx_len: torch.Tensor, max_ctx: int, n_accept: torch.Tensor, bonus: torch.Tensor,
+                         out_tokens: torch.Tensor, stats: Optional[torch.Tensor] = None,
+                         error_word: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Context-free greedy verify (library-owned static scratch; allocates nothing)."""
+    if target_logits.dim() != 3 or target_logits.shape[1] != n_d + 1:
+        raise ValueError("target_logits must be [batch, n_d + 1, vocab]")
+    b, vocab = target_logits.shape[0], target_logits.shape[2]
+    lp = _ptr(target_logits, torch.float32, name="target_logits")
+    if n_d > 0:
+        if draft_ids.dtype != torch.int32 or not draft_ids.is_cuda:
+            raise ValueError("draft_ids must be a device int32 tensor")
+        span = (b - 1) * draft_stride + n_d
+        if draft_ids.storage_offset() + span > draft_ids.untyped_storage().nbytes() // 4:
+            raise ValueError("draft_ids too small for batch * draft_stride")
+        dp = draft_ids.data_ptr()
+    else:
+        dp = None
+    sp = None if stats is None else _ptr(stats, torch.int64, 3, "stats")
+    ep = None if error_word is None else _ptr(error_word, torch.int32, 1, "error_word")
+    _check(lib().dflash_verify_static(b, vocab, lp, dp, draft_stride, n_d, _ptr(ctx_len, torch.int32, b, "ctx_len"),
+                                      int(max_ctx), _ptr(n_accept, torch.int32, b, "n_accept"),
+                                      _ptr(bonus, torch.int32, b, "bonus"),
+                                      _ptr(out_tokens, torch.int32, b * (n_d + 1), "out_tokens"), sp, ep,
+                                      _stream(stream)))
 
 
 def dflash_draft_block(ctx: Context, block_ids: torch.Tensor, draft_ids: torch.Tensor,

@@ -544,6 +544,47 @@ dflash_status dflash_verify(dflash_ctx* c, int32_t batch, const float* logits, c
   return hip_status(launch_verify(a, s), "verify launch");
 }
 
+dflash_status dflash_verify_static(int32_t batch, int32_t vocab, const float* logits, const int32_t* draft_ids,
+                                   int32_t draft_stride, int32_t n_d, int32_t* ctx_len, int32_t max_ctx,
+                                   int32_t* n_accept, int32_t* bonus, int32_t* out_tokens, uint64_t* stats,
+                                   uint32_t* error_word, void* stream) {
+  g_last_error.clear();
+  if (batch < 0) return fail(DFLASH_EINVAL, "batch out of range");
+  if (n_d < 0 || n_d > kMaxNd) return fail(DFLASH_EINVAL, "n_d out of range [0, 64]");
+  if (vocab <= 0 || vocab % 64) return fail(DFLASH_EINVAL, "vocab must be a positive multiple of 64");
+  if (max_ctx < 1) return fail(DFLASH_EINVAL, "max_ctx must be positive");
+  const int nchunks = (vocab + kVerifyChunk - 1) / kVerifyChunk;
+  const size_t keys = (size_t)batch * (size_t)(n_d + 1) * (size_t)nchunks;
+  if (keys > kStaticVerifyKeys)
+    return fail(DFLASH_EINVAL, "batch * (n_d + 1) * ceil(vocab / 8192) = " + std::to_string(keys) +
+                                   " exceeds the static scratch (" + std::to_string(kStaticVerifyKeys) + " keys)");
+  if (batch == 0) return DFLASH_OK;
+  if (!logits || !ctx_len || !n_accept || !bonus || !out_tokens || (n_d > 0 && !draft_ids))
+    return fail(DFLASH_EINVAL, "null argument");
+  if (reinterpret_cast<uintptr_t>(logits) % 16) return fail(DFLASH_EINVAL, "target_logits must be 16-byte aligned");
+  if (n_d > 0 && draft_stride < n_d) return fail(DFLASH_EINVAL, "draft_stride < n_d");
+  uint64_t* keys_dev = nullptr;
+  if (dflash_status st = hip_status(static_verify_scratch(&keys_dev), "static scratch lookup")) return st;
+  VerifyArgs a{};
+  a.logits = logits;
+  a.draft = draft_ids;
+  a.draft_stride = draft_stride;
+  a.n_d = n_d;
+  a.batch = batch;
+  a.V = vocab;
+  a.max_ctx = max_ctx;
+  a.chunk = kVerifyChunk;
+  a.nchunks = nchunks;
+  a.part = keys_dev;
+  a.n_accept = n_accept;
+  a.bonus = bonus;
+  a.out_tokens = out_tokens;
+  a.ctx_len = ctx_len;
+  a.stats = reinterpret_cast<unsigned long long*>(stats);
+  a.err = error_word;
+  return hip_status(launch_verify(a, static_cast<hipStream_t>(stream)), "verify launch");
+}
+
 dflash_status dflash_verify_sample(dflash_ctx* c, int32_t batch, const float* logits, const int32_t* draft_ids,
                                    int32_t draft_stride, int32_t n_d, float temperature, const float* uniforms,
                                    int32_t* n_accept, int32_t* bonus, int32_t* out_tokens, void* stream) {

@@ -173,8 +173,15 @@ struct VerifyArgs {
   const float* uniforms;  // [batch, n_d+1, 2]: (accept test, inverse-CDF draw) per row
 };
 // Two launches: the streaming argmax over the target logits, then the
-// per-sequence accepted prefix, bonus token, commit and counters.
+// per-sequence accepted prefix, bonus token, commit and counters (a null
+// stats or err pointer skips the counters / the error bit).
 hipError_t launch_verify(const VerifyArgs& a, hipStream_t stream);
+// Keys of the library-owned static scratch the context-free verify uses
+// (512 KB per device, for the life of the process).
+constexpr size_t kStaticVerifyKeys = 65536;
+// Device address of the current device's copy of that scratch (looked up
+// once per device with hipGetSymbolAddress, then cached).
+hipError_t static_verify_scratch(uint64_t** ptr);
 // Sampling mode, two launches: per (row, vocab chunk) the maximum and
 // exp-sum of logits / T (kept in the key slots), then per sequence the
 // accept tests, the inverse-CDF draw of the emitted token, commit, counters.

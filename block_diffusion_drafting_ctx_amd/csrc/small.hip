@@ -80,16 +80,45 @@ __global__ void __launch_bounds__(64) verify_commit_kernel(const VerifyArgs a) {
     a.bonus[b] = s_g[n];
     const int t0 = a.ctx_len[b];
     if (t0 < 0 || t0 + R > a.max_ctx) {
-      atomicOr(a.err, kErrVerifyOverflow);
+      if (a.err) atomicOr(a.err, kErrVerifyOverflow);
     } else {
       a.ctx_len[b] = t0 + n + 1;
     }
-    atomicAdd(&a.stats[0], 1ull);
-    atomicAdd(&a.stats[1], (unsigned long long)n);
-    atomicAdd(&a.stats[2], (unsigned long long)a.n_d);
+    if (a.stats) {
+      atomicAdd(&a.stats[0], 1ull);
+      atomicAdd(&a.stats[1], (unsigned long long)n);
+      atomicAdd(&a.stats[2], (unsigned long long)a.n_d);
+    }
   }
   __syncthreads();
   for (int i = tid; i < R; i += 64) a.out_tokens[(size_t)b * R + i] = i <= s_n ? s_g[i] : -1;
+}
+
+// ---------------------------------------------------------------- library-owned scratch
+// For callers that cannot allocate device memory: the (row, vocabulary chunk)
+// argmax keys of the context-free greedy verify live in this array, one copy
+// per device for the life of the process.  Every call on a device shares it
+// (and keeps the last call's keys; each key is written before it is read, so
+// nothing needs clearing): calls that overlap on one device race.
+static __device__ __align__(256) uint64_t scratch[kStaticVerifyKeys];
+
+hipError_t static_verify_scratch(uint64_t** ptr) {
+  static std::mutex mu;
+  static std::map<int, uint64_t*> addr;  // device -> device address of its copy of `scratch`
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = addr.find(dev);
+  if (it == addr.end()) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    it = addr.emplace(dev, static_cast<uint64_t*>(p)).first;
+  }
+  *ptr = it->second;
+  return hipSuccess;
 }
 
 hipError_t launch_verify(const VerifyArgs& a, hipStream_t stream) {

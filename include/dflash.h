@@ -207,6 +207,31 @@ dflash_status dflash_verify(dflash_ctx* ctx, int32_t batch, const float* target_
                             const int32_t* draft_ids, int32_t draft_stride, int32_t n_d,
                             int32_t* n_accept, int32_t* bonus, int32_t* out_tokens, void* stream);
 
+/* Greedy verification without a context, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same rule, kernels and outputs as
+ * dflash_verify, but nothing needs creating first.  Its only scratch, the
+ * (row, vocabulary chunk) argmax keys, lives in a library-owned static device
+ * array of 65536 keys (512 KB per device, held until the process ends), so
+ *     batch * (n_d + 1) * ceil(vocab / 8192) <= 65536
+ * (batch 32 at n_d 16 and vocab 151936 needs 10336), else DFLASH_EINVAL.
+ * The call allocates nothing.  Every call on a device shares that array:
+ * calls that overlap on one device (two streams, two threads) race, so they
+ * must be ordered.
+ *  target_logits: fp32 [batch, n_d + 1, vocab], 16-byte aligned; vocab a
+ *     positive multiple of 64.
+ *  ctx_len: device int32[batch], advanced by n + 1 per sequence unless
+ *     ctx_len[b] + n_d + 1 > max_ctx (then left as is and DFLASH_ERR_VERIFY_OVERFLOW
+ *     is or-ed into *error_word).
+ *  stats: nullable device uint64[3] {steps, accepted, drafted}, accumulated.
+ *  error_word: nullable device uint32, sticky bits as in dflash_check.
+ *  draft_ids, draft_stride, n_d, n_accept, bonus, out_tokens: as dflash_verify.
+ *  batch == 0 is a no-op. */
+dflash_status dflash_verify_static(int32_t batch, int32_t vocab, const float* target_logits,
+                                   const int32_t* draft_ids, int32_t draft_stride, int32_t n_d,
+                                   int32_t* ctx_len, int32_t max_ctx, int32_t* n_accept, int32_t* bonus,
+                                   int32_t* out_tokens, uint64_t* stats, uint32_t* error_word, void* stream);
+
 /* Verification when the target samples at temperature T > 0.  The pages
  * measure a sampling mode but give no rule ([P1] Real-world integration,
  * the thinking setting); the rule here is the standard lossless

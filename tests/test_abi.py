@@ -76,6 +76,17 @@ def test_calls_reject_null_context(lib):
     assert lib.dflash_verify(None, 1, None, None, 1, 1, None, None, None, None) == _abi.DFLASH_EINVAL
     assert lib.dflash_draft_block(None, 1, None, None, None, None, None) == _abi.DFLASH_EINVAL
     assert lib.dflash_reload_weights(None, None) == _abi.DFLASH_EINVAL
+    # the context-free verify checks its sizes on the host before any device call:
+    # beyond the static scratch (2000 x 17 x 19 keys), a bad vocabulary, bad n_d
+    assert lib.dflash_verify_static(2000, 151936, None, None, 16, 16, None, 100, None, None, None, None, None,
+                                    None) == _abi.DFLASH_EINVAL
+    assert "static scratch" in lib.dflash_last_error().decode()
+    assert lib.dflash_verify_static(1, 1000, None, None, 1, 1, None, 100, None, None, None, None, None,
+                                    None) == _abi.DFLASH_EINVAL
+    assert lib.dflash_verify_static(1, 1024, None, None, 1, 65, None, 100, None, None, None, None, None,
+                                    None) == _abi.DFLASH_EINVAL
+    assert lib.dflash_verify_static(0, 1024, None, None, 1, 1, None, 100, None, None, None, None, None,
+                                    None) == _abi.DFLASH_OK
     lib.dflash_destroy(None)
 
 
