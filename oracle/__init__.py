@@ -55,6 +55,13 @@ Parity status of each function (what pins it, in ``tests/test_oracle_*``):
                             target's softmax (the lossless property); the
                             low-temperature limit equals ``greedy_verify``;
                             full acceptance draws the bonus by inverse CDF.
+* ``kv8_quantize`` / 8-bit cache path -- pinned: brute-force nearest
+                            integer search with ties to even, the half-step
+                            error bound, exactly representable runs, zero
+                            runs, the stored context K equal to the 8-bit
+                            round trip of the 16-bit path's (rotated) K, and a
+                            single-key block whose attention output is the
+                            round trip of its own V.
 * ``AcceptanceStats``    -- pinned: the pages' printed (rate, mean length)
                             pairs (``tests/golden/acceptance_stats.txt``).
 * real-model acceptance behaviour -- parity unpinned (needs trained weights).
@@ -76,6 +83,9 @@ from .draft import (  # noqa: F401
     lm_head_logits,
     fuse_ctx,
     draft_block,
+    kv8_quantize,
+    kv8_dequantize,
+    kv8_roundtrip,
 )
 from .verify import argmax_lowest, greedy_verify, inverse_cdf, sample_verify, verify_step, AcceptanceStats  # noqa: F401
 from .tiny_target import TinyTarget  # noqa: F401

@@ -14,7 +14,11 @@ Readings taken where the pages are silent (each is restated at its function):
   no mask at all (non-causal over context and block);
 * the context feature goes through each layer's own K and V projections;
 * DFlash-2 local convolution: residual, width 3, centred taps, zero padding
-  at the block edges, after the attention residual and before the MLP norm.
+  at the block edges, after the attention residual and before the MLP norm;
+* optional 8-bit draft KV cache (the "q8" setting the DFlash-2 page measures
+  in its precision-cost section): every K/V entry attention reads, context
+  rows and the block's own rows alike, goes through the 8-bit format of
+  ``kv8_quantize``.
 """
 
 from __future__ import annotations
@@ -43,6 +47,7 @@ class OracleDims:
     rms_eps: float = 1e-6
     rope_theta: float = 1e6
     conv_width: int = 0  # 0 (DFlash) or 3 (DFlash-2 local convolution)
+    kv_int8: bool = False  # 8-bit draft KV cache (kv8_quantize) instead of the storage type
 
 
 @dataclass
@@ -161,6 +166,48 @@ def depthwise_conv3(x: np.ndarray, w: np.ndarray) -> np.ndarray:
     return y
 
 
+KV8_BLOCK = 32
+
+
+def kv8_quantize(x: np.ndarray):
+    """8-bit KV entries: symmetric integers with one scale per 32 values.
+
+    x: [..., D] with D a multiple of 32 (the last axis is one KV head's row).
+    Every run of 32 consecutive values of a row gets the scale
+    s = max|x| / 127 and the integers q = round-half-even(x / s), clipped to
+    [-127, 127]; a run of zeros gets s = 0 and q = 0.  Returns (q [..., D]
+    int64, s [..., D/32] float64); the stored value is q * s.
+
+    The DFlash-2 page's precision-cost section compares an f16 KV cache with
+    an 8-bit ("q8") one -- acceptance 78.06% -> 74.88% at its third coding
+    stage -- without defining the format.  q8 there is llama.cpp's 8-bit
+    block format (32 values, one scale); the scale is kept in float64 here
+    (float32 on the GPU) rather than float16.
+    """
+    x = np.asarray(x, dtype=F64)
+    d = x.shape[-1]
+    assert d % KV8_BLOCK == 0
+    blk = x.reshape(x.shape[:-1] + (d // KV8_BLOCK, KV8_BLOCK))
+    s = np.max(np.abs(blk), axis=-1) / 127.0
+    safe = np.where(s > 0, s, 1.0)
+    q = np.where(s[..., None] > 0, np.rint(blk / safe[..., None]), 0.0)
+    q = np.clip(q, -127.0, 127.0)
+    return q.reshape(x.shape).astype(np.int64), s
+
+
+def kv8_dequantize(q: np.ndarray, s: np.ndarray) -> np.ndarray:
+    """Values of 8-bit KV entries: q * s, s repeated over each run of 32."""
+    q = np.asarray(q, dtype=F64)
+    d = q.shape[-1]
+    blk = q.reshape(q.shape[:-1] + (d // KV8_BLOCK, KV8_BLOCK)) * np.asarray(s, dtype=F64)[..., None]
+    return blk.reshape(q.shape)
+
+
+def kv8_roundtrip(x: np.ndarray) -> np.ndarray:
+    """What an 8-bit cache entry holds after x is stored in it."""
+    return kv8_dequantize(*kv8_quantize(x))
+
+
 def swiglu_mlp(u: np.ndarray, lw: LayerWeights) -> np.ndarray:
     """SwiGLU feed-forward: (silu(u W_gate^T) * (u W_up^T)) W_down^T."""
     g = u @ np.asarray(lw.w_gate, F64).T
@@ -193,13 +240,16 @@ def context_kv(c: np.ndarray, lw: LayerWeights, pos: np.ndarray, dims: OracleDim
 
     KV-cache-integration bullet of the "Block-diffusion architecture"
     section: the feature goes directly into the Key and Value projections of
-    each draft layer.  K is stored after the rotary embedding.
-    Returns K, V: [n, Hkv, D].
+    each draft layer.  K is stored after the rotary embedding (and, with the
+    8-bit cache, quantised after it).  Returns the stored K, V: [n, Hkv, D].
     """
     n = c.shape[0]
     k = (c @ np.asarray(lw.w_k, F64).T).reshape(n, dims.n_kv_heads, dims.head_dim)
     v = (c @ np.asarray(lw.w_v, F64).T).reshape(n, dims.n_kv_heads, dims.head_dim)
-    return rope(k, pos, dims.rope_theta), v
+    k = rope(k, pos, dims.rope_theta)
+    if dims.kv_int8:
+        return kv8_roundtrip(k), kv8_roundtrip(v)
+    return k, v
 
 
 @dataclass
@@ -271,7 +321,10 @@ def draft_layer(x: np.ndarray, lw: LayerWeights, k_ctx: np.ndarray, v_ctx: np.nd
 
     x: [Bs, H] residual stream; k_ctx, v_ctx: [T, Hkv, D] this layer's cached
     context entries (T may be 0); pos: [Bs] positions of the block rows.
-    Block queries attend to [context keys ; block keys] with no mask.
+    Block queries attend to [context keys ; block keys] with no mask.  With
+    the 8-bit cache the block's own K/V are read back from it too (the
+    attention reads every key from the cache), so they take the 8-bit round
+    trip like the context rows.
     """
     n = x.shape[0]
     u = rmsnorm(x, lw.g_in, dims.rms_eps)
@@ -280,6 +333,8 @@ def draft_layer(x: np.ndarray, lw: LayerWeights, k_ctx: np.ndarray, v_ctx: np.nd
     v = (u @ np.asarray(lw.w_v, F64).T).reshape(n, dims.n_kv_heads, dims.head_dim)
     q = rope(q, pos, dims.rope_theta)
     k = rope(k, pos, dims.rope_theta)
+    if dims.kv_int8:
+        k, v = kv8_roundtrip(k), kv8_roundtrip(v)
     keys = np.concatenate([np.asarray(k_ctx, F64), k], axis=0)
     vals = np.concatenate([np.asarray(v_ctx, F64), v], axis=0)
     o = gqa_attention(q, keys, vals).reshape(n, dims.n_q_heads * dims.head_dim)
