@@ -43,7 +43,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="qwen3-8b-shape-b1")
-    ap.add_argument("--secondary", default="qwen3-8b-shape-b32-ragged,long-ctx-32k-b4,dflash2-27b-shape-conv-b8",
+    ap.add_argument("--secondary", default="qwen3-8b-shape-b32-ragged,long-ctx-32k-b4,long-ctx-32k-b4-kv8,"
+                                           "dflash2-27b-shape-conv-b8",
                     help="comma-separated extra workloads reported under 'secondary' ('' for none)")
     ap.add_argument("--prefill", default="qwen3-8b-shape-b1:4096:4096",
                     help="WORKLOAD:ROWS:CHUNK -- also time prompt-scale fusion of ROWS prompt rows per sequence "
@@ -68,6 +69,7 @@ def parse():
 def stage_bytes(wl, batch, ctx_lens):
     """Algorithmic HBM bytes per launch of each stage (weights once, inputs and outputs once)."""
     S = 2 if wl.storage == "bf16" else 4
+    KV = 1 + 4 / 32 if wl.kv == "int8" else S  # bytes per cache entry (8-bit: value + its share of a run scale)
     H, D, F, V = wl.hidden, wl.head_dim, wl.ffn, wl.vocab
     Nq, Nk = wl.n_q_heads * D, wl.n_kv_heads * D
     Md, Mf = batch * wl.block, batch * wl.t_new
@@ -75,11 +77,11 @@ def stage_bytes(wl, batch, ctx_lens):
     ctx = float(np.sum(ctx_lens))
     b = {
         "fuse_fc": H * wl.n_target_layers * H * S + Mf * wl.n_target_layers * H * S + Mf * H * (4 + act),
-        "ctx_kv": wl.n_layers * 2 * Nk * H * S + Mf * H * act + wl.n_layers * 2 * Mf * Nk * S,
+        "ctx_kv": wl.n_layers * 2 * Nk * H * S + Mf * H * act + wl.n_layers * 2 * Mf * Nk * KV,
         "verify": Mf * V * 4,
         "embed": Md * H * S + Md * H * (4 + act),
-        "qkv": (Nq + 2 * Nk) * H * S + Md * H * act + Md * (Nq * act + 2 * Nk * S),
-        "attn": (ctx + Md) * 2 * Nk * S + Md * Nq * 2 * act,
+        "qkv": (Nq + 2 * Nk) * H * S + Md * H * act + Md * (Nq * act + 2 * Nk * KV),
+        "attn": (ctx + Md) * 2 * Nk * KV + Md * Nq * 2 * act,
         "oproj": H * Nq * S + Md * Nq * act + Md * H * (8 + act),
         "gateup": 2 * F * H * S + Md * H * act + Md * F * act,
         "down": H * F * S + Md * F * act + Md * H * (8 + act),
@@ -207,7 +209,12 @@ class Workbench:
         ks, vs = gen.context_kv(wl, self.ctx_lens, seed + 1, dev)
         cfg = make_config(wl.hidden, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.n_layers, wl.ffn, wl.vocab,
                           wl.block, wl.n_target_layers, B, wl.max_ctx, wl.t_new, wl.conv_width, wl.storage,
-                          wl.rms_eps, wl.rope_theta)
+                          wl.rms_eps, wl.rope_theta, wl.kv)
+        if wl.kv == "int8":  # (values, run scales) pairs -> the library's raw 8-bit cache buffers
+            from block_diffusion_drafting_ctx_amd import kv8_buffer
+
+            ks = [kv8_buffer(q, sc, cfg) for q, sc in ks]
+            vs = [kv8_buffer(q, sc, cfg) for q, sc in vs]
         self.dr = Drafter(cfg, self.w, dev, ks, vs)
         self.ctx0 = torch.from_numpy(self.ctx_lens).to(dev)
         self.dr.ctx_len.copy_(self.ctx0)

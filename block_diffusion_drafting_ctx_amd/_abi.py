@@ -19,12 +19,13 @@ LIB_PATH = os.path.join(_HERE, "libdflash.so")
 
 DFLASH_OK, DFLASH_EINVAL, DFLASH_EUNSUPPORTED, DFLASH_EHIP, DFLASH_EDEVICE = 0, -1, -2, -3, -4
 DTYPE_F32, DTYPE_BF16 = 0, 1
+KV_STORAGE, KV_INT8 = 0, 1
 ERR_FUSE_OVERFLOW, ERR_TOKEN_RANGE, ERR_VERIFY_OVERFLOW, ERR_DRAFT_OVERFLOW = 1, 2, 4, 8
 STAGES = ["fuse_fc", "ctx_kv", "verify", "embed", "qkv", "attn", "oproj", "gateup", "down", "lmhead", "layer_gemm"]
 STAGE = {n: i for i, n in enumerate(STAGES)}
 
 EXPORTED = [
-    "dflash_workspace_bytes", "dflash_create", "dflash_reload_weights", "dflash_fuse_ctx", "dflash_verify",
+    "dflash_workspace_bytes", "dflash_kv_layer_bytes", "dflash_create", "dflash_reload_weights", "dflash_fuse_ctx", "dflash_verify",
     "dflash_verify_sample", "dflash_verify_static", "dflash_draft_block",
     "dflash_check", "dflash_clear_errors", "dflash_stats", "dflash_stage_timing", "dflash_stage_time",
     "dflash_destroy", "dflash_last_error", "dflash_version",
@@ -41,7 +42,7 @@ class Config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "hidden", "n_q_heads", "n_kv_heads", "head_dim", "n_layers", "ffn", "vocab", "block",
         "n_target_layers", "max_batch", "max_ctx", "max_fuse_rows", "conv_width", "dtype")] + [
-        ("rms_eps", ctypes.c_float), ("rope_theta", ctypes.c_float)]
+        ("rms_eps", ctypes.c_float), ("rope_theta", ctypes.c_float), ("kv_dtype", ctypes.c_int32)]
 
 
 _PP = ctypes.POINTER(ctypes.c_void_p)
@@ -66,6 +67,7 @@ def lib():
         vp, i32, u64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint64
         sig = {
             "dflash_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(Config)]),
+            "dflash_kv_layer_bytes": (ctypes.c_size_t, [ctypes.POINTER(Config)]),
             "dflash_create": (i32, [ctypes.POINTER(Config), ctypes.POINTER(Weights), _PP, _PP, vp, vp,
                                     ctypes.c_size_t, ctypes.POINTER(vp)]),
             "dflash_reload_weights": (i32, [vp, vp]),
@@ -118,15 +120,22 @@ def _ptr(t: Optional[torch.Tensor], dtype=None, numel=None, name="tensor") -> Op
 
 def make_config(hidden, n_q_heads, n_kv_heads, head_dim, n_layers, ffn, vocab, block, n_target_layers,
                 max_batch, max_ctx, max_fuse_rows, conv_width=0, dtype="bf16", rms_eps=1e-6,
-                rope_theta=1e6) -> Config:
+                rope_theta=1e6, kv="storage") -> Config:
+    """kv: "storage" (the KV cache in the storage dtype) or "int8" (8-bit cache)."""
+    if kv not in ("storage", "int8"):
+        raise ValueError("kv must be 'storage' or 'int8'")
     return Config(hidden, n_q_heads, n_kv_heads, head_dim, n_layers, ffn, vocab, block, n_target_layers,
                   max_batch, max_ctx, max_fuse_rows, conv_width,
                   DTYPE_BF16 if dtype in ("bf16", torch.bfloat16, DTYPE_BF16) else DTYPE_F32,
-                  rms_eps, rope_theta)
+                  rms_eps, rope_theta, KV_INT8 if kv == "int8" else KV_STORAGE)
 
 
 def dflash_workspace_bytes(cfg: Config) -> int:
     return int(lib().dflash_workspace_bytes(ctypes.byref(cfg)))
+
+
+def dflash_kv_layer_bytes(cfg: Config) -> int:
+    return int(lib().dflash_kv_layer_bytes(ctypes.byref(cfg)))
 
 
 class Context:
@@ -182,9 +191,18 @@ def dflash_create(cfg: Config, weights: dict, kv_k: Sequence[torch.Tensor], kv_v
                 raise ValueError(f"{k}: shape {tuple(t.shape)} != {shp}")
             ptrs.append(_ptr(t, dt, name=k))
         arrays[k] = (ctypes.c_void_p * nl)(*ptrs)
-    cache_numel = cfg.max_batch * cfg.max_ctx * cfg.n_kv_heads * d
-    kk = (ctypes.c_void_p * nl)(*[_ptr(t, dt, cache_numel, "kv_k") for t in kv_k])
-    vv = (ctypes.c_void_p * nl)(*[_ptr(t, dt, cache_numel, "kv_v") for t in kv_v])
+    kv_bytes = dflash_kv_layer_bytes(cfg)
+    if cfg.kv_dtype == KV_INT8:  # raw buffers of dflash_kv_layer_bytes bytes
+        def cache_ptr(t, name):
+            p = _ptr(t, None, None, name)
+            if t.numel() * t.element_size() < kv_bytes:
+                raise ValueError(f"{name} needs {kv_bytes} bytes")
+            return p
+    else:
+        def cache_ptr(t, name):
+            return _ptr(t, dt, kv_bytes // (2 if dt == torch.bfloat16 else 4), name)
+    kk = (ctypes.c_void_p * nl)(*[cache_ptr(t, "kv_k") for t in kv_k])
+    vv = (ctypes.c_void_p * nl)(*[cache_ptr(t, "kv_v") for t in kv_v])
     _ptr(ctx_len, torch.int32, cfg.max_batch, "ctx_len")
     need = dflash_workspace_bytes(cfg)
     if need == 0:

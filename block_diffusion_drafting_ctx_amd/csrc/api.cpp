@@ -72,6 +72,7 @@ const char* validate(const dflash_config* c) {
   if (c->conv_width != 0 && c->conv_width != 3) return "conv_width must be 0 or 3";
   if (c->conv_width == 3 && 16 % c->block) return "the block conv needs block to divide 16";
   if (c->dtype != DFLASH_DTYPE_F32 && c->dtype != DFLASH_DTYPE_BF16) return "unknown dtype";
+  if (c->kv_dtype != DFLASH_KV_STORAGE && c->kv_dtype != DFLASH_KV_INT8) return "unknown kv_dtype";
   if (!(c->rms_eps >= 0.f) || !(c->rope_theta > 0.f)) return "bad eps / theta";
   return nullptr;
 }
@@ -241,6 +242,19 @@ WsLayout layout(const dflash_config& c) {
   return L;
 }
 
+// Bytes of one layer's K (or V) cache and, for the 8-bit format, the byte
+// offset of its run scales.
+size_t kv_values_bytes(const dflash_config& c) {
+  const size_t n = (size_t)c.max_batch * c.max_ctx * c.n_kv_heads * c.head_dim;
+  if (c.kv_dtype == DFLASH_KV_INT8) return n;
+  return n * (c.dtype == DFLASH_DTYPE_BF16 ? 2 : 4);
+}
+size_t kv_layer_bytes(const dflash_config& c) {
+  if (c.kv_dtype != DFLASH_KV_INT8) return kv_values_bytes(c);
+  const size_t n = (size_t)c.max_batch * c.max_ctx * c.n_kv_heads * c.head_dim;
+  return align256(n) + n / 32 * 4;
+}
+
 struct EventPool {
   bool enabled = false;
   std::vector<hipEvent_t> begin, end;
@@ -260,6 +274,7 @@ struct dflash_ctx {
   const void* w_lm;
   std::vector<const void*> w_q, w_k, w_v, w_o, w_gate, w_up, w_down, g_in, g_post, conv;
   std::vector<void*> kv_k, kv_v;
+  std::vector<float*> kv_ks, kv_vs;  // run scales of an 8-bit cache (else null)
   int32_t* ctx_len;
   EventPool timing[DFLASH_N_STAGES];
 
@@ -358,6 +373,11 @@ size_t dflash_workspace_bytes(const dflash_config* cfg) {
   return layout(*cfg).total;
 }
 
+size_t dflash_kv_layer_bytes(const dflash_config* cfg) {
+  if (validate(cfg)) return 0;
+  return kv_layer_bytes(*cfg);
+}
+
 dflash_status dflash_create(const dflash_config* cfg, const dflash_weights* w, void* const* kv_k, void* const* kv_v,
                             int32_t* ctx_len, void* workspace, size_t workspace_bytes, dflash_ctx** out) {
   g_last_error.clear();
@@ -381,8 +401,11 @@ dflash_status dflash_create(const dflash_config* cfg, const dflash_weights* w, v
     for (int l = 0; l < nl; ++l)
       if (!w->conv[l]) return fail(DFLASH_EINVAL, "null conv taps");
   }
-  for (int l = 0; l < nl; ++l)
+  for (int l = 0; l < nl; ++l) {
     if (!kv_k[l] || !kv_v[l]) return fail(DFLASH_EINVAL, "null KV cache pointer");
+    if (reinterpret_cast<uintptr_t>(kv_k[l]) % 256 || reinterpret_cast<uintptr_t>(kv_v[l]) % 256)
+      return fail(DFLASH_EINVAL, "KV cache buffers must be 256-byte aligned");
+  }
 
   dflash_ctx* c = new (std::nothrow) dflash_ctx();
   if (!c) return fail(DFLASH_EINVAL, "out of host memory");
@@ -408,6 +431,15 @@ dflash_status dflash_create(const dflash_config* cfg, const dflash_weights* w, v
     for (int l = 0; l < nl; ++l) c->conv[l] = w->conv[l];
   c->kv_k.assign(kv_k, kv_k + nl);
   c->kv_v.assign(kv_v, kv_v + nl);
+  c->kv_ks.assign(nl, nullptr);
+  c->kv_vs.assign(nl, nullptr);
+  if (cfg->kv_dtype == DFLASH_KV_INT8) {
+    const size_t off = align256(kv_values_bytes(*cfg));
+    for (int l = 0; l < nl; ++l) {
+      c->kv_ks[l] = reinterpret_cast<float*>(static_cast<char*>(kv_k[l]) + off);
+      c->kv_vs[l] = reinterpret_cast<float*>(static_cast<char*>(kv_v[l]) + off);
+    }
+  }
   c->ctx_len = ctx_len;
   hipError_t e = hipMemset(workspace, 0, L.total);
   if (e == hipSuccess)
@@ -474,9 +506,11 @@ dflash_status dflash_fuse_ctx(dflash_ctx* c, int32_t batch, const void* const* h
     GemmLaunch l{};
     FinishArgs f{};
     a.wt = c->at<void>(L.wt_kv);
+    f.kv_int8 = cf.kv_dtype == DFLASH_KV_INT8;
     for (int l2 = 0; l2 < cf.n_layers; ++l2) {
       for (int kv = 0; kv < 2; ++kv) {
         f.kv_cache[2 * l2 + kv] = kv ? c->kv_v[l2] : c->kv_k[l2];
+        f.kv_scale[2 * l2 + kv] = kv ? c->kv_vs[l2] : c->kv_ks[l2];
         nkv += cf.n_kv_heads * D;
       }
     }
@@ -695,6 +729,9 @@ dflash_status dflash_draft_block(dflash_ctx* c, int32_t batch, const int32_t* bl
       f.out_lo = c->at<void>(L.q_lo);
       f.kv_cache[0] = c->kv_k[l];
       f.kv_cache[1] = c->kv_v[l];
+      f.kv_int8 = cf.kv_dtype == DFLASH_KV_INT8;
+      f.kv_scale[0] = c->kv_ks[l];
+      f.kv_scale[1] = c->kv_vs[l];
       f.err = c->at<uint32_t>(L.err);
       if ((st = finish(c, FIN_QKV, f, gl, M, Nq + 2 * Nk, s))) return st;
     }
@@ -705,6 +742,9 @@ dflash_status dflash_draft_block(dflash_ctx* c, int32_t batch, const int32_t* bl
       a.q_lo = c->at<void>(L.q_lo);
       a.kc = c->kv_k[l];
       a.vc = c->kv_v[l];
+      a.kv_int8 = cf.kv_dtype == DFLASH_KV_INT8;
+      a.ks = c->kv_ks[l];
+      a.vs = c->kv_vs[l];
       a.ctx_len = c->ctx_len;
       a.Bs = cf.block;
       a.Hq = cf.n_q_heads;

@@ -45,6 +45,14 @@ __device__ __forceinline__ void load_raw8_nt<float>(Raw8& r, const float* p) {
   r.hi = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p) + 1);
 }
 
+// 8-bit KV entries (int8 values; their run scales are loaded separately):
+// eight consecutive values in the low 8 bytes of a Raw8.
+template <>
+__device__ __forceinline__ void load_raw8<int8_t>(Raw8& r, const int8_t* p) {
+  const u32x2 t = *reinterpret_cast<const u32x2*>(p);
+  r.lo = u32x4{t[0], t[1], 0u, 0u};
+}
+
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
   return __uint_as_float(bits16 << 16);
 }
@@ -90,6 +98,15 @@ __device__ __forceinline__ void raw_to_f32x8<float>(const Raw8& r, float* out) {
   for (int i = 0; i < 4; ++i) {
     out[i] = __uint_as_float(r.lo[i]);
     out[4 + i] = __uint_as_float(r.hi[i]);
+  }
+}
+
+template <>
+__device__ __forceinline__ void raw_to_f32x8<int8_t>(const Raw8& r, float* out) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    out[i] = (float)((int32_t)(r.lo[0] << (24 - 8 * i)) >> 24);
+    out[4 + i] = (float)((int32_t)(r.lo[1] << (24 - 8 * i)) >> 24);
   }
 }
 

@@ -662,6 +662,48 @@ __device__ __forceinline__ void pick(const f32x4& v, int j, float (&o)[E]) {
   }
 }
 
+// 8-bit cache entries of this lane: E values at column c (lo) and c + half
+// (hi) of a cache row.  The 8 * SPL consecutive lanes holding 4 consecutive
+// rotation pairs each cover one run of 32 values in each half (the runs of a
+// head row are dims [0, 32), [32, 64), ...; D is 64 or 128, so a half holds
+// whole runs), and share its scale s = max|x| / 127; the values are
+// q = x / s rounded half to even (0 for a run of zeros).  The first lane of
+// the run writes its scale.
+template <int SPL, int E>
+__device__ __forceinline__ void store_kv8(int8_t* vals, float* scales, size_t c, int half, const float (&lo)[E],
+                                          const float (&hi)[E]) {
+  constexpr int RUN = 8 * SPL;  // lanes per run
+  float alo = 0.f, ahi = 0.f;
+#pragma unroll
+  for (int k = 0; k < E; ++k) {
+    alo = fmaxf(alo, fabsf(lo[k]));
+    ahi = fmaxf(ahi, fabsf(hi[k]));
+  }
+#pragma unroll
+  for (int o = 1; o < RUN; o <<= 1) {
+    alo = fmaxf(alo, __shfl_xor(alo, o));
+    ahi = fmaxf(ahi, __shfl_xor(ahi, o));
+  }
+  const float slo = alo / 127.0f, shi = ahi / 127.0f;
+  auto pack = [&](const float (&v)[E], float sc, int8_t* dst) {
+    uint32_t w = 0;
+#pragma unroll
+    for (int k = 0; k < E; ++k) {
+      const float q = sc > 0.f ? fminf(fmaxf(rintf(v[k] / sc), -127.f), 127.f) : 0.f;
+      w |= ((uint32_t)(int32_t)q & 0xffu) << (8 * k);
+    }
+    if constexpr (E == 4) *reinterpret_cast<uint32_t*>(dst) = w;
+    else if constexpr (E == 2) *reinterpret_cast<uint16_t*>(dst) = (uint16_t)w;
+    else *dst = (int8_t)w;
+  };
+  pack(lo, slo, vals + c);
+  pack(hi, shi, vals + c + half);
+  if ((threadIdx.x & (RUN - 1)) == 0) {
+    scales[c >> 5] = slo;
+    scales[(c + half) >> 5] = shi;
+  }
+}
+
 // Rotation of the pair (lo, hi) by the tabulated angle of (position, pair index).
 __device__ __forceinline__ void rope_apply(float& lo, float& hi, float2 cs) {
   const float a = lo, b = hi;
@@ -794,7 +836,7 @@ __global__ void __launch_bounds__(256) finish_swiglu_kernel(const FinishArgs f) 
 // and is flagged.  SPL lanes per 4 consecutive rotation pairs (row, head of
 // the concatenated [Q | K | V] output, d .. d + 3 < D/2); each lane finishes
 // 4/SPL of them.
-template <typename S, int SPL>
+template <typename S, int SPL, bool KV8>
 __global__ void __launch_bounds__(256) finish_qkv_kernel(const FinishArgs f) {
   constexpr int E = 4 / SPL;
   const int D = f.head_dim, half = D >> 1;
@@ -852,9 +894,14 @@ __global__ void __launch_bounds__(256) finish_qkv_kernel(const FinishArgs f) {
 #pragma unroll
     for (int k = 0; k < E; ++k) rope_apply(lo[k], hi[k], cs[k]);
   }
-  S* dst = reinterpret_cast<S*>(f.kv_cache[is_k ? 0 : 1]) + ((size_t)b * f.max_ctx + pos) * Nk + c;
-  store_n<S, E>(dst, lo);
-  store_n<S, E>(dst + half, hi);
+  const size_t at = ((size_t)b * f.max_ctx + pos) * Nk + c;
+  if constexpr (KV8) {
+    store_kv8<SPL, E>(reinterpret_cast<int8_t*>(f.kv_cache[is_k ? 0 : 1]), f.kv_scale[is_k ? 0 : 1], at, half, lo, hi);
+  } else {
+    S* dst = reinterpret_cast<S*>(f.kv_cache[is_k ? 0 : 1]) + at;
+    store_n<S, E>(dst, lo);
+    store_n<S, E>(dst + half, hi);
+  }
 }
 
 // Context K/V of every layer (segments K^0, V^0, K^1, V^1, ...): RoPE on K at
@@ -862,7 +909,7 @@ __global__ void __launch_bounds__(256) finish_qkv_kernel(const FinishArgs f) {
 // whose rows would pass max_ctx is skipped and flagged.  SPL lanes per 4
 // consecutive rotation pairs (row, head of the concatenated output, d .. d+3);
 // each lane finishes 4/SPL of them.
-template <typename S, int SPL>
+template <typename S, int SPL, bool KV8>
 __global__ void __launch_bounds__(256) finish_kv_kernel(const FinishArgs f) {
   constexpr int E = 4 / SPL;
   const int D = f.head_dim, half = D >> 1, Hkv = f.n_kv_heads;
@@ -902,9 +949,14 @@ __global__ void __launch_bounds__(256) finish_kv_kernel(const FinishArgs f) {
     hi[k] *= r;
     if ((seg & 1) == 0) rope_apply(lo[k], hi[k], cs[k]);
   }
-  S* dst = reinterpret_cast<S*>(f.kv_cache[seg]) + (((size_t)b * f.max_ctx + pos) * Hkv + head) * D + d + j * E;
-  store_n<S, E>(dst, lo);
-  store_n<S, E>(dst + half, hi);
+  const size_t at = (((size_t)b * f.max_ctx + pos) * Hkv + head) * D + d + j * E;
+  if constexpr (KV8) {
+    store_kv8<SPL, E>(reinterpret_cast<int8_t*>(f.kv_cache[seg]), f.kv_scale[seg], at, half, lo, hi);
+  } else {
+    S* dst = reinterpret_cast<S*>(f.kv_cache[seg]) + at;
+    store_n<S, E>(dst, lo);
+    store_n<S, E>(dst + half, hi);
+  }
 }
 
 // ------------------------------------------------------------------ weight tiling
@@ -1030,9 +1082,15 @@ hipError_t launch_argmax_reduce(const uint64_t* part, int ntiles, int ld, int M,
 
 template <typename S, int SPL>
 static void launch_finish_spl(FinishKind kind, const FinishArgs& f, int blocks, int threads, hipStream_t st) {
-  if (kind == FIN_SWIGLU) hipLaunchKernelGGL(finish_swiglu_kernel<SPL>, dim3(blocks), dim3(threads), 0, st, f);
-  else if (kind == FIN_QKV) hipLaunchKernelGGL((finish_qkv_kernel<S, SPL>), dim3(blocks), dim3(threads), 0, st, f);
-  else hipLaunchKernelGGL((finish_kv_kernel<S, SPL>), dim3(blocks), dim3(threads), 0, st, f);
+  if (kind == FIN_SWIGLU) {
+    hipLaunchKernelGGL(finish_swiglu_kernel<SPL>, dim3(blocks), dim3(threads), 0, st, f);
+  } else if (kind == FIN_QKV) {
+    if (f.kv_int8) hipLaunchKernelGGL((finish_qkv_kernel<S, SPL, true>), dim3(blocks), dim3(threads), 0, st, f);
+    else hipLaunchKernelGGL((finish_qkv_kernel<S, SPL, false>), dim3(blocks), dim3(threads), 0, st, f);
+  } else {
+    if (f.kv_int8) hipLaunchKernelGGL((finish_kv_kernel<S, SPL, true>), dim3(blocks), dim3(threads), 0, st, f);
+    else hipLaunchKernelGGL((finish_kv_kernel<S, SPL, false>), dim3(blocks), dim3(threads), 0, st, f);
+  }
 }
 
 template <typename S>

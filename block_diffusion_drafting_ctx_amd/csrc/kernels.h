@@ -121,6 +121,10 @@ struct FinishArgs {
   int head_dim, n_q_heads, n_kv_heads;
   float q_scale;
   void* kv_cache[kMaxSeg];  // FIN_KV: one per segment; FIN_QKV: this layer's K, V caches
+  // 8-bit caches: the values above are int8 and kv_scale[i] holds the float
+  // scale of every run of 32 values (flat value index / 32)
+  int kv_int8;
+  float* kv_scale[kMaxSeg];
   uint32_t* err;
 };
 hipError_t launch_finish(int storage, FinishKind kind, const FinishArgs& f, hipStream_t stream);
@@ -138,6 +142,9 @@ struct AttnArgs {
   const void* q_lo;
   const void* kc;  // storage [B, max_ctx, Hkv, D] this layer's cache; the block's
   const void* vc;  //   K/V (RoPE applied) at rows ctx_len[b] + i
+  int kv_int8;        // 8-bit cache: kc/vc are int8 and ks/vs the scales of
+  const float* ks;    //   every run of 32 values (flat value index / 32)
+  const float* vs;
   const int32_t* ctx_len;
   int Bs, Hq, Hkv, D, max_ctx;
   int nwg;           // workgroups the batch's key axis is cut over (grid of the split kernel)

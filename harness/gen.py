@@ -21,12 +21,16 @@ Workloads (no trained weights exist here; every tensor is random):
 * ``dflash2-27b-shape-conv-b8``: hidden 5120, 40/8 heads of 128, 5 layers,
   FFN 17408, vocab 151936, block 16, context 8192, batch 8, with the width-3
   per-channel block convolution (taps N(0, 0.1)); 5 target layers.
+* ``long-ctx-32k-b4-kv8`` / ``qwen3-8b-shape-b1-kv8``: those workloads with
+  the 8-bit draft KV cache.
 
 Value recipe: matrices, embedding and LM head N(0, 0.02); RMSNorm gains 1.0;
 target hidden states of fused layer j (0-based) N(0, (1 + j)^2) except the
 tiny workload (N(0, 1)); pre-filled context K/V entries N(0, (0.02 sqrt(H))^2),
-the spread a unit-RMS feature gets through an N(0, 0.02) projection; target
-logits N(0, 1) with planted agreement.
+the spread a unit-RMS feature gets through an N(0, 0.02) projection (with the
+8-bit cache: integers N(0, 32^2) rounded and clipped to +-127 times a scale
+0.02 sqrt(H) / 32 for every run of 32, the same spread); target logits
+N(0, 1) with planted agreement.
 """
 
 from __future__ import annotations
@@ -60,6 +64,7 @@ class Workload:
     scaled_hidden: bool = True
     rms_eps: float = 1e-6
     rope_theta: float = 1e6
+    kv: str = "storage"  # draft KV cache: "storage" (the storage dtype) or "int8"
 
     @property
     def mask_id(self) -> int:
@@ -100,6 +105,10 @@ WORKLOADS: Dict[str, Workload] = {
         Workload("long-ctx-32k-b4", 4096, 32, 8, 128, 8, 12288, 151936, 16, 5, 4, 32768, 32768, "bf16"),
         Workload("dflash2-27b-shape-conv-b8", 5120, 40, 8, 128, 5, 17408, 151936, 16, 5, 8, 8192, 8192,
                  "bf16", conv_width=3),
+        Workload("long-ctx-32k-b4-kv8", 4096, 32, 8, 128, 8, 12288, 151936, 16, 5, 4, 32768, 32768, "bf16",
+                 kv="int8"),
+        Workload("qwen3-8b-shape-b1-kv8", 4096, 32, 8, 128, 5, 12288, 151936, 16, 5, 1, 4096, 4096, "bf16",
+                 kv="int8"),
     ]
 }
 
@@ -172,12 +181,17 @@ def context_kv(wl: Workload, ctx_lens: np.ndarray, seed: int, device="cpu", pois
     """Pre-filled draft KV cache: per layer K and V tensors [B, max_ctx, Hkv, D].
 
     Rows below ctx_lens[b] hold N(0, (0.02 sqrt(H))^2) entries; the rest are
-    zero, or NaN with ``poison`` so that any read of them shows.
+    zero, or NaN with ``poison`` so that any read of them shows.  With the
+    8-bit cache every entry is a pair (values int8 [B, max_ctx, Hkv, D],
+    run scales float32 [B, max_ctx, Hkv, D/32]); rows past the context have
+    zero values and zero (NaN with ``poison``) scales.
     """
     g = _gen(seed, device)
     b = len(ctx_lens)
     shape = (b, wl.max_ctx, wl.n_kv_heads, wl.head_dim)
     std = 0.02 * float(np.sqrt(wl.hidden))
+    if wl.kv == "int8":
+        return _context_kv8(wl, ctx_lens, g, device, poison, shape, std)
     ks, vs = [], []
     for _ in range(wl.n_layers):
         for lst in (ks, vs):
@@ -187,6 +201,24 @@ def context_kv(wl: Workload, ctx_lens: np.ndarray, seed: int, device="cpu", pois
                 if n:
                     t[i, :n] = _normal((n,) + shape[2:], std, g, device, wl.torch_dtype)
             lst.append(t)
+    return ks, vs
+
+
+def _context_kv8(wl, ctx_lens, g, device, poison, shape, std):
+    b = len(ctx_lens)
+    sshape = shape[:-1] + (shape[-1] // 32,)
+    ks, vs = [], []
+    for _ in range(wl.n_layers):
+        for lst in (ks, vs):
+            q = torch.zeros(shape, device=device, dtype=torch.int8)
+            s = torch.full(sshape, float("nan") if poison else 0.0, device=device, dtype=torch.float32)
+            for i in range(b):
+                n = int(ctx_lens[i])
+                if n:
+                    z = torch.randn((n,) + shape[2:], generator=g, device=device, dtype=torch.float32)
+                    q[i, :n] = z.mul_(32.0).round_().clamp_(-127, 127).to(torch.int8)
+                    s[i, :n] = std / 32.0
+            lst.append((q, s))
     return ks, vs
 
 

@@ -68,6 +68,12 @@ typedef enum {
 
 enum { DFLASH_DTYPE_F32 = 0, DFLASH_DTYPE_BF16 = 1 };
 
+/* Format of the draft KV cache (dflash_config.kv_dtype). */
+enum {
+  DFLASH_KV_STORAGE = 0, /* the storage type S, like the weights */
+  DFLASH_KV_INT8 = 1     /* 8-bit integers with one float scale per 32 values (below) */
+};
+
 /* Device error-word bits (sticky until dflash_clear_errors). */
 enum {
   DFLASH_ERR_FUSE_OVERFLOW = 1u << 0,   /* ctx_len[b] + t_new > max_ctx in fuse_ctx */
@@ -115,6 +121,7 @@ typedef struct {
   int32_t dtype;           /* DFLASH_DTYPE_F32 or DFLASH_DTYPE_BF16 (storage "S") */
   float rms_eps;           /* RMSNorm epsilon (1e-6 in the synthetic drafts) */
   float rope_theta;        /* rotary base (1e6) */
+  int32_t kv_dtype;        /* DFLASH_KV_STORAGE (0) or DFLASH_KV_INT8 */
 } dflash_config;
 
 /* Draft weights (device pointers of storage type S).  Per-layer entries are
@@ -141,9 +148,26 @@ typedef struct {
  * (0 on an invalid configuration).  The workspace must be 256-byte aligned. */
 size_t dflash_workspace_bytes(const dflash_config* cfg);
 
+/* Bytes of ONE layer's K (or V) cache buffer (0 on an invalid configuration).
+ * [P2] "DFlash-2: z-lab boosts speculative-decoding throughput", Precision
+ * cost: an 8-bit KV cache is measured against f16 there (acceptance
+ * 78.06% -> 74.88%) without a definition; DFLASH_KV_INT8 stores every row of
+ * a KV head as 8-bit integers q in [-127, 127] with one float32 scale s per
+ * 32 consecutive values (s = max|x| / 127 of those values, q = x / s rounded
+ * half to even; the value read back is q * s; a run of zeros has s = 0).
+ * Layout of one buffer (256-byte aligned):
+ *   DFLASH_KV_STORAGE: S [max_batch, max_ctx, Hkv, D];
+ *   DFLASH_KV_INT8:    int8 q [max_batch, max_ctx, Hkv, D], then, at byte
+ *                      offset round_up(max_batch*max_ctx*Hkv*D, 256),
+ *                      float32 s [max_batch, max_ctx, Hkv, D/32].
+ * Every K/V entry the attention reads (the context rows and the block's own
+ * rows, staged in the cache) goes through this format. */
+size_t dflash_kv_layer_bytes(const dflash_config* cfg);
+
 /* Create a context.
  *  kv_k, kv_v: HOST arrays of n_layers device pointers, each the persistent
- *     draft KV cache of one layer, layout [max_batch, max_ctx, Hkv, D] of S.
+ *     draft KV cache of one layer, dflash_kv_layer_bytes(cfg) bytes laid out
+ *     as described there ([max_batch, max_ctx, Hkv, D] of S by default).
  *     K entries are stored after the rotary embedding.  [P1] "Block-diffusion
  *     architecture", KV-cache-integration bullet: the projected context
  *     features live in the draft KV cache and persist across iterations.

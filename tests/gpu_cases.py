@@ -30,7 +30,7 @@ import numpy as np
 import torch
 
 from harness import gen
-from oracle import DraftState, draft_block, fuse_ctx, verify_step, AcceptanceStats
+from oracle import DraftState, draft_block, fuse_ctx, kv8_dequantize, verify_step, AcceptanceStats
 from tests.oracle_adapt import dims_of, np64, weights_of
 
 REL_L2 = 1e-2
@@ -71,7 +71,51 @@ def config_for(wl: gen.Workload, batch: int, max_fuse_rows: Optional[int] = None
 
     return make_config(wl.hidden, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.n_layers, wl.ffn, wl.vocab,
                        wl.block, wl.n_target_layers, batch, wl.max_ctx,
-                       max_fuse_rows or wl.t_new, wl.conv_width, wl.storage, wl.rms_eps, wl.rope_theta)
+                       max_fuse_rows or wl.t_new, wl.conv_width, wl.storage, wl.rms_eps, wl.rope_theta, wl.kv)
+
+
+def oracle_cache(t, seqs):
+    """The oracle's float64 view of generated cache entries for sequences `seqs`
+    (an 8-bit entry is a (values, scales) pair: its value is values * scale)."""
+    if isinstance(t, tuple):
+        return kv8_dequantize(np64(t[0][seqs]), np64(t[1][seqs]))
+    return np64(t[seqs])
+
+
+def device_cache(t, cfg, device, batch):
+    """One generated cache entry as the library's buffer for a context of
+    cfg.max_batch sequences (the first `batch` filled)."""
+    from block_diffusion_drafting_ctx_amd import kv8_buffer
+
+    if isinstance(t, tuple):
+        return kv8_buffer(t[0].to(device), t[1].to(device), cfg)
+    t = t.to(device)
+    if cfg.max_batch == batch:
+        return t
+    full = torch.zeros((cfg.max_batch,) + tuple(t.shape[1:]), dtype=t.dtype, device=device)
+    full[:batch] = t
+    return full
+
+
+def cache_rows(dr, layer, kind, b, lo, hi):
+    """Rows [lo, hi) of sequence b of one layer's cache as the library left
+    them: a tensor, or (values, scales) for the 8-bit cache."""
+    if not dr.kv8:
+        return (dr.kv_k if kind == "K" else dr.kv_v)[layer][b, lo:hi].clone()
+    k = kind.lower()
+    return dr.kv_values(layer, k)[b, lo:hi].clone(), dr.kv_scales(layer, k)[b, lo:hi].clone()
+
+
+def cache_rows_f64(rows):
+    if isinstance(rows, tuple):
+        q, sc = np64(rows[0]), np64(rows[1])
+        # the format itself: integers in [-127, 127], and every non-zero run
+        # reaches +-127 (its scale is max|x| / 127)
+        assert np.all(np.abs(q) <= 127)
+        runs = np.abs(q).reshape(q.shape[:-1] + (-1, 32)).max(axis=-1)
+        assert np.all((runs == 127) | ((runs == 0) & (sc == 0))), "8-bit runs off their scale"
+        return kv8_dequantize(q, sc)
+    return np64(rows)
 
 
 @dataclass
@@ -129,21 +173,12 @@ def run_step(wl: gen.Workload, seed: int, device="cuda", seqs: Optional[Sequence
         if prefill:
             st = DraftState.empty(dims, len(seqs), wl.max_ctx)
         else:
-            st = DraftState(k=[np64(t[seqs]) for t in ks], v=[np64(t[seqs]) for t in vs],
+            st = DraftState(k=[oracle_cache(t, seqs) for t in ks], v=[oracle_cache(t, seqs) for t in vs],
                             ctx_len=ctx_lens[seqs].astype(np.int64).copy())
 
     cfg = config_for(wl, max_batch or B, max(t_new, wl.ctx_hi if prefill else 0))
-    mb = max_batch or B
-
-    def cache(t):  # [B, ...] -> the context's [max_batch, ...] layout (extra sequences zero)
-        t = t.to(device)
-        if mb == B:
-            return t
-        full = torch.zeros((mb,) + tuple(t.shape[1:]), dtype=t.dtype, device=device)
-        full[:B] = t
-        return full
-
-    kv_dev = None if ks is None else ([cache(t) for t in ks], [cache(t) for t in vs])
+    kv_dev = None if ks is None else ([device_cache(t, cfg, device, B) for t in ks],
+                                      [device_cache(t, cfg, device, B) for t in vs])
     dr = Drafter(cfg, w_dev, device, *(kv_dev or (None, None)))
     dr.ctx_len[:B].copy_(torch.from_numpy(ctx_lens))
     M_f = B * t_new
@@ -162,8 +197,8 @@ def run_step(wl: gen.Workload, seed: int, device="cuda", seqs: Optional[Sequence
             t0 = int(ctx_after_fuse[b])
             lo = 0 if prefill else t0
             for l in range(wl.n_layers):
-                fused_rows[(b, l, "K")] = dr.kv_k[l][b, lo:t0 + t_new].clone()
-                fused_rows[(b, l, "V")] = dr.kv_v[l][b, lo:t0 + t_new].clone()
+                for kind in ("K", "V"):
+                    fused_rows[(b, l, kind)] = cache_rows(dr, l, kind, b, lo, t0 + t_new)
     d_dev = torch.from_numpy(drafts).to(device)
     n_acc = torch.full((B,), -7, dtype=torch.int32, device=device)
     bonus = torch.full((B,), -7, dtype=torch.int32, device=device)
@@ -217,7 +252,7 @@ def run_step(wl: gen.Workload, seed: int, device="cuda", seqs: Optional[Sequence
         lo = 0 if prefill else t0
         for l in range(wl.n_layers):
             for name, ref in (("K", st.k[l]), ("V", st.v[l])):
-                got = np64(fused_rows[(b, l, name)])
+                got = cache_rows_f64(fused_rows[(b, l, name)])
                 e = rel_l2(got, ref[j, lo:t0 + t_new])
                 res.note(f"cache_{name}_rel_l2", e)
                 assert e <= REL_L2, f"seq {b} layer {l} cache {name} rel L2 {e}"

@@ -18,7 +18,7 @@ def dims_of(wl) -> OracleDims:
     return OracleDims(hidden=wl.hidden, n_q_heads=wl.n_q_heads, n_kv_heads=wl.n_kv_heads,
                       head_dim=wl.head_dim, n_layers=wl.n_layers, ffn=wl.ffn, vocab=wl.vocab,
                       block=wl.block, n_target_layers=wl.n_target_layers, rms_eps=wl.rms_eps,
-                      rope_theta=wl.rope_theta, conv_width=wl.conv_width)
+                      rope_theta=wl.rope_theta, conv_width=wl.conv_width, kv_int8=wl.kv == "int8")
 
 
 def weights_of(w: dict, layers=None) -> DraftWeights:

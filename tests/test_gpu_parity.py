@@ -168,11 +168,35 @@ def test_host_checks_reject_bad_sizes():
     dr.close()
 
 
+@pytest.mark.parametrize("storage,kv_conv", [("bf16", 0), ("f32", 0), ("bf16", 3)])
+def test_int8_kv_cache_ragged(storage, kv_conv):
+    # the 8-bit cache: pre-filled rows as (values, scales), NaN scales past
+    # the contexts; fused and staged rows quantised by the library; attention
+    # dequantises.  Several attention splits, ragged contexts, every sequence.
+    wl = gen.Workload("tiny-kv8", 256, 4, 2, 64, 2, 512, 1024, 8, 3, 5, 0, 700, storage, conv_width=kv_conv,
+                      accept_hi=8, kv="int8")
+    run_step(wl, seed=26, poison=True)
+
+
+def test_int8_kv_cache_head128_planned_attention():
+    # head_dim 128 (4 runs of 32 per row), 72 sequences x 2 KV heads: attention planned on the device
+    wl = gen.Workload("tiny-kv8-h128", 512, 8, 2, 128, 1, 512, 1024, 16, 2, 72, 0, 400, "bf16", kv="int8")
+    run_step(wl, seed=28, seqs=[0, 35, 71], poison=True)
+
+
+def test_int8_kv_cache_through_prefill():
+    wl = gen.Workload("tiny-kv8-pre", 256, 4, 2, 64, 2, 512, 1024, 8, 3, 1, 64, 64, "f32", accept_hi=8,
+                      scaled_hidden=False, kv="int8")
+    run_step(wl, seed=29, prefill=True)
+
+
 @pytest.mark.parametrize("name,seqs", [
     ("qwen3-8b-shape-b1", [0]),
     ("qwen3-8b-shape-b32-ragged", [0, 13, 31]),
     ("long-ctx-32k-b4", [3]),
     ("dflash2-27b-shape-conv-b8", [0, 7]),
+    ("qwen3-8b-shape-b1-kv8", [0]),
+    ("long-ctx-32k-b4-kv8", [1]),
 ])
 def test_full_size(name, seqs):
     # at these widths about 70% of the draft rows clear the 0.1 margin; a

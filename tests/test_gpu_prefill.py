@@ -17,7 +17,7 @@ import torch
 from harness import gen
 from oracle import fuse_features
 from oracle.draft import context_kv
-from tests.gpu_cases import REL_L2, _to, config_for, log, rel_l2
+from tests.gpu_cases import REL_L2, _to, cache_rows, cache_rows_f64, config_for, log, rel_l2
 from tests.oracle_adapt import dims_of, np64
 
 pytestmark = pytest.mark.gpu
@@ -28,6 +28,8 @@ pytestmark = pytest.mark.gpu
     ("qwen3-8b-shape-b1", 2, 3000, 1024, [0, 1, 517, 1023, 1024, 2047, 2048, 2500, 2999]),
     # fp32 storage, 3 sequences, every row compared (256 + 256 + 188)
     ("tiny-f32-b1", 3, 700, 256, None),
+    # the 8-bit cache: every fused row quantised on the way in
+    ("qwen3-8b-shape-b1-kv8", 2, 3000, 1024, [0, 1, 517, 1023, 1024, 2047, 2048, 2500, 2999]),
 ])
 def test_prompt_fusion_in_chunks(name, batch, rows, chunk, sample):
     from block_diffusion_drafting_ctx_amd import Drafter
@@ -64,8 +66,9 @@ def test_prompt_fusion_in_chunks(name, batch, rows, chunk, sample):
         assert e <= REL_L2, f"seq {b} feature rel L2 {e}"
         for l, lw in enumerate(proj):
             k, v = context_kv(c, lw, rows_sel, dims)
-            for nm, got, ref in (("K", dr.kv_k[l], k), ("V", dr.kv_v[l], v)):
-                e = rel_l2(np64(got[b, rows_sel]), ref)
+            for nm, ref in (("K", k), ("V", v)):
+                got = cache_rows_f64(cache_rows(dr, l, nm, b, 0, rows))[rows_sel]
+                e = rel_l2(got, ref)
                 worst[nm] = max(worst.get(nm, 0.0), e)
                 assert e <= REL_L2, f"seq {b} layer {l} cache {nm} rel L2 {e}"
     log(f"[case] prefill {name}: worst rel L2 {worst}")
