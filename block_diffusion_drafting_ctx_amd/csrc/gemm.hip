@@ -273,14 +273,20 @@ __global__ void __launch_bounds__(512) gemm_as_kernel(const GemmArgs g) {
 // Blocks are numbered so that the M blocks sharing a weight block are
 // dispatched back to back on the same XCD (workgroup L runs on XCD L % 8), so
 // the weight block is fetched from HBM once into that XCD's L2.
+// Stage depth: 32 at 256-row blocks (matrix-core bound; the two stages and
+// their hi/lo activations fill the LDS), 64 at 64- and 128-row blocks, where
+// the product streams weights and a 32-deep stage moved too few bytes per
+// barrier (the rows are then 160 bytes, also a conflict-free stride).
 template <int MF, int NF>
 struct MtShape {
   static constexpr int BM = 64 * MF;
   static constexpr int BN = 32 * NF;
-  static constexpr int BK = 32;
-  static constexpr int LDK = BK + 16;  // LDS row stride (elements): 96-byte rows, conflict-free fragment reads
-  static constexpr int APT = (BM * 4 + 511) / 512;  // activation pieces per thread per array
-  static constexpr int WPT = (BN * 4 + 511) / 512;  // weight pieces per thread
+  static constexpr int BK = MF >= 4 ? 32 : 64;
+  static constexpr int KST = BK / 32;  // 32-deep k-steps per stage
+  static constexpr int LDK = BK + 16;  // LDS row stride (elements): 96- or 160-byte rows, conflict-free fragment reads
+  static constexpr int APR = BK / 8;   // 8-element activation pieces per row and stage
+  static constexpr int APT = (BM * APR + 511) / 512;  // activation pieces per thread per array
+  static constexpr int WPT = (BN * 4 * KST + 511) / 512;  // weight pieces (16 bytes) per thread
 };
 
 template <int MF, int NF, int SRC, bool LO>
@@ -291,14 +297,15 @@ struct MtRegs {
 };
 
 size_t gemm_mt_lds_bytes(int MF, int NF, bool lo) {
-  const int BM = 64 * MF, BN = 32 * NF;
-  return (size_t)2 * ((lo ? 2 : 1) * BM + BN) * (32 + 16) * 2;
+  const int BM = 64 * MF, BN = 32 * NF, BK = MF >= 4 ? 32 : 64;
+  return (size_t)2 * ((lo ? 2 : 1) * BM + BN) * (BK + 16) * 2;
 }
 
 template <typename S, int MF, int NF, int SRC, bool LO, int OUT>
 __global__ void __launch_bounds__(512) gemm_mt_kernel(const GemmArgs g) {
   using Sh = MtShape<MF, NF>;
   constexpr int BM = Sh::BM, BN = Sh::BN, BK = Sh::BK, LDK = Sh::LDK, APT = Sh::APT, WPT = Sh::WPT;
+  constexpr int KST = Sh::KST, APR = Sh::APR;
   constexpr int NA = LO ? 2 : 1;
   constexpr int STAGE = (NA * BM + BN) * LDK;
   using Regs = MtRegs<MF, NF, SRC, LO>;
@@ -316,29 +323,29 @@ __global__ void __launch_bounds__(512) gemm_mt_kernel(const GemmArgs g) {
   const int kbeg = ks * g.kslice, nk = g.kslice / BK;
 
   // ---- per-thread load sources (fixed rows, k advances).  Weight piece q =
-  // tid + 512 i is lane q & 63 of tile q >> 6 of the block: 64 threads read
-  // one tile's 1 KB k-step block; past N the last tile is re-read (unused).
-  // When BN * 4 is not a multiple of 512 (NF = 6) a thread with no piece i
-  // repeats its piece 0 (same source, same LDS slot), so the loads stay
-  // unconditional.
-  auto wq = [&](int i) { return tid + i * 512 < BN * 4 ? tid + i * 512 : tid; };
+  // tid + 512 i is lane q & 63 of 1 KB block q >> 6 of the stage, block b
+  // being k-step b % KST of tile b / KST: 64 threads read one tile's 1 KB
+  // k-step block; past N the last tile is re-read (unused).  When the pieces
+  // are not a multiple of 512 (NF = 6) a thread with no piece i repeats its
+  // piece 0 (same source, same LDS slot), so the loads stay unconditional.
+  auto wq = [&](int i) { return tid + i * 512 < BN * 4 * KST ? tid + i * 512 : tid; };
   const bf16_t* wsrc[WPT];
   const int nks = g.K >> 5, ntl = g.N >> 4;
 #pragma unroll
   for (int i = 0; i < WPT; ++i) {
-    const int q = wq(i), t = min(n0 / 16 + (q >> 6), ntl - 1);
-    wsrc[i] = reinterpret_cast<const bf16_t*>(g.wt) + (((size_t)t * nks + kbeg / 32) * 64 + (q & 63)) * 8;
+    const int q = wq(i), b = q >> 6, t = min(n0 / 16 + b / KST, ntl - 1);
+    wsrc[i] = reinterpret_cast<const bf16_t*>(g.wt) + (((size_t)t * nks + kbeg / 32 + b % KST) * 64 + (q & 63)) * 8;
   }
-  auto wrow = [&](int i) { return ((wq(i) >> 6) << 4) + (tid & 15); };  // block row of weight piece i
-  const int wcol = ((tid >> 4) & 3) * 8;                                             // and its column in the stage
-  auto prow = [&](int i) { return (tid + i * 512) >> 2; };  // row of a thread's i-th activation piece
-  const int pc = (tid & 3) * 8;                             // its column within the stage
-  auto aok = [&](int i) { return (i + 1) * 512 <= BM * 4 || tid + i * 512 < BM * 4; };  // whole pieces: always
+  auto wrow = [&](int i) { return (((wq(i) >> 6) / KST) << 4) + (tid & 15); };  // block row of weight piece i
+  auto wcol = [&](int i) { return ((wq(i) >> 6) % KST) * 32 + ((tid >> 4) & 3) * 8; };  // and its stage column
+  auto prow = [&](int i) { return (tid + i * 512) / APR; };  // row of a thread's i-th activation piece
+  const int pc = (tid % APR) * 8;                            // its column within the stage
+  auto aok = [&](int i) { return (i + 1) * 512 <= BM * APR || tid + i * 512 < BM * APR; };  // whole pieces: always
 
   auto gload = [&](Regs& r, int kt) {
     const int k = kbeg + kt * BK;
 #pragma unroll
-    for (int i = 0; i < WPT; ++i) load_raw8<bf16_t>(r.w[i], wsrc[i] + kt * 512);
+    for (int i = 0; i < WPT; ++i) load_raw8<bf16_t>(r.w[i], wsrc[i] + kt * 512 * KST);
 #pragma unroll
     for (int i = 0; i < APT; ++i) {
       if (!aok(i)) continue;
@@ -358,7 +365,7 @@ __global__ void __launch_bounds__(512) gemm_mt_kernel(const GemmArgs g) {
     bf16_t* st = sm + buf * STAGE;
 #pragma unroll
     for (int i = 0; i < WPT; ++i)
-      *reinterpret_cast<bf16x8*>(&st[(NA * BM + wrow(i)) * LDK + wcol]) = raw_to_bf16x8<bf16_t>(r.w[i]);
+      *reinterpret_cast<bf16x8*>(&st[(NA * BM + wrow(i)) * LDK + wcol(i)]) = raw_to_bf16x8<bf16_t>(r.w[i]);
 #pragma unroll
     for (int i = 0; i < APT; ++i) {
       if (!aok(i)) continue;
@@ -393,20 +400,23 @@ __global__ void __launch_bounds__(512) gemm_mt_kernel(const GemmArgs g) {
     for (int fm = 0; fm < MF; ++fm) acc[fn][fm] = f32x4{0.f, 0.f, 0.f, 0.f};
   auto compute = [&](int buf) {
     const bf16_t* st = sm + buf * STAGE;
-    const int fr = (lane & 15) * LDK + 8 * (lane >> 4);
-    bf16x8 af[MF], al[MF];
 #pragma unroll
-    for (int fm = 0; fm < MF; ++fm) {
-      af[fm] = *reinterpret_cast<const bf16x8*>(&st[(16 * MF * wm + 16 * fm) * LDK + fr]);
-      if constexpr (LO) al[fm] = *reinterpret_cast<const bf16x8*>(&st[(BM + 16 * MF * wm + 16 * fm) * LDK + fr]);
-    }
-#pragma unroll
-    for (int fn = 0; fn < NF; ++fn) {
-      const bf16x8 wf = *reinterpret_cast<const bf16x8*>(&st[(NA * BM + 16 * NF * wn + 16 * fn) * LDK + fr]);
+    for (int kq = 0; kq < KST; ++kq) {
+      const int fr = (lane & 15) * LDK + 8 * (lane >> 4) + 32 * kq;
+      bf16x8 af[MF], al[MF];
 #pragma unroll
       for (int fm = 0; fm < MF; ++fm) {
-        acc[fn][fm] = mfma16x16x32(wf, af[fm], acc[fn][fm]);
-        if constexpr (LO) acc[fn][fm] = mfma16x16x32(wf, al[fm], acc[fn][fm]);
+        af[fm] = *reinterpret_cast<const bf16x8*>(&st[(16 * MF * wm + 16 * fm) * LDK + fr]);
+        if constexpr (LO) al[fm] = *reinterpret_cast<const bf16x8*>(&st[(BM + 16 * MF * wm + 16 * fm) * LDK + fr]);
+      }
+#pragma unroll
+      for (int fn = 0; fn < NF; ++fn) {
+        const bf16x8 wf = *reinterpret_cast<const bf16x8*>(&st[(NA * BM + 16 * NF * wn + 16 * fn) * LDK + fr]);
+#pragma unroll
+        for (int fm = 0; fm < MF; ++fm) {
+          acc[fn][fm] = mfma16x16x32(wf, af[fm], acc[fn][fm]);
+          if constexpr (LO) acc[fn][fm] = mfma16x16x32(wf, al[fm], acc[fn][fm]);
+        }
       }
     }
   };
