@@ -131,6 +131,34 @@ bool plan_gemm(int storage, int src, int out, bool lo, int M, int N, int K, Gemm
   int NF = MF >= 4 ? 8 : 4;
   int nbn = (N + 32 * NF - 1) / (32 * NF);
   int KS = split(nbn);
+  if (MF <= 2) {
+    // 64- and 128-row blocks stream weights (one workgroup per compute unit,
+    // each streaming its block's weights at a bounded per-unit rate): pick the
+    // block width and k-split that minimise the busiest unit's bytes --
+    // dispatch rounds x (the block's weight bytes + a ramp worth ~96 KB) +
+    // its share of the split-K partials (written, then read by the finish).
+    // (Counting the activation rows a block re-reads as well made the LM head
+    // at 64 rows 17% slower: it then preferred fewer, wider blocks.)
+    double best = 0;
+    for (int nf : {2, 4, 6, 8}) {
+      if (nf == 8 && MF == 2) continue;  // its two 64-deep stages would not fit the LDS
+      const int bn = (N + 32 * nf - 1) / (32 * nf);
+      for (int ks = 1; ks <= 32; ++ks) {
+        if (ks > 1 && out != OUT_PARTIAL) break;
+        if ((K / 128) % ks || K / ks < 256) continue;
+        const double wgs = (double)bn * nbm * ks;
+        const double rounds = std::ceil(wgs / kCUs);
+        const double cost = rounds * (32.0 * nf * (double)(K / ks) * 2.0 + 96e3) +
+                            (ks > 1 ? 8.0 * ks * (double)M * N / kCUs : 0.0);
+        if (best == 0 || cost < best) {
+          best = cost;
+          NF = nf;
+          nbn = bn;
+          KS = ks;
+        }
+      }
+    }
+  }
   if (MF >= 4 && out == OUT_PARTIAL) {
     // 192-column blocks when they fill the chip clearly better (gate/up at
     // 512 rows: 256 workgroups instead of 192); their wave tile reads ~11%

@@ -361,11 +361,16 @@ __global__ void __launch_bounds__(512) gemm_mt_kernel(const GemmArgs g) {
       }
     }
   };
-  auto sstore = [&](const Regs& r, int buf) {
+  // live = false (a stage past the end, three-set pipeline): the weights are
+  // stored as zeros by a select, so the stage adds nothing
+  auto sstore = [&](const Regs& r, int buf, bool live = true) {
     bf16_t* st = sm + buf * STAGE;
 #pragma unroll
-    for (int i = 0; i < WPT; ++i)
-      *reinterpret_cast<bf16x8*>(&st[(NA * BM + wrow(i)) * LDK + wcol(i)]) = raw_to_bf16x8<bf16_t>(r.w[i]);
+    for (int i = 0; i < WPT; ++i) {
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      *reinterpret_cast<bf16x8*>(&st[(NA * BM + wrow(i)) * LDK + wcol(i)]) =
+          __builtin_bit_cast(bf16x8, live ? r.w[i].lo : z);
+    }
 #pragma unroll
     for (int i = 0; i < APT; ++i) {
       if (!aok(i)) continue;
@@ -421,24 +426,38 @@ __global__ void __launch_bounds__(512) gemm_mt_kernel(const GemmArgs g) {
     }
   };
 
-  // ---- pipeline: registers r0 / r1 alternate; the stage count nk is even
-  // (the planner splits K into k-slices of a multiple of 64)
-  Regs r0, r1;
+  // ---- pipeline.  256-row blocks (matrix-core bound): registers r0 / r1
+  // alternate, loads two stages ahead; the stage count nk is even (the planner
+  // splits K into k-slices of a multiple of 64).  64- and 128-row blocks
+  // (weight streaming, where a stage's matrix work is short and the loop waits
+  // on memory latency): three register sets, loads three stages ahead; the
+  // loop runs in threes and a stage past the end is stored with zero weights.
+  constexpr bool R3 = MF <= 2;
+  Regs r0, r1, r2;
   gload(r0, 0);
   gload(r1, 1);
+  if constexpr (R3) gload(r2, min(2, nk - 1));
   sstore(r0, 0);
   __syncthreads();
+  // cur: free (its stage kt is in LDS);  nxt: stage kt+1, loaded
   auto step = [&](Regs& cur, Regs& nxt, int kt) {
-    // cur: free (its stage kt is in LDS);  nxt: stage kt+1 in flight
-    gload(cur, min(kt + 2, nk - 1));
+    gload(cur, min(kt + (R3 ? 3 : 2), nk - 1));
     __builtin_amdgcn_sched_barrier(0);  // the loads go out before the matrix work
     compute(kt & 1);
-    sstore(nxt, (kt + 1) & 1);  // after the last stage: into the idle buffer, unused
+    sstore(nxt, (kt + 1) & 1, !R3 || kt + 1 < nk);  // after the last stage: into the idle buffer, unused
     __syncthreads();
   };
-  for (int kt = 0; kt < nk; kt += 2) {
-    step(r0, r1, kt);
-    step(r1, r0, kt + 1);
+  if constexpr (R3) {
+    for (int kt = 0; kt < nk; kt += 3) {
+      step(r0, r1, kt);
+      step(r1, r2, kt + 1);
+      step(r2, r0, kt + 2);
+    }
+  } else {
+    for (int kt = 0; kt < nk; kt += 2) {
+      step(r0, r1, kt);
+      step(r1, r0, kt + 1);
+    }
   }
 
   // ---- epilogue.  lane holds Y[m = (lane & 15) + row base][n = 4*(lane >> 4) + i + column base]
@@ -1055,8 +1074,21 @@ static hipError_t dispatch_mr(const GemmArgs& a, const GemmLaunch& l, hipStream_
     return hipErrorInvalidValue;
   }
   switch (l.MR) {  // GEMM_MT: MR = MF
-    case 1: return launch_mt<S, 1, 4, SRC, LO, OUT>(a, l, st);
-    case 2: return launch_mt<S, 2, 4, SRC, LO, OUT>(a, l, st);
+    case 1:
+      switch (l.NF) {
+        case 2: return launch_mt<S, 1, 2, SRC, LO, OUT>(a, l, st);
+        case 4: return launch_mt<S, 1, 4, SRC, LO, OUT>(a, l, st);
+        case 6: return launch_mt<S, 1, 6, SRC, LO, OUT>(a, l, st);
+        case 8: return launch_mt<S, 1, 8, SRC, LO, OUT>(a, l, st);
+      }
+      return hipErrorInvalidValue;
+    case 2:
+      switch (l.NF) {
+        case 2: return launch_mt<S, 2, 2, SRC, LO, OUT>(a, l, st);
+        case 4: return launch_mt<S, 2, 4, SRC, LO, OUT>(a, l, st);
+        case 6: return launch_mt<S, 2, 6, SRC, LO, OUT>(a, l, st);
+      }
+      return hipErrorInvalidValue;
     case 4:
       if constexpr (OUT == OUT_PARTIAL)
         if (l.NF == 6) return launch_mt<S, 4, 6, SRC, LO, OUT>(a, l, st);
