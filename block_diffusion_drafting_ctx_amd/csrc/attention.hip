@@ -29,6 +29,11 @@
 // each split segment in a fixed order (deterministic; no cross-workgroup
 // atomics).  All of it runs in one dispatch round.
 //
+// Two forms compute a piece.  A bf16 cache streams through an LDS ring fed
+// by LDS-DMA loads in MFMA fragment order, V read through the transposing
+// LDS read (attention_ring_kernel, below).  An fp32 or 8-bit cache takes the
+// register-staged form described next, which converts while it stores.
+//
 // Inside a piece: one workgroup of 8 waves; its query rows are the G query
 // heads of the KV head times the Bs block rows (QR = G*Bs rows, 16-row
 // tiles).  The waves are (query tile, key group) pairs: the key groups split
@@ -201,6 +206,71 @@ __device__ __forceinline__ int upper_index(int B, int x, F key) {
   return lo;
 }
 
+// The piece a workgroup computes: segment (b, h) of length seg_len starting at
+// sstart on the flattened key axis; keys [pstart, pend) of it are the
+// workgroup's.
+struct Piece {
+  int b, h, seg_len, sstart, pstart, pend;
+};
+
+// First piece of this workgroup's range under the plan in LDS (segment mode:
+// one balanced piece of one segment; else the flattened range of weighted
+// keys).  False when the workgroup has no key.  g1: end of the range on the
+// flattened axis.
+__device__ __forceinline__ bool planned_first_piece(const AttnArgs& a, const int* pre, const int* wpre, int mode,
+                                                    Piece& p, int& g1) {
+  const int Hkv = a.Hkv;
+  if (mode != 0) {
+    const int w = blockIdx.x;
+    if (w >= wpre[a.batch]) return false;
+    p.b = __builtin_amdgcn_readfirstlane(upper_index(a.batch, w, [&](int i) { return wpre[i]; }));
+    p.seg_len = __builtin_amdgcn_readfirstlane(pre[p.b + 1] - pre[p.b]);
+    const int nb = (wpre[p.b + 1] - wpre[p.b]) / Hkv;
+    const int idx = w - wpre[p.b];
+    p.h = __builtin_amdgcn_readfirstlane(idx / nb);
+    const int k = idx - p.h * nb;
+    p.sstart = Hkv * pre[p.b] + p.h * p.seg_len;
+    p.pstart = (int)((int64_t)k * p.seg_len / nb);
+    p.pend = (int)((int64_t)(k + 1) * p.seg_len / nb);
+    g1 = p.sstart + p.pend;
+    return true;
+  }
+  const int wtot = flat_weight(pre, a.batch, Hkv);
+  const int Q = range_keys(wtot, gridDim.x);
+  const int w0 = blockIdx.x * Q;
+  if (w0 >= wtot) return false;
+  const int g0 = __builtin_amdgcn_readfirstlane(flat_key_of(w0, pre, a.batch, Hkv));
+  g1 = __builtin_amdgcn_readfirstlane(flat_key_of(min(wtot, w0 + Q), pre, a.batch, Hkv));
+  if (g0 >= g1) return false;  // the range holds no key (inside a segment's extra run)
+  p.b = __builtin_amdgcn_readfirstlane(upper_index(a.batch, g0, [&](int i) { return Hkv * pre[i]; }));
+  p.seg_len = __builtin_amdgcn_readfirstlane(pre[p.b + 1] - pre[p.b]);
+  const int base = Hkv * pre[p.b];
+  p.h = __builtin_amdgcn_readfirstlane((g0 - base) / p.seg_len);
+  p.sstart = base + p.h * p.seg_len;
+  p.pstart = g0 - p.sstart;
+  p.pend = min(p.seg_len, g1 - p.sstart);
+  return true;
+}
+
+// Next stage of a range (c: the stage's first key in segment coordinates,
+// advanced by `stage` keys); at a piece end the range moves on to the next
+// segment.  False when the range is done.
+__device__ __forceinline__ bool next_stage(Piece& q, int& c, int stage, int g1, const int* pre, int Hkv) {
+  c += stage;
+  if (c < q.pend) return true;
+  q.sstart += q.seg_len;
+  if (q.sstart >= g1) return false;
+  if (++q.h == Hkv) {
+    q.h = 0;
+    ++q.b;
+    q.seg_len = __builtin_amdgcn_readfirstlane(pre[q.b + 1] - pre[q.b]);
+  }
+  q.pstart = 0;
+  q.pend = min(q.seg_len, g1 - q.sstart);
+  c = 0;
+  return true;
+}
+
 // QTP (waves per key group, >= the query tiles) is a template parameter so
 // that a wave's key units unroll completely; PLO: probabilities enter the PV
 // product as a hi/lo pair (else plain bf16).
@@ -225,11 +295,6 @@ __global__ void __launch_bounds__(kThreads) attention_kernel(const AttnArgs a) {
   const bool computes = qt < QT && kg < KG;
   const int Hkv = a.Hkv, Bs = a.Bs;
 
-  // the piece being computed: segment (b, h) of length seg_len starting at
-  // sstart on the flattened axis; keys [pstart, pend) of it are this workgroup's
-  struct Piece {
-    int b, h, seg_len, sstart, pstart, pend;
-  };
   // ---- query rows of the current piece: lane's row r = 16*qt + (lane & 15)
   const int r = 16 * qt + (lane & 15);
   const bool qvalid = computes && r < QR;
@@ -401,53 +466,10 @@ __global__ void __launch_bounds__(kThreads) attention_kernel(const AttnArgs a) {
   } else {
     if (wave == 0) build_plan(a.ctx_len, a.batch, Bs, Hkv, a.max_ctx, gridDim.x, pre, wpre, mode, lane);
     __syncthreads();
-    if (*mode != 0) {
-      const int w = blockIdx.x;
-      if (w >= wpre[a.batch]) return;
-      p.b = __builtin_amdgcn_readfirstlane(upper_index(a.batch, w, [&](int i) { return wpre[i]; }));
-      p.seg_len = __builtin_amdgcn_readfirstlane(pre[p.b + 1] - pre[p.b]);
-      const int nb = (wpre[p.b + 1] - wpre[p.b]) / Hkv;
-      const int idx = w - wpre[p.b];
-      p.h = __builtin_amdgcn_readfirstlane(idx / nb);
-      const int k = idx - p.h * nb;
-      p.sstart = Hkv * pre[p.b] + p.h * p.seg_len;
-      p.pstart = (int)((int64_t)k * p.seg_len / nb);
-      p.pend = (int)((int64_t)(k + 1) * p.seg_len / nb);
-      g1 = p.sstart + p.pend;
-    } else {
-      const int wtot = flat_weight(pre, a.batch, Hkv);
-      const int Q = range_keys(wtot, gridDim.x);
-      const int w0 = blockIdx.x * Q;
-      if (w0 >= wtot) return;
-      const int g0 = __builtin_amdgcn_readfirstlane(flat_key_of(w0, pre, a.batch, Hkv));
-      g1 = __builtin_amdgcn_readfirstlane(flat_key_of(min(wtot, w0 + Q), pre, a.batch, Hkv));
-      if (g0 >= g1) return;  // the range holds no key (inside a segment's extra run)
-      p.b = __builtin_amdgcn_readfirstlane(upper_index(a.batch, g0, [&](int i) { return Hkv * pre[i]; }));
-      p.seg_len = __builtin_amdgcn_readfirstlane(pre[p.b + 1] - pre[p.b]);
-      const int base = Hkv * pre[p.b];
-      p.h = __builtin_amdgcn_readfirstlane((g0 - base) / p.seg_len);
-      p.sstart = base + p.h * p.seg_len;
-      p.pstart = g0 - p.sstart;
-      p.pend = min(p.seg_len, g1 - p.sstart);
-    }
+    if (!planned_first_piece(a, pre, wpre, *mode, p, g1)) return;
   }
   int c0 = p.pstart;  // first key of the current stage, in segment coordinates
-  // next stage; false when the range is done
-  auto advance = [&](Piece& q, int& c) -> bool {
-    c += kStage;
-    if (c < q.pend) return true;
-    q.sstart += q.seg_len;
-    if (q.sstart >= g1) return false;
-    if (++q.h == Hkv) {
-      q.h = 0;
-      ++q.b;
-      q.seg_len = __builtin_amdgcn_readfirstlane(pre[q.b + 1] - pre[q.b]);
-    }
-    q.pstart = 0;
-    q.pend = min(q.seg_len, g1 - q.sstart);
-    c = 0;
-    return true;
-  };
+  auto advance = [&](Piece& q, int& c) -> bool { return next_stage(q, c, kStage, g1, pre, Hkv); };
 
   float m_run = -INFINITY, l_run = 0.f;
   f32x4 o[D / 16];
@@ -708,6 +730,536 @@ __global__ void __launch_bounds__(kThreads) attention_kernel(const AttnArgs a) {
   }
 }
 
+// ---------------------------------------------------------------- bf16 cache: LDS ring fed by LDS-DMA
+// The bf16 cache takes a second form of the same piece computation, built on
+// two gfx950 LDS paths:
+//  * global_load_lds_dwordx4 writes a lane's 16 bytes straight into LDS at
+//    the wave-uniform block address + 16 * lane, so one load instruction fills
+//    one 1 KB block, in whatever order the lanes' global addresses pick.  No
+//    registers hold a stage and no store instructions move it.
+//  * ds_read_b64_tr_b16 reads 8 bytes per lane and transposes 16-bit elements
+//    inside every group of 16 lanes: lane i of a group receives, as element e,
+//    element i % 4 of the 8 bytes lane 4e + i / 4 of the group points at.
+// A stage of NU 32-key units is one slot of an NS-slot ring, in MFMA fragment
+// order:
+//  * K: 1 KB blocks [unit][half h][s], lane l of a block holding key
+//    16h + (l & 15), dims 32s + 8(l >> 4) .. +8: the A operand of S^T = K Q^T,
+//    read by one ds_read_b128 at 16 * lane.
+//  * V: 1 KB blocks [unit][key half kh][dim pair dp], each two 512-byte tiles
+//    [16 keys][16 dims] row-major (dims 32dp + 16t + [0, 16), t = 0, 1).  The
+//    transposing read of a tile at 8 * lane gives lane (G = lane >> 4,
+//    j = lane & 15) the values of dim j at keys 4G + [0, 4) of the tile; the
+//    two key halves make the A operand of O^T = V^T P^T with the same
+//    key-to-slot map as the probabilities' B operand.
+// Both reads are contiguous across the wave: conflict-free.  Loads of a stage
+// are issued NS - 1 stages ahead; each wave issues the same number of them for
+// every stage, so the wait for a stage is a fixed count of loads still in
+// flight.  The barriers are plain s_barrier with explicit waits: a fence would
+// wait for every LDS-DMA load in flight, the prefetched stages too.
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// s_waitcnt vmcnt(N) (expcnt and lgkmcnt untouched).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+// s_waitcnt lgkmcnt(0): this wave's LDS writes are done.
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+// Workgroup barrier without a memory fence (the compiler keeps memory
+// accesses on their side of it; the waits before it are explicit).
+__device__ __forceinline__ void raw_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// The V operands of one 32-key unit: for every 16-dim slice ds the two key
+// halves' transposing reads (tile offsets 512 * ds, plus FB KB for the second
+// half), all issued in one block that waits for them before it ends.  (As an
+// intrinsic, the compiler puts a wait for every LDS-DMA load in flight before
+// each such read.)  The outputs are early-clobber: a read in flight must not
+// land in the address register of a later one.
+template <int D>
+__device__ __forceinline__ void read_v_unit(const unsigned char* vbase, u32x2 (&v)[D / 16][2]);
+template <>
+__device__ __forceinline__ void read_v_unit<128>(const unsigned char* vbase, u32x2 (&v)[8][2]) {
+  const uint32_t a = (uint32_t)(uintptr_t)(lds_void_t*)vbase;
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %16 offset:0\n\t"
+      "ds_read_b64_tr_b16 %1, %16 offset:4096\n\t"
+      "ds_read_b64_tr_b16 %2, %16 offset:512\n\t"
+      "ds_read_b64_tr_b16 %3, %16 offset:4608\n\t"
+      "ds_read_b64_tr_b16 %4, %16 offset:1024\n\t"
+      "ds_read_b64_tr_b16 %5, %16 offset:5120\n\t"
+      "ds_read_b64_tr_b16 %6, %16 offset:1536\n\t"
+      "ds_read_b64_tr_b16 %7, %16 offset:5632\n\t"
+      "ds_read_b64_tr_b16 %8, %16 offset:2048\n\t"
+      "ds_read_b64_tr_b16 %9, %16 offset:6144\n\t"
+      "ds_read_b64_tr_b16 %10, %16 offset:2560\n\t"
+      "ds_read_b64_tr_b16 %11, %16 offset:6656\n\t"
+      "ds_read_b64_tr_b16 %12, %16 offset:3072\n\t"
+      "ds_read_b64_tr_b16 %13, %16 offset:7168\n\t"
+      "ds_read_b64_tr_b16 %14, %16 offset:3584\n\t"
+      "ds_read_b64_tr_b16 %15, %16 offset:7680\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(v[0][0]), "=&v"(v[0][1]), "=&v"(v[1][0]), "=&v"(v[1][1]), "=&v"(v[2][0]), "=&v"(v[2][1]), "=&v"(v[3][0]),
+        "=&v"(v[3][1]), "=&v"(v[4][0]), "=&v"(v[4][1]), "=&v"(v[5][0]), "=&v"(v[5][1]), "=&v"(v[6][0]), "=&v"(v[6][1]),
+        "=&v"(v[7][0]), "=&v"(v[7][1])
+      : "v"(a)
+      : "memory");
+}
+template <>
+__device__ __forceinline__ void read_v_unit<64>(const unsigned char* vbase, u32x2 (&v)[4][2]) {
+  const uint32_t a = (uint32_t)(uintptr_t)(lds_void_t*)vbase;
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %8 offset:0\n\t"
+      "ds_read_b64_tr_b16 %1, %8 offset:2048\n\t"
+      "ds_read_b64_tr_b16 %2, %8 offset:512\n\t"
+      "ds_read_b64_tr_b16 %3, %8 offset:2560\n\t"
+      "ds_read_b64_tr_b16 %4, %8 offset:1024\n\t"
+      "ds_read_b64_tr_b16 %5, %8 offset:3072\n\t"
+      "ds_read_b64_tr_b16 %6, %8 offset:1536\n\t"
+      "ds_read_b64_tr_b16 %7, %8 offset:3584\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(v[0][0]), "=&v"(v[0][1]), "=&v"(v[1][0]), "=&v"(v[1][1]), "=&v"(v[2][0]), "=&v"(v[2][1]), "=&v"(v[3][0]),
+        "=&v"(v[3][1])
+      : "v"(a)
+      : "memory");
+}
+
+// max / sum of v over lanes l, l ^ 16, l ^ 32, l ^ 48 (the four lanes of one
+// MFMA column), through the gfx950 row swaps: permlane16_swap of two copies
+// of v leaves v of the lane and of its xor-16 partner in the two results
+// (which one is where does not matter for max and sum), permlane32_swap the
+// same for the xor-32 partner.  Register to register, no LDS round trip.
+__device__ __forceinline__ float col4_max(float v) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float col4_sum(float v) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+template <int D, int NU, int W>
+struct RingSlot {
+  static constexpr int FB = D / 32;         // 1 KB blocks per (unit, half) of K and of V
+  static constexpr int KBLK = NU * 2 * FB;  // K blocks of a slot
+  static constexpr int BLK = 2 * KBLK;      // K then V blocks
+  static constexpr int BYTES = BLK * 1024;
+  static constexpr int PER_WAVE = BLK / W;  // loads per wave per stage
+  static_assert(BLK % W == 0, "a stage's blocks must split evenly over the waves");
+};
+// key groups of a W-wave workgroup with qtp waves per group and nu units a stage
+__host__ __device__ constexpr int ring_kg(int w, int qtp, int nu) { return w / qtp < nu ? w / qtp : nu; }
+
+template <int D, int W, int QTP, bool PLO, int NU, int NS, bool QSLOT>
+__global__ void __launch_bounds__(W * 64) attention_ring_kernel(const AttnArgs a) {
+  using R = RingSlot<D, NU, W>;
+  constexpr int kStage = kUnit * NU;
+  constexpr int KG = ring_kg(W, QTP, NU);  // key groups
+  constexpr int UPG = NU / KG;          // units per key group and stage
+  static_assert(KG * QTP <= W && UPG * KG == NU, "wave layout");
+  static_assert(NS >= 2 && NS - 2 <= 3, "ring depth");
+  static_assert((KG - 1) * QTP * (D / 16) * 64 * 16 <= R::BYTES, "key-group records fit a slot");
+  extern __shared__ __align__(16) unsigned char lds_raw[];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int G = a.Hq / a.Hkv;
+  const int QR = G * a.Bs;
+  const int QT = (QR + 15) / 16;
+  // LDS: ring [NS slots] | queries [QT tiles][hi/lo][D/32] 1 KB blocks (QSLOT:
+  // none; they pass through a ring slot that holds no stage) | key-group
+  // records | plan [2][batch + 1] + 1
+  static_assert(!QSLOT || QTP <= 2 * NU, "the queries of QTP tiles fill at most one slot");
+  unsigned char* ring = lds_raw;
+  unsigned char* qarea = lds_raw + NS * R::BYTES;
+  float* mml = reinterpret_cast<float*>(qarea + (QSLOT ? 0 : QT * 2 * R::FB * 1024));  // [KG-1][QTP][64][2]
+  int* pre = reinterpret_cast<int*>(mml + (KG > 1 ? KG - 1 : 1) * QTP * 64 * 2);
+  int* wpre = pre + a.batch + 1;
+  int* mode = wpre + a.batch + 1;
+  if constexpr (QSLOT) qarea = ring + (NS - 1) * R::BYTES;  // the slot the first stages leave free
+  const int qt = wave % QTP, kg = wave / QTP;
+  const bool computes = qt < QT && kg < KG;
+  const int Hkv = a.Hkv, Bs = a.Bs;
+
+  // ---- query rows of the current piece: lane's row r = 16*qt + (lane & 15)
+  const int r = 16 * qt + (lane & 15);
+  const bool qvalid = computes && r < QR;
+  const int rr = qvalid ? r : 0;
+  const int gq = rr / Bs, iq = rr - gq * Bs;
+  const int HqD = a.Hq * D;
+  // The queries of a piece reach the registers through LDS: LDS-DMA loads
+  // into the query area (block (tile, hi/lo, s): lane l holds row
+  // 16 tile + (l & 15), dims 32s + 8(l >> 4); rows past QR repeat the last
+  // row), then one ds_read_b128 per fragment.  (A register load followed by
+  // LDS-DMA loads makes the compiler wait for all of them before the
+  // register is used.)
+  bf16x8 qf[D / 32], qr[D / 32];  // query = qf + qr (hi/lo pair)
+  auto q_issue = [&](const Piece& q) {
+    const int qblk = QT * 2 * R::FB;
+    // hi or lo by arithmetic (a select of the two pointers became a load of
+    // the argument block at a computed offset)
+    const uintptr_t qh0 = reinterpret_cast<uintptr_t>(a.q_hi), dlo = reinterpret_cast<uintptr_t>(a.q_lo) - qh0;
+    for (int b = wave; b < qblk; b += W) {  // wave-uniform count
+      const int t = b / (2 * R::FB), hl = (b / R::FB) & 1, s = b % R::FB;
+      const int rq = min(16 * t + (lane & 15), QR - 1);
+      const int g = rq / Bs, iqr = rq - g * Bs;
+      const size_t off = (size_t)(q.b * Bs + iqr) * HqD + (q.h * G + g) * D + 32 * s + 8 * (lane >> 4);
+      const bf16_t* src = reinterpret_cast<const bf16_t*>(qh0 + (uintptr_t)hl * dlo) + off;
+      __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(qarea + b * 1024), 16, 0, 0);
+    }
+    asm volatile("" ::: "memory");
+  };
+  auto q_read = [&]() {
+    const int t = qt < QT ? qt : 0;
+#pragma unroll
+    for (int s = 0; s < D / 32; ++s) {
+      qf[s] = *reinterpret_cast<const bf16x8*>(qarea + ((t * 2 + 0) * R::FB + s) * 1024 + 16 * lane);
+      qr[s] = *reinterpret_cast<const bf16x8*>(qarea + ((t * 2 + 1) * R::FB + s) * 1024 + 16 * lane);
+    }
+  };
+
+  // ---- a stage's loads: this wave's blocks wave, wave + 8, ...  A key past
+  // the piece (or past the cache) re-reads the stage's last existing key; its
+  // score is masked and its probability is 0.  (A fixed chunk's first stages
+  // are requested before the context length is known, so there such keys can
+  // be any cache rows: their values are zeroed in the PV operand.)
+  const bf16_t* kc = reinterpret_cast<const bf16_t*>(a.kc);
+  const bf16_t* vc = reinterpret_cast<const bf16_t*>(a.vc);
+  const size_t row = (size_t)Hkv * D;
+  auto issue = [&](const Piece& q, int c, int slot) {
+    const int lim = min(a.max_ctx, q.pend) - 1 - c;
+    const size_t base = ((size_t)q.b * a.max_ctx + c) * row + q.h * D;
+    unsigned char* sl = ring + slot * R::BYTES;
+#pragma unroll
+    for (int i = 0; i < R::PER_WAVE; ++i) {
+      const int blk = wave + W * i;
+      const bf16_t* src;
+      if (blk < R::KBLK) {  // K block (unit, half, s): lane -> key 16h + (lane & 15), dims 32s + 8(lane >> 4)
+        const int u = blk / (2 * R::FB), h = (blk / R::FB) & 1, s = blk % R::FB;
+        const int key = kUnit * u + 16 * h + (lane & 15);
+        src = kc + base + (size_t)(min(key, lim) * (int)row + 32 * s + 8 * (lane >> 4));
+      } else {  // V block (unit, kh, dp): lane -> tile lane >> 5, key 16kh + (lane & 31) / 2, 8 dims
+        const int vb = blk - R::KBLK;
+        const int u = vb / (2 * R::FB), kh = (vb / R::FB) & 1, dp = vb % R::FB;
+        const int key = kUnit * u + 16 * kh + ((lane & 31) >> 1);
+        src = vc + base + (size_t)(min(key, lim) * (int)row + 32 * dp + 16 * (lane >> 5) + 8 * (lane & 1));
+      }
+      __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(sl + blk * 1024), 16, 0, 0);
+    }
+    asm volatile("" ::: "memory");  // stages are issued in order (the waits count them)
+  };
+  // wait until at most `ahead` stages' loads of this wave are in flight
+  auto wait_stage = [&](int ahead) {
+    if (ahead >= 3) wait_vm<3 * R::PER_WAVE>();
+    else if (ahead == 2) wait_vm<2 * R::PER_WAVE>();
+    else if (ahead == 1) wait_vm<R::PER_WAVE>();
+    else wait_vm<0>();
+  };
+
+  // ---- this workgroup's first piece; its queries and first stages in flight
+  Piece p;
+  int g1;
+  Piece ip;        // the last stage issued: piece and first key
+  int ic;
+  int ahead = 0;   // stages issued beyond the current one
+  bool more;       // the range has stages beyond the last one issued
+  if (a.fixed_chunk > 0) {
+    // fixed chunks: the segment and chunk follow from the workgroup index;
+    // the queries and the chunk's first stages (all inside the cache) are
+    // requested before the context length arrives
+    const int C = a.fixed_chunk;
+    const int sg = blockIdx.x / a.fixed_pieces, k = blockIdx.x - sg * a.fixed_pieces;
+    p.b = sg / Hkv;
+    p.h = sg - p.b * Hkv;
+    // a scalar load (constant address space): no vector-memory count to wait on
+    const int craw = ((const __attribute__((address_space(4))) int32_t*)a.ctx_len)[p.b];
+    p.pstart = k * C;
+    p.sstart = 0;
+    if (p.pstart >= a.max_ctx) return;
+    Piece ps = p;
+    ps.seg_len = a.max_ctx;
+    ps.pend = min(p.pstart + C, a.max_ctx);
+    q_issue(ps);  // the queries go out before the stages
+    // the first NS - 1 stages (a stage past the chunk re-reads its last one)
+    int n = 0;
+#pragma unroll
+    for (int j = 0; j < NS - 1; ++j) {
+      const int cj = ps.pstart + kStage * j;
+      if (cj < ps.pend) n = j + 1;
+      issue(ps, cj < ps.pend ? cj : ps.pstart + kStage * (n - 1), j);
+    }
+    p.seg_len = min(min(max(craw, 0), a.max_ctx) + Bs, a.max_ctx);
+    p.pend = min(p.pstart + C, p.seg_len);
+    if (p.pstart >= p.pend) {
+      wait_vm<0>();  // no load may still write this workgroup's LDS when it ends
+      return;
+    }
+    g1 = p.pend;
+    ip = p;
+    ic = p.pstart + kStage * (n - 1);
+    more = ic + kStage < p.pend;
+  } else {
+    if (wave == 0) build_plan(a.ctx_len, a.batch, Bs, Hkv, a.max_ctx, gridDim.x, pre, wpre, mode, lane);
+    __syncthreads();
+    if (!planned_first_piece(a, pre, wpre, *mode, p, g1)) return;
+    q_issue(p);  // the queries go out before the stages
+    // the first NS - 1 stages of the range (once the range is done, its last
+    // stage is requested again)
+    ip = p;
+    ic = p.pstart;
+    more = true;
+#pragma unroll
+    for (int j = 0; j < NS - 1; ++j) {
+      if (j > 0 && more) {
+        Piece t = ip;
+        int tc = ic;
+        more = next_stage(t, tc, kStage, g1, pre, Hkv);
+        if (more) {
+          ip = t;
+          ic = tc;
+        }
+      }
+      issue(ip, ic, j);
+    }
+    if (more) {  // is there a stage after the last one issued?
+      Piece t = ip;
+      int tc = ic;
+      more = next_stage(t, tc, kStage, g1, pre, Hkv);
+    }
+  }
+  // NS - 1 stages were requested (some possibly repeats); the wait for the
+  // first one also covers the queries, requested before it
+  ahead = NS - 2;
+  bool q_pending = true;  // the piece's queries are to be read from LDS at the next step
+  bool q_late = false;    // ... and were requested after stages still in flight
+
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x4 o[D / 16];
+#pragma unroll
+  for (int ds = 0; ds < D / 16; ++ds) o[ds] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // ---- matrix and softmax work of a wave's units of one stage (as in the
+  // register-staged form, with the operands read from the ring slot)
+  constexpr int UC = UPG < 3 ? UPG : 3;  // units per softmax update
+  auto compute_units = [&](const unsigned char* sl, int c, int j1, int ub) {
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    f32x4 sc[UC][2];
+#pragma unroll
+    for (int uu = 0; uu < UC; ++uu) {
+      const int u = ub + uu;
+      f32x4 lo[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) sc[uu][h] = lo[h] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (c + kUnit * u >= j1) continue;
+#pragma unroll
+      for (int s = 0; s < D / 32; ++s)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const bf16x8 kf = *reinterpret_cast<const bf16x8*>(sl + ((u * 2 + h) * R::FB + s) * 1024 + 16 * ln);
+          sc[uu][h] = mfma16x16x32(kf, qf[s], sc[uu][h]);
+          lo[h] = mfma16x16x32(kf, qr[s], lo[h]);
+        }
+#pragma unroll
+      for (int h = 0; h < 2; ++h) sc[uu][h] += lo[h];
+    }
+    // lane holds keys c + 32*u + 16*h + 4*(lane>>4) + e for query row (lane & 15)
+    if (c + kUnit * (ub + UC) > j1) {  // keys past the piece: masked
+#pragma unroll
+      for (int uu = 0; uu < UC; ++uu)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (c + kUnit * (ub + uu) + 16 * h + 4 * (lane >> 4) + e >= j1) sc[uu][h][e] = -INFINITY;
+    }
+    float cmax = -INFINITY;
+#pragma unroll
+    for (int uu = 0; uu < UC; ++uu)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) cmax = fmaxf(cmax, sc[uu][h][e]);
+    cmax = col4_max(cmax);
+    const float m_new = fmaxf(m_run, cmax);
+    if (m_new == -INFINITY) return;  // no valid key in these units
+    const float alpha = fast_exp2(m_run - m_new);
+    float psum = 0.f;
+#pragma unroll
+    for (int uu = 0; uu < UC; ++uu)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          sc[uu][h][e] = fast_exp2(sc[uu][h][e] - m_new);
+          psum += sc[uu][h][e];
+        }
+    l_run = l_run * alpha + psum;
+    // the output is rescaled only when some row's running max moved (alpha
+    // is 1 in every other row)
+    if (__builtin_amdgcn_ballot_w64(m_new != m_run)) {
+#pragma unroll
+      for (int ds = 0; ds < D / 16; ++ds) o[ds] *= alpha;
+    }
+    m_run = m_new;
+#pragma unroll
+    for (int uu = 0; uu < UC; ++uu) {
+      const int u = ub + uu;
+      if (c + kUnit * u >= j1) continue;
+      bf16x8 ph, pl;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        ph[e] = (__bf16)sc[uu][0][e];
+        ph[4 + e] = (__bf16)sc[uu][1][e];
+        if constexpr (PLO) {
+          pl[e] = (__bf16)(sc[uu][0][e] - (float)ph[e]);
+          pl[4 + e] = (__bf16)(sc[uu][1][e] - (float)ph[4 + e]);
+        }
+      }
+      u32x2 vr[D / 16][2];
+      read_v_unit<D>(sl + (R::KBLK + u * 2 * R::FB) * 1024 + 8 * ln, vr);
+#pragma unroll
+      for (int ds = 0; ds < D / 16; ++ds) {
+        bf16x8 vf = __builtin_bit_cast(bf16x8, u32x4{vr[ds][0][0], vr[ds][0][1], vr[ds][1][0], vr[ds][1][1]});
+        if (c + kUnit * (u + 1) > j1) {  // the piece ends inside this unit: keys past it hold 0
+          const int kb = c + kUnit * u + 4 * (ln >> 4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            if (kb + e >= j1) vf[e] = (__bf16)0.f;
+            if (kb + 16 + e >= j1) vf[4 + e] = (__bf16)0.f;
+          }
+        }
+        o[ds] = mfma16x16x32(vf, ph, o[ds]);
+        if constexpr (PLO) o[ds] = mfma16x16x32(vf, pl, o[ds]);
+      }
+    }
+  };
+  // the stage's units that hold keys are split evenly over the key groups
+  auto compute = [&](const unsigned char* sl, int c, int j1) {
+    if (!computes) return;
+    const int nu = min(NU, (j1 - c + kUnit - 1) / kUnit);
+    const int per = (nu + KG - 1) / KG;
+    const int u0 = kg * per;
+    const int jg = min(j1, c + kUnit * min(nu, u0 + per));
+    for (int cb = 0; cb < per; cb += UC) compute_units(sl, c, jg, u0 + cb);
+  };
+
+  // ---- close a piece: the key groups of each query tile merge through the
+  // slot just computed (group 0 keeps the result), then the output or the
+  // partial is written
+  auto close_piece = [&](const Piece& q, unsigned char* sl) {
+    if constexpr (KG > 1) {
+      raw_barrier();  // every wave is done reading the slot
+      f32x4* mo = reinterpret_cast<f32x4*>(sl);  // [KG-1][QTP][D/16][64]
+      if (computes && kg > 0) {
+        const int g = (kg - 1) * QTP + qt;
+#pragma unroll
+        for (int ds = 0; ds < D / 16; ++ds) mo[(g * (D / 16) + ds) * 64 + lane] = o[ds];
+        mml[(g * 64 + lane) * 2] = m_run;
+        mml[(g * 64 + lane) * 2 + 1] = l_run;
+      }
+      wait_lgkm0();
+      raw_barrier();
+      if (computes && kg == 0) {
+#pragma unroll
+        for (int g2 = 1; g2 < KG; ++g2) {
+          const int g = (g2 - 1) * QTP + qt;
+          const float m2 = mml[(g * 64 + lane) * 2], l2 = mml[(g * 64 + lane) * 2 + 1];
+          const float mn = fmaxf(m_run, m2);
+          if (mn == -INFINITY) continue;
+          const float w1 = m_run == -INFINITY ? 0.f : fast_exp2(m_run - mn);
+          const float w2 = m2 == -INFINITY ? 0.f : fast_exp2(m2 - mn);
+#pragma unroll
+          for (int ds = 0; ds < D / 16; ++ds) o[ds] = o[ds] * w1 + mo[(g * (D / 16) + ds) * 64 + lane] * w2;
+          l_run = l_run * w1 + l2 * w2;
+          m_run = mn;
+        }
+      }
+    }
+    if (computes && kg == 0) {
+      const float l_tot = col4_sum(l_run);
+      if (q.pstart == 0 && q.pend == q.seg_len) {  // the whole segment: final output
+        if (qvalid) {
+          bf16_t* out_h = reinterpret_cast<bf16_t*>(a.out_hi);
+          bf16_t* out_l = reinterpret_cast<bf16_t*>(a.out_lo);
+          const size_t qoff = (size_t)(q.b * Bs + iq) * HqD + (q.h * G + gq) * D;
+          const float inv = 1.0f / l_tot;
+#pragma unroll
+          for (int ds = 0; ds < D / 16; ++ds)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              split_out(out_h, out_l, qoff + 16 * ds + 4 * (lane >> 4) + e, o[ds][e] * inv);
+        }
+      } else if (qvalid) {
+        const size_t slot = (size_t)blockIdx.x + q.b * Hkv + q.h;
+        float* po = a.part_o + (slot * QR + r) * D;
+#pragma unroll
+        for (int ds = 0; ds < D / 16; ++ds) *reinterpret_cast<f32x4*>(po + 16 * ds + 4 * (lane >> 4)) = o[ds];
+        if ((lane >> 4) == 0) {
+          a.part_ml[(slot * QR + r) * 2 + 0] = m_run;
+          a.part_ml[(slot * QR + r) * 2 + 1] = l_tot;
+        }
+      }
+    }
+    m_run = -INFINITY;
+    l_run = 0.f;
+#pragma unroll
+    for (int ds = 0; ds < D / 16; ++ds) o[ds] = f32x4{0.f, 0.f, 0.f, 0.f};
+  };
+
+  // ---- the ring: stage i sits in slot i % NS; at the top of a step the
+  // stage NS - 1 ahead goes into the slot the previous stage freed
+  int c = p.pstart, slot = 0;
+  for (;;) {
+    if (q_late) wait_vm<0>();  // a new piece's queries: requested after the stages in flight
+    else wait_stage(ahead);
+    raw_barrier();  // the stage is in LDS for every wave; the previous slot is free
+    if (q_pending) {
+      q_read();
+      q_pending = q_late = false;
+      if constexpr (QSLOT) {  // the queries' slot is refilled below
+        wait_lgkm0();
+        raw_barrier();
+      }
+    }
+    if (more) {
+      more = next_stage(ip, ic, kStage, g1, pre, Hkv);
+      ++ahead;
+      issue(ip, ic, (slot + ahead) % NS);
+      Piece t = ip;
+      int tc = ic;
+      more = next_stage(t, tc, kStage, g1, pre, Hkv);
+    }
+    unsigned char* sl = ring + slot * R::BYTES;
+    compute(sl, c, p.pend);
+    Piece nx = p;
+    int nc = c;
+    const bool has_next = next_stage(nx, nc, kStage, g1, pre, Hkv);
+    const bool ends = !has_next || nx.sstart != p.sstart;
+    if (ends) close_piece(p, sl);
+    if (!has_next) break;
+    p = nx;
+    c = nc;
+    slot = slot + 1 == NS ? 0 : slot + 1;
+    --ahead;
+    if (ends) {  // the next piece's queries, waited for at the next step
+      if constexpr (QSLOT) {  // through the slot just computed (its records are read)
+        raw_barrier();
+        qarea = sl;
+      }
+      q_issue(p);
+      q_pending = q_late = true;
+    }
+  }
+  wait_vm<0>();  // no load may still write this workgroup's LDS when it ends
+}
+
 // Merge of the partial pieces of one segment (sequence, KV head).  Lanes are
 // (item, group) with SG groups per item (SG from the segment's piece count);
 // an item is one query row and 4 dims.  Group g takes pieces g, g+SG, ...,
@@ -839,14 +1391,62 @@ static hipError_t launch_attention_nu(const AttnArgs& a, int qtp, hipStream_t st
   return hipGetLastError();
 }
 
+// The bf16 ring, one 8-wave workgroup per compute unit.
+//  * Up to four query tiles: stages of four 32-key units (two 64 KB slots at
+//    D = 128, four 32 KB slots at D = 64), the queries passing through the
+//    slot the first stage leaves free.
+//  * More tiles: stages of two units and a query area of its own beside three
+//    slots (two at the largest shapes).
+// (Measured at the Qwen3-8B shapes: two 4-wave workgroups per unit, stages of
+// two units in four slots, and this form all stream the 32k-context batch-4
+// cache in 138-141 us per layer; the 4-wave form was 4% slower at batch 32.)
+constexpr size_t kLdsBytes = 160 * 1024;
+
+template <int D, int NU, int W>
+static size_t ring_lds_bytes(int NS, bool qslot, int QT, int qtp, int batch) {
+  const int kg = ring_kg(W, qtp, NU);
+  return (size_t)NS * RingSlot<D, NU, W>::BYTES + (qslot ? 0 : (size_t)QT * 2 * (D / 32) * 1024) +
+         (size_t)(kg > 1 ? kg - 1 : 1) * qtp * 64 * 2 * sizeof(float) + (size_t)(2 * (batch + 1) + 1) * sizeof(int);
+}
+
+template <int D, int W, int QTP, int NU, int NS, bool QSLOT>
+static hipError_t launch_ring(const AttnArgs& a, hipStream_t stream) {
+  const int QT = ((a.Hq / a.Hkv) * a.Bs + 15) / 16;
+  const size_t lds = ring_lds_bytes<D, NU, W>(NS, QSLOT, QT, QTP, a.batch);
+  if (lds > kLdsBytes) return hipErrorInvalidValue;
+  auto k = a.p_lo ? attention_ring_kernel<D, W, QTP, true, NU, NS, QSLOT>
+                  : attention_ring_kernel<D, W, QTP, false, NU, NS, QSLOT>;
+  (void)allow_dynamic_lds(reinterpret_cast<const void*>(k), lds);
+  hipLaunchKernelGGL(k, dim3(a.nwg), dim3(W * 64), lds, stream, a);
+  return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_attention_ring(const AttnArgs& a, int qtp, hipStream_t stream) {
+  constexpr int NSQ = D == 128 ? 2 : 4;  // slots of the four-unit ring
+  if (qtp <= 4)
+    return qtp == 1 ? launch_ring<D, 8, 1, 4, NSQ, true>(a, stream)
+                    : qtp == 2 ? launch_ring<D, 8, 2, 4, NSQ, true>(a, stream) : launch_ring<D, 8, 4, 4, NSQ, true>(a, stream);
+  const int QT = ((a.Hq / a.Hkv) * a.Bs + 15) / 16;
+  if (ring_lds_bytes<D, 2, 8>(4, false, QT, qtp, a.batch) <= kLdsBytes) return launch_ring<D, 8, 8, 2, 4, false>(a, stream);
+  if (ring_lds_bytes<D, 2, 8>(3, false, QT, qtp, a.batch) <= kLdsBytes) return launch_ring<D, 8, 8, 2, 3, false>(a, stream);
+  return launch_ring<D, 8, 8, 2, 2, false>(a, stream);
+}
+
 template <typename S, int D>
 static hipError_t launch_attention_d(const AttnArgs& a, hipStream_t stream) {
   const int QR = (a.Hq / a.Hkv) * a.Bs;
   if (QR > 16 * kWaves || a.nwg <= 0 || a.batch > kAttnMaxBatch) return hipErrorInvalidValue;
   const int qtp = attn_qtp((QR + 15) / 16);
-  // a fixed chunk that fits one 192-key stage takes the one-stage form
-  const bool one_stage = a.fixed_chunk > 0 && a.fixed_chunk <= 6 * kUnit;
-  hipError_t e = one_stage ? launch_attention_nu<S, D, 6>(a, qtp, stream) : launch_attention_nu<S, D, 4>(a, qtp, stream);
+  hipError_t e;
+  if constexpr (std::is_same<S, bf16_t>::value) {
+    e = launch_attention_ring<D>(a, qtp, stream);
+  } else {
+    // register-staged form; a fixed chunk that fits one 192-key stage takes
+    // the one-stage variant
+    const bool one_stage = a.fixed_chunk > 0 && a.fixed_chunk <= 6 * kUnit;
+    e = one_stage ? launch_attention_nu<S, D, 6>(a, qtp, stream) : launch_attention_nu<S, D, 4>(a, qtp, stream);
+  }
   if (e != hipSuccess) return e;
   // merge chunks per segment: enough for the finest grouping (16 items per
   // chunk) at small batches, about 2048 workgroups in all at large ones
