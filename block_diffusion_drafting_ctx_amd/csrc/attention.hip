@@ -756,23 +756,6 @@ __global__ void __launch_bounds__(kThreads) attention_kernel(const AttnArgs a) {
 // every stage, so the wait for a stage is a fixed count of loads still in
 // flight.  The barriers are plain s_barrier with explicit waits: a fence would
 // wait for every LDS-DMA load in flight, the prefetched stages too.
-typedef __attribute__((address_space(3))) void lds_void_t;
-
-// s_waitcnt vmcnt(N) (expcnt and lgkmcnt untouched).
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-// s_waitcnt lgkmcnt(0): this wave's LDS writes are done.
-__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
-// Workgroup barrier without a memory fence (the compiler keeps memory
-// accesses on their side of it; the waits before it are explicit).
-__device__ __forceinline__ void raw_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
 
 // The V operands of one 32-key unit: for every 16-dim slice ds the two key
 // halves' transposing reads (tile offsets 512 * ds, plus FB KB for the second

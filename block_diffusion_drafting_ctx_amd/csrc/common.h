@@ -184,6 +184,35 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // s_waitcnt vmcnt(0): every vector memory access of the wave has completed.
 __device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// ---------------------------------------------------------------- LDS-DMA
+// global_load_lds_dwordx4 (gfx950) writes lane l's 16 bytes at the
+// wave-uniform LDS address + 16 * l; the loads count in vmcnt like any other
+// and complete in issue order.  Waits for them are explicit: the compiler
+// treats a register load followed by LDS-DMA loads as possibly completing out
+// of order and waits for all of them before using the register, and a
+// workgroup fence waits for every LDS-DMA load in flight.
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+__device__ __forceinline__ void lds_dma16(const void* src, void* lds_dst) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void_t*)lds_dst, 16, 0, 0);
+}
+
+// s_waitcnt vmcnt(N) (expcnt and lgkmcnt untouched).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+// s_waitcnt lgkmcnt(0): this wave's LDS writes are done.
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+// Workgroup barrier without a memory fence (the compiler keeps memory
+// accesses on their side of it; the waits before it are explicit).
+__device__ __forceinline__ void raw_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 __device__ __forceinline__ float silu_f32(float x) {
   return x / (1.0f + fast_exp2(-x * 1.4426950408889634f));
 }
