@@ -283,28 +283,11 @@ struct MtShape {
   static constexpr int BN = 32 * NF;
   static constexpr int BK = MF >= 4 ? 32 : 64;
   static constexpr int KST = BK / 32;  // 32-deep k-steps per stage
-  static constexpr int LDK = BK;       // LDS row stride (elements), unpadded: see mt_lds
+  static constexpr int LDK = BK + 16;  // LDS row stride (elements): 96- or 160-byte rows, conflict-free fragment reads
   static constexpr int APR = BK / 8;   // 8-element activation pieces per row and stage
   static constexpr int APT = (BM * APR + 511) / 512;  // activation pieces per thread per array
   static constexpr int WPT = (BN * 4 * KST + 511) / 512;  // weight pieces (16 bytes) per thread
 };
-
-// LDS element offset of the 16-byte piece at (row, col) of a stage (col a
-// multiple of 8).  The LDS serves 16 lanes (256 bytes) at a time: 16
-// consecutive rows at one column (a fragment read, a weight store) or two
-// rows of eight pieces (an activation store) must fall on distinct 16-byte
-// bank groups.  Rows are unpadded (R = 256 / row bytes rows share a 256-byte
-// span) and the piece index within a row is XORed with (row / R): rows of
-// the same position in their span take distinct pieces.  (Padded 96- and
-// 160-byte rows repeat the bank pattern every 8 rows: rows r and r + 8 of a
-// fragment conflicted, measured as LDS bank-conflict cycles about equal to
-// the LDS busy cycles at batch 32.)
-template <int BK>
-__device__ __forceinline__ int mt_lds(int row, int col) {
-  constexpr int CH = BK / 8;     // pieces per row
-  constexpr int R = 256 / (2 * BK);  // rows per 256 bytes
-  return row * BK + ((((col >> 3) ^ (row / R)) & (CH - 1)) << 3);
-}
 
 template <int MF, int NF, int SRC, bool LO>
 struct MtRegs {
@@ -315,7 +298,7 @@ struct MtRegs {
 
 size_t gemm_mt_lds_bytes(int MF, int NF, bool lo) {
   const int BM = 64 * MF, BN = 32 * NF, BK = MF >= 4 ? 32 : 64;
-  return (size_t)2 * ((lo ? 2 : 1) * BM + BN) * BK * 2;
+  return (size_t)2 * ((lo ? 2 : 1) * BM + BN) * (BK + 16) * 2;
 }
 
 template <typename S, int MF, int NF, int SRC, bool LO, int OUT>
@@ -385,7 +368,7 @@ __global__ void __launch_bounds__(512) gemm_mt_kernel(const GemmArgs g) {
 #pragma unroll
     for (int i = 0; i < WPT; ++i) {
       const u32x4 z = {0u, 0u, 0u, 0u};
-      *reinterpret_cast<bf16x8*>(&st[mt_lds<BK>(NA * BM + wrow(i), wcol(i))]) =
+      *reinterpret_cast<bf16x8*>(&st[(NA * BM + wrow(i)) * LDK + wcol(i)]) =
           __builtin_bit_cast(bf16x8, live ? r.w[i].lo : z);
     }
 #pragma unroll
@@ -410,8 +393,8 @@ __global__ void __launch_bounds__(512) gemm_mt_kernel(const GemmArgs g) {
         }
         lv = f32x8_to_bf16x8(l0, l1);
       }
-      *reinterpret_cast<bf16x8*>(&st[mt_lds<BK>(prow(i), pc)]) = hv;
-      if constexpr (LO) *reinterpret_cast<bf16x8*>(&st[mt_lds<BK>(BM + prow(i), pc)]) = lv;
+      *reinterpret_cast<bf16x8*>(&st[prow(i) * LDK + pc]) = hv;
+      if constexpr (LO) *reinterpret_cast<bf16x8*>(&st[(BM + prow(i)) * LDK + pc]) = lv;
     }
   };
 
@@ -424,16 +407,16 @@ __global__ void __launch_bounds__(512) gemm_mt_kernel(const GemmArgs g) {
     const bf16_t* st = sm + buf * STAGE;
 #pragma unroll
     for (int kq = 0; kq < KST; ++kq) {
-      const int fc = 8 * (lane >> 4) + 32 * kq, fr = lane & 15;  // (row in the fragment, column)
+      const int fr = (lane & 15) * LDK + 8 * (lane >> 4) + 32 * kq;
       bf16x8 af[MF], al[MF];
 #pragma unroll
       for (int fm = 0; fm < MF; ++fm) {
-        af[fm] = *reinterpret_cast<const bf16x8*>(&st[mt_lds<BK>(16 * MF * wm + 16 * fm + fr, fc)]);
-        if constexpr (LO) al[fm] = *reinterpret_cast<const bf16x8*>(&st[mt_lds<BK>(BM + 16 * MF * wm + 16 * fm + fr, fc)]);
+        af[fm] = *reinterpret_cast<const bf16x8*>(&st[(16 * MF * wm + 16 * fm) * LDK + fr]);
+        if constexpr (LO) al[fm] = *reinterpret_cast<const bf16x8*>(&st[(BM + 16 * MF * wm + 16 * fm) * LDK + fr]);
       }
 #pragma unroll
       for (int fn = 0; fn < NF; ++fn) {
-        const bf16x8 wf = *reinterpret_cast<const bf16x8*>(&st[mt_lds<BK>(NA * BM + 16 * NF * wn + 16 * fn + fr, fc)]);
+        const bf16x8 wf = *reinterpret_cast<const bf16x8*>(&st[(NA * BM + 16 * NF * wn + 16 * fn) * LDK + fr]);
 #pragma unroll
         for (int fm = 0; fm < MF; ++fm) {
           acc[fn][fm] = mfma16x16x32(wf, af[fm], acc[fn][fm]);
