@@ -851,7 +851,8 @@ __global__ void __launch_bounds__(W * 64) attention_ring_kernel(const AttnArgs a
   static_assert(NS >= 2 && NS - 2 <= 3, "ring depth");
   static_assert((KG - 1) * QTP * (D / 16) * 64 * 16 <= R::BYTES, "key-group records fit a slot");
   extern __shared__ __align__(16) unsigned char lds_raw[];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // wave-uniform (readfirstlane): the wave's role and key ranges live in scalar registers
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int G = a.Hq / a.Hkv;
   const int QR = G * a.Bs;
   const int QT = (QR + 15) / 16;
@@ -1033,27 +1034,32 @@ __global__ void __launch_bounds__(W * 64) attention_ring_kernel(const AttnArgs a
   auto compute_units = [&](const unsigned char* sl, int c, int j1, int ub) {
     int ln = lane;
     asm volatile("" : "+v"(ln));
+    // (c and j1 are wave-uniform: the tests below are scalar branches, and
+    // the per-lane masking work stays inside them)
+    const int cu = __builtin_amdgcn_readfirstlane(c), j1u = __builtin_amdgcn_readfirstlane(j1);
     f32x4 sc[UC][2];
 #pragma unroll
     for (int uu = 0; uu < UC; ++uu) {
       const int u = ub + uu;
-      f32x4 lo[2];
 #pragma unroll
-      for (int h = 0; h < 2; ++h) sc[uu][h] = lo[h] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (c + kUnit * u >= j1) continue;
+      for (int h = 0; h < 2; ++h) sc[uu][h] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (cu + kUnit * u >= j1u) continue;
+      // the query's hi and lo halves accumulate into one sum (the two halves
+      // of a key tile alternate, so consecutive products are independent)
 #pragma unroll
-      for (int s = 0; s < D / 32; ++s)
+      for (int s = 0; s < D / 32; ++s) {
+        bf16x8 kf[2];
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const bf16x8 kf = *reinterpret_cast<const bf16x8*>(sl + ((u * 2 + h) * R::FB + s) * 1024 + 16 * ln);
-          sc[uu][h] = mfma16x16x32(kf, qf[s], sc[uu][h]);
-          lo[h] = mfma16x16x32(kf, qr[s], lo[h]);
-        }
+        for (int h = 0; h < 2; ++h)
+          kf[h] = *reinterpret_cast<const bf16x8*>(sl + ((u * 2 + h) * R::FB + s) * 1024 + 16 * ln);
 #pragma unroll
-      for (int h = 0; h < 2; ++h) sc[uu][h] += lo[h];
+        for (int h = 0; h < 2; ++h) sc[uu][h] = mfma16x16x32(kf[h], qf[s], sc[uu][h]);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) sc[uu][h] = mfma16x16x32(kf[h], qr[s], sc[uu][h]);
+      }
     }
     // lane holds keys c + 32*u + 16*h + 4*(lane>>4) + e for query row (lane & 15)
-    if (c + kUnit * (ub + UC) > j1) {  // keys past the piece: masked
+    if (cu + kUnit * (ub + UC) > j1u) {  // keys past the piece: masked
 #pragma unroll
       for (int uu = 0; uu < UC; ++uu)
 #pragma unroll
@@ -1094,30 +1100,45 @@ __global__ void __launch_bounds__(W * 64) attention_ring_kernel(const AttnArgs a
 #pragma unroll
     for (int uu = 0; uu < UC; ++uu) {
       const int u = ub + uu;
-      if (c + kUnit * u >= j1) continue;
+      if (cu + kUnit * u >= j1u) continue;
       bf16x8 ph, pl;
+      if constexpr (PLO) {
+        uint32_t hb[4], lb[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        ph[e] = (__bf16)sc[uu][0][e];
-        ph[4 + e] = (__bf16)sc[uu][1][e];
-        if constexpr (PLO) {
-          pl[e] = (__bf16)(sc[uu][0][e] - (float)ph[e]);
-          pl[4 + e] = (__bf16)(sc[uu][1][e] - (float)ph[4 + e]);
+        for (int e = 0; e < 2; ++e) {
+          split_bf16x2(sc[uu][0][2 * e], sc[uu][0][2 * e + 1], hb[e], lb[e]);
+          split_bf16x2(sc[uu][1][2 * e], sc[uu][1][2 * e + 1], hb[2 + e], lb[2 + e]);
+        }
+        ph = __builtin_bit_cast(bf16x8, u32x4{hb[0], hb[1], hb[2], hb[3]});
+        pl = __builtin_bit_cast(bf16x8, u32x4{lb[0], lb[1], lb[2], lb[3]});
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          ph[e] = (__bf16)sc[uu][0][e];
+          ph[4 + e] = (__bf16)sc[uu][1][e];
         }
       }
       u32x2 vr[D / 16][2];
       read_v_unit<D>(sl + (R::KBLK + u * 2 * R::FB) * 1024 + 8 * ln, vr);
+      if (cu + kUnit * (u + 1) > j1u) {
+        // the piece ends inside this unit: keys past it hold 0.  Dword d of
+        // key half kh holds keys kb + 16 kh + 2d (low half) and + 1 (high
+        // half) of every dim slice, so one mask per half serves all of them.
+        const int kb = cu + kUnit * u + 4 * (ln >> 4);
+        u32x2 mk[2];
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+          for (int d = 0; d < 2; ++d)
+            mk[kh][d] = (kb + 16 * kh + 2 * d < j1u ? 0x0000ffffu : 0u) | (kb + 16 * kh + 2 * d + 1 < j1u ? 0xffff0000u : 0u);
+#pragma unroll
+        for (int ds = 0; ds < D / 16; ++ds)
+#pragma unroll
+          for (int kh = 0; kh < 2; ++kh) vr[ds][kh] &= mk[kh];
+      }
 #pragma unroll
       for (int ds = 0; ds < D / 16; ++ds) {
-        bf16x8 vf = __builtin_bit_cast(bf16x8, u32x4{vr[ds][0][0], vr[ds][0][1], vr[ds][1][0], vr[ds][1][1]});
-        if (c + kUnit * (u + 1) > j1) {  // the piece ends inside this unit: keys past it hold 0
-          const int kb = c + kUnit * u + 4 * (ln >> 4);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            if (kb + e >= j1) vf[e] = (__bf16)0.f;
-            if (kb + 16 + e >= j1) vf[4 + e] = (__bf16)0.f;
-          }
-        }
+        const bf16x8 vf = __builtin_bit_cast(bf16x8, u32x4{vr[ds][0][0], vr[ds][0][1], vr[ds][1][0], vr[ds][1][1]});
         o[ds] = mfma16x16x32(vf, ph, o[ds]);
         if constexpr (PLO) o[ds] = mfma16x16x32(vf, pl, o[ds]);
       }

@@ -69,6 +69,17 @@ __device__ __forceinline__ bf16x8 f32x8_to_bf16x8(f32x4 a, f32x4 b) {
   return r;
 }
 
+// A pair of fp32 values as a bf16 hi/lo pair (x = hi + lo + O(2^-17 |x|)):
+// one packed conversion for the two hi values, whose fp32 values are the
+// packed word's halves (a shift and a mask), then one for the two remainders.
+__device__ __forceinline__ void split_bf16x2(float x0, float x1, uint32_t& hi, uint32_t& lo) {
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  hi = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{x0, x1}, bf16x2_t));
+  const float r0 = x0 - __uint_as_float(hi << 16), r1 = x1 - __uint_as_float(hi & 0xffff0000u);
+  lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{r0, r1}, bf16x2_t));
+}
+
 // Raw storage bits -> bf16x8 MFMA operand.
 template <typename S>
 __device__ __forceinline__ bf16x8 raw_to_bf16x8(const Raw8& r);
