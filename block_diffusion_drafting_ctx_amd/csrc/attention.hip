@@ -916,23 +916,32 @@ __global__ void __launch_bounds__(W * 64) attention_ring_kernel(const AttnArgs a
   const bf16_t* kc = reinterpret_cast<const bf16_t*>(a.kc);
   const bf16_t* vc = reinterpret_cast<const bf16_t*>(a.vc);
   const size_t row = (size_t)Hkv * D;
+  // A lane's key within a 16-key group and its byte offset within the key
+  // row, for K blocks and for V blocks (fixed over the stages): a block's
+  // source is then a wave-uniform base plus min(key, last) * row bytes + the
+  // column, one 24-bit multiply-add per block.
+  const int kkey = lane & 15, kcol = 2 * 8 * (lane >> 4);
+  const int vkey = (lane & 31) >> 1, vcol = 2 * (16 * (lane >> 5) + 8 * (lane & 1));
+  const unsigned rowb = 2u * (unsigned)row;
   auto issue = [&](const Piece& q, int c, int slot) {
     const int lim = min(a.max_ctx, q.pend) - 1 - c;
     const size_t base = ((size_t)q.b * a.max_ctx + c) * row + q.h * D;
+    const char* kbase = reinterpret_cast<const char*>(kc + base);
+    const char* vbase = reinterpret_cast<const char*>(vc + base);
     unsigned char* sl = ring + slot * R::BYTES;
 #pragma unroll
     for (int i = 0; i < R::PER_WAVE; ++i) {
       const int blk = wave + W * i;
-      const bf16_t* src;
+      const char* src;
       if (blk < R::KBLK) {  // K block (unit, half, s): lane -> key 16h + (lane & 15), dims 32s + 8(lane >> 4)
         const int u = blk / (2 * R::FB), h = (blk / R::FB) & 1, s = blk % R::FB;
-        const int key = kUnit * u + 16 * h + (lane & 15);
-        src = kc + base + (size_t)(min(key, lim) * (int)row + 32 * s + 8 * (lane >> 4));
+        const int key = min(kUnit * u + 16 * h + kkey, lim);
+        src = kbase + (__umul24((unsigned)key, rowb) + (unsigned)(64 * s + kcol));
       } else {  // V block (unit, kh, dp): lane -> tile lane >> 5, key 16kh + (lane & 31) / 2, 8 dims
         const int vb = blk - R::KBLK;
         const int u = vb / (2 * R::FB), kh = (vb / R::FB) & 1, dp = vb % R::FB;
-        const int key = kUnit * u + 16 * kh + ((lane & 31) >> 1);
-        src = vc + base + (size_t)(min(key, lim) * (int)row + 32 * dp + 16 * (lane >> 5) + 8 * (lane & 1));
+        const int key = min(kUnit * u + 16 * kh + vkey, lim);
+        src = vbase + (__umul24((unsigned)key, rowb) + (unsigned)(64 * dp + vcol));
       }
       __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(sl + blk * 1024), 16, 0, 0);
     }
