@@ -31,6 +31,7 @@ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 constexpr int kMaxNd = 64;
 constexpr int kVerifyChunk = 8192;  // vocab entries per workgroup of the verify argmax (8 loads per thread)
 constexpr int kMlpHiOnlyRows = 256;  // draft rows from which the MLP products take plain bf16 inputs
+constexpr bool kUseDmaGemm = true;
 constexpr int kMtTargetWgs = kCUs;   // gemm_mt workgroups to aim for (one per compute unit)
 // Attention workgroups: the batch's key axis is cut into this many ranges,
 // one 8-wave workgroup per compute unit (the attention kernel's registers and
@@ -171,13 +172,15 @@ bool plan_gemm(int storage, int src, int out, bool lo, int M, int N, int K, Gemm
     }
   }
   const int units = nbn * KS;
-  l->kind = GEMM_MT;
+  // 256-row blocks with bf16 operands stream their stages through LDS-DMA
+  const bool dma = kUseDmaGemm && MF >= 4 && storage == ST_BF16;
+  l->kind = dma ? GEMM_DMA : GEMM_MT;
   l->MR = MF;
   l->NF = NF;
   l->KS = KS;
   l->grid = dim3(((units + 7) / 8) * 8 * nbm);
   l->threads = 512;
-  l->lds = gemm_mt_lds_bytes(MF, NF, lo_eff);
+  l->lds = dma ? gemm_dma_lds_bytes(NF, lo_eff) : gemm_mt_lds_bytes(MF, NF, lo_eff);
   l->argmax_tiles = nbn;
   a->nbm = nbm;
   a->nbn = nbn;

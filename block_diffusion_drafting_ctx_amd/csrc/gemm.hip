@@ -20,6 +20,8 @@
 //    activations per wave from L2 halves the rate.
 //  * gemm_mt (M > 32, or no gemm_as fit): LDS-tiled 64*MF x 128 blocks,
 //    double-buffered 32-deep k stages, optional split-K.
+//  * gemm_dma (256-row blocks, bf16 operands): the gemm_mt block with its
+//    stages brought into LDS by LDS-DMA loads in MFMA fragment order.
 // Activations are a pair of bf16 arrays (hi, lo) with a = hi + lo (two MFMAs
 // per fragment); the stages whose outputs do not feed the residual stream
 // (context K/V, LM head) use hi only.  RMSNorm is a row scale applied by the
@@ -478,6 +480,197 @@ __global__ void __launch_bounds__(512) gemm_mt_kernel(const GemmArgs g) {
     if (g.rinv_out != nullptr && ks == 0) write_rinv(g, nb * g.nbm + mb, g.nbn * g.nbm);
   } else {
     uint64_t* sb = reinterpret_cast<uint64_t*>(sm);  // [2][BM]; the ring is idle after the last barrier
+#pragma unroll
+    for (int fm = 0; fm < MF; ++fm) {
+      uint64_t best = 0;
+#pragma unroll
+      for (int fn = 0; fn < NF; ++fn) {
+        const int n = n0 + 16 * NF * wn + 16 * fn;
+        if (n < g.N) {
+          const uint64_t t = tile_row_best(acc[fn][fm], n, lane);
+          best = t > best ? t : best;
+        }
+      }
+      if ((lane >> 4) == 0) sb[wn * BM + 16 * MF * wm + 16 * fm + (lane & 15)] = best;
+    }
+    if (g.logits_dbg != nullptr) {
+#pragma unroll
+      for (int fn = 0; fn < NF; ++fn) {
+        const int n = n0 + 16 * NF * wn + 16 * fn;
+        if (n >= g.N) continue;
+#pragma unroll
+        for (int fm = 0; fm < MF; ++fm) {
+          const int m = m0 + 16 * MF * wm + 16 * fm + (lane & 15);
+          if (m >= g.M) continue;
+          const float r = row_rinv(g.ssq_in, g.ssq_nparts, g.ld_ssq, m, g.K, g.eps);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) g.logits_dbg[(size_t)m * g.N + n + 4 * (lane >> 4) + i] = acc[fn][fm][i] * r;
+        }
+      }
+    }
+    __syncthreads();
+    for (int rr = tid; rr < BM; rr += 512) {
+      const uint64_t a = sb[rr], b = sb[BM + rr];
+      if (m0 + rr < g.M) g.best_part[(size_t)nb * g.ld_best + m0 + rr] = a > b ? a : b;
+    }
+  }
+}
+
+// ------------------------------------------------------------------ gemm_dma
+// The 256-row tiled product (bf16 operands) with its stages brought into LDS
+// by LDS-DMA loads in MFMA fragment order.  A stage is one 32-deep k-step:
+// the block's 2*NF weight tiles (the 1 KB k-step blocks of the tiled copy,
+// copied as they are) and 16 activation row groups per array (hi, lo), each
+// gathered into a 1 KB block whose lane l holds row 16g + (l & 15), columns
+// 8(l >> 4) .. + 7 of the k-step.  A fragment is then one ds_read_b128 at
+// 16*lane of its block (contiguous across the wave: no bank conflicts, no
+// padding), no stage passes through registers, and NS stages are in flight
+// (NS - 1 ahead of the one being computed).  Each wave issues the same
+// number of block loads for every stage (spare loads repeat the stage's last
+// block into its own place), so the wait for a stage is vmcnt((NS-2) * PW).
+template <int NF, bool LO>
+struct DmaShape {
+  static constexpr int BM = 256, NT = 2 * NF, NA = LO ? 2 : 1;
+  static constexpr int NB = NT + 16 * NA;          // 1 KB blocks per stage
+  static constexpr int PW = (NB + 7) / 8;          // block loads per wave and stage
+  static constexpr int SLOT = NB * 1024;
+  static constexpr int NS = (160 * 1024 - 4096) / SLOT >= 4 ? 4 : 3;  // stages in the LDS ring
+};
+
+size_t gemm_dma_lds_bytes(int NF, bool lo) {
+  const int nb = 2 * NF + 16 * (lo ? 2 : 1);
+  const int ns = (160 * 1024 - 4096) / (nb * 1024) >= 4 ? 4 : 3;
+  return (size_t)ns * nb * 1024;
+}
+
+template <int NF, int SRC, bool LO, int OUT>
+__global__ void __launch_bounds__(512) gemm_dma_kernel(const GemmArgs g) {
+  using Sh = DmaShape<NF, LO>;
+  constexpr int BM = Sh::BM, NT = Sh::NT, NB = Sh::NB, PW = Sh::PW, SLOT = Sh::SLOT, NS = Sh::NS;
+  constexpr int MF = 4;
+  static_assert((NS - 2) * PW < 64, "vmcnt range");
+  extern __shared__ __align__(16) unsigned char lds[];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave & 3, wn = wave >> 2;
+
+  // ---- block -> (n block, m block, k slice), as in gemm_mt
+  const int L = blockIdx.x, xcd = L & 7, slot0 = L >> 3;
+  const int mb = slot0 % g.nbm;
+  const int unit = (slot0 / g.nbm) * 8 + xcd;
+  if (unit >= g.nbn * g.KS) return;  // grid padding
+  const int nb = unit % g.nbn, ks = unit / g.nbn;
+  const int n0 = nb * (32 * NF), m0 = mb * BM;
+  const int kbeg = ks * g.kslice, nk = g.kslice / 32;
+  const int nks = g.K >> 5, ntl = g.N >> 4;
+
+  // ---- this wave's block loads of a stage: block b = wave + 8 i (the last
+  // block when past the stage).  Weight tile blocks are contiguous 1 KB; an
+  // activation block gathers 16 rows (rows past M repeat row M - 1).
+  const char* src0[PW];
+  int step[PW];  // bytes per k-step of the block's source
+  int dst[PW];
+#pragma unroll
+  for (int i = 0; i < PW; ++i) {
+    const int b = min(wave + 8 * i, NB - 1);
+    dst[i] = b * 1024;
+    if (b < NT) {
+      const int t = min(n0 / 16 + b, ntl - 1);
+      src0[i] = reinterpret_cast<const char*>(g.wt) + ((size_t)(t * nks + kbeg / 32) * 64 + lane) * 16;
+      step[i] = 1024;
+    } else {
+      const int a = b - NT, arr = a >> 4, grp = a & 15;
+      const int m = min(m0 + 16 * grp + (lane & 15), g.M - 1);
+      const int k = kbeg + 8 * (lane >> 4);
+      if constexpr (SRC == SRC_SPLIT) {
+        const void* base = arr ? g.a_lo : g.a_hi;
+        src0[i] = reinterpret_cast<const char*>(base) + ((size_t)m * g.lda + k) * 2;
+      } else {
+        src0[i] = nullptr;  // per stage: the source array holding the k-step
+      }
+      step[i] = 64;
+    }
+  }
+  auto issue = [&](int kt, int s) {
+    unsigned char* sl = lds + s * SLOT;
+#pragma unroll
+    for (int i = 0; i < PW; ++i) {
+      const char* src;
+      if constexpr (SRC == SRC_SPLIT) {
+        src = src0[i] + (size_t)kt * step[i];
+      } else {
+        const int b = min(wave + 8 * i, NB - 1);
+        if (b < NT) {
+          src = src0[i] + (size_t)kt * step[i];
+        } else {
+          const int grp = (b - NT) & 15;
+          const int m = min(m0 + 16 * grp + (lane & 15), g.M - 1);
+          const int k = kbeg + 32 * kt;  // one k-step lies in one source (src_width % 32 == 0)
+          const int j = k / g.src_width;
+          src = reinterpret_cast<const char*>(g.src[j]) +
+                ((size_t)m * g.src_width + (k - j * g.src_width) + 8 * (lane >> 4)) * 2;
+        }
+      }
+      __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(sl + dst[i]), 16, 0, 0);
+    }
+    asm volatile("" ::: "memory");
+  };
+
+  f32x4 acc[NF][MF];
+#pragma unroll
+  for (int fn = 0; fn < NF; ++fn)
+#pragma unroll
+    for (int fm = 0; fm < MF; ++fm) acc[fn][fm] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](int s) {
+    const unsigned char* sl = lds + s * SLOT + 16 * lane;
+    bf16x8 af[MF], al[MF];
+#pragma unroll
+    for (int fm = 0; fm < MF; ++fm) {
+      af[fm] = *reinterpret_cast<const bf16x8*>(sl + (NT + 4 * wm + fm) * 1024);
+      if constexpr (LO) al[fm] = *reinterpret_cast<const bf16x8*>(sl + (NT + 16 + 4 * wm + fm) * 1024);
+    }
+#pragma unroll
+    for (int fn = 0; fn < NF; ++fn) {
+      const bf16x8 wf = *reinterpret_cast<const bf16x8*>(sl + (NF * wn + fn) * 1024);
+#pragma unroll
+      for (int fm = 0; fm < MF; ++fm) {
+        acc[fn][fm] = mfma16x16x32(wf, af[fm], acc[fn][fm]);
+        if constexpr (LO) acc[fn][fm] = mfma16x16x32(wf, al[fm], acc[fn][fm]);
+      }
+    }
+  };
+
+  // ---- pipeline: NS - 1 stages requested ahead (past the end: the last
+  // stage again, into its own slot; never computed)
+#pragma unroll
+  for (int j = 0; j < NS - 1; ++j) issue(min(j, nk - 1), j);
+  for (int kt = 0; kt < nk; ++kt) {
+    wait_vm<(NS - 2) * PW>();  // this wave's loads of stage kt are in LDS
+    raw_barrier();             // ... every wave's, and every wave is done with stage kt - 1
+    issue(min(kt + NS - 1, nk - 1), (kt + NS - 1) % NS);
+    compute(kt % NS);
+  }
+  wait_vm<0>();  // no load may still write this workgroup's LDS
+  raw_barrier();
+
+  // ---- epilogue.  lane holds Y[m = (lane & 15) + row base][n = 4*(lane >> 4) + i + column base]
+  if constexpr (OUT == OUT_PARTIAL) {
+    const int ntiles = g.N >> 4;
+#pragma unroll
+    for (int fn = 0; fn < NF; ++fn) {
+      const int n = n0 + 16 * NF * wn + 16 * fn;
+      if (n >= g.N) continue;
+#pragma unroll
+      for (int fm = 0; fm < MF; ++fm) {
+        const int m = m0 + 16 * MF * wm + 16 * fm + (lane & 15);
+        if (m < g.M)
+          *reinterpret_cast<f32x4*>(g.part + (((size_t)ks * ntiles + (n >> 4)) * g.M + m) * 16 + 4 * (lane >> 4)) =
+              acc[fn][fm];
+      }
+    }
+    if (g.rinv_out != nullptr && ks == 0) write_rinv(g, nb * g.nbm + mb, g.nbn * g.nbm);
+  } else {
+    uint64_t* sb = reinterpret_cast<uint64_t*>(lds);  // [2][BM]; the ring is idle after the last barrier
 #pragma unroll
     for (int fm = 0; fm < MF; ++fm) {
       uint64_t best = 0;
@@ -1066,8 +1259,24 @@ static hipError_t launch_mt(const GemmArgs& a, const GemmLaunch& l, hipStream_t 
   return hipGetLastError();
 }
 
+template <int NF, int SRC, bool LO, int OUT>
+static hipError_t launch_dma(const GemmArgs& a, const GemmLaunch& l, hipStream_t st) {
+  auto k = gemm_dma_kernel<NF, SRC, LO, OUT>;
+  allow_lds(k, l.lds);
+  hipLaunchKernelGGL(k, l.grid, dim3(l.threads), l.lds, st, a);
+  return hipGetLastError();
+}
+
 template <typename S, int SRC, bool LO, int OUT>
 static hipError_t dispatch_mr(const GemmArgs& a, const GemmLaunch& l, hipStream_t st) {
+  if (l.kind == GEMM_DMA) {
+    if constexpr (sizeof(S) == 2) {
+      if (l.NF == 8) return launch_dma<8, SRC, LO, OUT>(a, l, st);
+      if constexpr (OUT == OUT_PARTIAL)
+        if (l.NF == 6) return launch_dma<6, SRC, LO, OUT>(a, l, st);
+    }
+    return hipErrorInvalidValue;
+  }
   if (l.kind == GEMM_AS) {
     if (l.MR == 1) return launch_as<S, 1, SRC, LO, OUT>(a, l, st);
     if (l.MR == 2) return launch_as<S, 2, SRC, LO, OUT>(a, l, st);

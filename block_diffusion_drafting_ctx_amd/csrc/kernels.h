@@ -26,7 +26,7 @@ enum SrcKind {
   SRC_CONCAT = 1   // A: concat of n_src arrays [M, src_width] of the storage type
 };
 enum OutKind { OUT_PARTIAL = 0, OUT_ARGMAX = 1 };
-enum GemmKind { GEMM_AS = 0, GEMM_MT = 1 };
+enum GemmKind { GEMM_AS = 0, GEMM_MT = 1, GEMM_DMA = 2 };
 
 constexpr int kMaxSeg = 16;  // context K/V caches one product writes (2 per layer)
 constexpr size_t kGemmAsSliceLds = 100 * 1024;  // split-K activation slice of a gemm_as workgroup
@@ -89,6 +89,9 @@ size_t gemm_as_lds(int M, int ksl, bool lo);
 // MF < 4; 8, or 6 for split-K outputs, at MF = 4); LDS bytes of its stage
 // ring (lo: hi/lo activation pair).
 size_t gemm_mt_lds_bytes(int MF, int NF, bool lo);
+// gemm_dma (256-row blocks, bf16 operands, stages through LDS-DMA): LDS bytes
+// of its stage ring for NF = 6 or 8.
+size_t gemm_dma_lds_bytes(int NF, bool lo);
 // ids[m] = index of the largest key over part[t][m], t < ntiles.
 hipError_t launch_argmax_reduce(const uint64_t* part, int ntiles, int ld, int M, int32_t* ids, hipStream_t stream);
 
