@@ -528,26 +528,31 @@ __global__ void __launch_bounds__(512) gemm_mt_kernel(const GemmArgs g) {
 // (NS - 1 ahead of the one being computed).  Each wave issues the same
 // number of block loads for every stage (spare loads repeat the stage's last
 // block into its own place), so the wait for a stage is vmcnt((NS-2) * PW).
-template <int NF, bool LO>
+// MF row fragments per wave (4 waves along M): 256-row blocks at MF = 4,
+// 512-row blocks at MF = 8 with NF = 6 (a 128 x 96 wave tile: a fifth fewer
+// fragment reads per matrix-core op than 64 x 128; its 192 accumulators are
+// what two waves per SIMD leave room for -- 128 x 128 spilled).
+template <int MF, int NF, bool LO>
 struct DmaShape {
-  static constexpr int BM = 256, NT = 2 * NF, NA = LO ? 2 : 1;
-  static constexpr int NB = NT + 16 * NA;          // 1 KB blocks per stage
+  static constexpr int BM = 64 * MF, NT = 2 * NF, NA = LO ? 2 : 1;
+  static constexpr int NB = NT + (BM / 16) * NA;   // 1 KB blocks per stage
   static constexpr int PW = (NB + 7) / 8;          // block loads per wave and stage
   static constexpr int SLOT = NB * 1024;
   static constexpr int NS = (160 * 1024 - 4096) / SLOT >= 4 ? 4 : 3;  // stages in the LDS ring
+  static_assert(3 * SLOT <= 160 * 1024, "three stages fit the LDS");
 };
 
-size_t gemm_dma_lds_bytes(int NF, bool lo) {
-  const int nb = 2 * NF + 16 * (lo ? 2 : 1);
+size_t gemm_dma_lds_bytes(int MF, int NF, bool lo) {
+  const int nb = 2 * NF + 4 * MF * (lo ? 2 : 1);
   const int ns = (160 * 1024 - 4096) / (nb * 1024) >= 4 ? 4 : 3;
   return (size_t)ns * nb * 1024;
 }
 
-template <int NF, int SRC, bool LO, int OUT>
+template <int MF, int NF, int SRC, bool LO, int OUT>
 __global__ void __launch_bounds__(512) gemm_dma_kernel(const GemmArgs g) {
-  using Sh = DmaShape<NF, LO>;
+  using Sh = DmaShape<MF, NF, LO>;
   constexpr int BM = Sh::BM, NT = Sh::NT, NB = Sh::NB, PW = Sh::PW, SLOT = Sh::SLOT, NS = Sh::NS;
-  constexpr int MF = 4;
+  constexpr int AG = BM / 16;  // activation row groups per array
   static_assert((NS - 2) * PW < 64, "vmcnt range");
   extern __shared__ __align__(16) unsigned char lds[];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -579,7 +584,7 @@ __global__ void __launch_bounds__(512) gemm_dma_kernel(const GemmArgs g) {
       src0[i] = reinterpret_cast<const char*>(g.wt) + ((size_t)(t * nks + kbeg / 32) * 64 + lane) * 16;
       step[i] = 1024;
     } else {
-      const int a = b - NT, arr = a >> 4, grp = a & 15;
+      const int a = b - NT, arr = a / AG, grp = a % AG;
       const int m = min(m0 + 16 * grp + (lane & 15), g.M - 1);
       const int k = kbeg + 8 * (lane >> 4);
       if constexpr (SRC == SRC_SPLIT) {
@@ -603,7 +608,7 @@ __global__ void __launch_bounds__(512) gemm_dma_kernel(const GemmArgs g) {
         if (b < NT) {
           src = src0[i] + (size_t)kt * step[i];
         } else {
-          const int grp = (b - NT) & 15;
+          const int grp = (b - NT) % AG;
           const int m = min(m0 + 16 * grp + (lane & 15), g.M - 1);
           const int k = kbeg + 32 * kt;  // one k-step lies in one source (src_width % 32 == 0)
           const int j = k / g.src_width;
@@ -626,18 +631,24 @@ __global__ void __launch_bounds__(512) gemm_dma_kernel(const GemmArgs g) {
     bf16x8 af[MF], al[MF];
 #pragma unroll
     for (int fm = 0; fm < MF; ++fm) {
-      af[fm] = *reinterpret_cast<const bf16x8*>(sl + (NT + 4 * wm + fm) * 1024);
-      if constexpr (LO) al[fm] = *reinterpret_cast<const bf16x8*>(sl + (NT + 16 + 4 * wm + fm) * 1024);
+      af[fm] = *reinterpret_cast<const bf16x8*>(sl + (NT + MF * wm + fm) * 1024);
+      if constexpr (LO) al[fm] = *reinterpret_cast<const bf16x8*>(sl + (NT + AG + MF * wm + fm) * 1024);
     }
+    // every fragment read of the stage goes out before the matrix work
+    // (measured: 2-8% faster products than reads interleaved with it)
+    bf16x8 wfa[NF];
+#pragma unroll
+    for (int fn = 0; fn < NF; ++fn) wfa[fn] = *reinterpret_cast<const bf16x8*>(sl + (NF * wn + fn) * 1024);
+    __builtin_amdgcn_sched_group_barrier(0x100, MF * (LO ? 2 : 1) + NF, 0);  // the DS reads
 #pragma unroll
     for (int fn = 0; fn < NF; ++fn) {
-      const bf16x8 wf = *reinterpret_cast<const bf16x8*>(sl + (NF * wn + fn) * 1024);
 #pragma unroll
       for (int fm = 0; fm < MF; ++fm) {
-        acc[fn][fm] = mfma16x16x32(wf, af[fm], acc[fn][fm]);
-        if constexpr (LO) acc[fn][fm] = mfma16x16x32(wf, al[fm], acc[fn][fm]);
+        acc[fn][fm] = mfma16x16x32(wfa[fn], af[fm], acc[fn][fm]);
+        if constexpr (LO) acc[fn][fm] = mfma16x16x32(wfa[fn], al[fm], acc[fn][fm]);
       }
     }
+    __builtin_amdgcn_sched_group_barrier(0x008, MF * NF * (LO ? 2 : 1), 0);  // then the MFMAs
   };
 
   // ---- pipeline: NS - 1 stages requested ahead (past the end: the last
@@ -1259,9 +1270,9 @@ static hipError_t launch_mt(const GemmArgs& a, const GemmLaunch& l, hipStream_t 
   return hipGetLastError();
 }
 
-template <int NF, int SRC, bool LO, int OUT>
+template <int MF, int NF, int SRC, bool LO, int OUT>
 static hipError_t launch_dma(const GemmArgs& a, const GemmLaunch& l, hipStream_t st) {
-  auto k = gemm_dma_kernel<NF, SRC, LO, OUT>;
+  auto k = gemm_dma_kernel<MF, NF, SRC, LO, OUT>;
   allow_lds(k, l.lds);
   hipLaunchKernelGGL(k, l.grid, dim3(l.threads), l.lds, st, a);
   return hipGetLastError();
@@ -1271,9 +1282,14 @@ template <typename S, int SRC, bool LO, int OUT>
 static hipError_t dispatch_mr(const GemmArgs& a, const GemmLaunch& l, hipStream_t st) {
   if (l.kind == GEMM_DMA) {
     if constexpr (sizeof(S) == 2) {
-      if (l.NF == 8) return launch_dma<8, SRC, LO, OUT>(a, l, st);
+      if (l.MR == 8) {  // 512-row blocks: hi-only operands, 96-column wave tiles
+        if constexpr (!LO)
+          if (l.NF == 6) return launch_dma<8, 6, SRC, LO, OUT>(a, l, st);
+        return hipErrorInvalidValue;
+      }
+      if (l.NF == 8) return launch_dma<4, 8, SRC, LO, OUT>(a, l, st);
       if constexpr (OUT == OUT_PARTIAL)
-        if (l.NF == 6) return launch_dma<6, SRC, LO, OUT>(a, l, st);
+        if (l.NF == 6) return launch_dma<4, 6, SRC, LO, OUT>(a, l, st);
     }
     return hipErrorInvalidValue;
   }
