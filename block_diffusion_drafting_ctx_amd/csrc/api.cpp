@@ -32,8 +32,6 @@ constexpr int kMaxNd = 64;
 constexpr int kVerifyChunk = 8192;  // vocab entries per workgroup of the verify argmax (8 loads per thread)
 constexpr int kMlpHiOnlyRows = 256;  // draft rows from which the MLP products take plain bf16 inputs
 constexpr bool kUseDmaGemm = true;
-constexpr bool kDma512 = false;
-constexpr double kDma512Rate = 1.4;
 constexpr int kMtTargetWgs = kCUs;   // gemm_mt workgroups to aim for (one per compute unit)
 // Attention workgroups: the batch's key axis is cut into this many ranges,
 // one 8-wave workgroup per compute unit (the attention kernel's registers and
@@ -119,8 +117,8 @@ bool plan_gemm(int storage, int src, int out, bool lo, int M, int N, int K, Gemm
   // as far as the grid stays within one dispatch round (one 8-wave workgroup
   // per compute unit): a second, partly filled round would cost a whole
   // workgroup's time, and every k-slice adds a partial-output round trip
-  int MF = M <= 64 ? 1 : (M <= 128 ? 2 : 4);
-  int nbm = (M + 64 * MF - 1) / (64 * MF);
+  const int MF = M <= 64 ? 1 : (M <= 128 ? 2 : 4);
+  const int nbm = (M + 64 * MF - 1) / (64 * MF);
   // (every k-slice keeps an even number of 32-deep stages: the kernel's
   // pipeline takes them in pairs)
   auto split = [&](int nbn) {
@@ -175,34 +173,6 @@ bool plan_gemm(int storage, int src, int out, bool lo, int M, int N, int K, Gemm
   }
   // 256-row blocks with bf16 operands stream their stages through LDS-DMA
   const bool dma = kUseDmaGemm && MF >= 4 && storage == ST_BF16;
-  if (dma && !lo_eff && kDma512 && 8 * (((M + 511) / 512) * 512 - M) <= M) {
-    // 512-row blocks (128 x 96 wave tiles, a fifth fewer fragment reads per
-    // matrix-core op) when the rows fill them: modelled time = dispatch
-    // rounds x the block's matrix work at the kernel's rate (kDma512Rate
-    // times the 256-row rate) + the split-K partials written and read
-    auto cost = [&](int mf, int nf, int ks, int wgs) {
-      const double rounds = std::ceil((double)wgs / kCUs);
-      const double work = 64.0 * mf * 32.0 * nf * (double)(K / ks) * 2.0 / 3.7e6 / (mf == 8 ? kDma512Rate : 1.0);
-      return rounds * work + (out == OUT_PARTIAL ? (double)ks * M * N * 8.0 / 5e6 : 0.0);
-    };
-    double best = cost(MF, NF, KS, nbn * nbm * KS);
-    const int nbm8 = (M + 511) / 512;
-    for (int nf : {6}) {
-      const int bn = (N + 32 * nf - 1) / (32 * nf);
-      int ks = 1;
-      if (out == OUT_PARTIAL)
-        while (bn * nbm8 * 2 * ks <= kMtTargetWgs && (K / 32) % (4 * ks) == 0 && K / (2 * ks) >= 256) ks *= 2;
-      const double c = cost(8, nf, ks, bn * nbm8 * ks);
-      if (c < best) {
-        best = c;
-        MF = 8;
-        nbm = nbm8;
-        NF = nf;
-        nbn = bn;
-        KS = ks;
-      }
-    }
-  }
   const int units = nbn * KS;
   l->kind = dma ? GEMM_DMA : GEMM_MT;
   l->MR = MF;

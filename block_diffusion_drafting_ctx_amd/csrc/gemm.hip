@@ -528,10 +528,7 @@ __global__ void __launch_bounds__(512) gemm_mt_kernel(const GemmArgs g) {
 // (NS - 1 ahead of the one being computed).  Each wave issues the same
 // number of block loads for every stage (spare loads repeat the stage's last
 // block into its own place), so the wait for a stage is vmcnt((NS-2) * PW).
-// MF row fragments per wave (4 waves along M): 256-row blocks at MF = 4,
-// 512-row blocks at MF = 8 with NF = 6 (a 128 x 96 wave tile: a fifth fewer
-// fragment reads per matrix-core op than 64 x 128; its 192 accumulators are
-// what two waves per SIMD leave room for -- 128 x 128 spilled).
+// MF row fragments per wave (4 waves along M): 256-row blocks at MF = 4.
 template <int MF, int NF, bool LO>
 struct DmaShape {
   static constexpr int BM = 64 * MF, NT = 2 * NF, NA = LO ? 2 : 1;
@@ -1282,11 +1279,6 @@ template <typename S, int SRC, bool LO, int OUT>
 static hipError_t dispatch_mr(const GemmArgs& a, const GemmLaunch& l, hipStream_t st) {
   if (l.kind == GEMM_DMA) {
     if constexpr (sizeof(S) == 2) {
-      if (l.MR == 8) {  // 512-row blocks: hi-only operands, 96-column wave tiles
-        if constexpr (!LO)
-          if (l.NF == 6) return launch_dma<8, 6, SRC, LO, OUT>(a, l, st);
-        return hipErrorInvalidValue;
-      }
       if (l.NF == 8) return launch_dma<4, 8, SRC, LO, OUT>(a, l, st);
       if constexpr (OUT == OUT_PARTIAL)
         if (l.NF == 6) return launch_dma<4, 6, SRC, LO, OUT>(a, l, st);
