@@ -30,7 +30,7 @@ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 constexpr int kMaxNd = 64;
 constexpr int kVerifyChunk = 8192;  // vocab entries per workgroup of the verify argmax (8 loads per thread)
-constexpr int kMlpHiOnlyRows = 256;  // draft rows from which the MLP products take plain bf16 inputs
+constexpr int kMlpHiOnlyRows = 128;  // draft rows from which the MLP products take plain bf16 inputs
 constexpr bool kUseDmaGemm = true;
 constexpr int kMtTargetWgs = kCUs;   // gemm_mt workgroups to aim for (one per compute unit)
 // Attention workgroups: the batch's key axis is cut into this many ranges,
