@@ -1437,9 +1437,16 @@ static hipError_t launch_ring(const AttnArgs& a, hipStream_t stream) {
 template <int D>
 static hipError_t launch_attention_ring(const AttnArgs& a, int qtp, hipStream_t stream) {
   constexpr int NSQ = D == 128 ? 2 : 4;  // slots of the four-unit ring
-  if (qtp <= 4)
+  if (qtp <= 4) {
+    // D = 128: stages of two units in four slots (three in flight) -- against
+    // four-unit stages in two slots, 32k-context batch 4 128 -> 120 us per
+    // layer, equal at batch 1 and 32
+    if constexpr (D == 128)
+      return qtp == 1 ? launch_ring<D, 8, 1, 2, 4, true>(a, stream)
+                      : qtp == 2 ? launch_ring<D, 8, 2, 2, 4, true>(a, stream) : launch_ring<D, 8, 4, 2, 4, true>(a, stream);
     return qtp == 1 ? launch_ring<D, 8, 1, 4, NSQ, true>(a, stream)
                     : qtp == 2 ? launch_ring<D, 8, 2, 4, NSQ, true>(a, stream) : launch_ring<D, 8, 4, 4, NSQ, true>(a, stream);
+  }
   const int QT = ((a.Hq / a.Hkv) * a.Bs + 15) / 16;
   if (ring_lds_bytes<D, 2, 8>(4, false, QT, qtp, a.batch) <= kLdsBytes) return launch_ring<D, 8, 8, 2, 4, false>(a, stream);
   if (ring_lds_bytes<D, 2, 8>(3, false, QT, qtp, a.batch) <= kLdsBytes) return launch_ring<D, 8, 8, 2, 3, false>(a, stream);
