@@ -1073,8 +1073,25 @@ __global__ void __launch_bounds__(256) finish_qkv_kernel(const FinishArgs f) {
   const int quads = f.N >> 3;  // 4-pair groups per row
   const int e = blockIdx.x * blockDim.x + threadIdx.x, e4 = e / SPL, j = e % SPL;
   if (e4 >= f.M * quads) return;  // whole lane groups leave together
-  const int m = e4 / quads, rem = e4 - m * quads;
-  const int hd = rem / (half >> 2), d = (rem - hd * (half >> 2)) * 4;
+  int m, hd, d;
+  if (KV8 || f.M < 256) {
+    // (row, head, pair): the lanes of one run of 32 values of a head row are
+    // consecutive (the 8-bit cache's run maximum is a shuffle reduction), and
+    // a row's stores are contiguous
+    m = e4 / quads;
+    const int rem = e4 - m * quads;
+    hd = rem / (half >> 2);
+    d = (rem - hd * (half >> 2)) * 4;
+  } else {
+    // from 256 rows on, where the partials dominate the traffic: (head,
+    // 16-pair group, row, quad), so 4 lanes read a row's 64 contiguous bytes
+    // of a partial tile and the lanes of 16 rows its whole 1 KB (batch 32:
+    // 89 -> 83 us per Q/K/V stage)
+    const int q = e4 & 3, r2 = e4 >> 2, pidx = r2 / f.M;
+    m = r2 - pidx * f.M;
+    hd = pidx / (half >> 4);
+    d = (pidx - hd * (half >> 4)) * 16 + 4 * q;
+  }
   const int n = hd * D + d, nj = n + j * E;  // nj: this lane's first pair
   const int Nq = f.n_q_heads * D, Nk = f.n_kv_heads * D;
   const int b = m / f.block, i = m - b * f.block;
@@ -1115,7 +1132,7 @@ __global__ void __launch_bounds__(256) finish_qkv_kernel(const FinishArgs f) {
     return;
   }
   if (T + f.block > f.max_ctx) {
-    if (rem == Nq / 8 && i == 0 && j == 0) atomicOr(f.err, kErrDraftOverflow);
+    if (n == Nq && i == 0 && j == 0) atomicOr(f.err, kErrDraftOverflow);
     return;
   }
   const bool is_k = n < Nq + Nk;
@@ -1146,8 +1163,18 @@ __global__ void __launch_bounds__(256) finish_kv_kernel(const FinishArgs f) {
   const int quads = f.N >> 3;
   const int e = blockIdx.x * blockDim.x + threadIdx.x, e4 = e / SPL, j = e % SPL;
   if (e4 >= f.M * quads) return;  // whole lane groups leave together
-  const int m = e4 / quads, rem = e4 - m * quads;
-  const int hd = rem / (half >> 2), d = (rem - hd * (half >> 2)) * 4;
+  int m, hd, d;
+  if (KV8 || f.M < 256) {  // lane order as in finish_qkv
+    m = e4 / quads;
+    const int rem = e4 - m * quads;
+    hd = rem / (half >> 2);
+    d = (rem - hd * (half >> 2)) * 4;
+  } else {
+    const int q = e4 & 3, r2 = e4 >> 2, pidx = r2 / f.M;
+    m = r2 - pidx * f.M;
+    hd = pidx / (half >> 4);
+    d = (pidx - hd * (half >> 4)) * 16 + 4 * q;
+  }
   const int seg = hd / Hkv, head = hd - seg * Hkv;
   const int b = m / f.block, i = m - b * f.block;
   const int n = hd * D + d;
@@ -1167,7 +1194,7 @@ __global__ void __launch_bounds__(256) finish_kv_kernel(const FinishArgs f) {
   group_sum<SPL>(v[0]);
   group_sum<SPL>(v[1]);
   if (bad) {
-    if (rem == 0 && i == 0 && j == 0) atomicOr(f.err, kErrFuseOverflow);
+    if (n == 0 && i == 0 && j == 0) atomicOr(f.err, kErrFuseOverflow);
     return;
   }
   float lo[E], hi[E];
