@@ -189,6 +189,11 @@ bool plan_gemm(int storage, int src, int out, bool lo, int M, int N, int K, Gemm
   return true;
 }
 
+// Whether the draft block's activations of M rows feed LDS-DMA products, and
+// so are stored in fragment blocks by the finish that writes them (the test
+// plan_gemm makes for GEMM_DMA: bf16 storage and 256-row blocks, M > 128).
+bool act_blocked(int storage, int M) { return kUseDmaGemm && storage == ST_BF16 && M > 128; }
+
 // Floats of partial tiles the planner needs for a product of this shape.
 size_t partial_floats(int storage, int src, bool lo, int Mmax, int N, int K) {
   size_t best = 0;
@@ -243,8 +248,9 @@ WsLayout layout(const dflash_config& c) {
   L.ssq = take((size_t)L.ssq_parts * L.mmax * 4);
   L.rinv = take((size_t)L.mmax * 4);
   L.y = take((size_t)L.mf * H * 4);
-  L.xs_hi = take((size_t)L.mmax * H * 2);
-  L.xs_lo = take((size_t)L.mmax * H * 2);
+  // (whole 16-row groups: the fragment-block layout stores them)
+  L.xs_hi = take((size_t)((L.mmax + 15) / 16 * 16) * H * 2);
+  L.xs_lo = take((size_t)((L.mmax + 15) / 16 * 16) * H * 2);
   L.q_hi = take((size_t)L.md * Nq * 2);
   L.q_lo = take((size_t)L.md * Nq * 2);
   L.o_hi = take((size_t)L.md * Nq * 2);
@@ -708,8 +714,8 @@ dflash_status dflash_draft_block(dflash_ctx* c, int32_t batch, const int32_t* bl
   dflash_status st;
   {
     StageScope sc(c, DFLASH_STAGE_EMBED, s);
-    st = hip_status(launch_embed(c->storage(), c->embed, c->g_in[0], block_ids, M, H, cf.vocab, x, xs_hi, xs_lo, ssq,
-                                 c->at<uint32_t>(L.err), s),
+    st = hip_status(launch_embed(c->storage(), c->embed, c->g_in[0], block_ids, M, H, cf.vocab, x, xs_hi, xs_lo,
+                                 act_blocked(c->storage(), M), ssq, c->at<uint32_t>(L.err), s),
                     "embed launch");
     if (st) return st;
   }
@@ -731,6 +737,11 @@ dflash_status dflash_draft_block(dflash_ctx* c, int32_t batch, const int32_t* bl
   // HBM bytes there); from kMlpHiOnlyRows rows on, where the products are
   // matrix-core bound, they enter as plain bf16.
   const bool mlp_lo = M < kMlpHiOnlyRows;
+  // The embedding and the row-tile finishes store the normalised residual for
+  // the next Q/K/V, gate/up or LM-head product in fragment blocks when that
+  // product runs on the LDS-DMA kernel (each stage's activation loads then
+  // move whole 128-byte lines).
+  const bool blk = act_blocked(c->storage(), M);
   // the main kernel of a layer product, timed on its own under DFLASH_STAGE_LAYER_GEMM
   auto layer_gemm = [&](GemmArgs& a, bool lo, int N, int K, GemmLaunch* gl) {
     StageScope sc(c, DFLASH_STAGE_LAYER_GEMM, s);
@@ -745,6 +756,7 @@ dflash_status dflash_draft_block(dflash_ctx* c, int32_t batch, const int32_t* bl
       a.a_hi = xs_hi;
       a.a_lo = xs_lo;
       a.lda = H;
+      a.a_blocked = blk;
       FinishArgs f{};
       norm(a, f);
       if ((st = layer_gemm(a, true, Nq + 2 * Nk, H, &gl))) return st;
@@ -807,6 +819,7 @@ dflash_status dflash_draft_block(dflash_ctx* c, int32_t batch, const int32_t* bl
       f.gnext = c->g_post[l];
       f.out_hi = xs_hi;
       f.out_lo = mlp_lo ? xs_lo : nullptr;
+      f.out_blocked = blk;
       f.ssq_out = ssq;
       f.ld_ssq = L.mmax;
       if ((st = finish(c, FIN_ROWTILE, f, gl, M, H, s))) return st;
@@ -820,6 +833,7 @@ dflash_status dflash_draft_block(dflash_ctx* c, int32_t batch, const int32_t* bl
       a.a_hi = xs_hi;
       a.a_lo = mlp_lo ? xs_lo : nullptr;
       a.lda = H;
+      a.a_blocked = blk;
       FinishArgs f{};
       norm(a, f);
       if ((st = layer_gemm(a, mlp_lo, 2 * F, H, &gl))) return st;
@@ -842,6 +856,7 @@ dflash_status dflash_draft_block(dflash_ctx* c, int32_t batch, const int32_t* bl
       f.gnext = l + 1 < cf.n_layers ? c->g_in[l + 1] : c->g_final;
       f.out_hi = xs_hi;
       f.out_lo = xs_lo;
+      f.out_blocked = blk;
       f.ssq_out = ssq;
       f.ld_ssq = L.mmax;
       if ((st = finish(c, FIN_ROWTILE, f, gl, M, H, s))) return st;
@@ -858,6 +873,7 @@ dflash_status dflash_draft_block(dflash_ctx* c, int32_t batch, const int32_t* bl
     a.wt = c->at<void>(L.wt_lm);
     a.a_hi = xs_hi;
     a.lda = H;
+    a.a_blocked = blk;
     a.best_part = c->at<uint64_t>(L.lm_best);
     a.ld_best = M;
     a.logits_dbg = logits_dbg;

@@ -80,6 +80,16 @@ __device__ __forceinline__ void split_bf16x2(float x0, float x1, uint32_t& hi, u
   lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{r0, r1}, bf16x2_t));
 }
 
+// Element (m, k) of an [M, K] bf16 activation stored in matrix-core fragment
+// blocks (K % 32 == 0): the 16 x 32 block (rows 16a.., columns 32s..) is 1 KB
+// at ((a * K/32 + s) * 64) * 8 elements, lane l of it holding row 16a + (l & 15),
+// columns 32s + 8(l >> 4) .. + 7 -- the order of the tiled weight copy, so a
+// 16-row k-step of activations is one contiguous kilobyte.
+__device__ __forceinline__ size_t frag_block_index(int m, int k, int K) {
+  return ((size_t)(m >> 4) * (size_t)(K >> 5) + (size_t)(k >> 5)) * 512 + (size_t)(((m & 15) | (k & 24) << 1) << 3) +
+         (size_t)(k & 7);
+}
+
 // Raw storage bits -> bf16x8 MFMA operand.
 template <typename S>
 __device__ __forceinline__ bf16x8 raw_to_bf16x8(const Raw8& r);

@@ -521,8 +521,10 @@ __global__ void __launch_bounds__(512) gemm_mt_kernel(const GemmArgs g) {
 // by LDS-DMA loads in MFMA fragment order.  A stage is one 32-deep k-step:
 // the block's 2*NF weight tiles (the 1 KB k-step blocks of the tiled copy,
 // copied as they are) and 16 activation row groups per array (hi, lo), each
-// gathered into a 1 KB block whose lane l holds row 16g + (l & 15), columns
-// 8(l >> 4) .. + 7 of the k-step.  A fragment is then one ds_read_b128 at
+// a 1 KB block whose lane l holds row 16g + (l & 15), columns 8(l >> 4) .. + 7
+// of the k-step: copied as it is from activations stored in fragment blocks
+// (a_blocked; eight whole 128-byte lines per load), else gathered from
+// row-major rows (sixteen 64-byte pieces per load).  A fragment is then one ds_read_b128 at
 // 16*lane of its block (contiguous across the wave: no bank conflicts, no
 // padding), no stage passes through registers, and NS stages are in flight
 // (NS - 1 ahead of the one being computed).  Each wave issues the same
@@ -584,13 +586,21 @@ __global__ void __launch_bounds__(512) gemm_dma_kernel(const GemmArgs g) {
       const int a = b - NT, arr = a / AG, grp = a % AG;
       const int m = min(m0 + 16 * grp + (lane & 15), g.M - 1);
       const int k = kbeg + 8 * (lane >> 4);
+      step[i] = 64;
       if constexpr (SRC == SRC_SPLIT) {
-        const void* base = arr ? g.a_lo : g.a_hi;
-        src0[i] = reinterpret_cast<const char*>(base) + ((size_t)m * g.lda + k) * 2;
+        const char* base = reinterpret_cast<const char*>(arr ? g.a_lo : g.a_hi);
+        if (g.a_blocked) {
+          // the group's k-steps are consecutive kilobytes (a last group past M
+          // reads the final 16-row block; its rows past M are never stored)
+          const int a16 = min(m0 / 16 + grp, (g.M + 15) / 16 - 1);
+          src0[i] = base + (((size_t)a16 * (g.K / 32) + kbeg / 32) * 64 + lane) * 16;
+          step[i] = 1024;
+        } else {
+          src0[i] = base + ((size_t)m * g.lda + k) * 2;
+        }
       } else {
         src0[i] = nullptr;  // per stage: the source array holding the k-step
       }
-      step[i] = 64;
     }
   }
   auto issue = [&](int kt, int s) {
@@ -959,7 +969,8 @@ __device__ __forceinline__ void rope_n(const FinishArgs& f, int pos, int d, floa
 }
 
 // y = sum (+ x residual, + width-3 block conv); x / out_f32 = y; hi/lo of
-// y * gnext; sums of squares per (tile, row).  grid: (tiles / (4/SPL), row
+// y * gnext (row-major, or in fragment blocks for an LDS-DMA consumer); sums
+// of squares per (tile, row).  grid: (tiles / (4/SPL), row
 // groups of 16); thread t: lane j = t % SPL of the group sharing column quad
 // q = (t / SPL) & 3 of row r = (t / 4SPL) & 15 of tile t / 64SPL, each lane
 // finishing 4/SPL columns.  The conv's neighbour rows come through LDS (a
@@ -1024,7 +1035,9 @@ __global__ void __launch_bounds__(256) finish_rowtile_kernel(const FinishArgs f)
       sv[e] = y[e] * gn[e];
       sq += y[e] * y[e];
     }
-    split_store<E>(reinterpret_cast<bf16_t*>(f.out_hi), reinterpret_cast<bf16_t*>(f.out_lo), idx, sv);
+    // (fragment blocks: the lane's E columns stay inside one 8-column piece)
+    const size_t oidx = f.out_blocked ? frag_block_index(m, n + j * E, f.N) : idx;
+    split_store<E>(reinterpret_cast<bf16_t*>(f.out_hi), reinterpret_cast<bf16_t*>(f.out_lo), oidx, sv);
   }
   // the row's 4 SPL lanes
   sq += quad_xor1(sq);
@@ -1357,6 +1370,8 @@ static hipError_t dispatch_s(const GemmArgs& a, const GemmLaunch& l, hipStream_t
 }
 
 hipError_t launch_gemm(int storage, const GemmArgs& a, const GemmLaunch& l, hipStream_t stream) {
+  // only the LDS-DMA kernel reads activations stored in fragment blocks
+  if (a.a_blocked && (l.kind != GEMM_DMA || l.src != SRC_SPLIT || a.K % 32)) return hipErrorInvalidValue;
   if (storage == ST_BF16) return dispatch_s<bf16_t>(a, l, stream);
   return dispatch_s<float>(a, l, stream);
 }
@@ -1389,6 +1404,7 @@ static hipError_t launch_finish_s(FinishKind kind, const FinishArgs& f, hipStrea
   // (a lane takes two slices a round: a group only as wide as keeps both useful)
   int spl = 1;
   if (few) spl = f.KS % 4 == 0 && f.KS >= 8 ? 4 : (f.KS % 2 == 0 && f.KS >= 4 ? 2 : 1);
+  if (f.out_blocked && (kind != FIN_ROWTILE || f.N % 32)) return hipErrorInvalidValue;
   if (kind == FIN_ROWTILE) {
     const dim3 grid((f.N / 16 + 4 / spl - 1) / (4 / spl), (f.M + 15) / 16);
     if (spl == 4) hipLaunchKernelGGL((finish_rowtile_kernel<S, 4>), grid, dim3(256), 0, st, f);

@@ -41,6 +41,9 @@ struct GemmArgs {
   const void* a_hi;
   const void* a_lo;
   int lda;
+  // SRC_SPLIT on GEMM_DMA only: a_hi / a_lo are stored in fragment blocks
+  // (frag_block_index, row length K, rows rounded up to 16; lda unused)
+  int a_blocked;
   const void* src[8];
   int n_src, src_width;
   // launch geometry (filled by the planner)
@@ -116,6 +119,7 @@ struct FinishArgs {
   float* ssq_out;     // [N/16][ld_ssq]
   void* out_hi;       // FIN_ROWTILE [M, N]; FIN_SWIGLU [M, N/2]; FIN_QKV query [M, Hq*D]
   void* out_lo;       //   (null: hi only)
+  int out_blocked;    // FIN_ROWTILE: out_hi / out_lo in fragment blocks (frag_block_index, row length N)
   int block;          // rows per sequence
   // FIN_QKV / FIN_KV
   const float2* rope;  // [max_ctx + max rows per sequence][head_dim / 2] (cos, sin)
@@ -198,8 +202,10 @@ hipError_t static_verify_scratch(uint64_t** ptr);
 // a.chunk must be 4 * 256 * 8 (one 16-byte load round per thread).
 hipError_t launch_verify_sample(const VerifyArgs& a, hipStream_t stream);
 
+// blocked: xs_hi / xs_lo in fragment blocks (frag_block_index, H % 32 == 0), else row-major.
 hipError_t launch_embed(int storage, const void* embed, const void* gain, const int32_t* ids, int M, int H, int V,
-                        float* x, void* xs_hi, void* xs_lo, float* ssq, uint32_t* err, hipStream_t stream);
+                        float* x, void* xs_hi, void* xs_lo, bool blocked, float* ssq, uint32_t* err,
+                        hipStream_t stream);
 hipError_t launch_commit(int32_t* ctx_len, int batch, int t_new, int max_ctx, hipStream_t stream);
 // table[p][i] = (cos, sin)(p * theta^(-2i/D)), evaluated in double precision.
 hipError_t launch_rope_table(float2* table, int rows, int head_dim, float theta, hipStream_t stream);

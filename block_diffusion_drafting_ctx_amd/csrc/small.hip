@@ -364,10 +364,11 @@ hipError_t launch_verify_sample(const VerifyArgs& a, hipStream_t stream) {
 
 // ---------------------------------------------------------------- embedding
 // x[m] = E[ids[m]] as fp32, the hi/lo pair of x * gain (the first layer's
-// RMSNorm gain) and the row's sum of squares (one partial per row).
+// RMSNorm gain; row-major or in fragment blocks) and the row's sum of squares
+// (one partial per row).
 template <typename S>
 __global__ void __launch_bounds__(256) embed_kernel(const S* embed, const S* gain, const int32_t* ids, int H, int V,
-                                                    float* x, bf16_t* xs_hi, bf16_t* xs_lo, float* ssq,
+                                                    float* x, bf16_t* xs_hi, bf16_t* xs_lo, int blocked, float* ssq,
                                                     uint32_t* err) {
   __shared__ float s_part[4];
   const int m = blockIdx.x, tid = threadIdx.x;
@@ -383,16 +384,21 @@ __global__ void __launch_bounds__(256) embed_kernel(const S* embed, const S* gai
     float f[8], gf[8];
     raw_to_f32x8<S>(raw, f);
     raw_to_f32x8<S>(graw, gf);
+    uint32_t hw[4], lw[4];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       f[i] = ok ? f[i] : 0.f;
       s += f[i] * f[i];
-      const size_t idx = (size_t)m * H + k + i;
       const float v = f[i] * gf[i];
-      const bf16_t hbits = f32_to_bf16_bits(v);
-      xs_hi[idx] = hbits;
-      xs_lo[idx] = f32_to_bf16_bits(v - bf16_bits_to_f32(hbits));
+      const uint32_t hbits = f32_to_bf16_bits(v);
+      const uint32_t lbits = f32_to_bf16_bits(v - bf16_bits_to_f32(hbits));
+      hw[i >> 1] = (i & 1) ? hw[i >> 1] | hbits << 16 : hbits;
+      lw[i >> 1] = (i & 1) ? lw[i >> 1] | lbits << 16 : lbits;
     }
+    // the 8 columns k .. k+7 are one 16-byte piece in either layout
+    const size_t idx = blocked ? frag_block_index(m, k, H) : (size_t)m * H + k;
+    *reinterpret_cast<u32x4*>(xs_hi + idx) = u32x4{hw[0], hw[1], hw[2], hw[3]};
+    *reinterpret_cast<u32x4*>(xs_lo + idx) = u32x4{lw[0], lw[1], lw[2], lw[3]};
     f32x4* dst = reinterpret_cast<f32x4*>(x + (size_t)m * H + k);
     dst[0] = f32x4{f[0], f[1], f[2], f[3]};
     dst[1] = f32x4{f[4], f[5], f[6], f[7]};
@@ -404,13 +410,15 @@ __global__ void __launch_bounds__(256) embed_kernel(const S* embed, const S* gai
 }
 
 hipError_t launch_embed(int storage, const void* embed, const void* gain, const int32_t* ids, int M, int H, int V,
-                        float* x, void* xs_hi, void* xs_lo, float* ssq, uint32_t* err, hipStream_t stream) {
+                        float* x, void* xs_hi, void* xs_lo, bool blocked, float* ssq, uint32_t* err,
+                        hipStream_t stream) {
+  if (H % 8 || (blocked && H % 32)) return hipErrorInvalidValue;
   if (storage == ST_BF16)
     hipLaunchKernelGGL(embed_kernel<bf16_t>, dim3(M), dim3(256), 0, stream, (const bf16_t*)embed,
-                       (const bf16_t*)gain, ids, H, V, x, (bf16_t*)xs_hi, (bf16_t*)xs_lo, ssq, err);
+                       (const bf16_t*)gain, ids, H, V, x, (bf16_t*)xs_hi, (bf16_t*)xs_lo, (int)blocked, ssq, err);
   else
     hipLaunchKernelGGL(embed_kernel<float>, dim3(M), dim3(256), 0, stream, (const float*)embed,
-                       (const float*)gain, ids, H, V, x, (bf16_t*)xs_hi, (bf16_t*)xs_lo, ssq, err);
+                       (const float*)gain, ids, H, V, x, (bf16_t*)xs_hi, (bf16_t*)xs_lo, (int)blocked, ssq, err);
   return hipGetLastError();
 }
 

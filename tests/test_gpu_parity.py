@@ -93,6 +93,14 @@ def test_many_ragged_sequences_flattened_attention():
     run_step(wl, seed=24, seqs=[0, 51, 159], poison=True)
 
 
+def test_half_filled_last_row_group_in_fragment_blocks():
+    # 17 sequences x block 8 = 136 draft rows: the products run on 256-row
+    # LDS-DMA blocks and the normalised residual is stored in 16-row fragment
+    # blocks, the last of them half filled (rows past the batch never stored)
+    wl = gen.Workload("tiny-b17-block8", 256, 4, 2, 64, 2, 512, 1024, 8, 3, 17, 0, 300, "bf16", accept_hi=8)
+    run_step(wl, seed=28, poison=True)
+
+
 @pytest.mark.parametrize("storage", ["bf16", "f32"])
 def test_batch1_finishes_split_k_slices_over_lanes(storage):
     # one sequence, hidden 1024: every product runs 4 or 8 k-slices over a grid
