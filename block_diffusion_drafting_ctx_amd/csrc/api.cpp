@@ -180,7 +180,7 @@ bool plan_gemm(int storage, int src, int out, bool lo, int M, int N, int K, Gemm
   l->KS = KS;
   l->grid = dim3(((units + 7) / 8) * 8 * nbm);
   l->threads = 512;
-  l->lds = dma ? gemm_dma_lds_bytes(MF, NF, lo_eff) : gemm_mt_lds_bytes(MF, NF, lo_eff);
+  l->lds = dma ? gemm_dma_lds_bytes(MF, NF, lo_eff, false) : gemm_mt_lds_bytes(MF, NF, lo_eff);
   l->argmax_tiles = nbn;
   a->nbm = nbm;
   a->nbn = nbn;
@@ -193,6 +193,36 @@ bool plan_gemm(int storage, int src, int out, bool lo, int M, int N, int K, Gemm
 // so are stored in fragment blocks by the finish that writes them (the test
 // plan_gemm makes for GEMM_DMA: bf16 storage and 256-row blocks, M > 128).
 bool act_blocked(int storage, int M) { return kUseDmaGemm && storage == ST_BF16 && M > 128; }
+
+// gate/up of M rows (K = hidden, F = ffn, plain bf16 input) with the SiLU
+// product in the LDS-DMA kernel's epilogue: 256-row blocks of 96 gate and the
+// matching 96 up columns, one k-slice, so no partials and no finish kernel.
+// Only where those blocks fill the chip (the split-K plan is the faster one
+// below that).
+bool plan_swiglu(int storage, int M, int F, int K, GemmArgs* a, GemmLaunch* l) {
+  if (!act_blocked(storage, M) || F % 96 || K % 32) return false;
+  const int nbm = (M + 255) / 256, nbn = F / 96;
+  if (nbn * nbm < kCUs) return false;
+  *l = GemmLaunch{};
+  l->kind = GEMM_DMA;
+  l->src = SRC_SPLIT;
+  l->out = OUT_SWIGLU;
+  l->lo = 0;
+  l->MR = 4;
+  l->NF = 6;
+  l->KS = 1;
+  l->grid = dim3(((nbn + 7) / 8) * 8 * nbm);
+  l->threads = 512;
+  l->lds = gemm_dma_lds_bytes(4, 6, false, true);
+  a->M = M;
+  a->N = 2 * F;
+  a->K = K;
+  a->nbm = nbm;
+  a->nbn = nbn;
+  a->KS = 1;
+  a->kslice = K;
+  return true;
+}
 
 // Floats of partial tiles the planner needs for a product of this shape.
 size_t partial_floats(int storage, int src, bool lo, int Mmax, int N, int K) {
@@ -836,10 +866,20 @@ dflash_status dflash_draft_block(dflash_ctx* c, int32_t batch, const int32_t* bl
       a.a_blocked = blk;
       FinishArgs f{};
       norm(a, f);
-      if ((st = layer_gemm(a, mlp_lo, 2 * F, H, &gl))) return st;
-      f.out_hi = c->at<void>(L.act_hi);
-      f.out_lo = mlp_lo ? c->at<void>(L.act_lo) : nullptr;
-      if ((st = finish(c, FIN_SWIGLU, f, gl, M, 2 * F, s))) return st;
+      if (!mlp_lo && plan_swiglu(c->storage(), M, F, H, &a, &gl)) {
+        // the SiLU product in the main kernel's epilogue (row scales from the sums of squares there)
+        StageScope sc2(c, DFLASH_STAGE_LAYER_GEMM, s);
+        a.rinv_out = nullptr;
+        a.act_out = c->at<void>(L.act_hi);
+        a.ld_act = F;
+        a.up_tile0 = F / 16;
+        if ((st = hip_status(launch_gemm(c->storage(), a, gl, s), "gate/up launch"))) return st;
+      } else {
+        if ((st = layer_gemm(a, mlp_lo, 2 * F, H, &gl))) return st;
+        f.out_hi = c->at<void>(L.act_hi);
+        f.out_lo = mlp_lo ? c->at<void>(L.act_lo) : nullptr;
+        if ((st = finish(c, FIN_SWIGLU, f, gl, M, 2 * F, s))) return st;
+      }
     }
     {  // down projection + residual; hi/lo of x * (next layer's g_in, or g_final)
       StageScope sc(c, DFLASH_STAGE_DOWN, s);

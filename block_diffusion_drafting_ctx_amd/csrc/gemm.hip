@@ -541,10 +541,10 @@ struct DmaShape {
   static_assert(3 * SLOT <= 160 * 1024, "three stages fit the LDS");
 };
 
-size_t gemm_dma_lds_bytes(int MF, int NF, bool lo) {
+size_t gemm_dma_lds_bytes(int MF, int NF, bool lo, bool swiglu) {
   const int nb = 2 * NF + 4 * MF * (lo ? 2 : 1);
   const int ns = (160 * 1024 - 4096) / (nb * 1024) >= 4 ? 4 : 3;
-  return (size_t)ns * nb * 1024;
+  return (size_t)ns * (nb * 1024 + (swiglu ? 2048 : 0));
 }
 
 template <int MF, int NF, int SRC, bool LO, int OUT>
@@ -552,7 +552,11 @@ __global__ void __launch_bounds__(512) gemm_dma_kernel(const GemmArgs g) {
   using Sh = DmaShape<MF, NF, LO>;
   constexpr int BM = Sh::BM, NT = Sh::NT, NB = Sh::NB, PW = Sh::PW, SLOT = Sh::SLOT, NS = Sh::NS;
   constexpr int AG = BM / 16;  // activation row groups per array
-  static_assert((NS - 2) * PW < 64, "vmcnt range");
+  constexpr bool SW = OUT == OUT_SWIGLU;
+  constexpr int PL = PW + (SW ? 1 : 0);  // loads per wave and stage (SW: + the stage's sums of squares)
+  static_assert((NS - 2) * PL < 64, "vmcnt range");
+  static_assert(!SW || (SRC == SRC_SPLIT && !LO && BM == 256 && NS * SLOT >= 4 * NF * MF * 1024 + 3072),
+                "SiLU epilogue: 256-row plain blocks, the exchange fits the ring");
   extern __shared__ __align__(16) unsigned char lds[];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -579,7 +583,8 @@ __global__ void __launch_bounds__(512) gemm_dma_kernel(const GemmArgs g) {
     const int b = min(wave + 8 * i, NB - 1);
     dst[i] = b * 1024;
     if (b < NT) {
-      const int t = min(n0 / 16 + b, ntl - 1);
+      // (SW: the waves of wn = 0 take gate tiles, those of wn = 1 the matching up tiles)
+      const int t = SW ? (b < NF ? nb * NF + b : g.up_tile0 + nb * NF + (b - NF)) : min(n0 / 16 + b, ntl - 1);
       src0[i] = reinterpret_cast<const char*>(g.wt) + ((size_t)(t * nks + kbeg / 32) * 64 + lane) * 16;
       step[i] = 1024;
     } else {
@@ -603,6 +608,12 @@ __global__ void __launch_bounds__(512) gemm_dma_kernel(const GemmArgs g) {
       }
     }
   }
+  // SW: thread tid sums, one per stage, the K/16 partial sums of squares of
+  // row m0 + (tid & 255): half tid >> 8 of them (K/32 = nk stages each).
+  // They arrive by a 4-byte LDS-DMA load per wave and stage beside the stage.
+  const float* ssq_src = nullptr;
+  float ssq_acc = 0.f;
+  if constexpr (SW) ssq_src = g.ssq_in + (size_t)((tid >> 8) * nk) * g.ld_ssq + min(m0 + (tid & 255), g.M - 1);
   auto issue = [&](int kt, int s) {
     unsigned char* sl = lds + s * SLOT;
 #pragma unroll
@@ -625,6 +636,9 @@ __global__ void __launch_bounds__(512) gemm_dma_kernel(const GemmArgs g) {
       }
       __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(sl + dst[i]), 16, 0, 0);
     }
+    if constexpr (SW)
+      __builtin_amdgcn_global_load_lds(ssq_src + (size_t)kt * g.ld_ssq,
+                                       (lds_void_t*)(lds + NS * SLOT + s * 2048 + wave * 256), 4, 0, 0);
     asm volatile("" ::: "memory");
   };
 
@@ -634,6 +648,8 @@ __global__ void __launch_bounds__(512) gemm_dma_kernel(const GemmArgs g) {
 #pragma unroll
     for (int fm = 0; fm < MF; ++fm) acc[fn][fm] = f32x4{0.f, 0.f, 0.f, 0.f};
   auto compute = [&](int s) {
+    float ssq_v = 0.f;
+    if constexpr (SW) ssq_v = reinterpret_cast<const float*>(lds + NS * SLOT)[s * 512 + tid];
     const unsigned char* sl = lds + s * SLOT + 16 * lane;
     bf16x8 af[MF], al[MF];
 #pragma unroll
@@ -656,6 +672,10 @@ __global__ void __launch_bounds__(512) gemm_dma_kernel(const GemmArgs g) {
       }
     }
     __builtin_amdgcn_sched_group_barrier(0x008, MF * NF * (LO ? 2 : 1), 0);  // then the MFMAs
+    if constexpr (SW) {
+      ssq_acc += ssq_v;
+      asm volatile("" : "+v"(ssq_acc));  // read and added before the next barrier releases the slot
+    }
   };
 
   // ---- pipeline: NS - 1 stages requested ahead (past the end: the last
@@ -663,7 +683,7 @@ __global__ void __launch_bounds__(512) gemm_dma_kernel(const GemmArgs g) {
 #pragma unroll
   for (int j = 0; j < NS - 1; ++j) issue(min(j, nk - 1), j);
   for (int kt = 0; kt < nk; ++kt) {
-    wait_vm<(NS - 2) * PW>();  // this wave's loads of stage kt are in LDS
+    wait_vm<(NS - 2) * PL>();  // this wave's loads of stage kt are in LDS
     raw_barrier();             // ... every wave's, and every wave is done with stage kt - 1
     issue(min(kt + NS - 1, nk - 1), (kt + NS - 1) % NS);
     compute(kt % NS);
@@ -687,6 +707,46 @@ __global__ void __launch_bounds__(512) gemm_dma_kernel(const GemmArgs g) {
       }
     }
     if (g.rinv_out != nullptr && ks == 0) write_rinv(g, nb * g.nbm + mb, g.nbn * g.nbm);
+  } else if constexpr (SW) {
+    // the up accumulators (waves wn = 1) meet the gate ones (wn = 0) of the
+    // same (row, column) through the idle ring; the rows' scales from the two
+    // halves' sums, in a fixed order
+    float* sx = reinterpret_cast<float*>(lds);
+    float* sh = sx + 4 * NF * MF * 256;  // [512] the halves' sums of squares
+    float* rs = sh + 512;                // [256] row scales
+    sh[tid] = ssq_acc;
+    if (wn == 1) {
+#pragma unroll
+      for (int fn = 0; fn < NF; ++fn)
+#pragma unroll
+        for (int fm = 0; fm < MF; ++fm)
+          *reinterpret_cast<f32x4*>(sx + (((wm * NF + fn) * MF + fm) * 64 + lane) * 4) = acc[fn][fm];
+    }
+    __syncthreads();
+    if (tid < 256) rs[tid] = 1.0f / sqrtf((sh[tid] + sh[tid + 256]) / (float)g.K + g.eps);
+    __syncthreads();
+    if (wn == 0) {
+      bf16_t* out = reinterpret_cast<bf16_t*>(g.act_out);
+#pragma unroll
+      for (int fm = 0; fm < MF; ++fm) {
+        const int row = 16 * MF * wm + 16 * fm + (lane & 15), m = m0 + row;
+        const float r = rs[row];
+        if (m >= g.M) continue;
+#pragma unroll
+        for (int fn = 0; fn < NF; ++fn) {
+          const f32x4 u = *reinterpret_cast<const f32x4*>(sx + (((wm * NF + fn) * MF + fm) * 64 + lane) * 4);
+          uint32_t w[2];
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const uint32_t b0 = f32_to_bf16_bits(silu_f32(acc[fn][fm][2 * h] * r) * (u[2 * h] * r));
+            const uint32_t b1 = f32_to_bf16_bits(silu_f32(acc[fn][fm][2 * h + 1] * r) * (u[2 * h + 1] * r));
+            w[h] = b0 | b1 << 16;
+          }
+          const int c = 16 * (nb * NF + fn) + 4 * (lane >> 4);
+          *reinterpret_cast<u32x2*>(out + (size_t)m * g.ld_act + c) = u32x2{w[0], w[1]};
+        }
+      }
+    }
   } else {
     uint64_t* sb = reinterpret_cast<uint64_t*>(lds);  // [2][BM]; the ring is idle after the last barrier
 #pragma unroll
@@ -1356,6 +1416,13 @@ static hipError_t dispatch_mr(const GemmArgs& a, const GemmLaunch& l, hipStream_
 
 template <typename S>
 static hipError_t dispatch_s(const GemmArgs& a, const GemmLaunch& l, hipStream_t st) {
+  if (l.out == OUT_SWIGLU) {
+    if constexpr (sizeof(S) == 2)
+      if (l.kind == GEMM_DMA && l.src == SRC_SPLIT && !l.lo && l.MR == 4 && l.NF == 6 && l.KS == 1 &&
+          a.ssq_nparts == a.K / 16 && a.kslice == a.K && a.N % 192 == 0)
+        return launch_dma<4, 6, SRC_SPLIT, false, OUT_SWIGLU>(a, l, st);
+    return hipErrorInvalidValue;
+  }
   if (l.src == SRC_CONCAT) {
     if (l.out != OUT_PARTIAL) return hipErrorInvalidValue;
     // fp32 sources are split on the fly; bf16 sources are exact

@@ -25,7 +25,11 @@ enum SrcKind {
   SRC_SPLIT = 0,   // A = a_hi (+ a_lo): bf16 arrays [M, lda]
   SRC_CONCAT = 1   // A: concat of n_src arrays [M, src_width] of the storage type
 };
-enum OutKind { OUT_PARTIAL = 0, OUT_ARGMAX = 1 };
+// OUT_SWIGLU (GEMM_DMA, SRC_SPLIT, one k-slice): N = 2F concatenates gate and
+// up; workgroup nb takes gate tiles 6nb.. and the matching up tiles
+// up_tile0 + 6nb.., and writes act_out[m, c] = silu(r y_gate) * (r y_up) in
+// bf16, r the row's RMSNorm scale summed from ssq_in in the kernel.
+enum OutKind { OUT_PARTIAL = 0, OUT_ARGMAX = 1, OUT_SWIGLU = 2 };
 enum GemmKind { GEMM_AS = 0, GEMM_MT = 1, GEMM_DMA = 2 };
 
 constexpr int kMaxSeg = 16;  // context K/V caches one product writes (2 per layer)
@@ -62,6 +66,9 @@ struct GemmArgs {
   // nullable: workgroup (0, 0) writes rinv_out[m] = 1/sqrt(sum_p ssq_in[p][m]/K + eps)
   // after its tiles, for the finish kernel of this product
   float* rinv_out;
+  // OUT_SWIGLU: bf16 [M, ld_act] output, first up tile (F / 16)
+  void* act_out;
+  int ld_act, up_tile0;
 };
 
 struct GemmLaunch {
@@ -93,8 +100,9 @@ size_t gemm_as_lds(int M, int ksl, bool lo);
 // ring (lo: hi/lo activation pair).
 size_t gemm_mt_lds_bytes(int MF, int NF, bool lo);
 // gemm_dma (64*MF-row blocks, MF = 4, bf16 operands, stages through
-// LDS-DMA): LDS bytes of its stage ring for NF = 6 or 8.
-size_t gemm_dma_lds_bytes(int MF, int NF, bool lo);
+// LDS-DMA): LDS bytes of its stage ring for NF = 6 or 8 (swiglu: with the
+// ring of per-stage sums of squares of OUT_SWIGLU).
+size_t gemm_dma_lds_bytes(int MF, int NF, bool lo, bool swiglu);
 // ids[m] = index of the largest key over part[t][m], t < ntiles.
 hipError_t launch_argmax_reduce(const uint64_t* part, int ntiles, int ld, int M, int32_t* ids, hipStream_t stream);
 

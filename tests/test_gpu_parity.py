@@ -101,6 +101,15 @@ def test_half_filled_last_row_group_in_fragment_blocks():
     run_step(wl, seed=28, poison=True)
 
 
+def test_full_size_silu_epilogue_with_a_partial_row_block():
+    # 17 sequences at the Qwen3-8B shape (272 draft rows): gate/up computes the
+    # SiLU product in its epilogue over two 256-row blocks, the second holding
+    # 16 rows; the row scales come from the sums of squares inside that kernel
+    wl = gen.WORKLOADS["qwen3-8b-shape-b32-ragged"].with_batch(17)
+    run_step(wl, seed=30, seqs=[0, 16], poison=True, min_sure=0.25)
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("storage", ["bf16", "f32"])
 def test_batch1_finishes_split_k_slices_over_lanes(storage):
     # one sequence, hidden 1024: every product runs 4 or 8 k-slices over a grid
