@@ -117,7 +117,11 @@ bool plan_gemm(int storage, int src, int out, bool lo, int M, int N, int K, Gemm
   // as far as the grid stays within one dispatch round (one 8-wave workgroup
   // per compute unit): a second, partly filled round would cost a whole
   // workgroup's time, and every k-slice adds a partial-output round trip
-  const int MF = M <= 64 ? 1 : (M <= 128 ? 2 : 4);
+  // (above 128 rows the LDS-DMA kernel also takes 192-row blocks where they
+  // pad the rows clearly less: 544 rows run as 3 x 192 instead of 3 x 256)
+  const bool dma_ok = kUseDmaGemm && storage == ST_BF16;
+  const int pad3 = 192 * ((M + 191) / 192), pad4 = 256 * ((M + 255) / 256);
+  const int MF = M <= 64 ? 1 : (M <= 128 ? 2 : (dma_ok && 5 * pad3 < 4 * pad4 ? 3 : 4));
   const int nbm = (M + 64 * MF - 1) / (64 * MF);
   // (every k-slice keeps an even number of 32-deep stages: the kernel's
   // pipeline takes them in pairs)
@@ -129,7 +133,7 @@ bool plan_gemm(int storage, int src, int out, bool lo, int M, int N, int K, Gemm
   };
   // share of the compute units the grid keeps busy over its dispatch rounds
   auto fill = [&](int wgs) { return (double)wgs / (double)(((wgs + kCUs - 1) / kCUs) * kCUs); };
-  int NF = MF >= 4 ? 8 : 4;
+  int NF = MF >= 3 ? 8 : 4;
   int nbn = (N + 32 * NF - 1) / (32 * NF);
   int KS = split(nbn);
   if (MF <= 2) {
@@ -160,7 +164,7 @@ bool plan_gemm(int storage, int src, int out, bool lo, int M, int N, int K, Gemm
       }
     }
   }
-  if (MF >= 4 && out == OUT_PARTIAL) {
+  if (MF >= 3 && out == OUT_PARTIAL) {
     // 192-column blocks when they fill the chip clearly better (gate/up at
     // 512 rows: 256 workgroups instead of 192); their wave tile reads ~11%
     // more LDS per matrix-core op
@@ -172,7 +176,7 @@ bool plan_gemm(int storage, int src, int out, bool lo, int M, int N, int K, Gemm
     }
   }
   // 256-row blocks with bf16 operands stream their stages through LDS-DMA
-  const bool dma = kUseDmaGemm && MF >= 4 && storage == ST_BF16;
+  const bool dma = dma_ok && MF >= 3;
   const int units = nbn * KS;
   l->kind = dma ? GEMM_DMA : GEMM_MT;
   l->MR = MF;

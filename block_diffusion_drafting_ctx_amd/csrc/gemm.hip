@@ -530,7 +530,8 @@ __global__ void __launch_bounds__(512) gemm_mt_kernel(const GemmArgs g) {
 // (NS - 1 ahead of the one being computed).  Each wave issues the same
 // number of block loads for every stage (spare loads repeat the stage's last
 // block into its own place), so the wait for a stage is vmcnt((NS-2) * PW).
-// MF row fragments per wave (4 waves along M): 256-row blocks at MF = 4.
+// MF row fragments per wave (4 waves along M): 256-row blocks at MF = 4,
+// 192-row blocks at MF = 3.
 template <int MF, int NF, bool LO>
 struct DmaShape {
   static constexpr int BM = 64 * MF, NT = 2 * NF, NA = LO ? 2 : 1;
@@ -1379,9 +1380,15 @@ template <typename S, int SRC, bool LO, int OUT>
 static hipError_t dispatch_mr(const GemmArgs& a, const GemmLaunch& l, hipStream_t st) {
   if (l.kind == GEMM_DMA) {
     if constexpr (sizeof(S) == 2) {
-      if (l.NF == 8) return launch_dma<4, 8, SRC, LO, OUT>(a, l, st);
-      if constexpr (OUT == OUT_PARTIAL)
-        if (l.NF == 6) return launch_dma<4, 6, SRC, LO, OUT>(a, l, st);
+      if (l.MR == 4) {
+        if (l.NF == 8) return launch_dma<4, 8, SRC, LO, OUT>(a, l, st);
+        if constexpr (OUT == OUT_PARTIAL)
+          if (l.NF == 6) return launch_dma<4, 6, SRC, LO, OUT>(a, l, st);
+      } else if (l.MR == 3) {
+        if (l.NF == 8) return launch_dma<3, 8, SRC, LO, OUT>(a, l, st);
+        if constexpr (OUT == OUT_PARTIAL)
+          if (l.NF == 6) return launch_dma<3, 6, SRC, LO, OUT>(a, l, st);
+      }
     }
     return hipErrorInvalidValue;
   }

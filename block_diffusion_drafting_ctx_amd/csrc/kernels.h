@@ -99,7 +99,7 @@ size_t gemm_as_lds(int M, int ksl, bool lo);
 // MF < 4; 8, or 6 for split-K outputs, at MF = 4); LDS bytes of its stage
 // ring (lo: hi/lo activation pair).
 size_t gemm_mt_lds_bytes(int MF, int NF, bool lo);
-// gemm_dma (64*MF-row blocks, MF = 4, bf16 operands, stages through
+// gemm_dma (64*MF-row blocks, MF = 3 or 4, bf16 operands, stages through
 // LDS-DMA): LDS bytes of its stage ring for NF = 6 or 8 (swiglu: with the
 // ring of per-stage sums of squares of OUT_SWIGLU).
 size_t gemm_dma_lds_bytes(int MF, int NF, bool lo, bool swiglu);
