@@ -555,6 +555,8 @@ __global__ void __launch_bounds__(512) gemm_dma_kernel(const GemmArgs g) {
   constexpr int AG = BM / 16;  // activation row groups per array
   constexpr bool SW = OUT == OUT_SWIGLU;
   constexpr int PL = PW + (SW ? 1 : 0);  // loads per wave and stage (SW: + the stage's sums of squares)
+  // stage operands double-buffered in registers where two sets fit beside the accumulators
+  constexpr bool DB = (MF * (LO ? 2 : 1) + NF) * 8 + MF * NF * 4 <= 224;
   static_assert((NS - 2) * PL < 64, "vmcnt range");
   static_assert(!SW || (SRC == SRC_SPLIT && !LO && BM == 256 && NS * SLOT >= 4 * NF * MF * 1024 + 3072),
                 "SiLU epilogue: 256-row plain blocks, the exchange fits the ring");
@@ -648,46 +650,83 @@ __global__ void __launch_bounds__(512) gemm_dma_kernel(const GemmArgs g) {
   for (int fn = 0; fn < NF; ++fn)
 #pragma unroll
     for (int fm = 0; fm < MF; ++fm) acc[fn][fm] = f32x4{0.f, 0.f, 0.f, 0.f};
-  auto compute = [&](int s) {
-    float ssq_v = 0.f;
-    if constexpr (SW) ssq_v = reinterpret_cast<const float*>(lds + NS * SLOT)[s * 512 + tid];
+  // A stage's operands in registers: MF activation (x2 for hi/lo) and NF
+  // weight fragments, and (SW) this thread's partial sum of squares.
+  struct Frags {
+    bf16x8 a[MF], l[MF], w[NF];
+    float ssq;
+  };
+  auto read = [&](int s, Frags& f) {
+    if constexpr (SW) f.ssq = reinterpret_cast<const float*>(lds + NS * SLOT)[s * 512 + tid];
     const unsigned char* sl = lds + s * SLOT + 16 * lane;
-    bf16x8 af[MF], al[MF];
 #pragma unroll
     for (int fm = 0; fm < MF; ++fm) {
-      af[fm] = *reinterpret_cast<const bf16x8*>(sl + (NT + MF * wm + fm) * 1024);
-      if constexpr (LO) al[fm] = *reinterpret_cast<const bf16x8*>(sl + (NT + AG + MF * wm + fm) * 1024);
+      f.a[fm] = *reinterpret_cast<const bf16x8*>(sl + (NT + MF * wm + fm) * 1024);
+      if constexpr (LO) f.l[fm] = *reinterpret_cast<const bf16x8*>(sl + (NT + AG + MF * wm + fm) * 1024);
     }
-    // every fragment read of the stage goes out before the matrix work
-    // (measured: 2-8% faster products than reads interleaved with it)
-    bf16x8 wfa[NF];
 #pragma unroll
-    for (int fn = 0; fn < NF; ++fn) wfa[fn] = *reinterpret_cast<const bf16x8*>(sl + (NF * wn + fn) * 1024);
-    __builtin_amdgcn_sched_group_barrier(0x100, MF * (LO ? 2 : 1) + NF, 0);  // the DS reads
+    for (int fn = 0; fn < NF; ++fn) f.w[fn] = *reinterpret_cast<const bf16x8*>(sl + (NF * wn + fn) * 1024);
+  };
+  auto mma = [&](const Frags& f) {
 #pragma unroll
     for (int fn = 0; fn < NF; ++fn) {
 #pragma unroll
       for (int fm = 0; fm < MF; ++fm) {
-        acc[fn][fm] = mfma16x16x32(wfa[fn], af[fm], acc[fn][fm]);
-        if constexpr (LO) acc[fn][fm] = mfma16x16x32(wfa[fn], al[fm], acc[fn][fm]);
+        acc[fn][fm] = mfma16x16x32(f.w[fn], f.a[fm], acc[fn][fm]);
+        if constexpr (LO) acc[fn][fm] = mfma16x16x32(f.w[fn], f.l[fm], acc[fn][fm]);
       }
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, MF * NF * (LO ? 2 : 1), 0);  // then the MFMAs
-    if constexpr (SW) {
-      ssq_acc += ssq_v;
-      asm volatile("" : "+v"(ssq_acc));  // read and added before the next barrier releases the slot
-    }
+    if constexpr (SW) ssq_acc += f.ssq;
   };
+  constexpr int NRD = MF * (LO ? 2 : 1) + NF + (SW ? 1 : 0);  // LDS reads of a stage
+  constexpr int NMF = MF * NF * (LO ? 2 : 1);                 // matrix ops of a stage
 
   // ---- pipeline: NS - 1 stages requested ahead (past the end: the last
   // stage again, into its own slot; never computed)
 #pragma unroll
   for (int j = 0; j < NS - 1; ++j) issue(min(j, nk - 1), j);
-  for (int kt = 0; kt < nk; ++kt) {
-    wait_vm<(NS - 2) * PL>();  // this wave's loads of stage kt are in LDS
-    raw_barrier();             // ... every wave's, and every wave is done with stage kt - 1
-    issue(min(kt + NS - 1, nk - 1), (kt + NS - 1) % NS);
-    compute(kt % NS);
+  if constexpr (DB) {
+    // Two register sets: each step reads the next stage's fragments and then
+    // runs the current stage's matrix ops, so the reads fly under them.  A
+    // slot is refilled once every wave's reads of it are done (lgkmcnt(0)
+    // before the barrier), one stage later than when the reads sit in the
+    // step that uses them; the ring keeps NS - 1 stages in flight.  Every
+    // step has the same loads, waits and reads (the last one reads a slot it
+    // never uses): a step without them would make the compiler wait for all
+    // reads in flight before the next step's matrix ops.
+    Frags f0, f1;
+    wait_vm<(NS - 2) * PL>();  // stage 0 is in LDS (every wave's, after the barrier)
+    raw_barrier();
+    issue(min(NS - 1, nk - 1), NS - 1);
+    read(0, f0);
+    auto step = [&](int kt, const Frags& cur, Frags& nxt) {
+      wait_vm<(NS - 2) * PL>();  // this wave's loads of stage kt + 1 are in LDS
+      wait_lgkm0();              // this wave's reads of stage kt are in registers
+      raw_barrier();             // ... every wave's: stage kt's slot is free
+      issue(min(kt + NS, nk - 1), kt % NS);
+      read((kt + 1) % NS, nxt);
+      __builtin_amdgcn_sched_group_barrier(0x100, NRD, 0);  // the next stage's reads go out first
+      mma(cur);
+      __builtin_amdgcn_sched_group_barrier(0x008, NMF, 0);
+    };
+    for (int kt = 0; kt < nk; kt += 2) {
+      step(kt, f0, f1);
+      if (kt + 1 < nk) step(kt + 1, f1, f0);
+    }
+  } else {
+    for (int kt = 0; kt < nk; ++kt) {
+      wait_vm<(NS - 2) * PL>();  // this wave's loads of stage kt are in LDS
+      raw_barrier();             // ... every wave's, and every wave is done with stage kt - 1
+      issue(min(kt + NS - 1, nk - 1), (kt + NS - 1) % NS);
+      Frags f;
+      read(kt % NS, f);
+      // every fragment read of the stage goes out before the matrix work
+      // (measured: 2-8% faster products than reads interleaved with it)
+      __builtin_amdgcn_sched_group_barrier(0x100, NRD, 0);
+      mma(f);
+      __builtin_amdgcn_sched_group_barrier(0x008, NMF, 0);
+      if constexpr (SW) asm volatile("" : "+v"(ssq_acc));  // read and added before the next barrier releases the slot
+    }
   }
   wait_vm<0>();  // no load may still write this workgroup's LDS
   raw_barrier();
