@@ -175,7 +175,7 @@ bool plan_gemm(int storage, int src, int out, bool lo, int M, int N, int K, Gemm
       KS = KS6;
     }
   }
-  // 256-row blocks with bf16 operands stream their stages through LDS-DMA
+  // 192- and 256-row blocks with bf16 operands stream their stages through LDS-DMA
   const bool dma = dma_ok && MF >= 3;
   const int units = nbn * KS;
   l->kind = dma ? GEMM_DMA : GEMM_MT;
@@ -194,8 +194,9 @@ bool plan_gemm(int storage, int src, int out, bool lo, int M, int N, int K, Gemm
 }
 
 // Whether the draft block's activations of M rows feed LDS-DMA products, and
-// so are stored in fragment blocks by the finish that writes them (the test
-// plan_gemm makes for GEMM_DMA: bf16 storage and 256-row blocks, M > 128).
+// so are stored in fragment blocks by the kernel that writes them (the test
+// plan_gemm makes for GEMM_DMA: bf16 storage and 192- or 256-row blocks,
+// M > 128).
 bool act_blocked(int storage, int M) { return kUseDmaGemm && storage == ST_BF16 && M > 128; }
 
 // gate/up of M rows (K = hidden, F = ffn, plain bf16 input) with the SiLU

@@ -524,12 +524,13 @@ __global__ void __launch_bounds__(512) gemm_mt_kernel(const GemmArgs g) {
 // a 1 KB block whose lane l holds row 16g + (l & 15), columns 8(l >> 4) .. + 7
 // of the k-step: copied as it is from activations stored in fragment blocks
 // (a_blocked; eight whole 128-byte lines per load), else gathered from
-// row-major rows (sixteen 64-byte pieces per load).  A fragment is then one ds_read_b128 at
-// 16*lane of its block (contiguous across the wave: no bank conflicts, no
+// row-major rows (sixteen 64-byte pieces per load).  A fragment is then one
+// ds_read_b128 at 16*lane of its block (contiguous across the wave: no bank conflicts, no
 // padding), no stage passes through registers, and NS stages are in flight
 // (NS - 1 ahead of the one being computed).  Each wave issues the same
 // number of block loads for every stage (spare loads repeat the stage's last
-// block into its own place), so the wait for a stage is vmcnt((NS-2) * PW).
+// block into its own place), so the wait for a stage is vmcnt((NS-2) * PL),
+// PL the loads per wave and stage.
 // MF row fragments per wave (4 waves along M): 256-row blocks at MF = 4,
 // 192-row blocks at MF = 3.
 template <int MF, int NF, bool LO>
