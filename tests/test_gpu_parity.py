@@ -5,6 +5,8 @@ the launch configuration the benchmark times and compare the sequences the
 oracle computes one by one (bars in tests/gpu_cases.py).
 """
 
+from dataclasses import replace
+
 import pytest
 import torch
 
@@ -107,6 +109,16 @@ def test_full_size_silu_epilogue_with_a_partial_row_block():
     # 16 rows; the row scales come from the sums of squares inside that kernel
     wl = gen.WORKLOADS["qwen3-8b-shape-b32-ragged"].with_batch(17)
     run_step(wl, seed=30, seqs=[0, 16], poison=True, min_sure=0.25)
+    torch.cuda.empty_cache()
+
+
+def test_full_size_block8_odd_rows_on_every_dma_path():
+    # 35 sequences x block 8 = 280 draft rows at the Qwen3-8B shape: gate/up
+    # with the SiLU epilogue over two 256-row blocks (24 rows in the second),
+    # the other products on 192-row blocks, and the normalised residual in
+    # fragment blocks whose last 16-row group holds 8 rows
+    wl = replace(gen.WORKLOADS["qwen3-8b-shape-b32-ragged"], name="qwen3-8b-shape-b35-block8", block=8, batch=35)
+    run_step(wl, seed=31, seqs=[0, 34], poison=True, min_sure=0.25)
     torch.cuda.empty_cache()
 
 
