@@ -243,7 +243,7 @@ size_t partial_floats(int storage, int src, bool lo, int Mmax, int N, int K) {
 struct WsLayout {
   size_t err, stats;
   size_t x, ssq, rinv, y, xs_hi, xs_lo, q_hi, q_lo, kb, vb, o_hi, o_lo, act_hi, act_lo, part, lm_best, ver_best,
-      part_o, part_ml, rope;
+      part_o, part_ml, seg, rope;
   // tiled bf16 copies of the projection matrices, one per product
   size_t wt_fc, wt_kv, wt_lm, wt_qkv[kMaxSeg / 2], wt_o[kMaxSeg / 2], wt_gu[kMaxSeg / 2], wt_down[kMaxSeg / 2];
   size_t total;
@@ -298,6 +298,7 @@ WsLayout layout(const dflash_config& c) {
   L.ver_best = take((size_t)c.max_batch * (kMaxNd + 1) * L.ver_chunks * 8);
   L.part_o = take(attn_slots * QR * D * 4);
   L.part_ml = take(attn_slots * QR * 2 * 4);
+  L.seg = take((size_t)c.max_batch * c.n_kv_heads * 8);
   // RoPE positions reach max_ctx + rows per sequence - 1 (block rows, or fused rows)
   L.rope_rows = c.max_ctx + std::max(c.block, c.max_fuse_rows);
   L.rope = take((size_t)L.rope_rows * (D / 2) * 8);
@@ -833,6 +834,7 @@ dflash_status dflash_draft_block(dflash_ctx* c, int32_t batch, const int32_t* bl
       a.p_lo = mlp_lo;
       a.part_o = c->at<float>(L.part_o);
       a.part_ml = c->at<float>(L.part_ml);
+      a.seg_info = c->at<int2>(L.seg);
       a.out_hi = c->at<void>(L.o_hi);
       a.out_lo = c->at<void>(L.o_lo);
       a.batch = batch;

@@ -194,6 +194,28 @@ __device__ __forceinline__ int flat_key_of(int w, const int* pre, int B, int Hkv
   return Hkv * pre[lo] + j * L + k;
 }
 
+// (first workgroup, pieces) of segment (b, h) under the plan in LDS: the
+// workgroups of nwg whose ranges hold its keys, whose slots the merge reads.
+__device__ __forceinline__ int2 segment_pieces(const int* pre, const int* wpre, int mode, int B, int Hkv, int nwg, int b,
+                                               int h) {
+  if (mode != 0) {
+    const int np = (wpre[b + 1] - wpre[b]) / Hkv;
+    return make_int2(wpre[b] + h * np, np);
+  }
+  const int Q = range_keys(flat_weight(pre, B, Hkv), nwg);
+  const int seg_len = pre[b + 1] - pre[b];
+  const int wk = flat_weight(pre, b, Hkv) + h * (seg_len + kPieceCost) + kPieceCost;  // its first key
+  const int w0 = wk / Q;
+  return make_int2(w0, (wk + seg_len - 1) / Q - w0 + 1);
+}
+// Workgroup 0 of a planned attention launch writes every segment's pieces
+// for the merge (which then reads one entry instead of building the plan).
+__device__ __forceinline__ void write_segment_pieces(const AttnArgs& a, const int* pre, const int* wpre, int mode) {
+  if (blockIdx.x != 0) return;
+  for (int s = threadIdx.x; s < a.batch * a.Hkv; s += blockDim.x)
+    a.seg_info[s] = segment_pieces(pre, wpre, mode, a.batch, a.Hkv, gridDim.x, s / a.Hkv, s % a.Hkv);
+}
+
 // Largest b in [0, B) with key(b) <= x, for key nondecreasing over [0, B].
 template <typename F>
 __device__ __forceinline__ int upper_index(int B, int x, F key) {
@@ -466,6 +488,7 @@ __global__ void __launch_bounds__(kThreads) attention_kernel(const AttnArgs a) {
   } else {
     if (wave == 0) build_plan(a.ctx_len, a.batch, Bs, Hkv, a.max_ctx, gridDim.x, pre, wpre, mode, lane);
     __syncthreads();
+    write_segment_pieces(a, pre, wpre, *mode);
     if (!planned_first_piece(a, pre, wpre, *mode, p, g1)) return;
   }
   int c0 = p.pstart;  // first key of the current stage, in segment coordinates
@@ -1000,6 +1023,7 @@ __global__ void __launch_bounds__(W * 64) attention_ring_kernel(const AttnArgs a
   } else {
     if (wave == 0) build_plan(a.ctx_len, a.batch, Bs, Hkv, a.max_ctx, gridDim.x, pre, wpre, mode, lane);
     __syncthreads();
+    write_segment_pieces(a, pre, wpre, *mode);
     if (!planned_first_piece(a, pre, wpre, *mode, p, g1)) return;
     q_issue(p);  // the queries go out before the stages
     // the first NS - 1 stages of the range (once the range is done, its last
@@ -1280,9 +1304,8 @@ __global__ void __launch_bounds__(W * 64) attention_ring_kernel(const AttnArgs a
 // fixed butterfly (deterministic).  grid: (item chunks, B * Hkv), 256 threads.
 template <int D>
 __global__ void __launch_bounds__(256) attention_combine_kernel(const AttnArgs a) {
-  __shared__ int pre[kAttnMaxBatch + 1], wpre[kAttnMaxBatch + 1], mode;
   const int s = blockIdx.y, b = s / a.Hkv, h = s - b * a.Hkv;
-  const int tid = threadIdx.x, lane = tid & 63;
+  const int tid = threadIdx.x;
   // this segment's pieces: workgroups w0 .. w0 + np - 1 (slots w + s); loads
   // go out for np_load pieces (fixed chunks: every chunk, before the context
   // length is known; the ones past the segment end are dropped after)
@@ -1294,19 +1317,9 @@ __global__ void __launch_bounds__(256) attention_combine_kernel(const AttnArgs a
     const int seg_len = min(min(max(craw, 0), a.max_ctx) + a.Bs, a.max_ctx);
     np = (seg_len + a.fixed_chunk - 1) / a.fixed_chunk;
   } else {
-    if (tid < 64) build_plan(a.ctx_len, a.batch, a.Bs, a.Hkv, a.max_ctx, a.nwg, pre, wpre, &mode, lane);
-    __syncthreads();
-    if (mode) {
-      np = (wpre[b + 1] - wpre[b]) / a.Hkv;
-      w0 = wpre[b] + h * np;
-    } else {
-      // the workgroups whose weighted ranges hold a key of this segment
-      const int Q = range_keys(flat_weight(pre, a.batch, a.Hkv), a.nwg);
-      const int seg_len = pre[b + 1] - pre[b];
-      const int wk = flat_weight(pre, b, a.Hkv) + h * (seg_len + kPieceCost) + kPieceCost;  // its first key
-      w0 = wk / Q;
-      np = (wk + seg_len - 1) / Q - w0 + 1;
-    }
+    const int2 si = a.seg_info[s];  // written by the attention launch from its plan
+    w0 = si.x;
+    np = si.y;
     np_load = np;
     if (np <= 1) return;  // written directly by the attention kernel
   }
@@ -1485,6 +1498,7 @@ static hipError_t launch_attention_s(const AttnArgs& a, hipStream_t stream) {
 }
 
 hipError_t launch_attention(int storage, const AttnArgs& a, hipStream_t stream) {
+  if (a.fixed_chunk <= 0 && a.seg_info == nullptr) return hipErrorInvalidValue;  // the merge reads the plan there
   if (a.kv_int8) return launch_attention_s<int8_t>(a, stream);
   if (storage == ST_BF16) return launch_attention_s<bf16_t>(a, stream);
   return launch_attention_s<float>(a, stream);

@@ -168,6 +168,7 @@ struct AttnArgs {
   int p_lo;          // probabilities as a hi/lo pair in the PV product (else plain bf16)
   float* part_o;   // [nwg + B*Hkv slots, QR, D]   unnormalised piece outputs
   float* part_ml;  // [nwg + B*Hkv slots, QR, 2]   piece running max and sum
+  int2* seg_info;  // [B*Hkv] planned launches: (first workgroup, pieces) of each segment, for the merge
   void* out_hi;    // bf16 hi/lo pair [B*Bs, Hq*D]
   void* out_lo;
   int batch;
