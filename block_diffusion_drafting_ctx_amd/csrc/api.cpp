@@ -140,10 +140,12 @@ bool plan_gemm(int storage, int src, int out, bool lo, int M, int N, int K, Gemm
     // 64- and 128-row blocks stream weights (one workgroup per compute unit,
     // each streaming its block's weights at a bounded per-unit rate): pick the
     // block width and k-split that minimise the busiest unit's bytes --
-    // dispatch rounds x (the block's weight bytes + a ramp worth ~96 KB) +
-    // its share of the split-K partials (written, then read by the finish).
-    // (Counting the activation rows a block re-reads as well made the LM head
-    // at 64 rows 17% slower: it then preferred fewer, wider blocks.)
+    // dispatch rounds x (the block's weight bytes + a ramp worth ~96 KB + a
+    // quarter of the activation bytes it re-reads, mostly L2 hits) + its share
+    // of the split-K partials (written, then read by the finish).  (The
+    // activation term: 32k-context batch-4 fusion product 75 -> 55 us, 27B
+    // batch-8 Q/K/V 58 -> 54.5 us; counted at full weight it made the LM
+    // head at 64 rows 17-20% slower, preferring fewer, wider blocks.)
     double best = 0;
     for (int nf : {2, 4, 6, 8}) {
       if (nf == 8 && MF == 2) continue;  // its two 64-deep stages would not fit the LDS
@@ -153,7 +155,8 @@ bool plan_gemm(int storage, int src, int out, bool lo, int M, int N, int K, Gemm
         if ((K / 128) % ks || K / ks < 256) continue;
         const double wgs = (double)bn * nbm * ks;
         const double rounds = std::ceil(wgs / kCUs);
-        const double cost = rounds * (32.0 * nf * (double)(K / ks) * 2.0 + 96e3) +
+        const double act = 64.0 * MF * (double)(K / ks) * 2.0 * (lo_eff ? 2 : 1);
+        const double cost = rounds * (32.0 * nf * (double)(K / ks) * 2.0 + 96e3 + 0.25 * act) +
                             (ks > 1 ? 8.0 * ks * (double)M * N / kCUs : 0.0);
         if (best == 0 || cost < best) {
           best = cost;
