@@ -30,7 +30,7 @@ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 constexpr int kMaxNd = 64;
 constexpr int kVerifyChunk = 8192;  // vocab entries per workgroup of the verify argmax (8 loads per thread)
-constexpr int kMlpHiOnlyRows = 128;  // draft rows from which the MLP products take plain bf16 inputs
+constexpr int kMlpHiOnlyRows = 128;  // draft rows from which the Q/K/V and MLP products take plain bf16 inputs
 constexpr bool kUseDmaGemm = true;
 constexpr int kMtTargetWgs = kCUs;   // gemm_mt workgroups to aim for (one per compute unit)
 // Attention workgroups: the batch's key axis is cut into this many ranges,
@@ -268,9 +268,9 @@ WsLayout layout(const dflash_config& c) {
   size_t parts = 0;
   parts = std::max(parts, partial_floats(st, SRC_CONCAT, false, L.mf, c.hidden, c.hidden * c.n_target_layers));
   parts = std::max(parts, partial_floats(st, SRC_SPLIT, false, L.mf, 2 * c.n_layers * Nk, c.hidden));
-  parts = std::max(parts, partial_floats(st, SRC_SPLIT, true, L.md, Nq + 2 * Nk, c.hidden));
   parts = std::max(parts, partial_floats(st, SRC_SPLIT, true, L.md, c.hidden, Nq));
-  for (bool lo : {true, false}) {  // the MLP products take hi/lo or plain activations
+  for (bool lo : {true, false}) {  // the Q/K/V and MLP products take hi/lo or plain activations
+    parts = std::max(parts, partial_floats(st, SRC_SPLIT, lo, L.md, Nq + 2 * Nk, c.hidden));
     parts = std::max(parts, partial_floats(st, SRC_SPLIT, lo, L.md, 2 * c.ffn, c.hidden));
     parts = std::max(parts, partial_floats(st, SRC_SPLIT, lo, L.md, c.hidden, c.ffn));
   }
@@ -770,11 +770,12 @@ dflash_status dflash_draft_block(dflash_ctx* c, int32_t batch, const int32_t* bl
     a.rinv_out = rinv;
     f.rinv = rinv;
   };
-  // The MLP inputs (normalised residual into gate/up, SiLU product into down)
-  // and the attention probabilities enter their products as a hi/lo pair
-  // while the products stream weights or wait on memory (the pair costs no
-  // HBM bytes there); from kMlpHiOnlyRows rows on, where the products are
-  // matrix-core bound, they enter as plain bf16.
+  // The Q/K/V and MLP inputs (normalised residual into Q/K/V and gate/up,
+  // SiLU product into down) and the attention probabilities enter their
+  // products as a hi/lo pair while the products stream weights or wait on
+  // memory (the pair costs no HBM bytes there); from kMlpHiOnlyRows rows on,
+  // where the products are matrix-core bound, they enter as plain bf16.  The
+  // queries and the O product's input keep the pair at every size.
   const bool mlp_lo = M < kMlpHiOnlyRows;
   // The embedding and the row-tile finishes store the normalised residual for
   // the next Q/K/V, gate/up or LM-head product in fragment blocks when that
@@ -793,12 +794,12 @@ dflash_status dflash_draft_block(dflash_ctx* c, int32_t batch, const int32_t* bl
       GemmLaunch gl{};
       a.wt = c->at<void>(L.wt_qkv[l]);
       a.a_hi = xs_hi;
-      a.a_lo = xs_lo;
+      a.a_lo = mlp_lo ? xs_lo : nullptr;
       a.lda = H;
       a.a_blocked = blk;
       FinishArgs f{};
       norm(a, f);
-      if ((st = layer_gemm(a, true, Nq + 2 * Nk, H, &gl))) return st;
+      if ((st = layer_gemm(a, mlp_lo, Nq + 2 * Nk, H, &gl))) return st;
       f.rope = c->at<float2>(L.rope);
       f.max_ctx = cf.max_ctx;
       f.block = cf.block;
@@ -905,7 +906,7 @@ dflash_status dflash_draft_block(dflash_ctx* c, int32_t batch, const int32_t* bl
       f.block = cf.block;
       f.gnext = l + 1 < cf.n_layers ? c->g_in[l + 1] : c->g_final;
       f.out_hi = xs_hi;
-      f.out_lo = xs_lo;
+      f.out_lo = mlp_lo ? xs_lo : nullptr;
       f.out_blocked = blk;
       f.ssq_out = ssq;
       f.ld_ssq = L.mmax;
