@@ -364,8 +364,8 @@ hipError_t launch_verify_sample(const VerifyArgs& a, hipStream_t stream) {
 
 // ---------------------------------------------------------------- embedding
 // x[m] = E[ids[m]] as fp32, the hi/lo pair of x * gain (the first layer's
-// RMSNorm gain; row-major or in fragment blocks) and the row's sum of squares
-// (one partial per row).
+// RMSNorm gain; row-major or in fragment blocks; a null xs_lo: hi only) and
+// the row's sum of squares (one partial per row).
 template <typename S>
 __global__ void __launch_bounds__(256) embed_kernel(const S* embed, const S* gain, const int32_t* ids, int H, int V,
                                                     float* x, bf16_t* xs_hi, bf16_t* xs_lo, int blocked, float* ssq,
@@ -398,7 +398,7 @@ __global__ void __launch_bounds__(256) embed_kernel(const S* embed, const S* gai
     // the 8 columns k .. k+7 are one 16-byte piece in either layout
     const size_t idx = blocked ? frag_block_index(m, k, H) : (size_t)m * H + k;
     *reinterpret_cast<u32x4*>(xs_hi + idx) = u32x4{hw[0], hw[1], hw[2], hw[3]};
-    *reinterpret_cast<u32x4*>(xs_lo + idx) = u32x4{lw[0], lw[1], lw[2], lw[3]};
+    if (xs_lo != nullptr) *reinterpret_cast<u32x4*>(xs_lo + idx) = u32x4{lw[0], lw[1], lw[2], lw[3]};
     f32x4* dst = reinterpret_cast<f32x4*>(x + (size_t)m * H + k);
     dst[0] = f32x4{f[0], f[1], f[2], f[3]};
     dst[1] = f32x4{f[4], f[5], f[6], f[7]};
