@@ -756,11 +756,11 @@ dflash_status dflash_draft_block(dflash_ctx* c, int32_t batch, const int32_t* bl
     // (the lo half only where the first Q/K/V product takes the pair)
     st = hip_status(launch_embed(c->storage(), c->embed, c->g_in[0], block_ids, M, H, cf.vocab, x, xs_hi,
                                  c->storage() == ST_F32 ? xs_lo : nullptr, act_blocked(c->storage(), M), ssq,
-                                 c->at<uint32_t>(L.err), s),
+                                 L.mmax, c->at<uint32_t>(L.err), s),
                     "embed launch");
     if (st) return st;
   }
-  int ssq_parts = 1;
+  int ssq_parts = H / 128;  // the embedding's partial sums of squares per row
   float* rinv = c->at<float>(L.rinv);
   // RMSNorm of the product's activation rows: its main kernel turns the
   // partial sums of squares into row scales for the finish kernel

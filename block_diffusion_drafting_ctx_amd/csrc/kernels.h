@@ -211,9 +211,11 @@ hipError_t static_verify_scratch(uint64_t** ptr);
 // a.chunk must be 4 * 256 * 8 (one 16-byte load round per thread).
 hipError_t launch_verify_sample(const VerifyArgs& a, hipStream_t stream);
 
-// blocked: xs_hi / xs_lo in fragment blocks (frag_block_index, H % 32 == 0), else row-major; xs_lo may be null (hi only).
+// blocked: xs_hi / xs_lo in fragment blocks (frag_block_index), else
+// row-major; xs_lo may be null (hi only).  ssq receives H/128 partial sums of
+// squares per row ([slice][ld_ssq]).  H % 128 == 0.
 hipError_t launch_embed(int storage, const void* embed, const void* gain, const int32_t* ids, int M, int H, int V,
-                        float* x, void* xs_hi, void* xs_lo, bool blocked, float* ssq, uint32_t* err,
+                        float* x, void* xs_hi, void* xs_lo, bool blocked, float* ssq, int ld_ssq, uint32_t* err,
                         hipStream_t stream);
 hipError_t launch_commit(int32_t* ctx_len, int batch, int t_new, int max_ctx, hipStream_t stream);
 // table[p][i] = (cos, sin)(p * theta^(-2i/D)), evaluated in double precision.

@@ -365,60 +365,62 @@ hipError_t launch_verify_sample(const VerifyArgs& a, hipStream_t stream) {
 // ---------------------------------------------------------------- embedding
 // x[m] = E[ids[m]] as fp32, the hi/lo pair of x * gain (the first layer's
 // RMSNorm gain; row-major or in fragment blocks; a null xs_lo: hi only) and
-// the row's sum of squares (one partial per row).
+// the row's sums of squares, one partial per 128-column slice
+// (ssq[slice * ld_ssq + m]).  grid: (16-row groups, H/128 slices); thread t
+// takes row t / 16 of the group and columns 8 (t % 16) .. + 7 of the slice,
+// so a workgroup writes whole 16 x 32 fragment blocks.
 template <typename S>
-__global__ void __launch_bounds__(256) embed_kernel(const S* embed, const S* gain, const int32_t* ids, int H, int V,
-                                                    float* x, bf16_t* xs_hi, bf16_t* xs_lo, int blocked, float* ssq,
-                                                    uint32_t* err) {
-  __shared__ float s_part[4];
-  const int m = blockIdx.x, tid = threadIdx.x;
-  const int id = ids[m];
+__global__ void __launch_bounds__(256) embed_kernel(const S* embed, const S* gain, const int32_t* ids, int M, int H,
+                                                    int V, float* x, bf16_t* xs_hi, bf16_t* xs_lo, int blocked,
+                                                    float* ssq, int ld_ssq, uint32_t* err) {
+  const int tid = threadIdx.x, m = 16 * blockIdx.x + (tid >> 4), k = 128 * blockIdx.y + 8 * (tid & 15);
+  const bool live = m < M;
+  const int id = live ? ids[m] : 0;
   const bool ok = id >= 0 && id < V;
-  if (!ok && tid == 0) atomicOr(err, kErrTokenRange);
-  const S* e = embed + (size_t)(ok ? id : 0) * H;
+  if (live && !ok && blockIdx.y == 0 && (tid & 15) == 0) atomicOr(err, kErrTokenRange);
+  Raw8 raw, graw;
+  load_raw8<S>(raw, embed + (size_t)(ok ? id : 0) * H + k);
+  load_raw8<S>(graw, gain + k);
+  float f[8], gf[8];
+  raw_to_f32x8<S>(raw, f);
+  raw_to_f32x8<S>(graw, gf);
+  uint32_t hw[4], lw[4];
   float s = 0.f;
-  for (int k = 8 * tid; k < H; k += 8 * 256) {
-    Raw8 raw, graw;
-    load_raw8<S>(raw, e + k);
-    load_raw8<S>(graw, gain + k);
-    float f[8], gf[8];
-    raw_to_f32x8<S>(raw, f);
-    raw_to_f32x8<S>(graw, gf);
-    uint32_t hw[4], lw[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      f[i] = ok ? f[i] : 0.f;
-      s += f[i] * f[i];
-      const float v = f[i] * gf[i];
-      const uint32_t hbits = f32_to_bf16_bits(v);
-      const uint32_t lbits = f32_to_bf16_bits(v - bf16_bits_to_f32(hbits));
-      hw[i >> 1] = (i & 1) ? hw[i >> 1] | hbits << 16 : hbits;
-      lw[i >> 1] = (i & 1) ? lw[i >> 1] | lbits << 16 : lbits;
-    }
-    // the 8 columns k .. k+7 are one 16-byte piece in either layout
-    const size_t idx = blocked ? frag_block_index(m, k, H) : (size_t)m * H + k;
-    *reinterpret_cast<u32x4*>(xs_hi + idx) = u32x4{hw[0], hw[1], hw[2], hw[3]};
-    if (xs_lo != nullptr) *reinterpret_cast<u32x4*>(xs_lo + idx) = u32x4{lw[0], lw[1], lw[2], lw[3]};
-    f32x4* dst = reinterpret_cast<f32x4*>(x + (size_t)m * H + k);
-    dst[0] = f32x4{f[0], f[1], f[2], f[3]};
-    dst[1] = f32x4{f[4], f[5], f[6], f[7]};
+  for (int i = 0; i < 8; ++i) {
+    f[i] = ok ? f[i] : 0.f;
+    s += f[i] * f[i];
+    const float v = f[i] * gf[i];
+    const uint32_t hbits = f32_to_bf16_bits(v);
+    const uint32_t lbits = f32_to_bf16_bits(v - bf16_bits_to_f32(hbits));
+    hw[i >> 1] = (i & 1) ? hw[i >> 1] | hbits << 16 : hbits;
+    lw[i >> 1] = (i & 1) ? lw[i >> 1] | lbits << 16 : lbits;
   }
-  s = wave_sum_f32(s);
-  if ((tid & 63) == 0) s_part[tid >> 6] = s;
-  __syncthreads();
-  if (tid == 0) ssq[m] = s_part[0] + s_part[1] + s_part[2] + s_part[3];
+  // the row's 16 lanes (a 16-lane group of one wave)
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) s += __shfl_xor(s, o);
+  if (!live) return;
+  // the 8 columns k .. k+7 are one 16-byte piece in either layout
+  const size_t idx = blocked ? frag_block_index(m, k, H) : (size_t)m * H + k;
+  *reinterpret_cast<u32x4*>(xs_hi + idx) = u32x4{hw[0], hw[1], hw[2], hw[3]};
+  if (xs_lo != nullptr) *reinterpret_cast<u32x4*>(xs_lo + idx) = u32x4{lw[0], lw[1], lw[2], lw[3]};
+  f32x4* dst = reinterpret_cast<f32x4*>(x + (size_t)m * H + k);
+  dst[0] = f32x4{f[0], f[1], f[2], f[3]};
+  dst[1] = f32x4{f[4], f[5], f[6], f[7]};
+  if ((tid & 15) == 0) ssq[(size_t)blockIdx.y * ld_ssq + m] = s;
 }
 
 hipError_t launch_embed(int storage, const void* embed, const void* gain, const int32_t* ids, int M, int H, int V,
-                        float* x, void* xs_hi, void* xs_lo, bool blocked, float* ssq, uint32_t* err,
+                        float* x, void* xs_hi, void* xs_lo, bool blocked, float* ssq, int ld_ssq, uint32_t* err,
                         hipStream_t stream) {
-  if (H % 8 || (blocked && H % 32)) return hipErrorInvalidValue;
+  if (H % 128 || M < 1 || ld_ssq < M) return hipErrorInvalidValue;
+  const dim3 grid((M + 15) / 16, H / 128);
   if (storage == ST_BF16)
-    hipLaunchKernelGGL(embed_kernel<bf16_t>, dim3(M), dim3(256), 0, stream, (const bf16_t*)embed,
-                       (const bf16_t*)gain, ids, H, V, x, (bf16_t*)xs_hi, (bf16_t*)xs_lo, (int)blocked, ssq, err);
+    hipLaunchKernelGGL(embed_kernel<bf16_t>, grid, dim3(256), 0, stream, (const bf16_t*)embed, (const bf16_t*)gain,
+                       ids, M, H, V, x, (bf16_t*)xs_hi, (bf16_t*)xs_lo, (int)blocked, ssq, ld_ssq, err);
   else
-    hipLaunchKernelGGL(embed_kernel<float>, dim3(M), dim3(256), 0, stream, (const float*)embed,
-                       (const float*)gain, ids, H, V, x, (bf16_t*)xs_hi, (bf16_t*)xs_lo, (int)blocked, ssq, err);
+    hipLaunchKernelGGL(embed_kernel<float>, grid, dim3(256), 0, stream, (const float*)embed, (const float*)gain, ids,
+                       M, H, V, x, (bf16_t*)xs_hi, (bf16_t*)xs_lo, (int)blocked, ssq, ld_ssq, err);
   return hipGetLastError();
 }
 
