@@ -29,11 +29,14 @@
  *    storage type chosen by dflash_config.dtype (float or bfloat16) for
  *    weights, gains, the KV cache and the target hidden states.  All matrix
  *    products run on the bf16 matrix cores with fp32 accumulation (fp32
- *    weights are rounded to bf16 on load).  Activations that feed the
- *    residual stream, the attention queries and the attention probabilities
- *    enter the products as a pair of bf16 values (value = hi + lo, two
- *    products each); the context K/V projection and the LM head take the hi
- *    part only.  The residual stream and the softmax stay fp32.
+ *    weights are rounded to bf16 on load).  The attention queries and the
+ *    attention output entering the O projection are a pair of bf16 values
+ *    (value = hi + lo, two products each); so are the MLP inputs and the
+ *    attention probabilities below 128 draft rows (batch * block), and the
+ *    Q/K/V input with fp32 storage.  The other inputs (the Q/K/V input with
+ *    bf16 storage, the MLP inputs and probabilities from 128 rows on, the
+ *    context K/V projection and the LM head) take plain bf16.  The residual
+ *    stream and the softmax stay fp32.
  *  - Errors the host can see (null pointer, bad size, unsupported shape)
  *    return DFLASH_EINVAL / DFLASH_EUNSUPPORTED before anything is enqueued;
  *    dflash_last_error() then holds a message.  HIP launch failures return
