@@ -352,10 +352,17 @@ __global__ void __launch_bounds__(kThreads) attention_kernel(const AttnArgs a) {
   constexpr int KPT = KITEMS / kThreads;
   constexpr int VPT = (VITEMS + kThreads - 1) / kThreads;
   static_assert(KITEMS % kThreads == 0 && VITEMS % 64 == 0, "stage items must fill whole waves");
+  // 8-bit cache: the D/32 run scales of one key row (one load per thread:
+  // K rows of the stage's keys, then V rows; threads past 2 kStage repeat a
+  // row so that every thread has the same loads in flight)
+  using RunScales = float __attribute__((ext_vector_type(D / 32)));
   struct StageRegs {
     Raw8 k[KPT], v[VPT][2];
-    float ks[I8 ? KPT : 1], vs[I8 ? VPT : 1][2];  // run scales of an 8-bit cache
+    RunScales sc;
   };
+  const int sc_item = tid % (2 * kStage);
+  const bool sc_v = sc_item >= kStage;
+  const int sc_key = sc_v ? sc_item - kStage : sc_item;
   auto v_item = [&](int idx, int& kp, int& pc) {
     pc = idx % PIECES;
     const int h = (idx / PIECES) & 1, rest = idx / (2 * PIECES);
@@ -377,7 +384,10 @@ __global__ void __launch_bounds__(kThreads) attention_kernel(const AttnArgs a) {
       const int key = idx / PIECES, p8 = (idx % PIECES) * 8;
       const int off = min(key, lim) * (int)row + p8;
       load_raw8<S>(R.k[i], kq + off);
-      if constexpr (I8) R.ks[i] = a.ks[(base + off) >> 5];
+    }
+    if constexpr (I8) {
+      const float* sb = sc_v ? a.vs : a.ks;
+      R.sc = *reinterpret_cast<const RunScales*>(sb + ((base + (size_t)min(sc_key, lim) * row) >> 5));
     }
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
@@ -389,7 +399,6 @@ __global__ void __launch_bounds__(kThreads) attention_kernel(const AttnArgs a) {
       for (int t = 0; t < 2; ++t) {
         const int off = min(2 * kp + t, lim) * (int)row + 8 * pc;
         load_raw8<S>(R.v[i][t], vq + off);
-        if constexpr (I8) R.vs[i][t] = a.vs[(base + off) >> 5];
       }
     }
   };
@@ -401,6 +410,14 @@ __global__ void __launch_bounds__(kThreads) attention_kernel(const AttnArgs a) {
     asm volatile("" : "+v"(t0));
     const int nvalid = q.pend - c;  // keys of the stage inside the piece
     const bool full = nvalid >= kStage;
+    if constexpr (I8) {  // run scales [run][key]; a key past the piece gets 0
+      if (tid < 2 * kStage) {
+        float* dst = sc_v ? L.vsc : L.ksc;
+        const bool ok = full || sc_key < nvalid;
+#pragma unroll
+        for (int rn = 0; rn < D / 32; ++rn) dst[rn * Lds::RS + sc_key] = ok ? R.sc[rn] : 0.f;
+      }
+    }
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
       const int idx = tid + i * kThreads;
@@ -411,7 +428,6 @@ __global__ void __launch_bounds__(kThreads) attention_kernel(const AttnArgs a) {
         raw_to_f32x8<S>(R.k[i], f);
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[e] = (__bf16)f[e];
-        if (p8 % 32 == 0) L.ksc[(p8 / 32) * Lds::RS + key] = full || key < nvalid ? R.ks[i] : 0.f;
       } else {
         v = raw_to_bf16x8<S>(R.k[i]);
       }
@@ -439,12 +455,6 @@ __global__ void __launch_bounds__(kThreads) attention_kernel(const AttnArgs a) {
         float v0[8], v1[8];
         raw_to_f32x8<S>(R.v[i][0], v0);
         raw_to_f32x8<S>(R.v[i][1], v1);
-        if constexpr (I8) {
-          if (pc % 4 == 0) {
-            L.vsc[(pc / 4) * Lds::RS + 2 * kp] = ok0 ? R.vs[i][0] : 0.f;
-            L.vsc[(pc / 4) * Lds::RS + 2 * kp + 1] = ok1 ? R.vs[i][1] : 0.f;
-          }
-        }
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int d = 8 * pc + e;
