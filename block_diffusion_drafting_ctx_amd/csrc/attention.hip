@@ -423,15 +423,20 @@ __global__ void __launch_bounds__(kThreads) attention_kernel(const AttnArgs a) {
       const int idx = tid + i * kThreads;
       const int key = idx / PIECES, p8 = (idx % PIECES) * 8;
       bf16x8 v;
-      if constexpr (I8) {  // the integers (exact in bf16); the run's scale beside them
+      if constexpr (I8) {
+        // the integers, exact in bf16: the high half of each one's fp32 bits.
+        // A key past the piece keeps its (finite) integers: its run scale is
+        // 0 and its score is masked.
         float f[8];
         raw_to_f32x8<S>(R.k[i], f);
+        u32x4 w;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = (__bf16)f[e];
+        for (int j = 0; j < 4; ++j) w[j] = __builtin_amdgcn_perm(__float_as_uint(f[2 * j + 1]), __float_as_uint(f[2 * j]), 0x07060302u);
+        v = __builtin_bit_cast(bf16x8, w);
       } else {
         v = raw_to_bf16x8<S>(R.k[i]);
+        if (!full && key >= nvalid) v = bf16x8{};
       }
-      if (!full && key >= nvalid) v = bf16x8{};
       *reinterpret_cast<bf16x8*>(&L.k[key * Lds::KS + p8]) = v;
     }
 #pragma unroll
@@ -450,6 +455,17 @@ __global__ void __launch_bounds__(kThreads) attention_kernel(const AttnArgs a) {
           const int d = 8 * pc + 2 * j;
           L.vt[d * Lds::VW + vt_col(d, kp)] = __builtin_amdgcn_perm(k1[j], k0[j], 0x05040100u);
           L.vt[(d + 1) * Lds::VW + vt_col(d + 1, kp)] = __builtin_amdgcn_perm(k1[j], k0[j], 0x07060302u);
+        }
+      } else if constexpr (I8) {
+        // integers as above; a key past the piece has probability 0 and run
+        // scale 0, and its integers are finite
+        float v0[8], v1[8];
+        raw_to_f32x8<S>(R.v[i][0], v0);
+        raw_to_f32x8<S>(R.v[i][1], v1);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int d = 8 * pc + e;
+          L.vt[d * Lds::VW + vt_col(d, kp)] = __builtin_amdgcn_perm(__float_as_uint(v1[e]), __float_as_uint(v0[e]), 0x07060302u);
         }
       } else {
         float v0[8], v1[8];
@@ -582,16 +598,25 @@ __global__ void __launch_bounds__(kThreads) attention_kernel(const AttnArgs a) {
       const int kp0 = (kUnit / 2) * u + 2 * (ln >> 4);  // keys 32*u + 4*(lane>>4) + [0, 4)
       // the probabilities (times the keys' run scales, 8-bit cache) as the B operand
       auto p_operand = [&](const f32x4& s0, const f32x4& s1, bf16x8& ph, bf16x8& pl) {
+        float p[8];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float p0 = sc[uu][0][e] * s0[e], p1 = sc[uu][1][e] * s1[e];
-          ph[e] = (__bf16)p0;
-          ph[4 + e] = (__bf16)p1;
+          p[e] = sc[uu][0][e] * s0[e];
+          p[4 + e] = sc[uu][1][e] * s1[e];
+        }
+        uint32_t hb[4], lb[4];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
           if constexpr (PLO) {
-            pl[e] = (__bf16)(p0 - (float)ph[e]);
-            pl[4 + e] = (__bf16)(p1 - (float)ph[4 + e]);
+            split_bf16x2(p[2 * w], p[2 * w + 1], hb[w], lb[w]);
+          } else {
+            typedef float f32x2_t __attribute__((ext_vector_type(2)));
+            typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+            hb[w] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{p[2 * w], p[2 * w + 1]}, bf16x2_t));
           }
         }
+        ph = __builtin_bit_cast(bf16x8, u32x4{hb[0], hb[1], hb[2], hb[3]});
+        if constexpr (PLO) pl = __builtin_bit_cast(bf16x8, u32x4{lb[0], lb[1], lb[2], lb[3]});
       };
       auto pv_slice = [&](int ds, const bf16x8& ph, const bf16x8& pl) {
         const int d = 16 * ds + (ln & 15);
