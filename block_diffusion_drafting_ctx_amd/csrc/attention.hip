@@ -342,16 +342,28 @@ __global__ void __launch_bounds__(kThreads) attention_kernel(const AttnArgs a) {
   const S* kc = reinterpret_cast<const S*>(a.kc);
   const S* vc = reinterpret_cast<const S*>(a.vc);
   const size_t row = (size_t)Hkv * D;  // elements between consecutive keys
-  // ---- staging through registers.  K: (key, 8-dim piece) items, 16 lanes per
-  // key row.  V: (key pair, piece) items in blocks of 32 key pairs; the two
-  // half-blocks of 16 take key pairs 16 apart (the bank pattern the V^T
-  // swizzle is built for).
-  constexpr int PIECES = D / 8;
+  // ---- staging through registers.  K: (key, piece) items, a piece being 8
+  // dims (16 for the 8-bit cache, one 16-byte load either way).  V: (key
+  // pair, piece) items in blocks of 32 key pairs; the two half-blocks of 16
+  // take key pairs 16 apart (the bank pattern the V^T swizzle is built for).
+  constexpr int PW = I8 && (kStage * D / 16) % kThreads == 0 ? 16 : 8;  // dims per piece
+  constexpr int PIECES = D / PW;
   constexpr int KITEMS = kStage * PIECES;
   constexpr int VITEMS = (kStage / 2) * PIECES;
   constexpr int KPT = KITEMS / kThreads;
   constexpr int VPT = (VITEMS + kThreads - 1) / kThreads;
   static_assert(KITEMS % kThreads == 0 && VITEMS % 64 == 0, "stage items must fill whole waves");
+  // 8-bit cache: PW integers per load (in Raw8::lo), to fp32 exactly
+  auto load_piece = [&](Raw8& r, const S* src) {
+    if constexpr (I8 && PW == 16) r.lo = *reinterpret_cast<const u32x4*>(src);
+    else load_raw8<S>(r, src);
+  };
+  auto i8_to_f32 = [](const Raw8& r, float (&f)[PW]) {
+#pragma unroll
+    for (int w = 0; w < PW / 4; ++w)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) f[4 * w + i] = (float)((int32_t)(r.lo[w] << (24 - 8 * i)) >> 24);
+  };
   // 8-bit cache: the D/32 run scales of one key row (one load per thread:
   // K rows of the stage's keys, then V rows; threads past 2 kStage repeat a
   // row so that every thread has the same loads in flight)
@@ -381,9 +393,9 @@ __global__ void __launch_bounds__(kThreads) attention_kernel(const AttnArgs a) {
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
       const int idx = tid + i * kThreads;
-      const int key = idx / PIECES, p8 = (idx % PIECES) * 8;
+      const int key = idx / PIECES, p8 = (idx % PIECES) * PW;
       const int off = min(key, lim) * (int)row + p8;
-      load_raw8<S>(R.k[i], kq + off);
+      load_piece(R.k[i], kq + off);
     }
     if constexpr (I8) {
       const float* sb = sc_v ? a.vs : a.ks;
@@ -397,8 +409,8 @@ __global__ void __launch_bounds__(kThreads) attention_kernel(const AttnArgs a) {
       v_item(idx, kp, pc);
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
-        const int off = min(2 * kp + t, lim) * (int)row + 8 * pc;
-        load_raw8<S>(R.v[i][t], vq + off);
+        const int off = min(2 * kp + t, lim) * (int)row + PW * pc;
+        load_piece(R.v[i][t], vq + off);
       }
     }
   };
@@ -421,23 +433,24 @@ __global__ void __launch_bounds__(kThreads) attention_kernel(const AttnArgs a) {
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
       const int idx = tid + i * kThreads;
-      const int key = idx / PIECES, p8 = (idx % PIECES) * 8;
-      bf16x8 v;
+      const int key = idx / PIECES, p8 = (idx % PIECES) * PW;
       if constexpr (I8) {
         // the integers, exact in bf16: the high half of each one's fp32 bits.
         // A key past the piece keeps its (finite) integers: its run scale is
         // 0 and its score is masked.
-        float f[8];
-        raw_to_f32x8<S>(R.k[i], f);
-        u32x4 w;
+        float f[PW];
+        i8_to_f32(R.k[i], f);
+        u32x4 w[PW / 8];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) w[j] = __builtin_amdgcn_perm(__float_as_uint(f[2 * j + 1]), __float_as_uint(f[2 * j]), 0x07060302u);
-        v = __builtin_bit_cast(bf16x8, w);
+        for (int j = 0; j < PW / 2; ++j)
+          w[j >> 2][j & 3] = __builtin_amdgcn_perm(__float_as_uint(f[2 * j + 1]), __float_as_uint(f[2 * j]), 0x07060302u);
+#pragma unroll
+        for (int j = 0; j < PW / 8; ++j) *reinterpret_cast<u32x4*>(&L.k[key * Lds::KS + p8 + 8 * j]) = w[j];
       } else {
-        v = raw_to_bf16x8<S>(R.k[i]);
+        bf16x8 v = raw_to_bf16x8<S>(R.k[i]);
         if (!full && key >= nvalid) v = bf16x8{};
+        *reinterpret_cast<bf16x8*>(&L.k[key * Lds::KS + p8]) = v;
       }
-      *reinterpret_cast<bf16x8*>(&L.k[key * Lds::KS + p8]) = v;
     }
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
@@ -459,12 +472,12 @@ __global__ void __launch_bounds__(kThreads) attention_kernel(const AttnArgs a) {
       } else if constexpr (I8) {
         // integers as above; a key past the piece has probability 0 and run
         // scale 0, and its integers are finite
-        float v0[8], v1[8];
-        raw_to_f32x8<S>(R.v[i][0], v0);
-        raw_to_f32x8<S>(R.v[i][1], v1);
+        float v0[PW], v1[PW];
+        i8_to_f32(R.v[i][0], v0);
+        i8_to_f32(R.v[i][1], v1);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int d = 8 * pc + e;
+        for (int e = 0; e < PW; ++e) {
+          const int d = PW * pc + e;
           L.vt[d * Lds::VW + vt_col(d, kp)] = __builtin_amdgcn_perm(__float_as_uint(v1[e]), __float_as_uint(v0[e]), 0x07060302u);
         }
       } else {
