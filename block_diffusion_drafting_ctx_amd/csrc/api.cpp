@@ -147,8 +147,12 @@ bool plan_gemm(int storage, int src, int out, bool lo, int M, int N, int K, Gemm
     // batch-8 Q/K/V 58 -> 54.5 us; counted at full weight it made the LM
     // head at 64 rows 17-20% slower, preferring fewer, wider blocks.)
     double best = 0;
-    for (int nf : {2, 4, 6, 8}) {
+    // (160-column blocks at 128 rows: the 27B-shaped gate/up fills 218
+    // compute units instead of 182, 116 -> 112 us; not for the LM head, where
+    // the cost model's pick of them was slower, 328 -> 356 us)
+    for (int nf : {2, 4, 5, 6, 8}) {
       if (nf == 8 && MF == 2) continue;  // its two 64-deep stages would not fit the LDS
+      if (nf == 5 && (MF != 2 || out == OUT_ARGMAX)) continue;
       const int bn = (N + 32 * nf - 1) / (32 * nf);
       for (int ks = 1; ks <= 32; ++ks) {
         if (ks > 1 && out != OUT_PARTIAL) break;

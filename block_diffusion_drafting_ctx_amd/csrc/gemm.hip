@@ -1450,6 +1450,7 @@ static hipError_t dispatch_mr(const GemmArgs& a, const GemmLaunch& l, hipStream_
       switch (l.NF) {
         case 2: return launch_mt<S, 2, 2, SRC, LO, OUT>(a, l, st);
         case 4: return launch_mt<S, 2, 4, SRC, LO, OUT>(a, l, st);
+        case 5: return launch_mt<S, 2, 5, SRC, LO, OUT>(a, l, st);
         case 6: return launch_mt<S, 2, 6, SRC, LO, OUT>(a, l, st);
       }
       return hipErrorInvalidValue;
