@@ -182,8 +182,12 @@ bool plan_gemm(int storage, int src, int out, bool lo, int M, int N, int K, Gemm
       KS = KS6;
     }
   }
-  // 192- and 256-row blocks with bf16 operands stream their stages through LDS-DMA
-  const bool dma = dma_ok && MF >= 3;
+  // 192- and 256-row blocks with bf16 operands stream their stages through
+  // LDS-DMA, and so does the fusion at 64 and 128 rows (its activation rows
+  // gathered from the target's hidden states by LDS-DMA: 32k-context batch-4
+  // fusion 55 -> 44 us; the 64- and 128-row layer products and LM heads were
+  // 5-30% slower on that kernel than on gemm_mt, also with deeper rings)
+  const bool dma = dma_ok && (MF >= 3 || src == SRC_CONCAT);
   const int units = nbn * KS;
   l->kind = dma ? GEMM_DMA : GEMM_MT;
   l->MR = MF;

@@ -532,7 +532,7 @@ __global__ void __launch_bounds__(512) gemm_mt_kernel(const GemmArgs g) {
 // block into its own place), so the wait for a stage is vmcnt((NS-2) * PL),
 // PL the loads per wave and stage.
 // MF row fragments per wave (4 waves along M): 256-row blocks at MF = 4,
-// 192-row blocks at MF = 3.
+// 192-row blocks at MF = 3, 64- and 128-row blocks (MF = 1, 2) for the fusion.
 template <int MF, int NF, bool LO>
 struct DmaShape {
   static constexpr int BM = 64 * MF, NT = 2 * NF, NA = LO ? 2 : 1;
@@ -1424,6 +1424,25 @@ static hipError_t dispatch_mr(const GemmArgs& a, const GemmLaunch& l, hipStream_
         if (l.NF == 8) return launch_dma<4, 8, SRC, LO, OUT>(a, l, st);
         if constexpr (OUT == OUT_PARTIAL)
           if (l.NF == 6) return launch_dma<4, 6, SRC, LO, OUT>(a, l, st);
+      } else if (l.MR <= 2) {
+        // (the fusion at 64 and 128 rows)
+        if constexpr (SRC == SRC_CONCAT && OUT == OUT_PARTIAL) {
+          if (l.MR == 1) {
+            switch (l.NF) {
+              case 2: return launch_dma<1, 2, SRC, LO, OUT>(a, l, st);
+              case 4: return launch_dma<1, 4, SRC, LO, OUT>(a, l, st);
+              case 6: return launch_dma<1, 6, SRC, LO, OUT>(a, l, st);
+              case 8: return launch_dma<1, 8, SRC, LO, OUT>(a, l, st);
+            }
+          } else {
+            switch (l.NF) {
+              case 2: return launch_dma<2, 2, SRC, LO, OUT>(a, l, st);
+              case 4: return launch_dma<2, 4, SRC, LO, OUT>(a, l, st);
+              case 5: return launch_dma<2, 5, SRC, LO, OUT>(a, l, st);
+              case 6: return launch_dma<2, 6, SRC, LO, OUT>(a, l, st);
+            }
+          }
+        }
       } else if (l.MR == 3) {
         if (l.NF == 8) return launch_dma<3, 8, SRC, LO, OUT>(a, l, st);
         if constexpr (OUT == OUT_PARTIAL)
