@@ -129,6 +129,16 @@ bool plan_gemm(int storage, int src, int out, bool lo, int M, int N, int K, Gemm
     int KS = 1;
     if (out == OUT_PARTIAL)
       while (nbn * nbm * 2 * KS <= kMtTargetWgs && (K / 32) % (4 * KS) == 0 && K / (2 * KS) >= 256) KS *= 2;
+    // then the largest split that still fits the round, where there are
+    // several row blocks (matrix-core bound: the 544-row fusion goes from 192
+    // to 240 workgroups, 137 -> 121 us; at one row block, weight streaming,
+    // the extra partials cancelled the gain)
+    if (out == OUT_PARTIAL && nbm >= 2)
+      for (int k2 = kMtTargetWgs / (nbn * nbm); k2 > KS; --k2)
+        if ((K / 32) % (2 * k2) == 0 && K / k2 >= 256) {
+          KS = k2;
+          break;
+        }
     return KS;
   };
   // share of the compute units the grid keeps busy over its dispatch rounds
